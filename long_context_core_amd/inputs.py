@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs: document-length mixes, CA-task tables and bf16
+tensors.
+
+This module holds no attention arithmetic.  It only draws lengths, lays out
+task descriptors and draws N(0, 1) tensors, so that the HIP library and the
+fp64 oracle are fed bit-identical inputs.  The public datasets the pages train
+on (ProLong, the Pile, LongAlign ...) are not available; the mixes below are
+synthetic stand-ins with the shapes the pages describe.
+
+Task-table columns (int64): q_off, kv_off, o_off, q_len, kv_len, q_pos0,
+kv_pos0 — key j of a task is visible to its query i iff
+kv_pos0 + j <= q_pos0 + i.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+TASK_COLUMNS = ("q_off", "kv_off", "o_off", "q_len", "kv_len", "q_pos0", "kv_pos0")
+
+
+@dataclass
+class Workload:
+    """One attention call: head geometry, task table and buffer row counts."""
+
+    name: str
+    hq: int
+    hkv: int
+    d: int
+    tasks: np.ndarray            # (n, 7) int64
+    q_rows: int
+    kv_rows: int
+    o_rows: int
+    n_parts: int = 1             # > 1: o_rows = n_parts * merged rows (partials)
+    doc_lens: list = field(default_factory=list)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def merged_rows(self) -> int:
+        return self.o_rows // self.n_parts
+
+
+# --------------------------------------------------------------------------
+# task tables
+# --------------------------------------------------------------------------
+
+def varlen_tasks(doc_lens):
+    """One causal task per packed document: {cu[i], cu[i], cu[i], l, l, 0, 0}."""
+    t = []
+    off = 0
+    for l in doc_lens:
+        t.append((off, off, off, l, l, 0, 0))
+        off += l
+    return np.array(t, dtype=np.int64).reshape(-1, 7)
+
+
+def lognormal_doc_lens(rng, total, median=2048, sigma=1.5, lo=16, hi=65536):
+    """ln l ~ N(ln median, sigma^2), rounded, clipped to [lo, hi], drawn until
+    ``total`` tokens are filled; the last document is truncated."""
+    lens = []
+    left = total
+    while left > 0:
+        l = int(round(math.exp(rng.normal(math.log(median), sigma))))
+        l = min(max(l, lo), hi, left)
+        lens.append(l)
+        left -= l
+    return lens
+
+
+# --------------------------------------------------------------------------
+# the workloads
+# --------------------------------------------------------------------------
+
+def tiny_forward():
+    """1,024 packed tokens, docs [512, 256, 128, 128]; 4 query heads over one
+    KV head, d = 64."""
+    lens = [512, 256, 128, 128]
+    return Workload("tiny-1k-docs-512-256-128-128", 4, 1, 64, varlen_tasks(lens),
+                    1024, 1024, 1024, doc_lens=lens)
+
+
+def llama8b_packed_131k(seed=102, total=131072):
+    """Llama-3-8B attention shape (32 query heads, 8 KV heads, d = 128) over
+    one packed chunk of ``total`` tokens with a long-tailed lognormal length
+    mix (median ~2K, at most 64K)."""
+    rng = np.random.default_rng(seed)
+    lens = lognormal_doc_lens(rng, total)
+    return Workload("llama3-8b-packed-%dk-lognormal" % (total // 1024), 32, 8, 128,
+                    varlen_tasks(lens), total, total, total, doc_lens=lens)
+
+
+def ca_tasks_34b(seed=103, n_tasks=64, total_q=262144, q_min=512, q_max=8192,
+                 doc_min=16384, doc_max=524288):
+    """Re-batched CA-tasks, LLaMA-34B attention shape (64 query heads, 8 KV
+    heads, d = 128).  Each task is a query shard cut at a random offset of its
+    own document (length log-uniform in [doc_min, doc_max]); its context is
+    the document prefix up to the shard end.  Shard lengths are uniform in
+    [q_min, q_max], then adjusted so that they total ``total_q`` exactly.
+    Every task carries its own copy of its context, as an attention server
+    receives one per task."""
+    rng = np.random.default_rng(seed)
+    docs = [int(round(math.exp(rng.uniform(math.log(doc_min), math.log(doc_max)))))
+            for _ in range(n_tasks)]
+    q = rng.integers(q_min, q_max + 1, size=n_tasks).astype(np.int64)
+    q = np.clip(np.floor(q * (total_q / q.sum())).astype(np.int64), q_min, q_max)
+    i = 0
+    while q.sum() != total_q:                     # deterministic fix-up
+        step = 1 if q.sum() < total_q else -1
+        if q_min <= q[i] + step <= q_max:
+            q[i] += step
+        i = (i + 1) % n_tasks
+    ends = [int(rng.integers(int(q[k]), docs[k] + 1)) for k in range(n_tasks)]
+    t = []
+    qo = ko = 0
+    for k in range(n_tasks):
+        ql, end = int(q[k]), ends[k]
+        t.append((qo, ko, qo, ql, end, end - ql, 0))
+        qo += ql
+        ko += end
+    return Workload("llama-34b-ca-tasks-64x-262k", 64, 8, 128, np.array(t, dtype=np.int64),
+                    qo, ko, qo, doc_lens=docs)
+
+
+def ring_prefill_405b_tp8(total=131072, n=8):
+    """One GPU's share of Llama3-405B under TP8 (16 query heads, 1 KV head,
+    d = 128): one causal document of ``total`` tokens split into n contiguous
+    query shards and n contiguous KV blocks.  Task (i, j <= i) is shard i over
+    block j and writes partial slot j: output rows o_off = j * total + i * S.
+    Slots j > i are never written (they are fully masked); their LSE must hold
+    -inf before the merge."""
+    S = total // n
+    t = []
+    for i in range(n):
+        for j in range(i + 1):
+            t.append((i * S, j * S, j * total + i * S, S, S, i * S, j * S))
+    return Workload("llama3-405b-tp8-ring-prefill-%dk-%dx%d" % (total // 1024, n, n), 16, 1, 128,
+                    np.array(t, dtype=np.int64), total, total, n * total, n_parts=n,
+                    doc_lens=[total])
+
+
+def ring_decode_405b_tp8(batch=32, context=131072, n=8):
+    """Pass-Q decode share: ``batch`` single-token queries (16 heads), each over
+    its own ``context``-entry KV cache (1 KV head, d = 128), the cache split
+    into n stationary blocks.  Task (b, s) writes partial slot s, row b."""
+    S = context // n
+    t = []
+    for b in range(batch):
+        for s in range(n):
+            t.append((b, b * context + s * S, s * batch + b, 1, S, context - 1, s * S))
+    return Workload("llama3-405b-tp8-decode-b%d-%dk" % (batch, context // 1024), 16, 1, 128,
+                    np.array(t, dtype=np.int64), batch, batch * context, n * batch, n_parts=n)
+
+
+def prolong_like_doc_lens(rng, total, long_lo, long_hi):
+    """Half of the tokens in long documents (length log-uniform in
+    [long_lo, long_hi], drawn until less than long_lo of that half remains),
+    the rest in lognormal short documents; order shuffled."""
+    long_budget = total // 2
+    left = long_budget
+    longs = []
+    while left >= long_lo:
+        l = int(round(math.exp(rng.uniform(math.log(long_lo), math.log(long_hi)))))
+        l = min(l, left)
+        longs.append(l)
+        left -= l
+    shorts = lognormal_doc_lens(rng, total - long_budget + left)
+    lens = longs + shorts
+    order = rng.permutation(len(lens))
+    return [lens[k] for k in order]
+
+
+def train_8b_prolong_512k(seed=105, total=524288, div=1):
+    """Training shape, Llama-3-8B attention (32 / 8 heads, d = 128): one packed
+    chunk of ``total // div`` tokens with a ProLong-like mix (50 % of tokens
+    in docs of 64K-512K, scaled by 1/div, the rest lognormal short docs)."""
+    rng = np.random.default_rng(seed)
+    tot = total // div
+    lens = prolong_like_doc_lens(rng, tot, 65536 // div, 524288 // div)
+    return Workload("llama3-8b-train-prolong-like-%dk" % (tot // 1024), 32, 8, 128,
+                    varlen_tasks(lens), tot, tot, tot, doc_lens=lens)
+
+
+# --------------------------------------------------------------------------
+# tensors
+# --------------------------------------------------------------------------
+
+def randn_bf16(shape, seed, device="cpu"):
+    """N(0, 1) float32 from a seeded torch generator, rounded to bfloat16
+    (round to nearest even)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def bf16_round_bits(x):
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even, with
+    numpy integer operations only (NaN kept quiet)."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    out = np.where(nan, (u >> 16) | 0x40, rounded)
+    return out.astype(np.uint16)
+
+
+def randn_bf16_bits(shape, seed):
+    """numpy-only variant: N(0, 1) float32 from PCG64, bfloat16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    return bf16_round_bits(rng.standard_normal(shape, dtype=np.float32))

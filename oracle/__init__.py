@@ -1,0 +1,33 @@
+"""fp64 CPU oracle for core attention — TEST INFRASTRUCTURE ONLY.
+
+This package is the checker, not the product.  Only the test suite, the
+``smoke()`` self-check and the benchmark's ``cpu_baseline`` leg may import it.
+It shares no code with the HIP library: it depends on numpy alone and imports
+nothing from ``long_context_core_amd``.
+
+Modules
+-------
+attention  forward / merge / backward / decode written as the plain definition
+           of softmax(scale * Q K^T + mask) V, in float64.
+counting   unmasked (query, key) pair counts and the FLOP convention.
+
+Parity status of every function is stated in its own docstring; all of them
+are pinned by ``tests/test_oracle_pins.py`` except where a docstring says
+"parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    TASK_FIELDS,
+    bf16_bits_to_f64,
+    visible_mask,
+    forward,
+    forward_rows,
+    merge,
+    backward,
+)
+from .counting import (  # noqa: F401
+    visible_pairs_task,
+    visible_pairs,
+    forward_flops,
+    backward_flops,
+)

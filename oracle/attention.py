@@ -1,0 +1,257 @@
+"""Plain float64 core attention on the CPU — the oracle (test infrastructure).
+
+Only the test suite, ``smoke()`` and the benchmark's ``cpu_baseline`` leg may
+use this module.  It imports numpy only and shares no code with the HIP path.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+* Core attention is the parameter-free softmax(Q K^T) V that sits between the
+  QKV and output projections (Efficient Long-context Language Model Training
+  by Core Attention Disaggregation, Sections 1 and 3.2).
+* A CA-task is a query shard q(t) plus its context kv(t): the keys and values
+  of every token from the document start up to and including the last query
+  token (same page, Section 3.4, "The CA-Task Abstraction").  The causal mask
+  lets the query at document position p see keys at positions 0..p, itself
+  included (Context Parallelism for Scalable Million-Token Inference,
+  Section 3.4, "Load-Balanced Sharding").
+* Packed documents never attend across a document boundary (Core Attention
+  Disaggregation, Section 2 on document packing).
+* Scores are scaled by 1/sqrt(d) before the exponential, and the per-query
+  log-sum-exp LSE_s = log sum_i exp(q . k_i / sqrt(d)) together with the
+  normalised output O_s is what each partial attention returns; partials
+  combine by Equation 4 (Context Parallelism ..., Section 3.4 "Merge
+  Attention" and Appendix B).
+* Grouped-query attention: query head h reads KV head floor(h * Hkv / Hq),
+  i.e. contiguous groups of Hq/Hkv query heads share one KV head
+  (Context Parallelism ..., "The CP+TP Nesting Design": GPU i holds KV head
+  i with query heads 16i..16i+15).
+
+Task table
+----------
+An ``(n, 7)`` int64 array, one row per CA-task, columns ``TASK_FIELDS``:
+
+  q_off   first row of the task's queries in Q (and dQ)
+  kv_off  first row of its context in K and V (and dK, dV)
+  o_off   first row of its outputs in O and LSE (and of O, dO in backward)
+  q_len   number of query rows
+  kv_len  number of context rows
+  q_pos0  document position of the first query
+  kv_pos0 document position of the first context row
+
+Key j of a task is visible to its query i  iff  kv_pos0 + j <= q_pos0 + i.
+A row with no visible key has O = 0 and LSE = -inf (a reading: the pages do
+not discuss empty rows; this is the value that gives the row zero weight in
+Equation 4).
+
+Tensors are float64: Q [Tq, Hq, d], K and V [Tk, Hkv, d], O [To, Hq, d],
+LSE [To, Hq].  bf16 inputs are widened exactly by ``bf16_bits_to_f64``.
+"""
+
+import numpy as np
+
+TASK_FIELDS = ("q_off", "kv_off", "o_off", "q_len", "kv_len", "q_pos0", "kv_pos0")
+
+# Row-chunk budget for materialised score blocks (elements of float64).
+_CHUNK_ELEMS = 1 << 24
+
+
+def bf16_bits_to_f64(bits):
+    """Exact widening of bfloat16 bit patterns (uint16 / int16) to float64.
+
+    A bfloat16 value is the upper half of the float32 with the same bits.
+    Pinned by test (against torch's own bfloat16 -> float32 conversion).
+    """
+    b = np.ascontiguousarray(np.asarray(bits)).view(np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _as_tasks(tasks):
+    t = np.asarray(tasks, dtype=np.int64)
+    if t.ndim == 1:
+        t = t.reshape(1, -1)
+    if t.shape[1] != len(TASK_FIELDS):
+        raise ValueError("task table must have columns %s" % (TASK_FIELDS,))
+    return t
+
+
+def _group_of(h, hq, hkv):
+    """KV head read by query head h: contiguous groups of hq // hkv."""
+    return (h * hkv) // hq
+
+
+def visible_mask(task, rows, n_keys):
+    """Boolean [len(rows), n_keys]: key j visible to task row i.
+
+    The definition of the causal CA-task mask: document position of key j is
+    kv_pos0 + j, of query i is q_pos0 + i; a key is visible iff its position
+    does not exceed the query's (diagonal included).
+    """
+    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task)
+    qpos = q_pos0 + np.asarray(rows, dtype=np.int64)
+    kpos = kv_pos0 + np.arange(n_keys, dtype=np.int64)
+    return kpos[None, :] <= qpos[:, None]
+
+
+def _context_len(task, rows):
+    """How many leading context rows any of ``rows`` can see (keys past this
+    are invisible to every row in the set)."""
+    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task)
+    if len(rows) == 0:
+        return 0
+    last = q_pos0 + int(np.max(rows)) - kv_pos0 + 1
+    return max(0, min(kv_len, last))
+
+
+def _row_chunks(task, rows):
+    n = max(1, _context_len(task, rows))
+    step = max(1, _CHUNK_ELEMS // n)
+    for s in range(0, len(rows), step):
+        yield rows[s:s + step]
+
+
+def _head_rows(task, rows, h, Q, K, V, scale, hq, hkv):
+    """Softmax attention of one query head over one task, for selected rows.
+
+    Returns (O [r, d], LSE [r], P [r, n], n) where P is the full materialised
+    probability block over the first n context keys (the rest are masked for
+    every selected row).  The plain definition: s = scale * q.k over visible
+    keys, m = max s, w = exp(s - m), l = sum w, O = sum w v / l,
+    LSE = m + ln l.  No online rescaling, no blocking of the key axis.
+    """
+    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task)
+    g = _group_of(h, hq, hkv)
+    n = _context_len(task, rows)
+    d = Q.shape[2]
+    r = len(rows)
+    O = np.zeros((r, d))
+    LSE = np.full(r, -np.inf)
+    if n == 0 or r == 0:
+        return O, LSE, np.zeros((r, 0)), 0
+    q = Q[q_off + rows, h, :]                      # [r, d]
+    k = K[kv_off:kv_off + n, g, :]                 # [n, d]
+    v = V[kv_off:kv_off + n, g, :]                 # [n, d]
+    s = scale * (q @ k.T)                          # [r, n]
+    vis = visible_mask(task, rows, n)
+    s = np.where(vis, s, -np.inf)
+    has = vis.any(axis=1)
+    m = np.where(has, np.max(np.where(vis, s, -np.inf), axis=1), 0.0)
+    w = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    l = w.sum(axis=1)
+    safe_l = np.where(has, l, 1.0)
+    P = w / safe_l[:, None]
+    O = P @ v
+    LSE = np.where(has, m + np.log(safe_l), -np.inf)
+    return O, LSE, P, n
+
+
+def forward_rows(task, rows, Q, K, V, scale, hq=None, hkv=None):
+    """O [r, Hq, d] and LSE [r, Hq] for the given rows (task-relative indices)
+    of one CA-task.  Used directly for sampled checks at full size."""
+    task = _as_tasks(task)[0]
+    hq = Q.shape[1] if hq is None else hq
+    hkv = K.shape[1] if hkv is None else hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    d = Q.shape[2]
+    O = np.zeros((len(rows), hq, d))
+    LSE = np.full((len(rows), hq), -np.inf)
+    pos = 0
+    for chunk in _row_chunks(task, rows):
+        for h in range(hq):
+            o, lse, _, _ = _head_rows(task, chunk, h, Q, K, V, scale, hq, hkv)
+            O[pos:pos + len(chunk), h, :] = o
+            LSE[pos:pos + len(chunk), h] = lse
+        pos += len(chunk)
+    return O, LSE
+
+
+def forward(tasks, Q, K, V, scale, o_rows=None):
+    """Core attention over every task of the table.
+
+    Returns O [o_rows, Hq, d] and LSE [o_rows, Hq] in float64.  Output rows
+    that no task covers hold NaN so that a comparison cannot pass on them by
+    accident.
+    """
+    tasks = _as_tasks(tasks)
+    hq, d = Q.shape[1], Q.shape[2]
+    if o_rows is None:
+        o_rows = int(max([t[2] + t[3] for t in tasks] + [0]))
+    O = np.full((o_rows, hq, d), np.nan)
+    LSE = np.full((o_rows, hq), np.nan)
+    for t in tasks:
+        q_len = int(t[3])
+        o_off = int(t[2])
+        o, lse = forward_rows(t, np.arange(q_len), Q, K, V, scale)
+        O[o_off:o_off + q_len] = o
+        LSE[o_off:o_off + q_len] = lse
+    return O, LSE
+
+
+def merge(O_parts, LSE_parts):
+    """Merge attention, Equation 4 of Context Parallelism for Scalable
+    Million-Token Inference (Appendix B).
+
+    O_parts [S, T, H, d] and LSE_parts [S, T, H] are S partial results of the
+    same queries against disjoint key sets.  With M = max_s LSE_s:
+        O   = sum_s O_s exp(LSE_s - M) / sum_s exp(LSE_s - M)
+        LSE = M + ln sum_s exp(LSE_s - M)
+    The merged LSE is not printed on the page; it follows from the LSE
+    definition there (log of the full normaliser).  A partial with
+    LSE = -inf weighs zero; if every partial is empty, O = 0 and LSE = -inf.
+    """
+    O_parts = np.asarray(O_parts, dtype=np.float64)
+    LSE_parts = np.asarray(LSE_parts, dtype=np.float64)
+    M = np.max(LSE_parts, axis=0)                       # [T, H]
+    finite = np.isfinite(M)
+    Ms = np.where(finite, M, 0.0)
+    w = np.where(np.isfinite(LSE_parts), np.exp(LSE_parts - Ms[None]), 0.0)  # [S, T, H]
+    den = w.sum(axis=0)
+    num = np.einsum("sth,sthd->thd", w, np.where(np.isfinite(LSE_parts)[..., None], O_parts, 0.0))
+    safe = np.where(finite, den, 1.0)
+    O = np.where(finite[..., None], num / safe[..., None], 0.0)
+    LSE = np.where(finite, Ms + np.log(safe), -np.inf)
+    return O, LSE
+
+
+def backward(tasks, Q, K, V, dO, scale, dq_rows=None, dkv_rows=None):
+    """Gradients of L = sum(O * dO) with respect to Q, K and V.
+
+    The pages only say that the backward recomputes the attention
+    probabilities from the saved per-row statistics instead of storing them
+    (Core Attention Disaggregation, Sections 3.2 and 3.4).  The oracle takes
+    the plain gradient of the forward definition: with P the softmax
+    probabilities of a row, D_i = <dO_i, O_i>,
+        dV_j = sum_i P_ij dO_i,    dP_ij = <dO_i, V_j>,
+        dS_ij = P_ij (dP_ij - D_i),
+        dQ_i = scale sum_j dS_ij K_j,    dK_j = scale sum_i dS_ij Q_i,
+    with dK and dV summed over every query head of the KV head's group and
+    over every task that reads the same context rows.  O and P come from the
+    oracle's own float64 forward of the same rows.
+    """
+    tasks = _as_tasks(tasks)
+    hq, d = Q.shape[1], Q.shape[2]
+    hkv = K.shape[1]
+    dq_rows = Q.shape[0] if dq_rows is None else dq_rows
+    dkv_rows = K.shape[0] if dkv_rows is None else dkv_rows
+    dQ = np.zeros((dq_rows, hq, d))
+    dK = np.zeros((dkv_rows, hkv, d))
+    dV = np.zeros((dkv_rows, hkv, d))
+    for t in tasks:
+        q_off, kv_off, o_off, q_len = int(t[0]), int(t[1]), int(t[2]), int(t[3])
+        for chunk in _row_chunks(t, np.arange(q_len)):
+            for h in range(hq):
+                g = _group_of(h, hq, hkv)
+                o, _, P, n = _head_rows(t, chunk, h, Q, K, V, scale, hq, hkv)
+                if n == 0:
+                    continue
+                do = dO[o_off + chunk, h, :]           # [r, d]
+                k = K[kv_off:kv_off + n, g, :]
+                v = V[kv_off:kv_off + n, g, :]
+                q = Q[q_off + chunk, h, :]
+                D = np.sum(do * o, axis=1)             # [r]
+                dV[kv_off:kv_off + n, g, :] += P.T @ do
+                dP = do @ v.T                          # [r, n]
+                dS = P * (dP - D[:, None])
+                dQ[q_off + chunk, h, :] += scale * (dS @ k)
+                dK[kv_off:kv_off + n, g, :] += scale * (dS.T @ q)
+    return dQ, dK, dV

@@ -1,0 +1,57 @@
+"""50-digit brute-force attention with mpmath, for inputs of a few tokens.
+
+Independent of the oracle: it walks every (output row, head, key) triple of
+the whole K buffer, decides visibility from document positions it derives
+itself, and forms the softmax with arbitrary-precision exp/log.  Used only to
+pin the oracle (tests)."""
+
+import mpmath as mp
+
+mp.mp.dps = 50
+
+
+def _val(x):
+    if isinstance(x, mp.mpf):
+        return x
+    return mp.mpf(float(x))
+
+
+def attention(tasks, Q, K, V, scale):
+    """Returns dict {(o_row, h): (O list of mpf, LSE mpf)}."""
+    out = {}
+    hq, d = Q.shape[1], Q.shape[2]
+    hkv = K.shape[1]
+    group = hq // hkv
+    sc = mp.mpf(scale) if not isinstance(scale, mp.mpf) else scale
+    for t in tasks:
+        q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in t)
+        for i in range(q_len):
+            my_pos = q_pos0 + i
+            for h in range(hq):
+                g = h // group
+                keys = []
+                for j in range(kv_len):
+                    if kv_pos0 + j > my_pos:
+                        continue
+                    s = mp.mpf(0)
+                    for c in range(d):
+                        s += _val(Q[q_off + i, h, c]) * _val(K[kv_off + j, g, c])
+                    keys.append((j, s * sc))
+                if not keys:
+                    out[(o_off + i, h)] = ([mp.mpf(0)] * d, -mp.inf)
+                    continue
+                z = mp.fsum(mp.exp(s) for _, s in keys)
+                o = [mp.fsum(mp.exp(s) * _val(V[kv_off + j, g, c]) for j, s in keys) / z
+                     for c in range(d)]
+                out[(o_off + i, h)] = (o, mp.log(z))
+    return out
+
+
+def loss(tasks, Q, K, V, dO, scale):
+    """L = sum over covered rows of <O, dO>, in 50 digits."""
+    res = attention(tasks, Q, K, V, scale)
+    total = mp.mpf(0)
+    for (row, h), (o, _) in res.items():
+        for c, oc in enumerate(o):
+            total += oc * _val(dO[row, h, c])
+    return total
