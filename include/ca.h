@@ -1,0 +1,180 @@
+/*
+ * ca.h — core attention on one MI355X (gfx950): the C ABI of libca.so.
+ *
+ * Core attention is the parameter-free softmax(Q K^T / sqrt(d)) V between the
+ * QKV and output projections of a transformer layer ("Efficient Long-context
+ * Language Model Training by Core Attention Disaggregation", Sections 1 and
+ * 3.2).  The library computes it over a table of CA-tasks — a query shard
+ * plus its key/value context, re-batched across documents into one fused
+ * launch (same page, Section 3.4, "The CA-Task Abstraction" and Property 2,
+ * Composability) — and returns per-row log-sum-exp so that partial results
+ * merge exactly by Equation 4 ("Context Parallelism for Scalable Million-Token
+ * Inference", Section 3.4 "Merge Attention", Appendix B).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers named *_host are host memory; every other pointer is device
+ *    memory on the current HIP device.  The caller allocates and owns every
+ *    buffer, including the workspace; the library allocates no device memory
+ *    and keeps no state between calls other than a reusable pinned host
+ *    staging buffer per thread and device, through which host-built work
+ *    queues are copied into the workspace.
+ *  - Calls are asynchronous on `stream` (a hipStream_t, passed as void*; NULL
+ *    is the default stream).  Buffers must stay valid until the stream work
+ *    completes.  Host arrays (*_host) are only read during the call.
+ *  - Arguments are validated before anything is enqueued: a call that returns
+ *    an error has no side effects on device memory.  Errors are return codes;
+ *    nothing is thrown across the ABI.  ca_last_error() gives a message for
+ *    the last failing call on the calling thread.
+ *  - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *
+ * Data layout (row-major, head-interleaved, as a packed varlen batch)
+ * -------------------------------------------------------------------
+ *  Q  [q_rows ][hq ][d]  bf16        dQ  same layout, bf16
+ *  K  [kv_rows][hkv][d]  bf16        dK  same layout, bf16
+ *  V  [kv_rows][hkv][d]  bf16        dV  same layout, bf16
+ *  O  [o_rows ][hq ][d]  bf16, or fp32 when flags has CA_OUT_F32
+ *  LSE[o_rows ][hq]      fp32, natural log of sum_j exp(scale * q.k_j)
+ *
+ *  Grouped-query attention: query head h reads KV head (h * hkv) / hq, i.e.
+ *  contiguous groups of hq/hkv query heads share a KV head ("Context
+ *  Parallelism ...", The CP+TP Nesting Design, Figure 5).
+ */
+#ifndef CA_H
+#define CA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CA_OK = 0,
+  CA_ERR_INVALID = -1,     /* bad shape, task or pointer                     */
+  CA_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head dim)      */
+  CA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  CA_ERR_HIP = -4          /* a HIP runtime call failed; see ca_last_error() */
+} ca_status;
+
+/*
+ * One CA-task: a contiguous query shard q(t) and its context kv(t)
+ * ("Core Attention Disaggregation", Section 3.4).  Key j of the task is
+ * visible to its query i iff  kv_pos0 + j <= q_pos0 + i  (document
+ * positions; the diagonal is included — a token attends to itself).
+ *   - packed causal document of length l at row r:  {r, r, r, l, l, 0, 0}
+ *   - shard of n queries ending at document position e (context = prefix):
+ *         {q, kv, o, n, e, e - n, 0}
+ *   - ring partial of query shard [a, a+n) over key block [b, b+m):
+ *         {a, b, o, n, m, a, b}
+ *   - decode of one token at position p over a cache block [b, b+m):
+ *         {q, kv, o, 1, m, p, b}
+ * A row that sees no key gets O = 0 and LSE = -inf.
+ * Output row ranges [o_off, o_off + q_len) of different tasks must not
+ * overlap (documented, not checked).  Context ranges may overlap.
+ */
+typedef struct {
+  int64_t q_off;   /* first row in Q (and dQ)                              */
+  int64_t kv_off;  /* first row in K, V (and dK, dV)                       */
+  int64_t o_off;   /* first row in O, LSE (and O, dO, LSE in backward)     */
+  int32_t q_len;   /* >= 0                                                 */
+  int32_t kv_len;  /* >= 0                                                 */
+  int64_t q_pos0;  /* document position of query row 0                     */
+  int64_t kv_pos0; /* document position of context row 0                   */
+} ca_task;
+
+enum {
+  CA_OUT_F32 = 1u << 0 /* forward/merge: write O as fp32 (partials for a later merge) */
+};
+
+typedef struct {
+  int32_t hq;      /* query heads, >= 1                                    */
+  int32_t hkv;     /* key/value heads, >= 1, divides hq                    */
+  int32_t d;       /* head dimension: 64 or 128                            */
+  float scale;     /* softmax scale applied to q.k (usually 1/sqrt(d))     */
+  uint32_t flags;  /* CA_OUT_F32                                           */
+  int64_t q_rows;  /* rows of Q (and dQ)                                   */
+  int64_t kv_rows; /* rows of K, V (and dK, dV)                            */
+  int64_t o_rows;  /* rows of O and LSE (and dO)                           */
+} ca_shape;
+
+/* ---------------------------------------------------------------------- */
+/* Forward                                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace ca_forward needs for this task table (0 on an
+ * invalid argument; check ca_forward's status for the reason). */
+size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks);
+
+/* O and LSE for every row of every task, in one fused launch over all tasks
+ * (fully masked key tiles are never visited).  Rows of O/LSE outside every
+ * task are not written.  Errors: CA_ERR_INVALID for a null pointer, hq/hkv
+ * not dividing, scale not finite, negative lengths or any row range past
+ * q_rows/kv_rows/o_rows; CA_ERR_UNSUPPORTED for d not in {64, 128};
+ * CA_ERR_WORKSPACE when ws_bytes < ca_forward_workspace(...). */
+ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks,
+                     const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Packed causal documents: document i occupies rows [cu[i], cu[i+1]) of Q,
+ * K, V, O and LSE (the task {cu[i], cu[i], cu[i], l, l, 0, 0}).
+ * cu_seqlens_host has n_docs + 1 non-decreasing entries starting at 0. */
+size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu_seqlens_host,
+                                   int32_t n_docs);
+ca_status ca_forward_varlen(const ca_shape* shape, const int32_t* cu_seqlens_host, int32_t n_docs,
+                            const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Merge (Equation 4 of "Context Parallelism ...", Appendix B)             */
+/* ---------------------------------------------------------------------- */
+
+/* Combine n_parts partial results of the same n_rows query rows:
+ *   O_parts  [n_parts][n_rows][hq][d] fp32   LSE_parts [n_parts][n_rows][hq] fp32
+ *   O        [n_rows][hq][d] bf16 (fp32 with CA_OUT_F32)   LSE [n_rows][hq] fp32
+ * With M = max_s LSE_s:  O = sum_s O_s e^(LSE_s - M) / sum_s e^(LSE_s - M),
+ * LSE = M + ln sum_s e^(LSE_s - M).  A partial whose LSE is -inf weighs zero
+ * and its O values are not read (so rows a forward never wrote need only
+ * LSE = -inf); if all partials are empty, O = 0 and LSE = -inf.
+ * Uses shape->hq, shape->d, shape->flags only.  No workspace. */
+ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows,
+                   const float* O_parts, const float* LSE_parts, void* O, float* LSE,
+                   void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Backward                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace ca_backward needs (includes an fp32 dQ
+ * accumulator of q_rows * hq * d floats). */
+size_t ca_backward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks);
+
+/* Gradients of sum(O * dO): dQ, dK, dV (bf16, accumulated in fp32).  O, dO
+ * (bf16) and LSE (fp32) are the forward's outputs at rows o_off..; the
+ * attention probabilities are recomputed from Q, K and LSE.  dK and dV sum
+ * over the query heads of each KV head's group and over every task whose
+ * context covers a row.  Every row of dQ, dK and dV is written (rows that no
+ * task touches get 0).  Errors as for ca_forward (CA_OUT_F32 is rejected). */
+ca_status ca_backward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks,
+                      const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Accounting and errors                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Number of visible (query, key) pairs of a task table, per query head
+ * (FLOPs = 4 d pairs hq forward, 10 d pairs hq backward).  -1 on an invalid
+ * table. */
+int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks);
+
+const char* ca_status_string(ca_status status);
+const char* ca_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CA_H */

@@ -1,0 +1,205 @@
+"""Python binding of libca.so (ctypes): argument marshalling only.
+
+Every step of the attention path runs inside libca's HIP kernels; this module
+only turns torch tensors into device pointers, task tables into ``ca_task``
+arrays, and status codes into exceptions.  There is no fallback: if the
+library is not built, ``lib()`` raises.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libca.so")
+
+CA_OK = 0
+CA_ERR_INVALID = -1
+CA_ERR_UNSUPPORTED = -2
+CA_ERR_WORKSPACE = -3
+CA_ERR_HIP = -4
+CA_OUT_F32 = 1
+
+EXPORTS = (
+    "ca_forward_workspace",
+    "ca_forward",
+    "ca_forward_varlen_workspace",
+    "ca_forward_varlen",
+    "ca_merge",
+    "ca_backward_workspace",
+    "ca_backward",
+    "ca_visible_pairs",
+    "ca_status_string",
+    "ca_last_error",
+)
+
+# numpy view of the C struct ca_task (48 bytes, natural alignment)
+TASK_DTYPE = np.dtype([("q_off", "<i8"), ("kv_off", "<i8"), ("o_off", "<i8"),
+                       ("q_len", "<i4"), ("kv_len", "<i4"),
+                       ("q_pos0", "<i8"), ("kv_pos0", "<i8")])
+assert TASK_DTYPE.itemsize == 48
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64), ("o_rows", ctypes.c_int64)]
+
+
+class CAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (status_name(status), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libca.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libca.so is not built (run long_context_core_amd.build.build()); "
+                               "there is no non-HIP fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sp = ctypes.POINTER(Shape)
+        L.ca_forward_workspace.argtypes = [sp, vp, i32]
+        L.ca_forward_workspace.restype = sz
+        L.ca_forward.argtypes = [sp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_forward.restype = ctypes.c_int
+        L.ca_forward_varlen_workspace.argtypes = [sp, vp, i32]
+        L.ca_forward_varlen_workspace.restype = sz
+        L.ca_forward_varlen.argtypes = [sp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_forward_varlen.restype = ctypes.c_int
+        L.ca_merge.argtypes = [sp, i32, i64, vp, vp, vp, vp, vp]
+        L.ca_merge.restype = ctypes.c_int
+        L.ca_backward_workspace.argtypes = [sp, vp, i32]
+        L.ca_backward_workspace.restype = sz
+        L.ca_backward.argtypes = [sp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_backward.restype = ctypes.c_int
+        L.ca_visible_pairs.argtypes = [vp, i32]
+        L.ca_visible_pairs.restype = i64
+        L.ca_status_string.argtypes = [ctypes.c_int]
+        L.ca_status_string.restype = ctypes.c_char_p
+        L.ca_last_error.argtypes = []
+        L.ca_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_name(status):
+    return lib().ca_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != CA_OK:
+        raise CAError(status, lib().ca_last_error().decode())
+
+
+def task_array(tasks):
+    """(n, 7) int table (q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0)
+    -> contiguous ca_task records (records pass through unchanged)."""
+    if isinstance(tasks, np.ndarray) and tasks.dtype == TASK_DTYPE:
+        return np.ascontiguousarray(tasks)
+    t = np.asarray(tasks, dtype=np.int64).reshape(-1, 7)
+    a = np.zeros(len(t), dtype=TASK_DTYPE)
+    for i, name in enumerate(TASK_DTYPE.names):
+        a[name] = t[:, i]
+    return a
+
+
+def make_shape(hq, hkv, d, q_rows, kv_rows, o_rows, scale=None, out_f32=False):
+    s = Shape()
+    s.hq, s.hkv, s.d = int(hq), int(hkv), int(d)
+    s.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    s.flags = CA_OUT_F32 if out_f32 else 0
+    s.q_rows, s.kv_rows, s.o_rows = int(q_rows), int(kv_rows), int(o_rows)
+    return s
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tasks_ptr(ta):
+    return ta.ctypes.data_as(ctypes.c_void_p) if len(ta) else None
+
+
+def visible_pairs(tasks):
+    ta = task_array(tasks)
+    n = lib().ca_visible_pairs(_tasks_ptr(ta), len(ta))
+    if n < 0:
+        raise CAError(CA_ERR_INVALID, "invalid task table")
+    return int(n)
+
+
+def forward_workspace(shape, tasks):
+    ta = task_array(tasks)
+    return int(lib().ca_forward_workspace(ctypes.byref(shape), _tasks_ptr(ta), len(ta)))
+
+
+def workspace_tensor(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None):
+    """ca_forward on torch tensors: Q [q_rows, hq, d] bf16, K/V [kv_rows, hkv, d]
+    bf16, O [o_rows, hq, d] bf16 (fp32 with out_f32), LSE [o_rows, hq] fp32."""
+    ta = task_array(tasks)
+    if ws is None:
+        ws = workspace_tensor(forward_workspace(shape, ta), Q.device)
+    st = lib().ca_forward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
+                          _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st)
+    return O, LSE
+
+
+def forward_varlen(shape, cu_seqlens, Q, K, V, O, LSE, ws=None, stream=None):
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    n = len(cu) - 1
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    if ws is None:
+        ws = workspace_tensor(lib().ca_forward_varlen_workspace(ctypes.byref(shape), cup, n), Q.device)
+    st = lib().ca_forward_varlen(ctypes.byref(shape), cup, n, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                 _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st)
+    return O, LSE
+
+
+def merge(shape, O_parts, LSE_parts, O, LSE, stream=None):
+    """ca_merge: O_parts [S, n_rows, hq, d] fp32, LSE_parts [S, n_rows, hq] fp32."""
+    S, n_rows = int(O_parts.shape[0]), int(O_parts.shape[1])
+    st = lib().ca_merge(ctypes.byref(shape), S, n_rows, _ptr(O_parts), _ptr(LSE_parts), _ptr(O),
+                        _ptr(LSE), _stream_ptr(stream))
+    _check(st)
+    return O, LSE
+
+
+def backward_workspace(shape, tasks):
+    ta = task_array(tasks)
+    return int(lib().ca_backward_workspace(ctypes.byref(shape), _tasks_ptr(ta), len(ta)))
+
+
+def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None):
+    ta = task_array(tasks)
+    if ws is None:
+        ws = workspace_tensor(backward_workspace(shape, ta), Q.device)
+    st = lib().ca_backward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
+                           _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
+                           ws.numel(), _stream_ptr(stream))
+    _check(st)
+    return dQ, dK, dV

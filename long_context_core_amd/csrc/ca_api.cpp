@@ -1,0 +1,347 @@
+// Host side of libca: argument validation, work-item expansion with exact
+// per-item cost, longest-first ordering, workspace layout and launches.
+//
+// The work queue applies the pages' balancing idea at the level of compute
+// units: every item's cost is its number of visible (query, key) pairs —
+// attention cost is quadratic in document length, FLOPs(l) = alpha l^2 +
+// beta l ("Efficient Long-context Language Model Training by Core Attention
+// Disaggregation", Section 3.4) — and items are issued longest first so that
+// the hardware dispatcher's greedy fill of free workgroup slots balances the
+// tail (the simple greedy fill of the CMU CSD blog post on Core Attention
+// Disaggregation, Figure 9 discussion).  Nothing here allocates device memory:
+// the task table and the queue are uploaded into the caller's workspace.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "ca_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ca_status fail(ca_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ca_status hip_fail(hipError_t e, const char* what) {
+  return fail(CA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sum over task rows i in [a, b] of clip(i + delta + 1, 0, kv_len): the
+// number of keys each row sees (key j visible iff j <= i + delta, j < kv_len).
+int64_t range_pairs(int64_t a, int64_t b, int64_t delta, int64_t kv_len) {
+  if (b < a || kv_len <= 0) return 0;
+  const int64_t s0 = kv_len - delta - 1;      // first row that sees all keys
+  int64_t total = 0;
+  const int64_t sat_lo = std::max(a, s0);
+  if (b >= sat_lo) total += kv_len * (b - sat_lo + 1);
+  const int64_t lo = std::max(a, -delta);     // first row that sees >= 1 key
+  const int64_t hi = std::min(b, s0 - 1);
+  if (hi >= lo) {
+    const int64_t n = hi - lo + 1;
+    const int64_t f_lo = lo + delta + 1, f_hi = hi + delta + 1;
+    total += (f_lo + f_hi) * n / 2;
+  }
+  return total;
+}
+
+ca_status check_shape(const ca_shape* s) {
+  if (!s) return fail(CA_ERR_INVALID, "shape is NULL");
+  if (s->hq < 1 || s->hkv < 1) return fail(CA_ERR_INVALID, "hq=%d hkv=%d must be >= 1", s->hq, s->hkv);
+  if (s->hq % s->hkv != 0) return fail(CA_ERR_INVALID, "hkv=%d does not divide hq=%d", s->hkv, s->hq);
+  if (s->d != 64 && s->d != 128) return fail(CA_ERR_UNSUPPORTED, "head dim d=%d not supported (64, 128)", s->d);
+  if (!std::isfinite(s->scale)) return fail(CA_ERR_INVALID, "scale is not finite");
+  if (s->q_rows < 0 || s->kv_rows < 0 || s->o_rows < 0)
+    return fail(CA_ERR_INVALID, "negative row count");
+  if (s->flags & ~(uint32_t)CA_OUT_F32) return fail(CA_ERR_INVALID, "unknown flags 0x%x", s->flags);
+  return CA_OK;
+}
+
+ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n) {
+  if (n < 0) return fail(CA_ERR_INVALID, "n_tasks=%d < 0", n);
+  if (n > 0 && !t) return fail(CA_ERR_INVALID, "tasks_host is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const ca_task& k = t[i];
+    if (k.q_len < 0 || k.kv_len < 0) return fail(CA_ERR_INVALID, "task %d: negative length", i);
+    if (k.q_off < 0 || k.kv_off < 0 || k.o_off < 0) return fail(CA_ERR_INVALID, "task %d: negative offset", i);
+    if (k.q_off + k.q_len > s->q_rows)
+      return fail(CA_ERR_INVALID, "task %d: query rows [%lld, %lld) past q_rows=%lld", i,
+                  (long long)k.q_off, (long long)(k.q_off + k.q_len), (long long)s->q_rows);
+    if (k.kv_off + k.kv_len > s->kv_rows)
+      return fail(CA_ERR_INVALID, "task %d: context rows [%lld, %lld) past kv_rows=%lld", i,
+                  (long long)k.kv_off, (long long)(k.kv_off + k.kv_len), (long long)s->kv_rows);
+    if (k.o_off + k.q_len > s->o_rows)
+      return fail(CA_ERR_INVALID, "task %d: output rows [%lld, %lld) past o_rows=%lld", i,
+                  (long long)k.o_off, (long long)(k.o_off + k.q_len), (long long)s->o_rows);
+    if (k.q_pos0 < -(int64_t(1) << 40) || k.q_pos0 > (int64_t(1) << 40) ||
+        k.kv_pos0 < -(int64_t(1) << 40) || k.kv_pos0 > (int64_t(1) << 40))
+      return fail(CA_ERR_INVALID, "task %d: positions out of range", i);
+  }
+  return CA_OK;
+}
+
+int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// Upload of a host-built work queue into the caller's workspace, through a
+// pinned staging buffer kept per thread and device (grown, never shrunk, held
+// until the process ends).  An event recorded after the copy guards reuse, so
+// the call never blocks on earlier stream work unless the previous upload of
+// this thread has not even started.
+struct Staging {
+  void* buf = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+constexpr int kMaxDevices = 64;
+thread_local Staging g_staging[kMaxDevices];
+
+ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CA_ERR_UNSUPPORTED, "device index %d", dev);
+  Staging& st = g_staging[dev];
+  if (st.pending) {
+    e = hipEventSynchronize(st.ev);
+    if (e != hipSuccess) return hip_fail(e, "waiting for the previous upload");
+    st.pending = false;
+  }
+  if (!st.ev) {
+    e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (st.cap < src.size()) {
+    if (st.buf) (void)hipHostFree(st.buf);
+    st.buf = nullptr;
+    st.cap = 0;
+    const size_t cap = std::max<size_t>(src.size() + src.size() / 2, 1 << 16);
+    e = hipHostMalloc(&st.buf, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "pinned staging allocation");
+    st.cap = cap;
+  }
+  std::memcpy(st.buf, src.data(), src.size());
+  e = hipMemcpyAsync(dst, st.buf, src.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "upload of the work queue");
+  e = hipEventRecord(st.ev, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  st.pending = true;
+  return CA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Forward plan
+// ---------------------------------------------------------------------------
+
+struct FwdPlan {
+  int hpw = 1, rt = 128, group = 1;
+  size_t n_items = 0;
+  size_t off_tasks = 0, off_items = 0, bytes = 0;
+};
+
+FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
+  FwdPlan p;
+  p.group = s->hq / s->hkv;
+  p.hpw = gcd_int(p.group, 4);
+  p.rt = 32 * (4 / p.hpw);
+  for (int32_t i = 0; i < n; ++i) {
+    if (t[i].q_len <= 0) continue;
+    const size_t tiles = (t[i].q_len + p.rt - 1) / p.rt;
+    p.n_items += tiles * (size_t)s->hkv * (size_t)(p.group / p.hpw);
+  }
+  p.off_tasks = 0;
+  p.off_items = align_up(sizeof(ca_task) * (size_t)n);
+  p.bytes = p.off_items + align_up(sizeof(ca::FwdItem) * p.n_items);
+  return p;
+}
+
+void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const FwdPlan& p,
+                         std::vector<ca::FwdItem>& items) {
+  struct Keyed {
+    int64_t cost;
+    ca::FwdItem it;
+  };
+  std::vector<Keyed> tmp;
+  tmp.reserve(p.n_items);
+  for (int32_t i = 0; i < n; ++i) {
+    const ca_task& k = t[i];
+    if (k.q_len <= 0) continue;
+    const int64_t delta = k.q_pos0 - k.kv_pos0;
+    for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
+      const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
+      // pairs of the tile (per head) plus a per-row epilogue term
+      const int64_t cost = range_pairs(r0, r1, delta, k.kv_len) * p.hpw + (r1 - r0 + 1) * 64;
+      for (int32_t g = 0; g < s->hkv; ++g)
+        for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
+    }
+  }
+  std::stable_sort(tmp.begin(), tmp.end(), [](const Keyed& a, const Keyed& b) { return a.cost > b.cost; });
+  items.resize(tmp.size());
+  for (size_t i = 0; i < tmp.size(); ++i) items[i] = tmp[i].it;
+}
+
+ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const void* Q, const void* K,
+                       const void* V, void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
+  ca_status st = check_shape(s);
+  if (st != CA_OK) return st;
+  st = check_tasks(s, t, n);
+  if (st != CA_OK) return st;
+  const FwdPlan p = plan_forward(s, t, n);
+  if (p.n_items == 0) return CA_OK;
+  if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
+  if (!ws || ws_bytes < p.bytes)
+    return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
+  if (p.n_items > 0x7fffffffu) return fail(CA_ERR_UNSUPPORTED, "too many work items");
+  std::vector<ca::FwdItem> items;
+  build_forward_items(s, t, n, p, items);
+  std::vector<char> host(p.bytes, 0);
+  std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
+  std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
+  hipStream_t hs = (hipStream_t)stream;
+  st = upload(ws, host, hs);
+  if (st != CA_OK) return st;
+  ca::FwdParams fp;
+  fp.Q = (const __bf16*)Q;
+  fp.K = (const __bf16*)K;
+  fp.V = (const __bf16*)V;
+  fp.O = O;
+  fp.LSE = LSE;
+  fp.tasks = (const ca_task*)((char*)ws + p.off_tasks);
+  fp.items = (const ca::FwdItem*)((char*)ws + p.off_items);
+  fp.n_items = (int32_t)items.size();
+  fp.hq = s->hq;
+  fp.hkv = s->hkv;
+  fp.group = p.group;
+  fp.hpw = p.hpw;
+  fp.scale_log2 = s->scale * 1.4426950408889634f;
+  fp.out_f32 = (s->flags & CA_OUT_F32) ? 1 : 0;
+  hipError_t e = ca::launch_forward(fp, s->d, hs);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return CA_OK;
+}
+
+bool varlen_to_tasks(const int32_t* cu, int32_t n_docs, std::vector<ca_task>& out) {
+  if (n_docs < 0 || (n_docs > 0 && !cu)) return false;
+  if (n_docs > 0 && cu[0] != 0) return false;
+  out.resize((size_t)n_docs);
+  for (int32_t i = 0; i < n_docs; ++i) {
+    if (cu[i + 1] < cu[i]) return false;
+    const int32_t l = cu[i + 1] - cu[i];
+    out[(size_t)i] = ca_task{cu[i], cu[i], cu[i], l, l, 0, 0};
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks) {
+  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK) return 0;
+  return plan_forward(shape, tasks_host, n_tasks).bytes;
+}
+
+ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks, const void* Q,
+                     const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return forward_impl(shape, tasks_host, n_tasks, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu, int32_t n_docs) {
+  std::vector<ca_task> t;
+  if (!varlen_to_tasks(cu, n_docs, t)) return 0;
+  return ca_forward_workspace(shape, t.data(), n_docs);
+}
+
+ca_status ca_forward_varlen(const ca_shape* shape, const int32_t* cu, int32_t n_docs, const void* Q,
+                            const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
+                            void* stream) {
+  std::vector<ca_task> t;
+  if (!varlen_to_tasks(cu, n_docs, t))
+    return fail(CA_ERR_INVALID, "cu_seqlens must start at 0 and be non-decreasing");
+  return forward_impl(shape, t.data(), n_docs, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows, const float* O_parts,
+                   const float* LSE_parts, void* O, float* LSE, void* stream) {
+  if (!shape) return fail(CA_ERR_INVALID, "shape is NULL");
+  if (shape->hq < 1) return fail(CA_ERR_INVALID, "hq=%d must be >= 1", shape->hq);
+  if (shape->d != 64 && shape->d != 128) return fail(CA_ERR_UNSUPPORTED, "head dim d=%d not supported", shape->d);
+  if (shape->flags & ~(uint32_t)CA_OUT_F32) return fail(CA_ERR_INVALID, "unknown flags 0x%x", shape->flags);
+  if (n_parts < 1) return fail(CA_ERR_INVALID, "n_parts=%d must be >= 1", n_parts);
+  if (n_rows < 0) return fail(CA_ERR_INVALID, "n_rows < 0");
+  if (n_rows == 0) return CA_OK;
+  if (!O_parts || !LSE_parts || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
+  if (n_rows * shape->hq * (shape->d / 4) / 256 >= 0x7fffffffLL) return fail(CA_ERR_UNSUPPORTED, "too many rows");
+  ca::MergeParams mp;
+  mp.O_parts = O_parts;
+  mp.LSE_parts = LSE_parts;
+  mp.O = O;
+  mp.LSE = LSE;
+  mp.n_parts = n_parts;
+  mp.n_rows = n_rows;
+  mp.hq = shape->hq;
+  mp.out_f32 = (shape->flags & CA_OUT_F32) ? 1 : 0;
+  hipError_t e = ca::launch_merge(mp, shape->d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return CA_OK;
+}
+
+size_t ca_backward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks) {
+  (void)shape;
+  (void)tasks_host;
+  (void)n_tasks;
+  return 0;
+}
+
+ca_status ca_backward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks, const void* Q,
+                      const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                      void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  (void)shape; (void)tasks_host; (void)n_tasks; (void)Q; (void)K; (void)V; (void)O; (void)dO;
+  (void)LSE; (void)dQ; (void)dK; (void)dV; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(CA_ERR_UNSUPPORTED, "backward not built yet");
+}
+
+int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks) {
+  if (n_tasks < 0 || (n_tasks > 0 && !tasks_host)) return -1;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_tasks; ++i) {
+    const ca_task& k = tasks_host[i];
+    if (k.q_len < 0 || k.kv_len < 0) return -1;
+    total += range_pairs(0, (int64_t)k.q_len - 1, k.q_pos0 - k.kv_pos0, k.kv_len);
+  }
+  return total;
+}
+
+const char* ca_status_string(ca_status s) {
+  switch (s) {
+    case CA_OK: return "CA_OK";
+    case CA_ERR_INVALID: return "CA_ERR_INVALID";
+    case CA_ERR_UNSUPPORTED: return "CA_ERR_UNSUPPORTED";
+    case CA_ERR_WORKSPACE: return "CA_ERR_WORKSPACE";
+    case CA_ERR_HIP: return "CA_ERR_HIP";
+  }
+  return "CA_UNKNOWN_STATUS";
+}
+
+const char* ca_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Internal declarations shared by the host API and the HIP kernels of libca.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ca.h"
+
+namespace ca {
+
+// One forward work item: a tile of query rows of one task, for a subset of
+// the query heads that share one KV head.  The workgroup's four waves cover
+// hpw heads x (4 / hpw) blocks of 32 rows.
+struct FwdItem {
+  int32_t task;
+  int32_t kv_head;
+  int32_t head_sub;  // which group of hpw heads inside the KV head's group
+  int32_t row0;      // first task-relative query row
+};
+
+// Split-KV decode work item: one task (a single query row), one KV head, all
+// query heads of its group, keys [k_begin, k_end) of the task's context.
+// Writes a partial (O, LSE) to slot `part` of the decode staging area, or
+// straight to the output when the task is not split.
+struct DecItem {
+  int32_t task;
+  int32_t kv_head;
+  int32_t k_begin;
+  int32_t k_end;
+  int32_t part;    // staging slot, or -1: write the final O/LSE of the task
+  int32_t pad[3];
+};
+
+// Backward work item: one tile of 64 context rows of a task for one KV head.
+struct BwdItem {
+  int32_t task;
+  int32_t kv_head;
+  int32_t key0;      // first task-relative context row of the tile
+  int32_t pad;
+};
+
+struct FwdParams {
+  const __bf16* Q;
+  const __bf16* K;
+  const __bf16* V;
+  void* O;
+  float* LSE;
+  const ca_task* tasks;
+  const FwdItem* items;
+  int32_t n_items;
+  int32_t hq, hkv, group, hpw;
+  float scale_log2;   // softmax scale * log2(e)
+  int32_t out_f32;
+};
+
+struct DecParams {
+  const __bf16* Q;
+  const __bf16* K;
+  const __bf16* V;
+  void* O;
+  float* LSE;
+  float* part_O;      // [n_parts][group][d] fp32 staging for split tasks
+  float* part_LSE;    // [n_parts][group]
+  const ca_task* tasks;
+  const DecItem* items;
+  int32_t n_items;
+  int32_t hq, hkv, group;
+  float scale_log2;
+  int32_t out_f32;
+};
+
+struct DecMergeParams {
+  const float* part_O;
+  const float* part_LSE;
+  const int32_t* first_part;   // per split task: first staging slot
+  const int32_t* n_parts;      // per split task: number of slots
+  const int32_t* task_of;      // per split task: task index
+  const int32_t* head_of;      // per split task: KV head
+  const ca_task* tasks;
+  void* O;
+  float* LSE;
+  int32_t n_split;
+  int32_t hq, group;
+  int32_t out_f32;
+};
+
+struct MergeParams {
+  const float* O_parts;
+  const float* LSE_parts;
+  void* O;
+  float* LSE;
+  int32_t n_parts;
+  int64_t n_rows;
+  int32_t hq;
+  int32_t out_f32;
+};
+
+struct BwdParams {
+  const __bf16* Q;
+  const __bf16* K;
+  const __bf16* V;
+  const __bf16* O;
+  const __bf16* dO;
+  const float* LSE;
+  float* Dvec;        // [o_rows][hq] rowsum(dO * O)
+  float* dQacc;       // [q_rows][hq][d] fp32
+  __bf16* dQ;
+  __bf16* dK;
+  __bf16* dV;
+  const ca_task* tasks;
+  const BwdItem* items;
+  int32_t n_items;
+  int32_t hq, hkv, group;
+  float scale;
+  float scale_log2;
+  int64_t q_rows, kv_rows, o_rows;
+};
+
+// Kernel launchers (defined in the .hip files).
+hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_decode(const DecParams& p, int d, hipStream_t s);
+hipError_t launch_decode_merge(const DecMergeParams& p, int d, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
+hipError_t launch_backward(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_zero_bf16(__bf16* p, int64_t n, hipStream_t s);
+
+}  // namespace ca

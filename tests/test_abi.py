@@ -1,0 +1,104 @@
+"""Host-side checks of libca.so that need no GPU: it loads, exports every
+symbol include/ca.h declares, rejects bad arguments before touching the
+device, and counts visible pairs exactly like the oracle."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_core_amd import ca
+from long_context_core_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ca.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ca_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ca.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ca.EXPORTS)
+
+
+def test_status_strings():
+    assert ca.status_name(0) == "CA_OK"
+    assert ca.status_name(-3) == "CA_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_visible_pairs_match_oracle(seed):
+    rng = np.random.default_rng(seed)
+    n = 40
+    t = np.zeros((n, 7), np.int64)
+    t[:, 3] = rng.integers(0, 3000, n)
+    t[:, 4] = rng.integers(0, 3000, n)
+    t[:, 5] = rng.integers(-500, 5000, n)
+    t[:, 6] = rng.integers(-500, 5000, n)
+    assert ca.visible_pairs(t) == oracle.visible_pairs(t)
+
+
+def test_visible_pairs_of_workloads():
+    for w in (I.tiny_forward(), I.llama8b_packed_131k(), I.ca_tasks_34b(), I.ring_prefill_405b_tp8(),
+              I.ring_decode_405b_tp8(), I.train_8b_prolong_512k()):
+        assert ca.visible_pairs(w.tasks) == oracle.visible_pairs(w.tasks)
+    assert ca.visible_pairs(I.ring_prefill_405b_tp8().tasks) == 131072 * 131073 // 2
+
+
+def call_forward(shape, tasks, ws_bytes=1 << 20, ptr=FAKE):
+    ta = ca.task_array(tasks)
+    return ca.lib().ca_forward(ctypes.byref(shape) if shape is not None else None,
+                               ta.ctypes.data_as(ctypes.c_void_p), len(ta),
+                               ptr, ptr, ptr, ptr, ptr, FAKE, ws_bytes, None)
+
+
+def test_forward_rejects_bad_arguments_without_launching():
+    good = [(0, 0, 0, 10, 10, 0, 0)]
+    s = ca.make_shape(8, 2, 128, 10, 10, 10)
+    assert call_forward(None, good) == ca.CA_ERR_INVALID
+    assert call_forward(ca.make_shape(8, 3, 128, 10, 10, 10), good) == ca.CA_ERR_INVALID
+    assert call_forward(ca.make_shape(8, 2, 96, 10, 10, 10), good) == ca.CA_ERR_UNSUPPORTED
+    assert call_forward(ca.make_shape(8, 2, 128, 10, 10, 10, scale=float("nan")), good) == ca.CA_ERR_INVALID
+    assert call_forward(s, [(0, 0, 0, 11, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past q_rows
+    assert call_forward(s, [(0, 1, 0, 10, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past kv_rows
+    assert call_forward(s, [(0, 0, 5, 10, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past o_rows
+    assert call_forward(s, [(0, 0, 0, -1, 10, 0, 0)]) == ca.CA_ERR_INVALID
+    assert call_forward(s, good, ptr=None) == ca.CA_ERR_INVALID                # NULL tensors
+    need = ca.forward_workspace(s, good)
+    assert need > 0
+    assert call_forward(s, good, ws_bytes=need - 1) == ca.CA_ERR_WORKSPACE
+    assert "workspace" in ca.lib().ca_last_error().decode()
+    # nothing to do: OK without touching the device
+    assert call_forward(s, [(0, 0, 0, 0, 10, 0, 0)]) == ca.CA_OK
+
+
+def test_merge_rejects_bad_arguments():
+    L = ca.lib()
+    s = ca.make_shape(4, 1, 128, 0, 0, 0)
+    assert L.ca_merge(ctypes.byref(s), 0, 10, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_ERR_INVALID
+    assert L.ca_merge(ctypes.byref(s), 2, -1, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_ERR_INVALID
+    assert L.ca_merge(ctypes.byref(s), 2, 10, None, FAKE, FAKE, FAKE, None) == ca.CA_ERR_INVALID
+    s2 = ca.make_shape(4, 1, 80, 0, 0, 0)
+    assert L.ca_merge(ctypes.byref(s2), 2, 10, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_ERR_UNSUPPORTED
+    assert L.ca_merge(ctypes.byref(s), 2, 0, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_OK
+
+
+def test_varlen_rejects_bad_cu_seqlens():
+    L = ca.lib()
+    s = ca.make_shape(4, 1, 64, 100, 100, 100)
+    for cu in ([1, 10], [0, 10, 5]):
+        a = np.array(cu, np.int32)
+        st = L.ca_forward_varlen(ctypes.byref(s), a.ctypes.data_as(ctypes.c_void_p), len(a) - 1,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+        assert st == ca.CA_ERR_INVALID
