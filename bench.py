@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the core-attention hot path on one MI355X.
+
+Default workload: Llama-3-8B attention shape (32 query heads, 8 KV heads,
+d = 128, bf16) over one packed 131,072-token chunk of seeded lognormal
+documents with per-document causal masks.  One step = one ca_forward_varlen
+call (host work-queue build + upload + the fused K1 launch) over the whole
+chunk, inputs resident in HBM.  Prints ONE JSON line on stdout:
+
+  value       core-attention TFLOP/s counting only visible (query, key) pairs
+              (4 d FLOPs per pair and query head), whole job
+  roofline    the dominant kernel against the published dense bf16 MFMA peak
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_file, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        data = json.load(open(p))
+        ent = data.get(workload)
+        src = os.path.join(ROOT, "long_context_core_amd", "csrc", kernel_file)
+        if not ent or ent.get("kernel_source_sha") != source_sha(src):
+            return None
+        return float(ent["fetch_bytes_per_launch"]) + float(ent["write_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, Q, K, V, seconds_hint):
+    """The oracle as it stands, on a bounded sample: 256 random query rows of
+    the workload's largest task, all query heads."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t = w.tasks[int(np.argmax(w.tasks[:, 3]))]
+    q_off, kv_off, o_off, q_len, kv_len = (int(x) for x in t[:5])
+    rng = np.random.default_rng(0)
+    n_rows = min(256, q_len)
+    rows = np.sort(rng.choice(q_len, n_rows, replace=False))
+    import torch
+    # widen only the slices the sample reads
+    n_ctx = int(min(kv_len, int(t[5]) - int(t[6]) + int(rows.max()) + 1))
+    qs = oracle.bf16_bits_to_f64(Q[q_off:q_off + q_len].cpu().view(torch.int16).numpy())
+    ks = oracle.bf16_bits_to_f64(K[kv_off:kv_off + n_ctx].cpu().view(torch.int16).numpy())
+    vs = oracle.bf16_bits_to_f64(V[kv_off:kv_off + n_ctx].cpu().view(torch.int16).numpy())
+    local = np.array([0, 0, 0, q_len, n_ctx, t[5], t[6]], dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.forward_rows(local, rows, qs, ks, vs, w.scale)
+    dt = time.perf_counter() - t0
+    pairs = int(np.sum(np.clip(int(t[5]) + rows - int(t[6]) + 1, 0, n_ctx)))
+    flops = oracle.forward_flops(pairs, w.hq, w.d)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d random query rows of the largest task (%d tokens), all %d query heads; "
+                      "%d visible pairs per head in %.1f s" % (n_rows, q_len, w.hq, pairs, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b-131k",
+                    choices=["llama8b-131k", "tiny", "ca-tasks-34b", "train-8b-512k-fwd"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X and has no "
+              "multi-GPU mode (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_core_amd import ca
+    from long_context_core_amd import inputs as I
+    import oracle
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = {"llama8b-131k": I.llama8b_packed_131k, "tiny": I.tiny_forward,
+         "ca-tasks-34b": I.ca_tasks_34b, "train-8b-512k-fwd": I.train_8b_prolong_512k}[args.workload]()
+    log("workload %s: %d tasks, hq=%d hkv=%d d=%d, q_rows=%d kv_rows=%d"
+        % (w.name, len(w.tasks), w.hq, w.hkv, w.d, w.q_rows, w.kv_rows))
+
+    seed = 202
+    Q = I.randn_bf16((w.q_rows, w.hq, w.d), seed, device=dev)
+    K = I.randn_bf16((w.kv_rows, w.hkv, w.d), seed + 1, device=dev)
+    V = I.randn_bf16((w.kv_rows, w.hkv, w.d), seed + 2, device=dev)
+    O = torch.empty((w.o_rows, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((w.o_rows, w.hq), dtype=torch.float32, device=dev)
+    shape = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
+    tasks = ca.task_array(w.tasks)
+    ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+    pairs = ca.visible_pairs(tasks)
+    assert pairs == oracle.visible_pairs(w.tasks)
+    flops = oracle.forward_flops(pairs, w.hq, w.d)
+    log("visible pairs per head %d, %.3f TFLOP per step" % (pairs, flops / 1e12))
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step / 1e3) / 1e12
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    achieved = flops / avg_launch_s / 1e12
+    log("steps %d: wall %.3f ms/step, event avg %.3f ms (min %.3f), %.1f TFLOP/s"
+        % (args.steps, ms_per_step, avg_launch_s * 1e3, min(launch_ms), value))
+
+    traffic = traffic_for("ca_fwd.hip", w.name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "ca::fwd_kernel<128>",
+                "per_launch_flops": flops, "avg_launch_ms": round(avg_launch_s * 1e3, 4)}
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample ...")
+        base = cpu_baseline(w, Q, K, V, 20)
+        log("oracle: %.4g TFLOP/s on %d threads" % (base["value"], base["cores"]))
+
+    out = {
+        "metric": "core-attention TFLOP/s (unmasked pairs) and % of bf16 MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "tokens": int(w.q_rows), "docs": len(w.tasks), "hq": w.hq,
+                   "hkv": w.hkv, "d": w.d, "visible_pairs_per_head": pairs, "flops_per_step": flops,
+                   "length_seed": 102, "tensor_seed": seed},
+        "roofline": roofline,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,14 @@
 
 namespace ca {
 
+// Row statistics are kept relative to a running max m2 that is only raised
+// when some row's max grows by more than kRescaleLog2 (in log2 units); until
+// then probabilities may reach 2^kRescaleLog2, which fp32 accumulators and
+// bf16 operands hold exactly in range.  O and the row sum share the same
+// reference, so the final O = acc / l and LSE = ln2 (m2 + log2 l) are exact
+// regardless of when the reference moved.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BN = 64;          // keys per tile
@@ -54,8 +62,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int hh = lane >> 5;       // half-wave
 
   const int hpw = p.hpw;
-  const int head = it.kv_head * p.group + it.head_sub * hpw + (wave % hpw);
-  const int wrow0 = it.row0 + (wave / hpw) * 32;
+  // wave-uniform values, kept in scalar registers
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
+  const int wrow0 = it.row0 + (wave_u / hpw) * 32;
   const int64_t delta = t.q_pos0 - t.kv_pos0;
   const int kv_len = t.kv_len;
 
@@ -65,6 +75,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
   const int w_last = min(wrow0 + 32, t.q_len) - 1;
   const int w_kv_hi = (w_last < wrow0) ? 0 : (int)clamp64((int64_t)w_last + delta + 1, 0, kv_len);
+  // Tiles [0, w_full) are visible to every row of the wave: no mask.
+  const int w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
 
   // Q^T operand: this lane's query row, channels 16 s + 8 hh .. + 7.
   const int qrow = wrow0 + l32;
@@ -79,28 +91,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   f32x16 o_acc[NCB];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) o_acc[c] = f32x16_zero();
-  float m2 = -INFINITY;   // running max of scale*log2(e)*s
-  float lsum = 0.f;       // running sum of exp2(...)
+  float m2 = -INFINITY;   // reference max, log2 units
+  float lsum = 0.f;       // sum of exp2(s * c - m2)
 
   const int n_tiles = (kv_hi + BN - 1) / BN;
   const int64_t kv_stride = (int64_t)p.hkv * D;
+  const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
   const __bf16* kbase = p.K + t.kv_off * kv_stride + it.kv_head * D;
   const __bf16* vbase = p.V + t.kv_off * kv_stride + it.kv_head * D;
+  // Rows >= kv_hi read as zeros (range-checked buffer loads).
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)kv_hi * row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)kv_hi * row_bytes);
   const int ld_row = tid / CH;
   const int ld_chunk = tid % CH;
+  const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
 
   uint4 kreg[PASSES], vreg[PASSES];
   auto gload = [&](int tile) {
+    const uint32_t soff = (uint32_t)tile * BN * row_bytes;
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      const int row = tile * BN + r * RPP + ld_row;
-      if (row < kv_hi) {
-        kreg[r] = *(const uint4*)(kbase + row * kv_stride + ld_chunk * 8);
-        vreg[r] = *(const uint4*)(vbase + row * kv_stride + ld_chunk * 8);
-      } else {
-        kreg[r] = make_uint4(0, 0, 0, 0);
-        vreg[r] = make_uint4(0, 0, 0, 0);
-      }
+      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
+      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
     }
   };
   auto swrite = [&](int buf) {
@@ -120,8 +132,91 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int k_lane_off = l32 * KS + 8 * hh;
   const int g16 = lane >> 4;
   const int j16 = lane & 15;
-  const int v_lane_off = (j16 >> 2) * VS + 16 * (g16 & 1) + 4 * (j16 & 3);
-  const int v_h = (g16 >> 1);     // == hh
+  const int v_lane_off = ((j16 >> 2) + 4 * hh) * VS + 16 * (g16 & 1) + 4 * (j16 & 3);
+
+  // One key tile for this wave.
+  auto do_tile = [&](int tile, int buf) {
+    const int k0 = tile * BN;
+    f32x16 s_acc[2];
+    const __bf16* kl = &lds_k[buf][k_lane_off];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kl + mb * 32 * KS), qf[0],
+                                                          f32x16_zero(), 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 1; s < NKS; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf = *(const bf16x8*)(kl + mb * 32 * KS + 16 * s);
+        s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s_acc[mb], 0, 0, 0);
+      }
+    }
+    // Mask only where the tile straddles the diagonal or the context end:
+    // key k0 + r (r in [0, 64)) is visible iff r <= lim.
+    if (tile >= w_full) {
+      keep_branch();
+      const int lim = (int)clamp64(min((int64_t)qrow + delta, (int64_t)kv_len - 1) - k0, -1, BN);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          s_acc[mb][j] = (r <= lim) ? s_acc[mb][j] : -INFINITY;
+        }
+    }
+    // Tile max of this row, both half-waves.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s_acc[mb][j], s_acc[mb][j + 1]));
+    mx = max_halves(mx);
+    const float m_tile = mx * p.scale_log2;
+    // Raise the reference only when some row of the wave outgrew it.
+    if (__any(m_tile > m2 + kRescaleLog2)) {
+      keep_branch();
+      const float m_new = fmaxf(m2, m_tile);
+      const float alpha = exp2_fast(m2 - m_new);   // 0 when m2 = -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o_acc[c][j] *= alpha;
+      m2 = m_new;
+    }
+    const float m_use = (m2 == -INFINITY) ? 0.f : m2;
+    // P^T fragments: registers 8*half .. 8*half+7 of score block mb; the row
+    // sum is taken in fp32 before rounding (two independent add chains).
+    bf16x8 pf[2][2];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = exp2_fast(fmaf(s_acc[mb][8 * half + i], p.scale_log2, -m_use));
+          if (i & 1) rs1 += e; else rs0 += e;
+          pf[mb][half][i] = (__bf16)e;
+        }
+    lsum += sum_halves(rs0 + rs1);
+
+    const __bf16* vl = &lds_v[buf][v_lane_off];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kb = mb * 32 + 16 * half;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+          const __bf16* a0 = vl + kb * VS + c * 32;
+          const bf16x8 vf = concat_bf16x4(ds_read_tr16(a0), ds_read_tr16(a0 + 8 * VS));
+          o_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[mb][half], o_acc[c], 0, 0, 0);
+        }
+      }
+    }
+  };
 
   if (n_tiles > 0) gload(0);
   for (int tile = 0; tile < n_tiles; ++tile) {
@@ -129,86 +224,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     swrite(buf);
     __syncthreads();
     if (tile + 1 < n_tiles) gload(tile + 1);
-    const int k0 = tile * BN;
-    if (k0 < w_kv_hi) {
-      f32x16 s_acc[2];
-      s_acc[0] = f32x16_zero();
-      s_acc[1] = f32x16_zero();
-      const __bf16* kl = &lds_k[buf][k_lane_off];
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 kf = *(const bf16x8*)(kl + mb * 32 * KS + 16 * s);
-          s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s_acc[mb], 0, 0, 0);
-        }
-      }
-      // Mask only where the tile straddles the diagonal or the context end.
-      const bool need_mask = ((int64_t)k0 + BN - 1 > (int64_t)wrow0 + delta) || (k0 + BN > kv_len);
-      if (need_mask) {
-        const int64_t lim = (int64_t)qrow + delta;   // last visible key of this row
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (key >= kv_len || (int64_t)key > lim) s_acc[mb][j] = -INFINITY;
-          }
-        }
-      }
-      // Online softmax, exp2 domain.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s_acc[mb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m2, mx * p.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m2 - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = exp2_fast(fmaf(s_acc[mb][j], p.scale_log2, -m_use));
-          s_acc[mb][j] = e;
-          rs += e;
-        }
-      rs += __shfl_xor(rs, 32);
-      lsum = lsum * alpha + rs;
-      m2 = m_new;
-#pragma unroll
-      for (int c = 0; c < NCB; ++c)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o_acc[c][j] *= alpha;
-
-      // P^T fragments: registers 8*half .. 8*half+7 of score block mb.
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pf[mb][half][i] = (__bf16)s_acc[mb][8 * half + i];
-
-      const __bf16* vl = &lds_v[buf][v_lane_off];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int kb = mb * 32 + 16 * half + 4 * v_h;
-#pragma unroll
-          for (int c = 0; c < NCB; ++c) {
-            const __bf16* a0 = vl + kb * VS + c * 32;
-            const bf16x4 lo = ds_read_tr16(a0);
-            const bf16x4 hi = ds_read_tr16(a0 + 8 * VS);
-            const bf16x8 vf = concat_bf16x4(lo, hi);
-            o_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[mb][half], o_acc[c], 0, 0, 0);
-          }
-        }
-      }
-    }
+    if (tile * BN < w_kv_hi) do_tile(tile, buf);
   }
 
   // Epilogue: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty rows: 0, -inf.
