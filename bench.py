@@ -97,7 +97,20 @@ def main():
     ap.add_argument("--workload", default="llama8b-131k",
                     choices=["llama8b-131k", "tiny", "ca-tasks-34b", "train-8b-512k-fwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times), the reference for "
+                         "scaling the HBM byte counters")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)      # one elementwise kernel: 1 GiB read, 1 GiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 1 << 30, "calibrate_copy_bytes_written": 1 << 30}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X and has no "

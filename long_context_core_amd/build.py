@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
     # no packed fp32 ALU ops (v_pk_{add,mul,fma}_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # inputs are finite by contract and the kernels use -inf but never NaN:
+    # without this, every fmaxf on an MFMA result is preceded by a
+    # canonicalising v_max (IEEE mode), tripling the cost of row maxima
+    "-fno-honor-nans",
     "-I" + os.path.join(ROOT, "include"),
 ]
 
