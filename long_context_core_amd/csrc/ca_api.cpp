@@ -150,11 +150,32 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Forward plan
 // ---------------------------------------------------------------------------
+//
+// Tasks with a single query row and at most 16 query heads per KV head go to
+// the split-KV decode kernel (the heads of a group share one K/V stream); all
+// others go to the tiled kernel.  Decode tasks are cut into key chunks so that
+// the launch has enough work items to cover the chip; chunks of one task are
+// merged by log-sum-exp afterwards.
+
+constexpr int kDecTargetItems = 2048;
+constexpr int kDecMinChunk = 512;
+constexpr int kDecMaxGroup = 16;
+
+bool is_decode_task(const ca_task& k, int group) { return k.q_len == 1 && group <= kDecMaxGroup; }
+
+// keys of a decode task that its single row can see: [0, vis)
+int64_t decode_visible(const ca_task& k) {
+  return std::min<int64_t>(k.kv_len, std::max<int64_t>(0, k.q_pos0 - k.kv_pos0 + 1));
+}
 
 struct FwdPlan {
   int hpw = 1, rt = 128, group = 1;
-  size_t n_items = 0;
-  size_t off_tasks = 0, off_items = 0, bytes = 0;
+  size_t n_items = 0;        // tiled-kernel items
+  size_t n_dec_items = 0;    // decode items
+  size_t n_split = 0;        // decode (task, kv head) pairs cut into > 1 chunk
+  size_t n_parts = 0;        // staging slots for those chunks
+  int64_t dec_chunk = 0;
+  size_t off_tasks = 0, off_items = 0, off_dec = 0, off_split = 0, off_part_o = 0, off_part_l = 0, bytes = 0;
 };
 
 FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
@@ -162,14 +183,35 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, 4);
   p.rt = 32 * (4 / p.hpw);
+  int64_t dec_keys = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (t[i].q_len <= 0) continue;
+    if (is_decode_task(t[i], p.group)) {
+      dec_keys += decode_visible(t[i]) * s->hkv;
+      continue;
+    }
     const size_t tiles = (t[i].q_len + p.rt - 1) / p.rt;
     p.n_items += tiles * (size_t)s->hkv * (size_t)(p.group / p.hpw);
   }
+  const int64_t per_item = (dec_keys + kDecTargetItems - 1) / kDecTargetItems;
+  p.dec_chunk = std::max<int64_t>(kDecMinChunk, (per_item + 127) / 128 * 128);
+  for (int32_t i = 0; i < n; ++i) {
+    if (t[i].q_len <= 0 || !is_decode_task(t[i], p.group)) continue;
+    const int64_t vis = decode_visible(t[i]);
+    const int64_t chunks = std::max<int64_t>(1, (vis + p.dec_chunk - 1) / p.dec_chunk);
+    p.n_dec_items += (size_t)chunks * s->hkv;
+    if (chunks > 1) {
+      p.n_split += s->hkv;
+      p.n_parts += (size_t)chunks * s->hkv;
+    }
+  }
   p.off_tasks = 0;
   p.off_items = align_up(sizeof(ca_task) * (size_t)n);
-  p.bytes = p.off_items + align_up(sizeof(ca::FwdItem) * p.n_items);
+  p.off_dec = p.off_items + align_up(sizeof(ca::FwdItem) * p.n_items);
+  p.off_split = p.off_dec + align_up(sizeof(ca::DecItem) * p.n_dec_items);
+  p.off_part_o = p.off_split + align_up(4 * sizeof(int32_t) * p.n_split);
+  p.off_part_l = p.off_part_o + align_up(sizeof(float) * p.n_parts * p.group * s->d);
+  p.bytes = p.off_part_l + align_up(sizeof(float) * p.n_parts * p.group);
   return p;
 }
 
@@ -183,7 +225,7 @@ void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const F
   tmp.reserve(p.n_items);
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& k = t[i];
-    if (k.q_len <= 0) continue;
+    if (k.q_len <= 0 || is_decode_task(k, p.group)) continue;
     const int64_t delta = k.q_pos0 - k.kv_pos0;
     for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
       const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
@@ -198,6 +240,44 @@ void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const F
   for (size_t i = 0; i < tmp.size(); ++i) items[i] = tmp[i].it;
 }
 
+// Decode items (longest chunk first) and the merge records of split tasks:
+// split[0..n) first staging slot, [n..2n) chunk count, [2n..3n) task,
+// [3n..4n) KV head.
+void build_decode_items(const ca_shape* s, const ca_task* t, int32_t n, const FwdPlan& p,
+                        std::vector<ca::DecItem>& items, std::vector<int32_t>& split) {
+  items.clear();
+  split.assign(4 * p.n_split, 0);
+  size_t rec = 0;
+  int32_t part = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const ca_task& k = t[i];
+    if (k.q_len <= 0 || !is_decode_task(k, p.group)) continue;
+    const int64_t vis = decode_visible(k);
+    const int64_t chunks = std::max<int64_t>(1, (vis + p.dec_chunk - 1) / p.dec_chunk);
+    for (int32_t g = 0; g < s->hkv; ++g) {
+      if (chunks > 1) {
+        split[rec] = part;
+        split[p.n_split + rec] = (int32_t)chunks;
+        split[2 * p.n_split + rec] = i;
+        split[3 * p.n_split + rec] = g;
+        ++rec;
+      }
+      for (int64_t c = 0; c < chunks; ++c) {
+        ca::DecItem it{};
+        it.task = i;
+        it.kv_head = g;
+        it.k_begin = (int32_t)(c * p.dec_chunk);
+        it.k_end = (int32_t)std::min<int64_t>(vis, (c + 1) * p.dec_chunk);
+        it.part = chunks > 1 ? part++ : -1;
+        items.push_back(it);
+      }
+    }
+  }
+  std::stable_sort(items.begin(), items.end(), [](const ca::DecItem& a, const ca::DecItem& b) {
+    return (a.k_end - a.k_begin) > (b.k_end - b.k_begin);
+  });
+}
+
 ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const void* Q, const void* K,
                        const void* V, void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
   ca_status st = check_shape(s);
@@ -205,36 +285,90 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const voi
   st = check_tasks(s, t, n);
   if (st != CA_OK) return st;
   const FwdPlan p = plan_forward(s, t, n);
-  if (p.n_items == 0) return CA_OK;
+  if (p.n_items == 0 && p.n_dec_items == 0) return CA_OK;
   if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
   if (!ws || ws_bytes < p.bytes)
     return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
-  if (p.n_items > 0x7fffffffu) return fail(CA_ERR_UNSUPPORTED, "too many work items");
+  if (p.n_items > 0x7fffffffu || p.n_dec_items > 0x7fffffffu || p.n_parts > 0x7fffffffu)
+    return fail(CA_ERR_UNSUPPORTED, "too many work items");
+  // 32-bit buffer offsets inside one task's context
+  for (int32_t i = 0; i < n; ++i)
+    if ((int64_t)t[i].kv_len * s->hkv * s->d * 2 >= (int64_t(1) << 31))
+      return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
   std::vector<ca::FwdItem> items;
   build_forward_items(s, t, n, p, items);
-  std::vector<char> host(p.bytes, 0);
+  std::vector<ca::DecItem> ditems;
+  std::vector<int32_t> split;
+  build_decode_items(s, t, n, p, ditems, split);
+  std::vector<char> host(p.off_part_o, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
-  std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
+  if (!items.empty()) std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
+  if (!ditems.empty()) std::memcpy(host.data() + p.off_dec, ditems.data(), sizeof(ca::DecItem) * ditems.size());
+  if (!split.empty()) std::memcpy(host.data() + p.off_split, split.data(), sizeof(int32_t) * split.size());
   hipStream_t hs = (hipStream_t)stream;
   st = upload(ws, host, hs);
   if (st != CA_OK) return st;
-  ca::FwdParams fp;
-  fp.Q = (const __bf16*)Q;
-  fp.K = (const __bf16*)K;
-  fp.V = (const __bf16*)V;
-  fp.O = O;
-  fp.LSE = LSE;
-  fp.tasks = (const ca_task*)((char*)ws + p.off_tasks);
-  fp.items = (const ca::FwdItem*)((char*)ws + p.off_items);
-  fp.n_items = (int32_t)items.size();
-  fp.hq = s->hq;
-  fp.hkv = s->hkv;
-  fp.group = p.group;
-  fp.hpw = p.hpw;
-  fp.scale_log2 = s->scale * 1.4426950408889634f;
-  fp.out_f32 = (s->flags & CA_OUT_F32) ? 1 : 0;
-  hipError_t e = ca::launch_forward(fp, s->d, hs);
-  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  char* w = (char*)ws;
+  const float scale_log2 = s->scale * 1.4426950408889634f;
+  const int out_f32 = (s->flags & CA_OUT_F32) ? 1 : 0;
+  if (!items.empty()) {
+    ca::FwdParams fp;
+    fp.Q = (const __bf16*)Q;
+    fp.K = (const __bf16*)K;
+    fp.V = (const __bf16*)V;
+    fp.O = O;
+    fp.LSE = LSE;
+    fp.tasks = (const ca_task*)(w + p.off_tasks);
+    fp.items = (const ca::FwdItem*)(w + p.off_items);
+    fp.n_items = (int32_t)items.size();
+    fp.hq = s->hq;
+    fp.hkv = s->hkv;
+    fp.group = p.group;
+    fp.hpw = p.hpw;
+    fp.scale_log2 = scale_log2;
+    fp.out_f32 = out_f32;
+    hipError_t e = ca::launch_forward(fp, s->d, hs);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
+  if (!ditems.empty()) {
+    ca::DecParams dp;
+    dp.Q = (const __bf16*)Q;
+    dp.K = (const __bf16*)K;
+    dp.V = (const __bf16*)V;
+    dp.O = O;
+    dp.LSE = LSE;
+    dp.part_O = (float*)(w + p.off_part_o);
+    dp.part_LSE = (float*)(w + p.off_part_l);
+    dp.tasks = (const ca_task*)(w + p.off_tasks);
+    dp.items = (const ca::DecItem*)(w + p.off_dec);
+    dp.n_items = (int32_t)ditems.size();
+    dp.hq = s->hq;
+    dp.hkv = s->hkv;
+    dp.group = p.group;
+    dp.scale_log2 = scale_log2;
+    dp.out_f32 = out_f32;
+    hipError_t e = ca::launch_decode(dp, s->d, hs);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (p.n_split > 0) {
+      ca::DecMergeParams mp;
+      const int32_t* sp = (const int32_t*)(w + p.off_split);
+      mp.part_O = dp.part_O;
+      mp.part_LSE = dp.part_LSE;
+      mp.first_part = sp;
+      mp.n_parts = sp + p.n_split;
+      mp.task_of = sp + 2 * p.n_split;
+      mp.head_of = sp + 3 * p.n_split;
+      mp.tasks = dp.tasks;
+      mp.O = O;
+      mp.LSE = LSE;
+      mp.n_split = (int32_t)p.n_split;
+      mp.hq = s->hq;
+      mp.group = p.group;
+      mp.out_f32 = out_f32;
+      e = ca::launch_decode_merge(mp, s->d, hs);
+      if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+    }
+  }
   return CA_OK;
 }
 

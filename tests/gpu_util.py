@@ -35,8 +35,11 @@ def announce(msg):
 
 
 def widen(t):
-    """bf16 / fp32 torch tensor (any device) -> float64 numpy."""
+    """bf16 / fp32 torch tensor (any device) -> float64 numpy (numpy passes
+    through as float64)."""
     import torch
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return oracle.bf16_bits_to_f64(t.view(torch.int16).numpy())

@@ -162,3 +162,22 @@ def test_probe_mask_parity_small():
     err = np.abs(o - expect[:, None, None]).max(axis=(1, 2))
     assert np.all(err < 0.25 / (pos + 1))
     assert np.allclose(widen(LSE), np.log(pos + 1.0)[:, None], atol=1e-5)
+
+
+@pytest.mark.parametrize("hq,hkv,d,out_f32", [(16, 2, 128, False), (8, 1, 64, True), (64, 2, 128, False)])
+def test_decode_gqa_variants(hq, hkv, d, out_f32):
+    """Single-token tasks: G <= 16 uses the split-KV decode kernel (chunked
+    and unchunked), G = 32 falls back to the tiled kernel; one row sees no
+    key and one sees a prefix only."""
+    announce("decode variants hq%d hkv%d d%d f32=%s" % (hq, hkv, d, out_f32))
+    ctx = [5000, 700, 1, 300, 64]
+    tasks, off = [], 0
+    for b, c in enumerate(ctx):
+        tasks.append((b, off, b, 1, c, c - 1, 0))
+        off += c
+    tasks.append((len(ctx), 0, len(ctx), 1, 100, 10, 50))       # sees no key (q_pos0 < kv_pos0)
+    tasks.append((len(ctx) + 1, 0, len(ctx) + 1, 1, 900, 400, 0))  # sees keys 0..400 only
+    tasks = np.array(tasks)
+    n = len(tasks)
+    O, LSE, Or, Lr = run_case(tasks, hq, hkv, d, n, off, n, 650 + hq + d, out_f32=out_f32)
+    check_forward(O, LSE, Or, Lr, "decode hq%d hkv%d d%d" % (hq, hkv, d))
