@@ -372,6 +372,134 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const voi
   return CA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Backward plan
+// ---------------------------------------------------------------------------
+//
+// dQ rows and dK/dV rows may be shared by several tasks (ring partials share
+// query shards and KV blocks).  Tasks are split into passes whose row ranges
+// are pairwise disjoint (greedy interval partitioning), so a pass can write
+// without atomics; with more than one pass the gradients accumulate in fp32
+// workspace buffers and are converted at the end.  With one pass the kernels
+// store bf16 directly.
+
+constexpr int kBwdKeyTile = 128;
+
+// pass index of every task for intervals [start, start + len); len == 0 tasks
+// get pass 0.  Returns the number of passes.
+int partition_passes(const std::vector<std::pair<int64_t, int64_t>>& iv, std::vector<int>& pass_of) {
+  const size_t n = iv.size();
+  pass_of.assign(n, 0);
+  std::vector<size_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return iv[a].first < iv[b].first; });
+  std::vector<int64_t> pass_end;  // end of the last interval in each pass
+  for (size_t k : order) {
+    if (iv[k].second <= 0) continue;
+    int chosen = -1;
+    for (size_t q = 0; q < pass_end.size(); ++q)
+      if (pass_end[q] <= iv[k].first) { chosen = (int)q; break; }
+    if (chosen < 0) {
+      chosen = (int)pass_end.size();
+      pass_end.push_back(0);
+    }
+    pass_end[chosen] = iv[k].first + iv[k].second;
+    pass_of[k] = chosen;
+  }
+  return std::max<int>(1, (int)pass_end.size());
+}
+
+struct BwdPlan {
+  int group = 1, hpw = 1, rt = 128;
+  int q_passes = 1, kv_passes = 1;
+  std::vector<int> q_pass_of, kv_pass_of;
+  bool q_full = false, kv_full = false;          // every row covered by some task
+  size_t n_qitems = 0, n_kvitems = 0;
+  size_t off_tasks = 0, off_qitems = 0, off_kvitems = 0, off_d = 0, off_dq = 0, off_dk = 0, off_dv = 0, bytes = 0;
+};
+
+BwdPlan plan_backward(const ca_shape* s, const ca_task* t, int32_t n) {
+  BwdPlan p;
+  p.group = s->hq / s->hkv;
+  p.hpw = gcd_int(p.group, 4);
+  p.rt = 32 * (4 / p.hpw);
+  std::vector<std::pair<int64_t, int64_t>> qiv(n), kviv(n);
+  int64_t q_cover = 0, kv_cover = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const bool active = t[i].q_len > 0;
+    qiv[i] = {t[i].q_off, active ? t[i].q_len : 0};
+    kviv[i] = {t[i].kv_off, active ? t[i].kv_len : 0};
+    if (active) {
+      p.n_qitems += (size_t)((t[i].q_len + p.rt - 1) / p.rt) * s->hkv * (p.group / p.hpw);
+      p.n_kvitems += (size_t)((t[i].kv_len + kBwdKeyTile - 1) / kBwdKeyTile) * s->hkv;
+      q_cover += t[i].q_len;
+      kv_cover += t[i].kv_len;
+    }
+  }
+  p.q_passes = partition_passes(qiv, p.q_pass_of);
+  p.kv_passes = partition_passes(kviv, p.kv_pass_of);
+  p.q_full = p.q_passes == 1 && q_cover == s->q_rows;
+  p.kv_full = p.kv_passes == 1 && kv_cover == s->kv_rows;
+  p.off_tasks = 0;
+  p.off_qitems = align_up(sizeof(ca_task) * (size_t)n);
+  p.off_kvitems = p.off_qitems + align_up(sizeof(ca::FwdItem) * p.n_qitems);
+  p.off_d = p.off_kvitems + align_up(sizeof(ca::BwdItem) * p.n_kvitems);
+  p.off_dq = p.off_d + align_up(sizeof(float) * (size_t)s->o_rows * s->hq);
+  const size_t dq_bytes = p.q_passes > 1 ? sizeof(float) * (size_t)s->q_rows * s->hq * s->d : 0;
+  const size_t dkv_bytes = p.kv_passes > 1 ? sizeof(float) * (size_t)s->kv_rows * s->hkv * s->d : 0;
+  p.off_dk = p.off_dq + align_up(dq_bytes);
+  p.off_dv = p.off_dk + align_up(dkv_bytes);
+  p.bytes = p.off_dv + align_up(dkv_bytes);
+  return p;
+}
+
+// Items of every pass, pass-major, each pass longest first; pass_begin has
+// passes + 1 entries.
+void build_backward_items(const ca_shape* s, const ca_task* t, int32_t n, const BwdPlan& p,
+                          std::vector<ca::FwdItem>& qitems, std::vector<size_t>& q_begin,
+                          std::vector<ca::BwdItem>& kvitems, std::vector<size_t>& kv_begin) {
+  qitems.clear();
+  kvitems.clear();
+  q_begin.assign(1, 0);
+  kv_begin.assign(1, 0);
+  for (int pass = 0; pass < p.q_passes; ++pass) {
+    struct K { int64_t c; ca::FwdItem it; };
+    std::vector<K> tmp;
+    for (int32_t i = 0; i < n; ++i) {
+      const ca_task& k = t[i];
+      if (k.q_len <= 0 || p.q_pass_of[i] != pass) continue;
+      const int64_t delta = k.q_pos0 - k.kv_pos0;
+      for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
+        const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
+        const int64_t cost = range_pairs(r0, r1, delta, k.kv_len) * p.hpw + (r1 - r0 + 1) * 64;
+        for (int32_t g = 0; g < s->hkv; ++g)
+          for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
+      }
+    }
+    std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
+    for (auto& k : tmp) qitems.push_back(k.it);
+    q_begin.push_back(qitems.size());
+  }
+  for (int pass = 0; pass < p.kv_passes; ++pass) {
+    struct K { int64_t c; ca::BwdItem it; };
+    std::vector<K> tmp;
+    for (int32_t i = 0; i < n; ++i) {
+      const ca_task& k = t[i];
+      if (k.q_len <= 0 || p.kv_pass_of[i] != pass) continue;
+      const int64_t delta = k.q_pos0 - k.kv_pos0;
+      for (int32_t k0 = 0; k0 < k.kv_len; k0 += kBwdKeyTile) {
+        // rows that see key k0: i >= k0 - delta
+        const int64_t r_lo = std::min<int64_t>(k.q_len, std::max<int64_t>(0, k0 - delta));
+        const int64_t cost = (k.q_len - r_lo) * p.group * kBwdKeyTile + 64 * kBwdKeyTile;
+        for (int32_t g = 0; g < s->hkv; ++g) tmp.push_back({cost, {i, g, k0, 0}});
+      }
+    }
+    std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
+    for (auto& k : tmp) kvitems.push_back(k.it);
+    kv_begin.push_back(kvitems.size());
+  }
+}
+
 bool varlen_to_tasks(const int32_t* cu, int32_t n_docs, std::vector<ca_task>& out) {
   if (n_docs < 0 || (n_docs > 0 && !cu)) return false;
   if (n_docs > 0 && cu[0] != 0) return false;
@@ -440,18 +568,109 @@ ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows, const
 }
 
 size_t ca_backward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks) {
-  (void)shape;
-  (void)tasks_host;
-  (void)n_tasks;
-  return 0;
+  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK) return 0;
+  return plan_backward(shape, tasks_host, n_tasks).bytes;
 }
 
-ca_status ca_backward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks, const void* Q,
-                      const void* K, const void* V, const void* O, const void* dO, const float* LSE,
-                      void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
-  (void)shape; (void)tasks_host; (void)n_tasks; (void)Q; (void)K; (void)V; (void)O; (void)dO;
-  (void)LSE; (void)dQ; (void)dK; (void)dV; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(CA_ERR_UNSUPPORTED, "backward not built yet");
+ca_status ca_backward(const ca_shape* s, const ca_task* t, int32_t n, const void* Q, const void* K,
+                      const void* V, const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
+                      void* dV, void* ws, size_t ws_bytes, void* stream) {
+  ca_status st = check_shape(s);
+  if (st != CA_OK) return st;
+  if (s->flags & CA_OUT_F32) return fail(CA_ERR_INVALID, "CA_OUT_F32 is a forward/merge flag");
+  st = check_tasks(s, t, n);
+  if (st != CA_OK) return st;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return fail(CA_ERR_INVALID, "NULL tensor pointer");
+  const BwdPlan p = plan_backward(s, t, n);
+  if (!ws || ws_bytes < p.bytes)
+    return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
+  if (p.n_qitems > 0x7fffffffu || p.n_kvitems > 0x7fffffffu) return fail(CA_ERR_UNSUPPORTED, "too many work items");
+  for (int32_t i = 0; i < n; ++i)
+    if ((int64_t)t[i].kv_len * s->hkv * s->d * 2 >= (int64_t(1) << 31))
+      return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
+  std::vector<ca::FwdItem> qitems;
+  std::vector<ca::BwdItem> kvitems;
+  std::vector<size_t> q_begin, kv_begin;
+  build_backward_items(s, t, n, p, qitems, q_begin, kvitems, kv_begin);
+  std::vector<char> host(p.off_d, 0);
+  std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
+  if (!qitems.empty()) std::memcpy(host.data() + p.off_qitems, qitems.data(), sizeof(ca::FwdItem) * qitems.size());
+  if (!kvitems.empty()) std::memcpy(host.data() + p.off_kvitems, kvitems.data(), sizeof(ca::BwdItem) * kvitems.size());
+  hipStream_t hs = (hipStream_t)stream;
+  st = upload(ws, host, hs);
+  if (st != CA_OK) return st;
+  char* w = (char*)ws;
+  float* Dv = (float*)(w + p.off_d);
+  const int64_t q_elems = s->q_rows * s->hq * (int64_t)s->d;
+  const int64_t kv_elems = s->kv_rows * s->hkv * (int64_t)s->d;
+  hipError_t e = ca::launch_bwd_prep((const __bf16*)O, (const __bf16*)dO, Dv, s->o_rows * (int64_t)s->hq, s->d, hs);
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  const bool acc_q = p.q_passes > 1, acc_kv = p.kv_passes > 1;
+  // rows no kernel writes must read as zero
+  if (acc_q) e = ca::launch_zero_f32((float*)(w + p.off_dq), q_elems, hs);
+  else if (!p.q_full) e = ca::launch_zero_bf16((__bf16*)dQ, q_elems, hs);
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+  if (acc_kv) {
+    e = ca::launch_zero_f32((float*)(w + p.off_dk), kv_elems, hs);
+    if (e == hipSuccess) e = ca::launch_zero_f32((float*)(w + p.off_dv), kv_elems, hs);
+  } else if (!p.kv_full) {
+    e = ca::launch_zero_bf16((__bf16*)dK, kv_elems, hs);
+    if (e == hipSuccess) e = ca::launch_zero_bf16((__bf16*)dV, kv_elems, hs);
+  }
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+
+  ca::BwdParams bp;
+  bp.Q = (const __bf16*)Q;
+  bp.K = (const __bf16*)K;
+  bp.V = (const __bf16*)V;
+  bp.dO = (const __bf16*)dO;
+  bp.LSE = LSE;
+  bp.Dvec = Dv;
+  bp.dQ = (__bf16*)dQ;
+  bp.dK = (__bf16*)dK;
+  bp.dV = (__bf16*)dV;
+  bp.dQacc = (float*)(w + p.off_dq);
+  bp.dKacc = (float*)(w + p.off_dk);
+  bp.dVacc = (float*)(w + p.off_dv);
+  bp.tasks = (const ca_task*)(w + p.off_tasks);
+  bp.hq = s->hq;
+  bp.hkv = s->hkv;
+  bp.group = p.group;
+  bp.hpw = p.hpw;
+  bp.scale = s->scale;
+  bp.scale_log2 = s->scale * 1.4426950408889634f;
+  const ca::FwdItem* qi = (const ca::FwdItem*)(w + p.off_qitems);
+  const ca::BwdItem* ki = (const ca::BwdItem*)(w + p.off_kvitems);
+  for (int pass = 0; pass < p.q_passes; ++pass) {
+    ca::BwdParams pp = bp;
+    pp.accumulate = acc_q ? 1 : 0;
+    pp.qitems = qi + q_begin[pass];
+    pp.n_qitems = (int32_t)(q_begin[pass + 1] - q_begin[pass]);
+    pp.items = nullptr;
+    pp.n_items = 0;
+    e = ca::launch_bwd_q(pp, s->d, hs);
+    if (e != hipSuccess) return hip_fail(e, "dQ launch");
+  }
+  for (int pass = 0; pass < p.kv_passes; ++pass) {
+    ca::BwdParams pp = bp;
+    pp.accumulate = acc_kv ? 1 : 0;
+    pp.items = ki + kv_begin[pass];
+    pp.n_items = (int32_t)(kv_begin[pass + 1] - kv_begin[pass]);
+    pp.qitems = nullptr;
+    pp.n_qitems = 0;
+    e = ca::launch_bwd_kv(pp, s->d, hs);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  }
+  if (acc_q) {
+    e = ca::launch_f32_to_bf16(bp.dQacc, (__bf16*)dQ, q_elems, hs);
+    if (e != hipSuccess) return hip_fail(e, "dQ conversion");
+  }
+  if (acc_kv) {
+    e = ca::launch_f32_to_bf16(bp.dKacc, (__bf16*)dK, kv_elems, hs);
+    if (e == hipSuccess) e = ca::launch_f32_to_bf16(bp.dVacc, (__bf16*)dV, kv_elems, hs);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV conversion");
+  }
+  return CA_OK;
 }
 
 int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks) {

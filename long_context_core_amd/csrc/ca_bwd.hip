@@ -1,0 +1,469 @@
+// Backward of core attention over a CA-task table (gfx950), without atomics.
+//
+// The pages fix only that the backward recomputes the attention
+// probabilities from the per-row statistics saved by the forward instead of
+// storing them ("Efficient Long-context Language Model Training by Core
+// Attention Disaggregation", Sections 3.2 and 3.4, Property 1).  With
+// P = exp(scale S - LSE) and D_i = <dO_i, O_i>:
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = scale dS^T Q,
+//   dQ = scale dS K.
+//
+//   bwd_prep_kernel  D_i = rowsum(dO_i o O_i)                      (HBM-bound)
+//   bwd_kv_kernel    K/V-stationary: a workgroup owns 128 context rows of one
+//                    KV head (32 per wave, K and V held as MFMA operands in
+//                    registers) and sweeps every query tile and every query
+//                    head of the group that sees them; dK and dV accumulate in
+//                    registers across heads and tiles.  Per 32x32 block:
+//                      S = Q K^T, dP = dO V^T          (lane = key)
+//                      dV^T += dO^T P,  dK^T += Q^T dS (dO^T, Q^T by LDS transpose reads)
+//   bwd_q_kernel     Q-stationary, shaped like the forward: S^T = K Q^T,
+//                    dP^T = V dO^T, dQ^T += K^T dS^T (K^T by transpose reads).
+// Rows are written once per pass (read-modify-write in fp32 when several
+// tasks share rows), so results are deterministic.
+
+#include "ca_internal.h"
+#include "ca_kernel_util.h"
+
+namespace ca {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+
+// LSE (natural log) -> log2 units; an empty row (-inf) becomes +inf so that
+// exp2(s - lse) = 0 for every key.
+__device__ __forceinline__ float lse_log2(float lse) {
+  return lse == -INFINITY ? INFINITY : lse * kLog2e;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO[i][h][c] * O[i][h][c], for every output row and head.
+// 16 lanes per (row, head), 8 channels each (D = 128) or 4 (D = 64).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* O, const __bf16* dO, float* Dv, int64_t n_pairs) {
+  constexpr int EPL = D / 16;
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (pair < n_pairs) {
+    const __bf16* o = O + pair * D + sub * EPL;
+    const __bf16* g = dO + pair * D + sub * EPL;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc = fmaf((float)o[i], (float)g[i], acc);
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (pair < n_pairs && sub == 0) Dv[pair] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (task, KV head, 128 context rows).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
+  constexpr int BQ = 32;            // query rows per step
+  constexpr int QS = D + 16;        // LDS row stride (elements) of the Q / dO tiles
+  constexpr int NKS = D / 16;       // 16-channel reduction steps
+  constexpr int NCB = D / 32;       // 32-channel output blocks
+  constexpr int CH = D / 8;         // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) __bf16 lds_q[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_do[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float lds_d[2][BQ];
+
+  const BwdItem it = p.items[blockIdx.x];
+  const ca_task t = p.tasks[it.task];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t delta = t.q_pos0 - t.kv_pos0;
+  const int G = p.group;
+  const int kw0 = it.key0 + 32 * wave;           // first (task-relative) key of this wave
+  const int my_key = kw0 + l32;
+  const bool key_ok = my_key < t.kv_len;
+
+  // Stationary operands: K and V rows of this lane's key (B of S = Q K^T and of dP = dO V^T).
+  const int64_t kv_stride = (int64_t)p.hkv * D;
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const int64_t roff = (t.kv_off + (key_ok ? my_key : 0)) * kv_stride + it.kv_head * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      kf[s] = key_ok ? *(const bf16x8*)(p.K + roff + 16 * s) : bf16x8_zero();
+      vf[s] = key_ok ? *(const bf16x8*)(p.V + roff + 16 * s) : bf16x8_zero();
+    }
+  }
+  f32x16 dk_acc[NCB], dv_acc[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    dk_acc[c] = f32x16_zero();
+    dv_acc[c] = f32x16_zero();
+  }
+
+  // Query rows that see at least one key of the workgroup: i + delta >= key0.
+  const int wg_keys = min(128, t.kv_len - it.key0);
+  const int r_lo = (int)clamp64((int64_t)it.key0 - delta, 0, t.q_len);
+  const int r_first = (r_lo / BQ) * BQ;
+  const int n_rt = (t.q_len - r_first + BQ - 1) / BQ;
+  const int n_steps = (wg_keys > 0 && t.q_len > r_lo) ? n_rt * G : 0;
+
+  // Tile loads: Q and dO rows (32 x D bf16 each), LSE and D values.
+  const int ld_row = tid / CH;                    // 0..(256/CH - 1)
+  const int ld_chunk = tid % CH;
+  constexpr int RPP = 256 / CH;
+  constexpr int PASSES = BQ / RPP;
+  const int64_t q_stride = (int64_t)p.hq * D;
+  uint4 qreg[PASSES], oreg[PASSES];
+  float lse_reg = 0.f, d_reg = 0.f;
+  auto gload = [&](int step) {
+    const int r0 = r_first + (step / G) * BQ;
+    const int head = it.kv_head * G + (step % G);
+#pragma unroll
+    for (int r = 0; r < PASSES; ++r) {
+      const int row = r0 + r * RPP + ld_row;
+      if (row < t.q_len) {
+        qreg[r] = *(const uint4*)(p.Q + (t.q_off + row) * q_stride + head * D + ld_chunk * 8);
+        oreg[r] = *(const uint4*)(p.dO + (t.o_off + row) * q_stride + head * D + ld_chunk * 8);
+      } else {
+        qreg[r] = make_uint4(0, 0, 0, 0);
+        oreg[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < BQ) {
+      const int row = r0 + tid;
+      if (row < t.q_len) {
+        lse_reg = lse_log2(p.LSE[(t.o_off + row) * p.hq + head]);
+        d_reg = p.Dvec[(t.o_off + row) * p.hq + head];
+      } else {
+        lse_reg = INFINITY;                      // invalid row: P = 0
+        d_reg = 0.f;
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PASSES; ++r) {
+      const int row = r * RPP + ld_row;
+      *(uint4*)(&lds_q[buf][row * QS + ld_chunk * 8]) = qreg[r];
+      *(uint4*)(&lds_do[buf][row * QS + ld_chunk * 8]) = oreg[r];
+    }
+    if (tid < BQ) {
+      lds_lse[buf][tid] = lse_reg;
+      lds_d[buf][tid] = d_reg;
+    }
+  };
+
+  // Operand offsets.  Row-major A operands (Q, dO: m = query l32, k = 16 s + 8 hh);
+  // transpose reads for Q^T and dO^T as in the forward's V^T.
+  const int a_off = l32 * QS + 8 * hh;
+  const int g16 = lane >> 4;
+  const int j16 = lane & 15;
+  const int t_off = ((j16 >> 2) + 4 * hh) * QS + 16 * (g16 & 1) + 4 * (j16 & 3);
+
+  if (n_steps > 0) gload(0);
+  for (int step = 0; step < n_steps; ++step) {
+    const int buf = step & 1;
+    swrite(buf);
+    __syncthreads();
+    if (step + 1 < n_steps) gload(step + 1);
+    const int r0 = r_first + (step / G) * BQ;
+    // Skip blocks where no row of the step sees any key of this wave.
+    if ((int64_t)r0 + BQ - 1 + delta < kw0) continue;
+
+    // S = Q K^T and dP = dO V^T (lane = key l32; rows m = 8 (j/4) + 4 hh + j%4)
+    f32x16 s_acc = f32x16_zero(), dp_acc = f32x16_zero();
+    const __bf16* qa = &lds_q[buf][a_off];
+    const __bf16* oa = &lds_do[buf][a_off];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qa + 16 * s), kf[s], s_acc, 0, 0, 0);
+      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(oa + 16 * s), vf[s], dp_acc, 0, 0, 0);
+    }
+    // P = exp2(scale log2e S - LSE2), dS = P (dP - D); masked pairs: 0.
+    const bool need_mask = (int64_t)r0 + delta < (int64_t)kw0 + 31;
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 l4 = *(const float4*)(&lds_lse[buf][8 * q4 + 4 * hh]);
+      const float4 d4 = *(const float4*)(&lds_d[buf][8 * q4 + 4 * hh]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int reg = 4 * q4 + j;
+        float pv = exp2_fast(fmaf(s_acc[reg], p.scale_log2, -lv[j]));
+        if (need_mask) {
+          const int64_t row = (int64_t)r0 + 8 * q4 + 4 * hh + j;
+          pv = ((int64_t)my_key <= row + delta) ? pv : 0.f;
+        }
+        const float ds = pv * (dp_acc[reg] - dv[j]);
+        pf[reg >> 3][reg & 7] = (__bf16)pv;
+        dsf[reg >> 3][reg & 7] = (__bf16)ds;
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, reduction over the 32 rows
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const __bf16* o0 = &lds_do[buf][t_off + (16 * half) * QS + 32 * c];
+        const bf16x8 dot = concat_bf16x4(ds_read_tr16(o0), ds_read_tr16(o0 + 8 * QS));
+        dv_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pf[half], dv_acc[c], 0, 0, 0);
+        const __bf16* q0 = &lds_q[buf][t_off + (16 * half) * QS + 32 * c];
+        const bf16x8 qt = concat_bf16x4(ds_read_tr16(q0), ds_read_tr16(q0 + 8 * QS));
+        dk_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf[half], dk_acc[c], 0, 0, 0);
+      }
+    }
+  }
+
+  // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
+  if (!key_ok) return;
+  const int64_t base = (t.kv_off + my_key) * kv_stride + it.kv_head * D;
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ch = c * 32 + 8 * q4 + 4 * hh;
+      float k4[4], v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        k4[j] = dk_acc[c][4 * q4 + j] * p.scale;
+        v4[j] = dv_acc[c][4 * q4 + j];
+      }
+      if (p.accumulate) {
+        float* ka = p.dKacc + base + ch;
+        float* va = p.dVacc + base + ch;
+        float4 ko = *(float4*)ka, vo = *(float4*)va;
+        *(float4*)ka = make_float4(ko.x + k4[0], ko.y + k4[1], ko.z + k4[2], ko.w + k4[3]);
+        *(float4*)va = make_float4(vo.x + v4[0], vo.y + v4[1], vo.z + v4[2], vo.w + v4[3]);
+      } else {
+        bf16x4 kb, vb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kb[j] = (__bf16)k4[j];
+          vb[j] = (__bf16)v4[j];
+        }
+        *(bf16x4*)(p.dK + base + ch) = kb;
+        *(bf16x4*)(p.dV + base + ch) = vb;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: work items as in the forward (hpw heads x 4/hpw blocks of 32 rows).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
+  constexpr int BN = 64;
+  constexpr int KS = D + 16;      // K is read row-wise and by transpose reads
+  constexpr int VS = D + 8;       // V is read row-wise only
+  constexpr int NCB = D / 32;
+  constexpr int NKS = D / 16;
+  constexpr int CH = D / 8;
+  constexpr int RPP = 256 / CH;
+  constexpr int PASSES = BN / RPP;
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][BN * VS];
+
+  const FwdItem it = p.qitems[blockIdx.x];
+  const ca_task t = p.tasks[it.task];
+  const int tid = threadIdx.x;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int hpw = p.hpw;
+  const int head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
+  const int wrow0 = it.row0 + (wave_u / hpw) * 32;
+  const int64_t delta = t.q_pos0 - t.kv_pos0;
+  const int kv_len = t.kv_len;
+  const int rt = 32 * (4 / hpw);
+  const int wg_last = min(it.row0 + rt, t.q_len) - 1;
+  const int kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
+  const int w_last = min(wrow0 + 32, t.q_len) - 1;
+  const int w_kv_hi = (w_last < wrow0) ? 0 : (int)clamp64((int64_t)w_last + delta + 1, 0, kv_len);
+  const int w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
+
+  const int qrow = wrow0 + l32;
+  const bool qvalid = qrow < t.q_len;
+  const int64_t q_stride = (int64_t)p.hq * D;
+  bf16x8 qf[NKS], of[NKS];
+  {
+    const __bf16* qp = p.Q + (t.q_off + qrow) * q_stride + head * D + 8 * hh;
+    const __bf16* op = p.dO + (t.o_off + qrow) * q_stride + head * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      qf[s] = qvalid ? *(const bf16x8*)(qp + 16 * s) : bf16x8_zero();
+      of[s] = qvalid ? *(const bf16x8*)(op + 16 * s) : bf16x8_zero();
+    }
+  }
+  const float lse2 = qvalid ? lse_log2(p.LSE[(t.o_off + qrow) * p.hq + head]) : INFINITY;
+  const float dval = qvalid ? p.Dvec[(t.o_off + qrow) * p.hq + head] : 0.f;
+
+  f32x16 dq_acc[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) dq_acc[c] = f32x16_zero();
+
+  const int n_tiles = (kv_hi + BN - 1) / BN;
+  const int64_t kv_stride = (int64_t)p.hkv * D;
+  const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.K + t.kv_off * kv_stride + it.kv_head * D, (uint32_t)kv_hi * row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.V + t.kv_off * kv_stride + it.kv_head * D, (uint32_t)kv_hi * row_bytes);
+  const int ld_row = tid / CH;
+  const int ld_chunk = tid % CH;
+  const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
+  uint4 kreg[PASSES], vreg[PASSES];
+  auto gload = [&](int tile) {
+    const uint32_t soff = (uint32_t)tile * BN * row_bytes;
+#pragma unroll
+    for (int r = 0; r < PASSES; ++r) {
+      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
+      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PASSES; ++r) {
+      const int row = r * RPP + ld_row;
+      *(uint4*)(&lds_k[buf][row * KS + ld_chunk * 8]) = kreg[r];
+      *(uint4*)(&lds_v[buf][row * VS + ld_chunk * 8]) = vreg[r];
+    }
+  };
+  const int k_row_off = l32 * KS + 8 * hh;       // A of S^T  (key l32, ch 16 s + 8 hh)
+  const int v_row_off = l32 * VS + 8 * hh;       // A of dP^T (key l32, ch 16 s + 8 hh)
+  const int g16 = lane >> 4;
+  const int j16 = lane & 15;
+  const int kt_off = ((j16 >> 2) + 4 * hh) * KS + 16 * (g16 & 1) + 4 * (j16 & 3);
+
+  if (n_tiles > 0) gload(0);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    swrite(buf);
+    __syncthreads();
+    if (tile + 1 < n_tiles) gload(tile + 1);
+    const int k0 = tile * BN;
+    if (k0 >= w_kv_hi) continue;
+    f32x16 s_acc[2], dp_acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s_acc[mb] = f32x16_zero();
+      dp_acc[mb] = f32x16_zero();
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 ka = *(const bf16x8*)(&lds_k[buf][k_row_off + mb * 32 * KS + 16 * s]);
+        s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s_acc[mb], 0, 0, 0);
+        const bf16x8 va = *(const bf16x8*)(&lds_v[buf][v_row_off + mb * 32 * VS + 16 * s]);
+        dp_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[s], dp_acc[mb], 0, 0, 0);
+      }
+    }
+    const bool need_mask = tile >= w_full;
+    const int lim = (int)clamp64(min((int64_t)qrow + delta, (int64_t)kv_len - 1) - k0, -1, BN);
+    bf16x8 dsf[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float pv = exp2_fast(fmaf(s_acc[mb][j], p.scale_log2, -lse2));
+        if (need_mask) {
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          pv = (r <= lim) ? pv : 0.f;
+        }
+        dsf[mb][j >> 3][j & 7] = (__bf16)(pv * (dp_acc[mb][j] - dval));
+      }
+    // dQ^T += K^T dS^T (K^T through transpose reads, keys permuted like dS^T)
+    const __bf16* kl = &lds_k[buf][kt_off];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kb = mb * 32 + 16 * half;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+          const __bf16* a0 = kl + kb * KS + c * 32;
+          const bf16x8 kt = concat_bf16x4(ds_read_tr16(a0), ds_read_tr16(a0 + 8 * KS));
+          dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[mb][half], dq_acc[c], 0, 0, 0);
+        }
+      }
+  }
+
+  if (!qvalid) return;
+  const int64_t base = (t.q_off + qrow) * q_stride + head * D;
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ch = c * 32 + 8 * q4 + 4 * hh;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = dq_acc[c][4 * q4 + j] * p.scale;
+      if (p.accumulate) {
+        float* a = p.dQacc + base + ch;
+        const float4 o = *(float4*)a;
+        *(float4*)a = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+      } else {
+        bf16x4 b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = (__bf16)v[j];
+        *(bf16x4*)(p.dQ + base + ch) = b;
+      }
+    }
+  }
+}
+
+__global__ void f32_to_bf16_kernel(const float* src, __bf16* dst, int64_t n) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 + 3 < n) {
+    const float4 v = *(const float4*)(src + i4);
+    bf16x4 b;
+    b[0] = (__bf16)v.x; b[1] = (__bf16)v.y; b[2] = (__bf16)v.z; b[3] = (__bf16)v.w;
+    *(bf16x4*)(dst + i4) = b;
+  } else {
+    for (int64_t i = i4; i < n; ++i) dst[i] = (__bf16)src[i];
+  }
+}
+
+hipError_t launch_bwd_prep(const __bf16* O, const __bf16* dO, float* Dv, int64_t n_pairs, int d, hipStream_t s) {
+  if (n_pairs <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n_pairs * 16 + 255) / 256);
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(blocks), dim3(256), 0, s, O, dO, Dv, n_pairs);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(blocks), dim3(256), 0, s, O, dO, Dv, n_pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const BwdParams& p, int d, hipStream_t s) {
+  if (p.n_items <= 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_kv_kernel<128>, dim3(p.n_items), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_kv_kernel<64>, dim3(p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const BwdParams& p, int d, hipStream_t s) {
+  if (p.n_qitems <= 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_q_kernel<128>, dim3(p.n_qitems), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_q_kernel<64>, dim3(p.n_qitems), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* src, __bf16* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n / 4 + 256) / 256);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace ca

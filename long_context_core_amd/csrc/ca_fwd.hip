@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     if (__any(m_tile > m2 + kRescaleLog2)) {
       keep_branch();
       const float m_new = fmaxf(m2, m_tile);
-      const float alpha = exp2_fast(m2 - m_new);   // 0 when m2 = -inf
+      const float alpha = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - m_new);   // rows still empty: acc is 0
       lsum *= alpha;
 #pragma unroll
       for (int c = 0; c < NCB; ++c)

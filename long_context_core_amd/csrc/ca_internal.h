@@ -31,7 +31,7 @@ struct DecItem {
   int32_t pad[3];
 };
 
-// Backward work item: one tile of 64 context rows of a task for one KV head.
+// Backward work item (dK/dV kernel): 128 context rows of a task, one KV head.
 struct BwdItem {
   int32_t task;
   int32_t kv_head;
@@ -99,21 +99,24 @@ struct BwdParams {
   const __bf16* Q;
   const __bf16* K;
   const __bf16* V;
-  const __bf16* O;
   const __bf16* dO;
   const float* LSE;
-  float* Dvec;        // [o_rows][hq] rowsum(dO * O)
-  float* dQacc;       // [q_rows][hq][d] fp32
+  const float* Dvec;  // [o_rows][hq] rowsum(dO * O)
   __bf16* dQ;
   __bf16* dK;
   __bf16* dV;
+  float* dQacc;       // [q_rows][hq][d] fp32, used when accumulate != 0 (dQ kernel)
+  float* dKacc;       // [kv_rows][hkv][d] fp32, used when accumulate != 0 (dK/dV kernel)
+  float* dVacc;
   const ca_task* tasks;
-  const BwdItem* items;
+  const BwdItem* items;   // dK/dV kernel
   int32_t n_items;
-  int32_t hq, hkv, group;
+  const FwdItem* qitems;  // dQ kernel
+  int32_t n_qitems;
+  int32_t hq, hkv, group, hpw;
   float scale;
   float scale_log2;
-  int64_t q_rows, kv_rows, o_rows;
+  int32_t accumulate;
 };
 
 // Kernel launchers (defined in the .hip files).
@@ -121,7 +124,10 @@ hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int d, hipStream_t s);
 hipError_t launch_decode_merge(const DecMergeParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
-hipError_t launch_backward(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_prep(const __bf16* O, const __bf16* dO, float* Dv, int64_t n_pairs, int d, hipStream_t s);
+hipError_t launch_bwd_kv(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_q(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* src, __bf16* dst, int64_t n, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_zero_bf16(__bf16* p, int64_t n, hipStream_t s);
 

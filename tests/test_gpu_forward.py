@@ -181,3 +181,14 @@ def test_decode_gqa_variants(hq, hkv, d, out_f32):
     n = len(tasks)
     O, LSE, Or, Lr = run_case(tasks, hq, hkv, d, n, off, n, 650 + hq + d, out_f32=out_f32)
     check_forward(O, LSE, Or, Lr, "decode hq%d hkv%d d%d" % (hq, hkv, d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rows_without_keys_next_to_rows_with_keys(d):
+    """Context blocks that start after the first queries (kv_pos0 > q_pos0):
+    in one 32-row block some rows see no key while others do, so the
+    running-max update must leave the empty rows at O = 0, LSE = -inf."""
+    announce("forward partially empty row blocks d%d" % d)
+    tasks = np.array([(0, 0, 0, 40, 50, 0, 30), (40, 50, 40, 70, 100, 5, 60), (110, 150, 110, 33, 64, 0, 31)])
+    O, LSE, Or, Lr = run_case(tasks, 16, 2, d, 143, 214, 143, 660 + d)
+    check_forward(O, LSE, Or, Lr, "partially-empty d%d" % d)
