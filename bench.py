@@ -59,7 +59,7 @@ def traffic_for(kernel_file, workload):
 
 
 def cpu_baseline(w, Q, K, V, seconds_hint):
-    """The oracle as it stands, on a bounded sample: 256 random query rows of
+    """The oracle as it stands, on a bounded sample: 1,024 random query rows of
     the workload's largest task, all query heads."""
     import oracle
     try:
@@ -70,7 +70,7 @@ def cpu_baseline(w, Q, K, V, seconds_hint):
     t = w.tasks[int(np.argmax(w.tasks[:, 3]))]
     q_off, kv_off, o_off, q_len, kv_len = (int(x) for x in t[:5])
     rng = np.random.default_rng(0)
-    n_rows = min(256, q_len)
+    n_rows = min(1024, q_len)
     rows = np.sort(rng.choice(q_len, n_rows, replace=False))
     import torch
     # widen only the slices the sample reads
@@ -89,6 +89,118 @@ def cpu_baseline(w, Q, K, V, seconds_hint):
                       "%d visible pairs per head in %.1f s" % (n_rows, q_len, w.hq, pairs, dt)}
 
 
+def timed(fn, steps, warmup, stream):
+    """Average device time (ms) of fn() with HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def secondary(steps=3, warmup=1):
+    """The other configurations, each on its own freshly generated inputs."""
+    import torch
+    import oracle
+    from long_context_core_amd import ca
+    from long_context_core_amd import inputs as I
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def fwd_setup(w, seed, out_f32=False):
+        Q = I.randn_bf16((w.q_rows, w.hq, w.d), seed, device=dev)
+        K = I.randn_bf16((w.kv_rows, w.hkv, w.d), seed + 1, device=dev)
+        V = I.randn_bf16((w.kv_rows, w.hkv, w.d), seed + 2, device=dev)
+        O = torch.empty((w.o_rows, w.hq, w.d), device=dev, dtype=torch.float32 if out_f32 else torch.bfloat16)
+        LSE = torch.full((w.o_rows, w.hq), -float("inf"), device=dev)
+        shape = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, out_f32=out_f32)
+        tasks = ca.task_array(w.tasks)
+        ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+        return Q, K, V, O, LSE, shape, tasks, ws
+
+    # CA-tasks re-batched forward (LLaMA-34B shape)
+    w = I.ca_tasks_34b()
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 203)
+    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    ms = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
+    out["ca_tasks_34b_fwd"] = {"workload": w.name, "ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+                               "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    log("CA-tasks fwd: %.2f ms, %.1f TFLOP/s" % (ms, fl / ms / 1e9))
+    del Q, K, V, O, LSE, ws
+    torch.cuda.empty_cache()
+
+    # Ring pass-KV prefill share: 36 partials (fp32) + Equation-4 merge
+    w = I.ring_prefill_405b_tp8()
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 204, out_f32=True)
+    T = w.merged_rows
+    Om = torch.empty((T, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    Lm = torch.empty((T, w.hq), device=dev)
+    mshape = ca.make_shape(w.hq, w.hkv, w.d, T, T, T)
+    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    ms_f = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
+    Ov, Lv = O.view(w.n_parts, T, w.hq, w.d), LSE.view(w.n_parts, T, w.hq)
+    ms_m = timed(lambda: ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream), steps, warmup, stream)
+    # merge bytes: O of every written partial row, all partial LSEs, merged O (bf16) + LSE
+    mb = len(w.tasks) * (T // w.n_parts) * w.hq * w.d * 4 + w.n_parts * T * w.hq * 4 + T * w.hq * (w.d * 2 + 4)
+    out["ring_prefill_405b_tp8"] = {"workload": w.name, "partials_ms": round(ms_f, 3),
+                                    "partials_tflops": round(fl / ms_f / 1e9, 1),
+                                    "merge_ms": round(ms_m, 3), "merge_bytes": mb,
+                                    "merge_gbs": round(mb / ms_m / 1e6, 1)}
+    log("ring prefill: partials %.2f ms (%.1f TFLOP/s), merge %.3f ms (%.0f GB/s)"
+        % (ms_f, fl / ms_f / 1e9, ms_m, mb / ms_m / 1e6))
+    del Q, K, V, O, LSE, ws, Om, Lm
+    torch.cuda.empty_cache()
+
+    # Pass-Q decode share: 32 tokens x 128K caches, 8 stationary blocks, merge
+    w = I.ring_decode_405b_tp8()
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 205, out_f32=True)
+    B = w.merged_rows
+    Om = torch.empty((B, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    Lm = torch.empty((B, w.hq), device=dev)
+    mshape = ca.make_shape(w.hq, w.hkv, w.d, B, B, B)
+    Ov, Lv = O.view(w.n_parts, B, w.hq, w.d), LSE.view(w.n_parts, B, w.hq)
+
+    def dec_step():
+        ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
+        ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream)
+
+    ms = timed(dec_step, max(steps, 10), warmup, stream)
+    kv_bytes = 2 * w.kv_rows * w.hkv * w.d * 2
+    out["ring_decode_405b_tp8"] = {"workload": w.name, "ms": round(ms, 4), "kv_bytes": kv_bytes,
+                                   "gbs": round(kv_bytes / ms / 1e6, 1),
+                                   "pct_of_hbm_peak": round(100 * kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 2)}
+    log("decode: %.3f ms, %.0f GB/s of K+V" % (ms, kv_bytes / ms / 1e6))
+    del Q, K, V, O, LSE, ws, Om, Lm
+    torch.cuda.empty_cache()
+
+    # Training forward + backward (Llama-3-8B shape, 512K ProLong-like)
+    w = I.train_8b_prolong_512k()
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 205)
+    dO = I.randn_bf16((w.o_rows, w.hq, w.d), 208, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    bws = ca.workspace_tensor(ca.backward_workspace(shape, tasks), dev)
+    pairs = ca.visible_pairs(tasks)
+    ms_f = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
+    ms_b = timed(lambda: ca.backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
+                 steps, warmup, stream)
+    ff = oracle.forward_flops(pairs, w.hq, w.d)
+    bf = oracle.backward_flops(pairs, w.hq, w.d)
+    out["train_8b_512k"] = {"workload": w.name, "fwd_ms": round(ms_f, 2), "fwd_tflops": round(ff / ms_f / 1e9, 1),
+                            "bwd_ms": round(ms_b, 2), "bwd_tflops_10d": round(bf / ms_b / 1e9, 1),
+                            "bwd_tflops_8d": round(0.8 * bf / ms_b / 1e9, 1),
+                            "pct_of_bf16_peak_bwd": round(100 * bf / ms_b / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    log("train 512k: fwd %.1f ms (%.1f TFLOP/s), bwd %.1f ms (%.1f TFLOP/s at 10d)"
+        % (ms_f, ff / ms_f / 1e9, ms_b, bf / ms_b / 1e9))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +209,9 @@ def main():
     ap.add_argument("--workload", default="llama8b-131k",
                     choices=["llama8b-131k", "tiny", "ca-tasks-34b", "train-8b-512k-fwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other configurations (CA-tasks, ring prefill + merge, "
+                         "decode, training backward)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), the reference for "
                          "scaling the HBM byte counters")
@@ -177,9 +292,20 @@ def main():
                 "traffic": traffic, "kernel": "ca::fwd_kernel<128>",
                 "per_launch_flops": flops, "avg_launch_ms": round(avg_launch_s * 1e3, 4)}
 
+    sec = None
+    if not args.no_secondary and args.workload == "llama8b-131k":
+        del Q, K, V, O, LSE
+        torch.cuda.empty_cache()
+        sec = secondary()
+        Q = K = V = None
+
     base = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample ...")
+        if Q is None:
+            Q = I.randn_bf16((w.q_rows, w.hq, w.d), seed, device=dev)
+            K = I.randn_bf16((w.kv_rows, w.hkv, w.d), seed + 1, device=dev)
+            V = I.randn_bf16((w.kv_rows, w.hkv, w.d), seed + 2, device=dev)
         base = cpu_baseline(w, Q, K, V, 20)
         log("oracle: %.4g TFLOP/s on %d threads" % (base["value"], base["cores"]))
 
@@ -202,6 +328,7 @@ def main():
                    "length_seed": 102, "tensor_seed": seed},
         "roofline": roofline,
         "cpu_baseline": base,
+        "secondary": sec,
     }
     print(json.dumps(out), flush=True)
 
