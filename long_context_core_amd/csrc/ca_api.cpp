@@ -24,6 +24,10 @@
 
 #include "ca_internal.h"
 
+#ifndef CA_FWD_WAVES
+#define CA_FWD_WAVES 8
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -157,6 +161,7 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
 // the launch has enough work items to cover the chip; chunks of one task are
 // merged by log-sum-exp afterwards.
 
+constexpr int kFwdWaves = CA_FWD_WAVES;   // waves per forward workgroup (4 or 8)
 constexpr int kDecTargetItems = 2048;
 constexpr int kDecMinChunk = 512;
 constexpr int kDecMaxGroup = 16;
@@ -181,8 +186,8 @@ struct FwdPlan {
 FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
   FwdPlan p;
   p.group = s->hq / s->hkv;
-  p.hpw = gcd_int(p.group, 4);
-  p.rt = 32 * (4 / p.hpw);
+  p.hpw = gcd_int(p.group, kFwdWaves);
+  p.rt = 32 * (kFwdWaves / p.hpw);
   int64_t dec_keys = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (t[i].q_len <= 0) continue;
@@ -235,6 +240,9 @@ void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const F
         for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
     }
   }
+  // Longest first.  Items of equal cost (the KV heads of one query tile) stay
+  // adjacent, so they land on different XCDs and spread the K/V streams; the
+  // re-reads of long contexts are served by the shared last-level cache.
   std::stable_sort(tmp.begin(), tmp.end(), [](const Keyed& a, const Keyed& b) { return a.cost > b.cost; });
   items.resize(tmp.size());
   for (size_t i = 0; i < tmp.size(); ++i) items[i] = tmp[i].it;
@@ -327,6 +335,7 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const voi
     fp.hpw = p.hpw;
     fp.scale_log2 = scale_log2;
     fp.out_f32 = out_f32;
+    fp.waves = kFwdWaves;
     hipError_t e = ca::launch_forward(fp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
   }

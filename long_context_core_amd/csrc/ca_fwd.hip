@@ -39,15 +39,16 @@ namespace ca {
 // regardless of when the reference moved.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
+  constexpr int NT = 64 * NW;     // threads
   constexpr int BN = 64;          // keys per tile
   constexpr int KS = D + 8;       // K row stride in LDS (elements): 16 B pad
   constexpr int VS = D + 16;      // V row stride in LDS (elements): 32 B pad
   constexpr int NCB = D / 32;     // 32-channel output blocks
   constexpr int NKS = D / 16;     // 16-channel reduction steps of Q.K
   constexpr int CH = D / 8;       // 16-byte chunks per row
-  constexpr int RPP = 256 / CH;   // rows per load pass
+  constexpr int RPP = NT / CH;    // rows per load pass
   constexpr int PASSES = BN / RPP;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KS];
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int kv_len = t.kv_len;
 
   // Key range of the workgroup and of this wave.
-  const int rt = 32 * (4 / hpw);
+  const int rt = 32 * (NW / hpw);
   const int wg_last = min(it.row0 + rt, t.q_len) - 1;
   const int kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
   const int w_last = min(wrow0 + 32, t.q_len) - 1;
@@ -260,10 +261,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s) {
   if (p.n_items <= 0) return hipSuccess;
-  if (d == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, dim3(p.n_items), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(fwd_kernel<64>, dim3(p.n_items), dim3(256), 0, s, p);
+  if (p.waves == 8) {
+    if (d == 128)
+      hipLaunchKernelGGL((fwd_kernel<128, 8>), dim3(p.n_items), dim3(512), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<64, 8>), dim3(p.n_items), dim3(512), 0, s, p);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((fwd_kernel<128, 4>), dim3(p.n_items), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<64, 4>), dim3(p.n_items), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ struct FwdParams {
   int32_t hq, hkv, group, hpw;
   float scale_log2;   // softmax scale * log2(e)
   int32_t out_f32;
+  int32_t waves;      // 4 or 8 waves per workgroup
 };
 
 struct DecParams {
