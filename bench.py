@@ -207,7 +207,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b-131k",
-                    choices=["llama8b-131k", "tiny", "ca-tasks-34b", "train-8b-512k-fwd"])
+                    choices=["llama8b-131k", "tiny", "ca-tasks-34b", "train-8b-512k-fwd",
+                             "train-8b-512k-bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other configurations (CA-tasks, ring prefill + merge, "
@@ -242,7 +243,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     w = {"llama8b-131k": I.llama8b_packed_131k, "tiny": I.tiny_forward,
-         "ca-tasks-34b": I.ca_tasks_34b, "train-8b-512k-fwd": I.train_8b_prolong_512k}[args.workload]()
+         "ca-tasks-34b": I.ca_tasks_34b, "train-8b-512k-fwd": I.train_8b_prolong_512k,
+         "train-8b-512k-bwd": I.train_8b_prolong_512k}[args.workload]()
+    backward = args.workload.endswith("-bwd")
     log("workload %s: %d tasks, hq=%d hkv=%d d=%d, q_rows=%d kv_rows=%d"
         % (w.name, len(w.tasks), w.hq, w.hkv, w.d, w.q_rows, w.kv_rows))
 
@@ -258,12 +261,22 @@ def main():
     pairs = ca.visible_pairs(tasks)
     assert pairs == oracle.visible_pairs(w.tasks)
     flops = oracle.forward_flops(pairs, w.hq, w.d)
-    log("visible pairs per head %d, %.3f TFLOP per step" % (pairs, flops / 1e12))
-
     stream = torch.cuda.current_stream()
 
     def step():
         ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
+
+    if backward:
+        # the step is the backward pass, on the forward's own O and LSE
+        step()
+        dO = I.randn_bf16((w.o_rows, w.hq, w.d), seed + 3, device=dev)
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        bws = ca.workspace_tensor(ca.backward_workspace(shape, tasks), dev)
+        flops = oracle.backward_flops(pairs, w.hq, w.d)
+
+        def step():
+            ca.backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream)
+    log("visible pairs per head %d, %.3f TFLOP per step" % (pairs, flops / 1e12))
 
     for _ in range(args.warmup):
         step()

@@ -33,6 +33,10 @@ HIPCC_FLAGS = [
     # without this, every fmaxf on an MFMA result is preceded by a
     # canonicalising v_max (IEEE mode), tripling the cost of row maxima
     "-fno-honor-nans",
+    # keep MFMA accumulators in the VGPR form: with the AGPR form the register
+    # allocator shuttles loop-carried accumulators between AGPRs and VGPRs
+    # every iteration (hundreds of v_accvgpr moves per tile in the backward)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -185,25 +185,34 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(oa + 16 * s), vf[s], dp_acc, 0, 0, 0);
     }
     // P = exp2(scale log2e S - LSE2), dS = P (dP - D); masked pairs: 0.
-    const bool need_mask = (int64_t)r0 + delta < (int64_t)kw0 + 31;
-    bf16x8 pf[2], dsf[2];
+    // Row m (= 8 q4 + 4 hh + j) sees key l32 of the wave iff
+    // l32 - 4 hh - (r0 + delta - kw0) <= 8 q4 + j.
+    float pv[16];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 l4 = *(const float4*)(&lds_lse[buf][8 * q4 + 4 * hh]);
-      const float4 d4 = *(const float4*)(&lds_d[buf][8 * q4 + 4 * hh]);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv[4 * q4 + j] = exp2_fast(fmaf(s_acc[4 * q4 + j], p.scale_log2, -lv[j]));
+    }
+    if ((int64_t)r0 + delta < (int64_t)kw0 + 31) {
+      keep_branch();
+      const int x = l32 - 4 * hh - (int)clamp64((int64_t)r0 + delta - kw0, -64, 64);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[4 * q4 + j] = (x <= 8 * q4 + j) ? pv[4 * q4 + j] : 0.f;
+    }
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 d4 = *(const float4*)(&lds_d[buf][8 * q4 + 4 * hh]);
       const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int reg = 4 * q4 + j;
-        float pv = exp2_fast(fmaf(s_acc[reg], p.scale_log2, -lv[j]));
-        if (need_mask) {
-          const int64_t row = (int64_t)r0 + 8 * q4 + 4 * hh + j;
-          pv = ((int64_t)my_key <= row + delta) ? pv : 0.f;
-        }
-        const float ds = pv * (dp_acc[reg] - dv[j]);
-        pf[reg >> 3][reg & 7] = (__bf16)pv;
-        dsf[reg >> 3][reg & 7] = (__bf16)ds;
+        pf[reg >> 3][reg & 7] = (__bf16)pv[reg];
+        dsf[reg >> 3][reg & 7] = (__bf16)(pv[reg] * (dp_acc[reg] - dv[j]));
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS, reduction over the 32 rows
@@ -365,20 +374,27 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
         dp_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[s], dp_acc[mb], 0, 0, 0);
       }
     }
-    const bool need_mask = tile >= w_full;
-    const int lim = (int)clamp64(min((int64_t)qrow + delta, (int64_t)kv_len - 1) - k0, -1, BN);
+    float pv[2][16];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pv[mb][j] = exp2_fast(fmaf(s_acc[mb][j], p.scale_log2, -lse2));
+    if (tile >= w_full) {
+      keep_branch();
+      const int lim = (int)clamp64(min((int64_t)qrow + delta, (int64_t)kv_len - 1) - k0, -1, BN);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          pv[mb][j] = (r <= lim) ? pv[mb][j] : 0.f;
+        }
+    }
     bf16x8 dsf[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float pv = exp2_fast(fmaf(s_acc[mb][j], p.scale_log2, -lse2));
-        if (need_mask) {
-          const int r = mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          pv = (r <= lim) ? pv : 0.f;
-        }
-        dsf[mb][j >> 3][j & 7] = (__bf16)(pv * (dp_acc[mb][j] - dval));
-      }
+      for (int j = 0; j < 16; ++j) dsf[mb][j >> 3][j & 7] = (__bf16)(pv[mb][j] * (dp_acc[mb][j] - dval));
     // dQ^T += K^T dS^T (K^T through transpose reads, keys permuted like dS^T)
     const __bf16* kl = &lds_k[buf][kt_off];
 #pragma unroll

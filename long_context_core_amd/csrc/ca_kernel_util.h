@@ -66,6 +66,16 @@ __device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
+// 16 bytes per lane from a raw buffer straight into LDS (no registers): lane i
+// of the wave writes lds_block + 16 i; lds_block must be wave-uniform.
+__device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, void* lds_block, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, soff, 0, 0);
+}
+
+// Wait for this wave's outstanding vector-memory operations (including loads
+// into LDS); other counters untouched.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Value of lane l and of lane l ^ 32 combined (v_permlane32_swap, no LDS).
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
