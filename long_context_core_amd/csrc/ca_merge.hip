@@ -14,26 +14,38 @@ namespace ca {
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   constexpr int LPP = D / 4;                    // lanes per (row, head)
+  constexpr int CHUNK = 8;                      // partials loaded together
   const int64_t n_pairs = p.n_rows * p.hq;
   const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPP;
   const int sub = threadIdx.x % LPP;
   if (pair >= n_pairs) return;
   const int64_t part_stride_o = n_pairs * D;    // floats per partial
+  const float* lse = p.LSE_parts + pair;
+  const float* op = p.O_parts + pair * D + sub * 4;
   float M = -INFINITY;
-  for (int s = 0; s < p.n_parts; ++s) M = fmaxf(M, p.LSE_parts[s * n_pairs + pair]);
+  for (int s = 0; s < p.n_parts; ++s) M = fmaxf(M, lse[s * n_pairs]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < p.n_parts; ++s) {
-      const float l = p.LSE_parts[s * n_pairs + pair];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - M);
-      const float4 o = *(const float4*)(p.O_parts + s * part_stride_o + pair * D + sub * 4);
-      acc.x = fmaf(w, o.x, acc.x);
-      acc.y = fmaf(w, o.y, acc.y);
-      acc.z = fmaf(w, o.z, acc.z);
-      acc.w = fmaf(w, o.w, acc.w);
-      den += w;
+    for (int s0 = 0; s0 < p.n_parts; s0 += CHUNK) {
+      float w[CHUNK];
+      float4 o[CHUNK];
+#pragma unroll
+      for (int k = 0; k < CHUNK; ++k) {       // all loads of the chunk first
+        const int s = s0 + k;
+        const float l = s < p.n_parts ? lse[s * n_pairs] : -INFINITY;
+        w[k] = (l == -INFINITY) ? 0.f : __expf(l - M);
+        o[k] = (l == -INFINITY) ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                : *(const float4*)(op + s * part_stride_o);
+      }
+#pragma unroll
+      for (int k = 0; k < CHUNK; ++k) {
+        acc.x = fmaf(w[k], o[k].x, acc.x);
+        acc.y = fmaf(w[k], o[k].y, acc.y);
+        acc.z = fmaf(w[k], o[k].z, acc.z);
+        acc.w = fmaf(w[k], o[k].w, acc.w);
+        den += w[k];
+      }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
