@@ -162,7 +162,7 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
 // merged by log-sum-exp afterwards.
 
 constexpr int kFwdWaves = CA_FWD_WAVES;   // waves per forward workgroup (4 or 8)
-constexpr int kDecTargetItems = 2048;
+constexpr int kDecTargetItems = 1024;      // two rounds of two 4-wave items per CU
 constexpr int kDecMinChunk = 512;
 constexpr int kDecMaxGroup = 16;
 

@@ -223,48 +223,28 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
   }
 }
 
-// Merge of the key chunks of each split decode task (Equation 4).  One group
-// of D/4 lanes per (split task, head).
+// Merge of the key chunks of each split decode task (Equation 4).  D / 8
+// lanes per (split task, head), two float4s each.
+constexpr int kDecMergeVec = 2;
+
 template <int D>
 __global__ __launch_bounds__(256) void dec_merge_kernel(DecMergeParams p) {
-  constexpr int LPP = D / 4;
+  constexpr int LPP = D / (4 * kDecMergeVec);
   const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPP;
   const int sub = threadIdx.x % LPP;
   if (pair >= (int64_t)p.n_split * p.group) return;
   const int rec = (int)(pair / p.group);
   const int h = (int)(pair % p.group);
-  const int first = p.first_part[rec];
-  const int n = p.n_parts[rec];
+  const int64_t first = p.first_part[rec];
   const ca_task t = p.tasks[p.task_of[rec]];
   const int head = p.head_of[rec] * p.group + h;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_LSE[(int64_t)(first + s) * p.group + h]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n; ++s) {
-      const float l = p.part_LSE[(int64_t)(first + s) * p.group + h];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - M);
-      const float4 o = *(const float4*)(p.part_O + ((int64_t)(first + s) * p.group + h) * D + sub * 4);
-      acc.x = fmaf(w, o.x, acc.x);
-      acc.y = fmaf(w, o.y, acc.y);
-      acc.z = fmaf(w, o.z, acc.z);
-      acc.w = fmaf(w, o.w, acc.w);
-      den += w;
-    }
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-  const int64_t ob = t.o_off * (int64_t)(p.hq * D) + (int64_t)head * D + sub * 4;
-  if (p.out_f32) {
-    *(float4*)((float*)p.O + ob) = acc;
-  } else {
-    bf16x4 v;
-    v[0] = (__bf16)acc.x; v[1] = (__bf16)acc.y; v[2] = (__bf16)acc.z; v[3] = (__bf16)acc.w;
-    *(bf16x4*)((__bf16*)p.O + ob) = v;
-  }
-  if (sub == 0) p.LSE[t.o_off * p.hq + head] = den > 0.f ? M + __logf(den) : -INFINITY;
+  float4 r[kDecMergeVec];
+  const float lse = merge_lse_parts<D, kDecMergeVec>(p.part_LSE + first * p.group + h, p.group,
+                                                     p.part_O + (first * p.group + h) * D + sub * 4,
+                                                     (int64_t)p.group * D, p.n_parts[rec], r);
+  store_row_part<D, kDecMergeVec>(p.O, t.o_off * (int64_t)(p.hq * D) + (int64_t)head * D + sub * 4,
+                                  p.out_f32 != 0, r);
+  if (sub == 0) p.LSE[t.o_off * p.hq + head] = lse;
 }
 
 hipError_t launch_decode(const DecParams& p, int d, hipStream_t s) {
@@ -277,7 +257,7 @@ hipError_t launch_decode(const DecParams& p, int d, hipStream_t s) {
 }
 
 hipError_t launch_decode_merge(const DecMergeParams& p, int d, hipStream_t s) {
-  const int64_t threads = (int64_t)p.n_split * p.group * (d / 4);
+  const int64_t threads = (int64_t)p.n_split * p.group * (d / (4 * kDecMergeVec));
   if (threads <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (d == 128)

@@ -66,16 +66,6 @@ __device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
-// 16 bytes per lane from a raw buffer straight into LDS (no registers): lane i
-// of the wave writes lds_block + 16 i; lds_block must be wave-uniform.
-__device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, void* lds_block, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, soff, 0, 0);
-}
-
-// Wait for this wave's outstanding vector-memory operations (including loads
-// into LDS); other counters untouched.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // Value of lane l and of lane l ^ 32 combined (v_permlane32_swap, no LDS).
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -86,21 +76,85 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// sum of the 8 bf16 values of v, accumulated into acc in fp32 (v_dot2 with 1s)
-__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, one, acc, false);
-  return acc;
-}
-
 __device__ __forceinline__ bf16x8 concat_bf16x4(bf16x4 lo, bf16x4 hi) {
   bf16x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
+}
+
+// Log-sum-exp merge of n partial results of one (row, head) ("Context
+// Parallelism for Scalable Million-Token Inference", Section 3.4, Equation 4):
+//   M = max_s LSE_s,  O = sum_s e^(LSE_s - M) O_s / sum_s e^(LSE_s - M),
+//   LSE = M + ln sum_s e^(LSE_s - M).
+// The calling lane owns VEC float4s of the row, at o + v * (D / VEC) of each
+// partial; partial s sits at lse[s * lse_stride] and o + s * o_stride.  A
+// partial with LSE = -inf is skipped without reading its O.  Eight partials'
+// LSEs and O's are loaded together; earlier chunks are rescaled when the
+// running maximum grows.  out receives the merged O (0 if every LSE is -inf);
+// the merged LSE is returned (-inf then).
+template <int D, int VEC>
+__device__ __forceinline__ float merge_lse_parts(const float* lse, int64_t lse_stride, const float* o,
+                                                 int64_t o_stride, int n, float4 (&out)[VEC]) {
+  constexpr int CHUNK = 8;
+  float M = -INFINITY, den = 0.f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) out[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < n; s0 += CHUNK) {
+    float l[CHUNK];
+    float4 x[CHUNK][VEC];
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) l[k] = s0 + k < n ? lse[(s0 + k) * lse_stride] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+        x[k][v] = (l[k] == -INFINITY) ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                      : *(const float4*)(o + (s0 + k) * o_stride + v * (D / VEC));
+    float mc = M;
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) mc = fmaxf(mc, l[k]);
+    if (mc == -INFINITY) continue;
+    if (mc != M) {
+      const float a = (M == -INFINITY) ? 0.f : __expf(M - mc);
+      den *= a;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) { out[v].x *= a; out[v].y *= a; out[v].z *= a; out[v].w *= a; }
+      M = mc;
+    }
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) {
+      const float w = (l[k] == -INFINITY) ? 0.f : __expf(l[k] - M);
+      den += w;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        out[v].x = fmaf(w, x[k][v].x, out[v].x);
+        out[v].y = fmaf(w, x[k][v].y, out[v].y);
+        out[v].z = fmaf(w, x[k][v].z, out[v].z);
+        out[v].w = fmaf(w, x[k][v].w, out[v].w);
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) { out[v].x *= inv; out[v].y *= inv; out[v].z *= inv; out[v].w *= inv; }
+  return den > 0.f ? M + __logf(den) : -INFINITY;
+}
+
+// Store VEC float4s (at dst + v * (D / VEC)) as fp32 or rounded to bf16.
+template <int D, int VEC>
+__device__ __forceinline__ void store_row_part(void* O, int64_t base, bool f32, const float4 (&r)[VEC]) {
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const int64_t at = base + v * (D / VEC);
+    if (f32) {
+      *(float4*)((float*)O + at) = r[v];
+    } else {
+      bf16x4 b;
+      b[0] = (__bf16)r[v].x; b[1] = (__bf16)r[v].y; b[2] = (__bf16)r[v].z; b[3] = (__bf16)r[v].w;
+      *(bf16x4*)((__bf16*)O + at) = b;
+    }
+  }
 }
 
 }  // namespace ca
