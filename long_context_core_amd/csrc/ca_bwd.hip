@@ -60,17 +60,40 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* O, const __
 }
 
 // ---------------------------------------------------------------------------
+// LDS tile of 32 query rows x D bf16 (Q or dO) in the dK/dV kernel.  It is read
+// row-wise (MFMA A operand: 16 rows, one 16-byte chunk each) and by transpose
+// reads (4 consecutive rows, 4 consecutive chunks).  D = 128: unpadded 256-byte
+// rows with chunk c of row r stored at chunk c ^ swz(r), a layout in which
+// both patterns hit every bank once.  D = 64: rows padded to 80 elements.
+// ---------------------------------------------------------------------------
+template <int D>
+struct QTile {
+  static constexpr int kRow = D + 16;
+  static constexpr int kElems = 32 * kRow;
+  __device__ static int off(int r, int chunk) { return r * kRow + chunk * 8; }
+};
+template <>
+struct QTile<128> {
+  static constexpr int kRow = 128;
+  static constexpr int kElems = 32 * kRow;
+  __device__ static int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+  __device__ static int off(int r, int chunk) { return r * kRow + ((chunk ^ swz(r)) << 3); }
+};
+
+// ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (task, KV head, 128 context rows).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
+  using Tile = QTile<D>;
   constexpr int BQ = 32;            // query rows per step
-  constexpr int QS = D + 16;        // LDS row stride (elements) of the Q / dO tiles
   constexpr int NKS = D / 16;       // 16-channel reduction steps
   constexpr int NCB = D / 32;       // 32-channel output blocks
   constexpr int CH = D / 8;         // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) __bf16 lds_q[2][BQ * QS];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_do[2][BQ * QS];
+  constexpr int RPP = 256 / CH;     // rows per load pass
+  constexpr int PASSES = BQ / RPP;
+  __shared__ __attribute__((aligned(16))) __bf16 lds_q[2][Tile::kElems];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_do[2][Tile::kElems];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][BQ];
   __shared__ __attribute__((aligned(16))) float lds_d[2][BQ];
 
@@ -112,79 +135,102 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int n_rt = (t.q_len - r_first + BQ - 1) / BQ;
   const int n_steps = (wg_keys > 0 && t.q_len > r_lo) ? n_rt * G : 0;
 
-  // Tile loads: Q and dO rows (32 x D bf16 each), LSE and D values.
-  const int ld_row = tid / CH;                    // 0..(256/CH - 1)
-  const int ld_chunk = tid % CH;
-  constexpr int RPP = 256 / CH;
-  constexpr int PASSES = BQ / RPP;
+  // Tile loads through range-checked buffers based at the step's first row:
+  // rows past the task read as 0 (Q = dO = 0 there, so such rows add nothing
+  // to dK or dV whatever their P), and every address is a lane constant plus
+  // a wave-uniform base.
   const int64_t q_stride = (int64_t)p.hq * D;
+  const uint32_t row_bytes = (uint32_t)(q_stride * 2);
+  const int ld_row = tid / CH;
+  const int ld_chunk = tid % CH;
+  const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
+  const uint32_t lse_voff = (uint32_t)tid * (uint32_t)p.hq * 4;
   uint4 qreg[PASSES], oreg[PASSES];
   float lse_reg = 0.f, d_reg = 0.f;
-  auto gload = [&](int step) {
-    const int r0 = r_first + (step / G) * BQ;
-    const int head = it.kv_head * G + (step % G);
+  auto gload = [&](int r0, int head) {
+    const uint32_t nvalid = (uint32_t)min(BQ, t.q_len - r0);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.Q + (t.q_off + r0) * q_stride + head * D, nvalid * row_bytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.dO + (t.o_off + r0) * q_stride + head * D, nvalid * row_bytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      const int row = r0 + r * RPP + ld_row;
-      if (row < t.q_len) {
-        qreg[r] = *(const uint4*)(p.Q + (t.q_off + row) * q_stride + head * D + ld_chunk * 8);
-        oreg[r] = *(const uint4*)(p.dO + (t.o_off + row) * q_stride + head * D + ld_chunk * 8);
-      } else {
-        qreg[r] = make_uint4(0, 0, 0, 0);
-        oreg[r] = make_uint4(0, 0, 0, 0);
-      }
+      qreg[r] = buffer_load_16(qr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
+      oreg[r] = buffer_load_16(orr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
+    const int64_t lo = (t.o_off + r0) * p.hq + head;
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(nvalid * (uint32_t)p.hq * 4);
     if (tid < BQ) {
-      const int row = r0 + tid;
-      if (row < t.q_len) {
-        lse_reg = lse_log2(p.LSE[(t.o_off + row) * p.hq + head]);
-        d_reg = p.Dvec[(t.o_off + row) * p.hq + head];
-      } else {
-        lse_reg = INFINITY;                      // invalid row: P = 0
-        d_reg = 0.f;
-      }
+      lse_reg = buffer_load_f32(make_rsrc(p.LSE + lo, lb), lse_voff, 0);
+      d_reg = buffer_load_f32(make_rsrc(p.Dvec + lo, lb), lse_voff, 0);
     }
   };
   auto swrite = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      const int row = r * RPP + ld_row;
-      *(uint4*)(&lds_q[buf][row * QS + ld_chunk * 8]) = qreg[r];
-      *(uint4*)(&lds_do[buf][row * QS + ld_chunk * 8]) = oreg[r];
+      const int o = Tile::off(r * RPP + ld_row, ld_chunk);
+      *(uint4*)(&lds_q[buf][o]) = qreg[r];
+      *(uint4*)(&lds_do[buf][o]) = oreg[r];
     }
     if (tid < BQ) {
-      lds_lse[buf][tid] = lse_reg;
+      lds_lse[buf][tid] = lse_log2(lse_reg);
       lds_d[buf][tid] = d_reg;
     }
   };
 
-  // Operand offsets.  Row-major A operands (Q, dO: m = query l32, k = 16 s + 8 hh);
-  // transpose reads for Q^T and dO^T as in the forward's V^T.
-  const int a_off = l32 * QS + 8 * hh;
+  // Row-wise operand offsets (A of S and dP: m = query l32, k = 16 s + 8 hh) and
+  // transpose-read offsets (Q^T, dO^T: rows 4 hh + j16 / 4 (+8, +16 half),
+  // columns 32 c + 16 (g16 & 1) + 4 (j16 & 3)).
+  int a_off[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) a_off[s] = Tile::off(l32, 2 * s + hh);
   const int g16 = lane >> 4;
   const int j16 = lane & 15;
-  const int t_off = ((j16 >> 2) + 4 * hh) * QS + 16 * (g16 & 1) + 4 * (j16 & 3);
+  int tr_off[NCB][2];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      tr_off[c][u] = Tile::off(8 * u + 4 * hh + (j16 >> 2), 4 * c + 2 * (g16 & 1) + ((j16 & 3) >> 1)) + 4 * (j16 & 1);
 
-  if (n_steps > 0) gload(0);
+  // step = (query tile, head of the group), head fastest
+  int cur_rt = 0, cur_g = 0;
+  if (n_steps > 0) gload(r_first, it.kv_head * G);
   for (int step = 0; step < n_steps; ++step) {
     const int buf = step & 1;
+    const int r0 = r_first + cur_rt * BQ;
     swrite(buf);
     __syncthreads();
-    if (step + 1 < n_steps) gload(step + 1);
-    const int r0 = r_first + (step / G) * BQ;
+    if (++cur_g == G) {
+      cur_g = 0;
+      ++cur_rt;
+    }
+    if (step + 1 < n_steps) gload(r_first + cur_rt * BQ, it.kv_head * G + cur_g);
     // Skip blocks where no row of the step sees any key of this wave.
     if ((int64_t)r0 + BQ - 1 + delta < kw0) continue;
 
     // S = Q K^T and dP = dO V^T (lane = key l32; rows m = 8 (j/4) + 4 hh + j%4)
-    f32x16 s_acc = f32x16_zero(), dp_acc = f32x16_zero();
-    const __bf16* qa = &lds_q[buf][a_off];
-    const __bf16* oa = &lds_do[buf][a_off];
+    const __bf16* lq = &lds_q[buf][0];
+    const __bf16* lo = &lds_do[buf][0];
+    bf16x8 qa[NKS], oa[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qa + 16 * s), kf[s], s_acc, 0, 0, 0);
-      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(oa + 16 * s), vf[s], dp_acc, 0, 0, 0);
+      qa[s] = *(const bf16x8*)(lq + a_off[s]);
+      oa[s] = *(const bf16x8*)(lo + a_off[s]);
     }
-    // P = exp2(scale log2e S - LSE2), dS = P (dP - D); masked pairs: 0.
+    f32x16 s_acc = f32x16_zero(), dp_acc = f32x16_zero();
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], s_acc, 0, 0, 0);
+      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vf[s], dp_acc, 0, 0, 0);
+    }
+    // dO^T operands (independent of P)
+    bf16x8 dot[2][NCB];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        dot[half][c] = concat_bf16x4(ds_read_tr16(lo + tr_off[c][0] + 16 * half * Tile::kRow),
+                                     ds_read_tr16(lo + tr_off[c][1] + 16 * half * Tile::kRow));
+    // P = exp2(scale log2e S - LSE2); masked pairs: 0.
     // Row m (= 8 q4 + 4 hh + j) sees key l32 of the wave iff
     // l32 - 4 hh - (r0 + delta - kw0) <= 8 q4 + j.
     float pv[16];
@@ -203,7 +249,24 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[4 * q4 + j] = (x <= 8 * q4 + j) ? pv[4 * q4 + j] : 0.f;
     }
-    bf16x8 pf[2], dsf[2];
+    bf16x8 pf[2];
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) pf[reg >> 3][reg & 7] = (__bf16)pv[reg];
+    // dV^T += dO^T P (reduction over the 32 rows)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        dv_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot[half][c], pf[half], dv_acc[c], 0, 0, 0);
+    // Q^T operands, then dS = P (dP - D) and dK^T += Q^T dS
+    bf16x8 qt[2][NCB];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        qt[half][c] = concat_bf16x4(ds_read_tr16(lq + tr_off[c][0] + 16 * half * Tile::kRow),
+                                    ds_read_tr16(lq + tr_off[c][1] + 16 * half * Tile::kRow));
+    bf16x8 dsf[2];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 d4 = *(const float4*)(&lds_d[buf][8 * q4 + 4 * hh]);
@@ -211,23 +274,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int reg = 4 * q4 + j;
-        pf[reg >> 3][reg & 7] = (__bf16)pv[reg];
         dsf[reg >> 3][reg & 7] = (__bf16)(pv[reg] * (dp_acc[reg] - dv[j]));
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, reduction over the 32 rows
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const __bf16* o0 = &lds_do[buf][t_off + (16 * half) * QS + 32 * c];
-        const bf16x8 dot = concat_bf16x4(ds_read_tr16(o0), ds_read_tr16(o0 + 8 * QS));
-        dv_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pf[half], dv_acc[c], 0, 0, 0);
-        const __bf16* q0 = &lds_q[buf][t_off + (16 * half) * QS + 32 * c];
-        const bf16x8 qt = concat_bf16x4(ds_read_tr16(q0), ds_read_tr16(q0 + 8 * QS));
-        dk_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf[half], dk_acc[c], 0, 0, 0);
-      }
-    }
+      for (int c = 0; c < NCB; ++c)
+        dk_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[half][c], dsf[half], dk_acc[c], 0, 0, 0);
   }
 
   // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
