@@ -21,6 +21,8 @@
 // Rows are written once per pass (read-modify-write in fp32 when several
 // tasks share rows), so results are deterministic.
 
+#include <type_traits>
+
 #include "ca_internal.h"
 #include "ca_kernel_util.h"
 
@@ -135,32 +137,50 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int n_rt = (t.q_len - r_first + BQ - 1) / BQ;
   const int n_steps = (wg_keys > 0 && t.q_len > r_lo) ? n_rt * G : 0;
 
-  // Tile loads through range-checked buffers based at the step's first row:
+  // Tile loads through range-checked buffers based at the tile's first row:
   // rows past the task read as 0 (Q = dO = 0 there, so such rows add nothing
-  // to dK or dV whatever their P), and every address is a lane constant plus
-  // a wave-uniform base.
+  // to dK or dV whatever their P).  The wave-uniform bases advance by fixed
+  // strides from tile to tile; the lane offsets are constants.
   const int64_t q_stride = (int64_t)p.hq * D;
   const uint32_t row_bytes = (uint32_t)(q_stride * 2);
   const int ld_row = tid / CH;
   const int ld_chunk = tid % CH;
   const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
   const uint32_t lse_voff = (uint32_t)tid * (uint32_t)p.hq * 4;
+  const int head0 = it.kv_head * G;
+  // next tile to load: head nx_g of the group, rows from the one nq points at
+  const __bf16* nq = p.Q + (t.q_off + r_first) * q_stride + head0 * D;
+  const __bf16* no = p.dO + (t.o_off + r_first) * q_stride + head0 * D;
+  const float* nl = p.LSE + (t.o_off + r_first) * p.hq + head0;
+  const float* nd = p.Dvec + (t.o_off + r_first) * p.hq + head0;
+  int nx_g = 0;
+  int nx_left = t.q_len - r_first;               // task rows from the next tile's first row
   uint4 qreg[PASSES], oreg[PASSES];
   float lse_reg = 0.f, d_reg = 0.f;
-  auto gload = [&](int r0, int head) {
-    const uint32_t nvalid = (uint32_t)min(BQ, t.q_len - r0);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.Q + (t.q_off + r0) * q_stride + head * D, nvalid * row_bytes);
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.dO + (t.o_off + r0) * q_stride + head * D, nvalid * row_bytes);
+  auto gload = [&]() {
+    const uint32_t nvalid = (uint32_t)min(BQ, nx_left);
+    const uint32_t qbytes = nvalid * row_bytes;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(nq + nx_g * D, qbytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(no + nx_g * D, qbytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       qreg[r] = buffer_load_16(qr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
       oreg[r] = buffer_load_16(orr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
-    const int64_t lo = (t.o_off + r0) * p.hq + head;
-    const uint32_t lb = __builtin_amdgcn_readfirstlane(nvalid * (uint32_t)p.hq * 4);
+    const uint32_t lbytes = nvalid * (uint32_t)p.hq * 4;
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(nl + nx_g, lbytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(nd + nx_g, lbytes);
     if (tid < BQ) {
-      lse_reg = buffer_load_f32(make_rsrc(p.LSE + lo, lb), lse_voff, 0);
-      d_reg = buffer_load_f32(make_rsrc(p.Dvec + lo, lb), lse_voff, 0);
+      lse_reg = buffer_load_f32(lr, lse_voff, 0);
+      d_reg = buffer_load_f32(dr, lse_voff, 0);
+    }
+    if (++nx_g == G) {
+      nx_g = 0;
+      nq += BQ * q_stride;
+      no += BQ * q_stride;
+      nl += BQ * p.hq;
+      nd += BQ * p.hq;
+      nx_left -= BQ;
     }
   };
   auto swrite = [&](int buf) {
@@ -191,23 +211,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     for (int u = 0; u < 2; ++u)
       tr_off[c][u] = Tile::off(8 * u + 4 * hh + (j16 >> 2), 4 * c + 2 * (g16 & 1) + ((j16 & 3) >> 1)) + 4 * (j16 & 1);
 
-  // step = (query tile, head of the group), head fastest
-  int cur_rt = 0, cur_g = 0;
-  if (n_steps > 0) gload(r_first, it.kv_head * G);
-  for (int step = 0; step < n_steps; ++step) {
-    const int buf = step & 1;
-    const int r0 = r_first + cur_rt * BQ;
-    swrite(buf);
-    __syncthreads();
-    if (++cur_g == G) {
-      cur_g = 0;
-      ++cur_rt;
-    }
-    if (step + 1 < n_steps) gload(r_first + cur_rt * BQ, it.kv_head * G + cur_g);
-    // Skip blocks where no row of the step sees any key of this wave.
-    if ((int64_t)r0 + BQ - 1 + delta < kw0) continue;
-
-    // S = Q K^T and dP = dO V^T (lane = key l32; rows m = 8 (j/4) + 4 hh + j%4)
+  // One step: 32 query rows of one head against the wave's 32 keys, in the
+  // diagonal band, where a wave may see none or only some of the (row, key)
+  // pairs.
+  auto diag_body = [&](int buf, int r0) {
     const __bf16* lq = &lds_q[buf][0];
     const __bf16* lo = &lds_do[buf][0];
     bf16x8 qa[NKS], oa[NKS];
@@ -216,13 +223,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       qa[s] = *(const bf16x8*)(lq + a_off[s]);
       oa[s] = *(const bf16x8*)(lo + a_off[s]);
     }
+    // S = Q K^T (lane = key l32; rows m = 8 (j/4) + 4 hh + j%4), dP = dO V^T
     f32x16 s_acc = f32x16_zero(), dp_acc = f32x16_zero();
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], s_acc, 0, 0, 0);
       dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vf[s], dp_acc, 0, 0, 0);
     }
-    // dO^T operands (independent of P)
     bf16x8 dot[2][NCB];
 #pragma unroll
     for (int half = 0; half < 2; ++half)
@@ -230,9 +237,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       for (int c = 0; c < NCB; ++c)
         dot[half][c] = concat_bf16x4(ds_read_tr16(lo + tr_off[c][0] + 16 * half * Tile::kRow),
                                      ds_read_tr16(lo + tr_off[c][1] + 16 * half * Tile::kRow));
-    // P = exp2(scale log2e S - LSE2); masked pairs: 0.
-    // Row m (= 8 q4 + 4 hh + j) sees key l32 of the wave iff
-    // l32 - 4 hh - (r0 + delta - kw0) <= 8 q4 + j.
+    // P = exp2(scale log2e S - LSE2); masked pairs: 0.  Row m (= 8 q4 + 4 hh + j)
+    // sees key l32 of the wave iff l32 - 4 hh - (r0 + delta - kw0) <= 8 q4 + j.
     float pv[16];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     }
     bf16x8 pf[2];
 #pragma unroll
-    for (int reg = 0; reg < 16; ++reg) pf[reg >> 3][reg & 7] = (__bf16)pv[reg];
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)pv[r];
     // dV^T += dO^T P (reduction over the 32 rows)
 #pragma unroll
     for (int half = 0; half < 2; ++half)
@@ -282,7 +288,134 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
         dk_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[half][c], dsf[half], dk_acc[c], 0, 0, 0);
+  };
+
+  // The same step where every (row, key) pair is visible: one basic block in
+  // a fixed issue order (sched_barrier fences) for a single wave per SIMD, so
+  // that each MFMA runs in the shadow of independent work: the S chain with
+  // the dO^T reads, the dP chain with exp(S) and the Q^T reads, the dV chain
+  // with dS.
+  static_assert(NKS == 2 * NCB && 16 % NKS == 0, "step layout assumes D in {64, 128}");
+  auto full_body = [&](int buf) {
+    const __bf16* lq = &lds_q[buf][0];
+    const __bf16* lo = &lds_do[buf][0];
+    bf16x8 qa[NKS], oa[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) qa[s] = *(const bf16x8*)(lq + a_off[s]);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) oa[s] = *(const bf16x8*)(lo + a_off[s]);
+    float lv[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 l4 = *(const float4*)(&lds_lse[buf][8 * q4 + 4 * hh]);
+      lv[4 * q4 + 0] = l4.x; lv[4 * q4 + 1] = l4.y; lv[4 * q4 + 2] = l4.z; lv[4 * q4 + 3] = l4.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // S chain + dO^T reads
+    f32x16 s_acc = f32x16_zero(), dp_acc = f32x16_zero();
+    bf16x4 dtr[2][NCB][2];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], s_acc, 0, 0, 0);
+      const int half = s / NCB, c = s % NCB;
+      dtr[half][c][0] = ds_read_tr16(lo + tr_off[c][0] + 16 * half * Tile::kRow);
+      dtr[half][c][1] = ds_read_tr16(lo + tr_off[c][1] + 16 * half * Tile::kRow);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dP chain + exp(S) + Q^T reads
+    float pv[16];
+    bf16x4 qtr[2][NCB][2];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vf[s], dp_acc, 0, 0, 0);
+      asm volatile("" : "+v"(dp_acc));   // keep the chain step here (IR passes sink pure calls)
+#pragma unroll
+      for (int k = 0; k < 16 / NKS; ++k) {
+        const int r = s * (16 / NKS) + k;
+        pv[r] = exp2_fast(fmaf(s_acc[r], p.scale_log2, -lv[r]));
+      }
+      const int half = s / NCB, c = s % NCB;
+      qtr[half][c][0] = ds_read_tr16(lq + tr_off[c][0] + 16 * half * Tile::kRow);
+      qtr[half][c][1] = ds_read_tr16(lq + tr_off[c][1] + 16 * half * Tile::kRow);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)pv[r];
+    float dvv[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 d4 = *(const float4*)(&lds_d[buf][8 * q4 + 4 * hh]);
+      dvv[4 * q4 + 0] = d4.x; dvv[4 * q4 + 1] = d4.y; dvv[4 * q4 + 2] = d4.z; dvv[4 * q4 + 3] = d4.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dV chain + dS = P (dP - D)
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int i = 0; i < 2 * NCB; ++i) {
+      const int half = i / NCB, c = i % NCB;
+      dv_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(dtr[half][c][0], dtr[half][c][1]), pf[half],
+                                                          dv_acc[c], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 16 / (2 * NCB); ++k) {
+        const int r = i * (16 / (2 * NCB)) + k;
+        dsf[r >> 3][r & 7] = (__bf16)(pv[r] * (dp_acc[r] - dvv[r]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dK chain
+#pragma unroll
+    for (int i = 0; i < 2 * NCB; ++i) {
+      const int half = i / NCB, c = i % NCB;
+      dk_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(qtr[half][c][0], qtr[half][c][1]), dsf[half],
+                                                          dk_acc[c], 0, 0, 0);
+    }
+  };
+
+  // step = (query tile, head of the group), head fastest.  Row tiles before
+  // n_diag_rt may hold rows that do not see every key of the workgroup.  Steps
+  // alternate between the two LDS buffers and run in pairs, so that every LDS
+  // address is a lane constant plus an immediate; the band is rounded up to an
+  // even number of steps (its body is correct for any step).
+  const int n_diag_rt = (int)clamp64(((int64_t)it.key0 + 127 - delta - r_first + BQ - 1) / BQ, 0, n_rt);
+  const int n_diag = min(n_steps, (n_diag_rt * G + 1) & ~1);
+  int cur_g = 0, cur_r0 = r_first;
+  auto do_step = [&](auto buf_tag, auto diag_tag, int step) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    const int r0 = cur_r0;
+    swrite(BUF);
+    __syncthreads();
+    if (++cur_g == G) {
+      cur_g = 0;
+      cur_r0 += BQ;
+    }
+    if (step + 1 < n_steps) gload();
+    if constexpr (DIAG) {
+      // Skip blocks where no row of the step sees any key of this wave.
+      if ((int64_t)r0 + BQ - 1 + delta < kw0) return;
+      diag_body(BUF, r0);
+    } else {
+      full_body(BUF);
+    }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int step = 0;
+  if (n_steps > 0) gload();
+  for (; step + 1 < n_diag; step += 2) {
+    do_step(B0{}, std::true_type{}, step);
+    do_step(B1{}, std::true_type{}, step + 1);
   }
+  if (step < n_diag) {                          // odd step count, all in the band
+    do_step(B0{}, std::true_type{}, step);
+    ++step;
+  }
+  for (; step + 1 < n_steps; step += 2) {
+    do_step(B0{}, std::false_type{}, step);
+    do_step(B1{}, std::false_type{}, step + 1);
+  }
+  if (step < n_steps) do_step(B0{}, std::false_type{}, step);
 
   // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
   if (!key_ok) return;
