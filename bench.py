@@ -299,10 +299,15 @@ def main():
     log("steps %d: wall %.3f ms/step, event avg %.3f ms (min %.3f), %.1f TFLOP/s"
         % (args.steps, ms_per_step, avg_launch_s * 1e3, min(launch_ms), value))
 
-    traffic = traffic_for("ca_fwd.hip", w.name)
+    if backward:
+        traffic = traffic_for("ca_bwd.hip", w.name + ":backward")
+        kernel = "ca_backward: bwd_prep_kernel, bwd_q_kernel, bwd_kv_kernel"
+    else:
+        traffic = traffic_for("ca_fwd.hip", w.name)
+        kernel = "ca::fwd_kernel<%d, 8>" % w.d
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "ca::fwd_kernel<128>",
+                "traffic": traffic, "kernel": kernel,
                 "per_launch_flops": flops, "avg_launch_ms": round(avg_launch_s * 1e3, 4)}
 
     sec = None
