@@ -537,14 +537,14 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int j16 = lane & 15;
   const int kt_off = ((j16 >> 2) + 4 * hh) * KS + 16 * (g16 & 1) + 4 * (j16 & 3);
 
-  if (n_tiles > 0) gload(0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    swrite(buf);
-    __syncthreads();
-    if (tile + 1 < n_tiles) gload(tile + 1);
+  // Key tiles [0, n_full) are visible to every row of the workgroup (no mask,
+  // no skip); the rest go through the general body.  Tiles run in LDS-buffer
+  // pairs so that every LDS address is a lane constant plus an immediate.
+  const int n_full = min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN)) & ~1;
+
+  auto diag_body = [&](int buf, int tile) {
     const int k0 = tile * BN;
-    if (k0 >= w_kv_hi) continue;
+    if (k0 >= w_kv_hi) return;
     f32x16 s_acc[2], dp_acc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -596,7 +596,125 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
           dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[mb][half], dq_acc[c], 0, 0, 0);
         }
       }
+    };
+
+  // Fully visible tile, in a fixed issue order (sched_barrier fences; the
+  // empty asm statements keep each chain step where it is written, since IR
+  // passes sink pure calls towards their uses) for a single wave per SIMD:
+  // S^T chains with the next operand reads, dP^T chains with exp, dQ with dS.
+  auto full_body = [&](int buf) {
+    const __bf16* kb = &lds_k[buf][0];
+    const __bf16* vb = &lds_v[buf][0];
+    bf16x8 ka[2][NKS], va[2][NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) ka[0][s] = *(const bf16x8*)(kb + k_row_off + 16 * s);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s_acc[2], dp_acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s_acc[mb] = f32x16_zero();
+      dp_acc[mb] = f32x16_zero();
+    }
+    // S^T mb 0, K rows of mb 1
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      s_acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], qf[s], s_acc[0], 0, 0, 0);
+      asm volatile("" : "+v"(s_acc[0]));
+      ka[1][s] = *(const bf16x8*)(kb + k_row_off + 32 * KS + 16 * s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // S^T mb 1, V rows of mb 0
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      s_acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], qf[s], s_acc[1], 0, 0, 0);
+      asm volatile("" : "+v"(s_acc[1]));
+      va[0][s] = *(const bf16x8*)(vb + v_row_off + 16 * s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dP^T mb 0, exp of S^T mb 0, V rows of mb 1
+    float pv[2][16];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      dp_acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][s], of[s], dp_acc[0], 0, 0, 0);
+      asm volatile("" : "+v"(dp_acc[0]));
+#pragma unroll
+      for (int k = 0; k < 16 / NKS; ++k) {
+        const int r = s * (16 / NKS) + k;
+        pv[0][r] = exp2_fast(fmaf(s_acc[0][r], p.scale_log2, -lse2));
+      }
+      va[1][s] = *(const bf16x8*)(vb + v_row_off + 32 * VS + 16 * s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dP^T mb 1, exp of S^T mb 1, K^T operands of mb 0
+    bf16x4 ktr[2][2][NCB][2];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      dp_acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][s], of[s], dp_acc[1], 0, 0, 0);
+      asm volatile("" : "+v"(dp_acc[1]));
+#pragma unroll
+      for (int k = 0; k < 16 / NKS; ++k) {
+        const int r = s * (16 / NKS) + k;
+        pv[1][r] = exp2_fast(fmaf(s_acc[1][r], p.scale_log2, -lse2));
+      }
+      const int half = s / NCB, c = s % NCB;
+      const __bf16* a0 = kb + kt_off + (16 * half) * KS + c * 32;
+      ktr[0][half][c][0] = ds_read_tr16(a0);
+      ktr[0][half][c][1] = ds_read_tr16(a0 + 8 * KS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dS^T of mb 0
+    bf16x8 dsf[2][2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dsf[0][j >> 3][j & 7] = (__bf16)(pv[0][j] * (dp_acc[0][j] - dval));
+    __builtin_amdgcn_sched_barrier(0);
+    // dQ^T += K^T dS^T for mb 0, dS^T of mb 1, K^T operands of mb 1
+#pragma unroll
+    for (int i = 0; i < 2 * NCB; ++i) {
+      const int half = i / NCB, c = i % NCB;
+      dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(ktr[0][half][c][0], ktr[0][half][c][1]),
+                                                          dsf[0][half], dq_acc[c], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 16 / (2 * NCB); ++k) {
+        const int j = i * (16 / (2 * NCB)) + k;
+        dsf[1][j >> 3][j & 7] = (__bf16)(pv[1][j] * (dp_acc[1][j] - dval));
+      }
+      const __bf16* a0 = kb + kt_off + (32 + 16 * half) * KS + c * 32;
+      ktr[1][half][c][0] = ds_read_tr16(a0);
+      ktr[1][half][c][1] = ds_read_tr16(a0 + 8 * KS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dQ^T for mb 1
+#pragma unroll
+    for (int i = 0; i < 2 * NCB; ++i) {
+      const int half = i / NCB, c = i % NCB;
+      dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(ktr[1][half][c][0], ktr[1][half][c][1]),
+                                                          dsf[1][half], dq_acc[c], 0, 0, 0);
+    }
+  };
+
+  auto do_tile = [&](auto buf_tag, auto full_tag, int tile) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    swrite(BUF);
+    __syncthreads();
+    if (tile + 1 < n_tiles) gload(tile + 1);
+    if constexpr (decltype(full_tag)::value)
+      full_body(BUF);
+    else
+      diag_body(BUF, tile);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int tile = 0;
+  if (n_tiles > 0) gload(0);
+  for (; tile < n_full; tile += 2) {
+    do_tile(B0{}, std::true_type{}, tile);
+    do_tile(B1{}, std::true_type{}, tile + 1);
   }
+  for (; tile + 1 < n_tiles; tile += 2) {
+    do_tile(B0{}, std::false_type{}, tile);
+    do_tile(B1{}, std::false_type{}, tile + 1);
+  }
+  if (tile < n_tiles) do_tile(B0{}, std::false_type{}, tile);
 
   if (!qvalid) return;
   const int64_t base = (t.q_off + qrow) * q_stride + head * D;
