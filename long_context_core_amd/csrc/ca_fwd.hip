@@ -138,20 +138,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // One key tile for this wave.
   auto do_tile = [&](int tile, int buf) {
     const int k0 = tile * BN;
+    // S^T chain with the K operands read KPF steps ahead (fixed by fences:
+    // left alone, the schedule waits on each read right before its MFMA;
+    // 2 steps measured best against 1, 3 and 4).
+    constexpr int KPF = 2;
     f32x16 s_acc[2];
     const __bf16* kl = &lds_k[buf][k_lane_off];
+    bf16x8 kf[NKS][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kl + mb * 32 * KS), qf[0],
-                                                          f32x16_zero(), 0, 0, 0);
-    }
+    for (int s = 0; s < KPF; ++s)
 #pragma unroll
-    for (int s = 1; s < NKS; ++s) {
+      for (int mb = 0; mb < 2; ++mb) kf[s][mb] = *(const bf16x8*)(kl + mb * 32 * KS + 16 * s);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 kf = *(const bf16x8*)(kl + mb * 32 * KS + 16 * s);
-        s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s_acc[mb], 0, 0, 0);
+    for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][mb], qf[s], s == 0 ? f32x16_zero() : s_acc[mb],
+                                                            0, 0, 0);
+      if (s + KPF < NKS) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) kf[s + KPF][mb] = *(const bf16x8*)(kl + mb * 32 * KS + 16 * (s + KPF));
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Mask only where the tile straddles the diagonal or the context end:
     // key k0 + r (r in [0, 64)) is visible iff r <= lim.
