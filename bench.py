@@ -180,6 +180,20 @@ def secondary(steps=3, warmup=1):
     del Q, K, V, O, LSE, ws, Om, Lm
     torch.cuda.empty_cache()
 
+    # Throughput vs shard length in one fused 32K-token chunk
+    sweep = {}
+    for shard in (32, 64, 128, 256, 512, 1024, 2048, 4096, 8192):
+        w = I.shard_sweep_32k(shard)
+        Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 206)
+        fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+        ms = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
+        sweep[str(shard)] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+        del Q, K, V, O, LSE, ws
+    torch.cuda.empty_cache()
+    out["shard_sweep_32k"] = {"workload": "llama3-8b-shards-of-32k (contexts uniform in [0, 8K))",
+                              "by_shard_tokens": sweep}
+    log("shard sweep (32K tokens): " + ", ".join("%s: %.0f" % (k, v["tflops"]) for k, v in sweep.items()))
+
     # Training forward + backward (Llama-3-8B shape, 512K ProLong-like)
     w = I.train_8b_prolong_512k()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 205)
@@ -292,6 +306,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
+    # host side of one call on an idle device: validation, queue build, upload
+    # and launch enqueue (in the timed loop the host runs one call ahead and
+    # waits for the previous upload, so the call time there is not this)
+    host_s = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        step()
+        host_s.append(time.perf_counter() - h0)
+    torch.cuda.synchronize()
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step / 1e3) / 1e12
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
@@ -308,7 +332,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": kernel,
-                "per_launch_flops": flops, "avg_launch_ms": round(avg_launch_s * 1e3, 4)}
+                "per_launch_flops": flops, "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                "host_plan_ms": round(float(np.median(host_s)) * 1e3, 3)}
 
     sec = None
     if not args.no_secondary and args.workload == "llama8b-131k":

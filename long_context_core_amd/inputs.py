@@ -125,6 +125,25 @@ def ca_tasks_34b(seed=103, n_tasks=64, total_q=262144, q_min=512, q_max=8192,
                     qo, ko, qo, doc_lens=docs)
 
 
+def shard_sweep_32k(shard, seed=106, total_q=32768, ctx_max=8192):
+    """One fused 32K-token chunk of query shards of ``shard`` tokens each
+    (Llama-3-8B attention shape: 32 query heads, 8 KV heads, d = 128).  Shard
+    k is the last ``shard`` tokens of its own document, whose earlier context
+    is uniform in [0, ctx_max); every shard carries its own context.  The
+    shard length is the swept variable; the aggregate query tokens are fixed."""
+    rng = np.random.default_rng(seed)
+    n = total_q // shard
+    ctx = rng.integers(0, ctx_max, size=n)
+    t = []
+    ko = 0
+    for k in range(n):
+        c = int(ctx[k])
+        t.append((k * shard, ko, k * shard, shard, c + shard, c, 0))
+        ko += c + shard
+    return Workload("llama3-8b-shards-%d-of-32k" % shard, 32, 8, 128, np.array(t, dtype=np.int64),
+                    n * shard, ko, n * shard)
+
+
 def ring_prefill_405b_tp8(total=131072, n=8):
     """One GPU's share of Llama3-405B under TP8 (16 query heads, 1 KV head,
     d = 128): one causal document of ``total`` tokens split into n contiguous

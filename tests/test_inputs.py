@@ -76,3 +76,15 @@ def test_prolong_like():
     assert lens.sum() == 524288
     long_tokens = lens[lens >= 65536].sum()
     assert 196608 <= long_tokens <= 262144
+
+
+@pytest.mark.parametrize("shard", [32, 128, 8192])
+def test_shard_sweep(shard):
+    w = I.shard_sweep_32k(shard)
+    check_table(w)
+    t = w.tasks
+    assert w.q_rows == 32768 and (t[:, 3] == shard).all()
+    # each shard ends its document: last query sees the whole context
+    assert (t[:, 5] + t[:, 3] == t[:, 4]).all() and (t[:, 6] == 0).all()
+    assert (t[:, 5] >= 0).all() and (t[:, 5] < 8192).all()
+    assert np.array_equal(I.shard_sweep_32k(shard).tasks, t)
