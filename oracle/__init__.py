@@ -10,6 +10,8 @@ Modules
 attention  forward / merge / backward / decode written as the plain definition
            of softmax(scale * Q K^T + mask) V, in float64.
 counting   unmasked (query, key) pair counts and the FLOP convention.
+scheduler  the profiler cost model, Appendix-B shard sizing and the
+           communication-aware greedy placement of CA-tasks on servers.
 
 Parity status of every function is stated in its own docstring; all of them
 are pinned by ``tests/test_oracle_pins.py`` except where a docstring says
