@@ -194,6 +194,50 @@ def secondary(steps=3, warmup=1):
                               "by_shard_tokens": sweep}
     log("shard sweep (32K tokens): " + ", ".join("%s: %.0f" % (k, v["tflops"]) for k, v in sweep.items()))
 
+    # CA-task scheduling of the 512K training batch onto 8 attention servers:
+    # profiled forward cost grid -> greedy placement -> each server's tasks
+    # timed on this GPU, before (equal token blocks) and after scheduling
+    from long_context_core_amd import sched
+    w = I.train_8b_prolong_512k()
+    docs = [int(x) for x in w.doc_lens]
+    gq, gkv = [128, 1024, 8192], [1024, 16384, 131072, 524288]
+    grid = sched.profile_grid(gq, gkv, w.hq, w.hkv, w.d)
+    fpp = 4 * w.d * w.hq
+    k = 8
+    init = ca.schedule(docs, k, gq, gkv, grid, fpp, w.hq, w.hkv, w.d, max_moves=0)
+    res = ca.schedule(docs, k, gq, gkv, grid, fpp, w.hq, w.hkv, w.d, eps=0.05)
+    Q = I.randn_bf16((w.q_rows, w.hq, w.d), 207, device=dev)
+    K = I.randn_bf16((w.kv_rows, w.hkv, w.d), 208, device=dev)
+    V = I.randn_bf16((w.kv_rows, w.hkv, w.d), 209, device=dev)
+    O = torch.empty((w.o_rows, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((w.o_rows, w.hq), device=dev)
+    shape = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
+
+    def server_ms(items):
+        ms = []
+        for s in range(k):
+            tasks = ca.sched_tasks(items[items["server"] == s], docs)
+            ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+            ms.append(timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream),
+                            steps, warmup, stream))
+        return ms
+
+    ms_before, ms_after = server_ms(init[0]), server_ms(res[0])
+    out["sched_512k_8_servers"] = {
+        "workload": w.name + ", forward, 8 attention servers",
+        "cost_grid": {"n_q": gq, "n_kv": gkv, "seconds_per_task": grid},
+        "predicted_ms_before": [round(x * 1e3, 2) for x in init[1]],
+        "predicted_ms_after": [round(x * 1e3, 2) for x in res[2]],
+        "measured_ms_before": [round(x, 2) for x in ms_before],
+        "measured_ms_after": [round(x, 2) for x in ms_after],
+        "max_over_mean_before": round(max(ms_before) / (sum(ms_before) / k), 3),
+        "max_over_mean_after": round(max(ms_after) / (sum(ms_after) / k), 3),
+        "bytes_moved": res[3], "migrations": res[4], "items": int(len(res[0]))}
+    log("schedule 512K on 8 servers: measured max/mean %.3f -> %.3f, %d migrations, %.1f MB moved"
+        % (max(ms_before) / (sum(ms_before) / k), max(ms_after) / (sum(ms_after) / k), res[4], res[3] / 1e6))
+    del Q, K, V, O, LSE
+    torch.cuda.empty_cache()
+
     # Training forward + backward (Llama-3-8B shape, 512K ProLong-like)
     w = I.train_8b_prolong_512k()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 205)

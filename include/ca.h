@@ -162,6 +162,73 @@ ca_status ca_backward(const ca_shape* shape, const ca_task* tasks_host, int32_t 
                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* CA-task scheduling (host only; no device memory, no HIP calls)          */
+/* ---------------------------------------------------------------------- */
+/* The profiler cost model and the communication-aware greedy scheduler of
+ * "Efficient Long-context Language Model Training by Core Attention
+ * Disaggregation", Section 4.2 (The Profiler and Cost Model; The
+ * Communication-Aware Greedy Scheduler, Steps 1-4) and Appendix B (Optimal
+ * Shard Dimension Computation).  A batch of documents, first placed on k
+ * devices in equal token blocks, is rebalanced across k attention servers by
+ * migrating whole Items or Appendix-B-sized shards, the move that carries the
+ * most predicted time per byte of communication first.
+ *
+ * Cost model: a measured grid of times (seconds) of one attention call with
+ * n_q queries that are the last n_q tokens of an n_kv-token causal context,
+ * at grid_q[i] x grid_kv[j] (both strictly increasing, >= 1), row-major
+ * [n_gq][n_gkv].  Inside the grid: bilinear interpolation of time.  Beyond
+ * it in both coordinates: FLOPs / the best measured throughput (saturated).
+ * Beyond it in one coordinate: FLOPs / the throughput at the point clamped
+ * into the grid.  FLOPs = flops_per_pair x visible pairs of the block, with
+ * the query count capped at n_kv. */
+typedef struct {
+  int32_t k;               /* attention servers (>= 1)                                */
+  int32_t hq, hkv, d;      /* attention shape; bytes per token sent: q hq*d*2, kv hkv*d*2 */
+  double eps;              /* stop when a deficit is <= eps * target load (>= 0)      */
+  double e_min;            /* migrations need E = dF / bytes > e_min                  */
+  int64_t min_shard;       /* shortest query range a split may move (>= 1)           */
+  int32_t max_moves;       /* cap on migrations (>= 0)                                */
+  double flops_per_pair;   /* FLOPs the profiled call counts per visible pair (> 0)   */
+} ca_sched_params;
+
+typedef struct {
+  int32_t server;          /* attention server 0..k-1                                 */
+  int32_t doc;             /* document index                                          */
+  int64_t q_begin, q_end;  /* query range [q_begin, q_end) of the document; its
+                              context is the document prefix [0, q_end)              */
+} ca_sched_item;           /* 24 bytes                                                */
+
+/* Predicted seconds of an (n_q, n_kv) block under the cost model above; NaN
+ * for an invalid grid. */
+double ca_cost_time(const double* grid_q_host, int32_t n_gq, const double* grid_kv_host, int32_t n_gkv,
+                    const double* grid_time_host, double flops_per_pair, int64_t n_q, int64_t n_kv);
+
+/* Upper bound of the number of Items ca_schedule can return (-1 if invalid). */
+int32_t ca_schedule_max_items(int32_t n_docs, int32_t k, int32_t max_moves);
+
+/* Schedules the documents (lengths >= 0, in batch order) onto p->k servers.
+ * Writes the Items (every document's query positions partitioned exactly
+ * once), the per-server predicted loads before and after [k], the bytes moved
+ * and the number of migrations.  All pointers are host memory owned by the
+ * caller.  Deterministic.  Errors: CA_ERR_INVALID for bad parameters or grid;
+ * CA_ERR_WORKSPACE (with *n_items set to the count needed) when the Items do
+ * not fit in max_items. */
+ca_status ca_schedule(const ca_sched_params* p, const int64_t* doc_lens_host, int32_t n_docs,
+                      const double* grid_q_host, int32_t n_gq, const double* grid_kv_host, int32_t n_gkv,
+                      const double* grid_time_host, ca_sched_item* items_host, int32_t max_items,
+                      int32_t* n_items, double* load_before_host, double* load_after_host,
+                      double* comm_bytes, int32_t* n_moves);
+
+/* CA-task records of Items over the packed batch (documents back to back in
+ * Q, K, V and O): q_off = o_off = start(doc) + q_begin, kv_off = start(doc),
+ * q_len = q_end - q_begin, kv_len = q_end, q_pos0 = q_begin, kv_pos0 = 0.
+ * Running the records of every server reproduces the causal attention of the
+ * whole batch.  Errors: CA_ERR_INVALID for an Item outside its document or
+ * kv_len beyond int32. */
+ca_status ca_sched_tasks(const ca_sched_item* items_host, int32_t n_items, const int64_t* doc_lens_host,
+                         int32_t n_docs, ca_task* tasks_host);
+
+/* ---------------------------------------------------------------------- */
 /* Accounting and errors                                                   */
 /* ---------------------------------------------------------------------- */
 

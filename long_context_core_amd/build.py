@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libca.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["ca_api.cpp", "ca_fwd.hip", "ca_merge.hip", "ca_decode.hip", "ca_bwd.hip"]
+SOURCES = ["ca_api.cpp", "ca_sched.cpp", "ca_fwd.hip", "ca_merge.hip", "ca_decode.hip", "ca_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -29,10 +29,6 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
     # no packed fp32 ALU ops (v_pk_{add,mul,fma}_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # inputs are finite by contract and the kernels use -inf but never NaN:
-    # without this, every fmaxf on an MFMA result is preceded by a
-    # canonicalising v_max (IEEE mode), tripling the cost of row maxima
-    "-fno-honor-nans",
     # keep MFMA accumulators in the VGPR form: with the AGPR form the register
     # allocator shuttles loop-carried accumulators between AGPRs and VGPRs
     # every iteration (hundreds of v_accvgpr moves per tile in the backward)
@@ -48,9 +44,17 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libca.so)")
 
 
+# Kernel sources only (.hip): inputs are finite by contract and the kernels
+# use -inf but never NaN; without this, every fmaxf on an MFMA result is
+# preceded by a canonicalising v_max (IEEE mode), tripling the cost of row
+# maxima.  Host sources (.cpp) keep IEEE NaN semantics for argument checks.
+KERNEL_ONLY_FLAGS = ["-fno-honor-nans"]
+
+
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    kflags = KERNEL_ONLY_FLAGS if src.endswith(".hip") else []
+    cmd = [hipcc()] + HIPCC_FLAGS + kflags + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)

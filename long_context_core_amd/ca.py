@@ -31,6 +31,10 @@ EXPORTS = (
     "ca_backward_workspace",
     "ca_backward",
     "ca_visible_pairs",
+    "ca_cost_time",
+    "ca_schedule_max_items",
+    "ca_schedule",
+    "ca_sched_tasks",
     "ca_status_string",
     "ca_last_error",
 )
@@ -46,6 +50,17 @@ class Shape(ctypes.Structure):
     _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
                 ("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64), ("o_rows", ctypes.c_int64)]
+
+
+class SchedParams(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("eps", ctypes.c_double), ("e_min", ctypes.c_double), ("min_shard", ctypes.c_int64),
+                ("max_moves", ctypes.c_int32), ("flops_per_pair", ctypes.c_double)]
+
+
+# numpy view of the C struct ca_sched_item (24 bytes)
+SCHED_ITEM_DTYPE = np.dtype([("server", "<i4"), ("doc", "<i4"), ("q_begin", "<i8"), ("q_end", "<i8")])
+assert SCHED_ITEM_DTYPE.itemsize == 24
 
 
 class CAError(RuntimeError):
@@ -83,6 +98,16 @@ def lib():
         L.ca_backward.restype = ctypes.c_int
         L.ca_visible_pairs.argtypes = [vp, i32]
         L.ca_visible_pairs.restype = i64
+        dbl = ctypes.c_double
+        L.ca_cost_time.argtypes = [vp, i32, vp, i32, vp, dbl, i64, i64]
+        L.ca_cost_time.restype = dbl
+        L.ca_schedule_max_items.argtypes = [i32, i32, i32]
+        L.ca_schedule_max_items.restype = i32
+        L.ca_schedule.argtypes = [ctypes.POINTER(SchedParams), vp, i32, vp, i32, vp, i32, vp, vp, i32,
+                                  vp, vp, vp, vp, vp]
+        L.ca_schedule.restype = ctypes.c_int
+        L.ca_sched_tasks.argtypes = [vp, i32, vp, i32, vp]
+        L.ca_sched_tasks.restype = ctypes.c_int
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
         L.ca_last_error.argtypes = []
@@ -203,3 +228,53 @@ def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None
                            ws.numel(), _stream_ptr(stream))
     _check(st)
     return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------
+# CA-task scheduling (host)
+# ---------------------------------------------------------------------------
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def cost_time(grid_q, grid_kv, grid_time, flops_per_pair, n_q, n_kv):
+    """Predicted seconds of an (n_q, n_kv) block under the measured grid."""
+    gq, gkv, gt = _f64(grid_q), _f64(grid_kv), _f64(grid_time)
+    return lib().ca_cost_time(gq.ctypes.data, len(gq), gkv.ctypes.data, len(gkv), gt.ctypes.data,
+                              float(flops_per_pair), int(n_q), int(n_kv))
+
+
+def schedule(doc_lens, k, grid_q, grid_kv, grid_time, flops_per_pair, hq, hkv, d,
+             eps=0.05, e_min=0.0, min_shard=128, max_moves=10000):
+    """Greedy placement of the documents on k attention servers.  Returns
+    (items as SCHED_ITEM_DTYPE records, loads_before[k], loads_after[k],
+    bytes moved, number of migrations)."""
+    L = lib()
+    docs = np.ascontiguousarray(np.asarray(doc_lens, dtype=np.int64))
+    gq, gkv, gt = _f64(grid_q), _f64(grid_kv), _f64(grid_time)
+    p = SchedParams(int(k), int(hq), int(hkv), int(d), float(eps), float(e_min), int(min_shard),
+                    int(max_moves), float(flops_per_pair))
+    cap = L.ca_schedule_max_items(len(docs), int(k), int(max_moves))
+    if cap < 0:
+        raise CAError(CA_ERR_INVALID, "bad schedule size")
+    items = np.zeros(max(cap, 1), dtype=SCHED_ITEM_DTYPE)
+    before = np.zeros(int(k), dtype=np.float64)
+    after = np.zeros(int(k), dtype=np.float64)
+    n_items = ctypes.c_int32(0)
+    comm = ctypes.c_double(0.0)
+    moves = ctypes.c_int32(0)
+    _check(L.ca_schedule(ctypes.byref(p), docs.ctypes.data, len(docs), gq.ctypes.data, len(gq),
+                         gkv.ctypes.data, len(gkv), gt.ctypes.data, items.ctypes.data, len(items),
+                         ctypes.byref(n_items), before.ctypes.data, after.ctypes.data,
+                         ctypes.byref(comm), ctypes.byref(moves)))
+    return items[:n_items.value].copy(), before, after, comm.value, moves.value
+
+
+def sched_tasks(items, doc_lens):
+    """ca_task records of scheduled Items over the packed batch."""
+    it = np.ascontiguousarray(items, dtype=SCHED_ITEM_DTYPE)
+    docs = np.ascontiguousarray(np.asarray(doc_lens, dtype=np.int64))
+    out = np.zeros(len(it), dtype=TASK_DTYPE)
+    _check(lib().ca_sched_tasks(it.ctypes.data, len(it), docs.ctypes.data, len(docs), out.ctypes.data))
+    return out

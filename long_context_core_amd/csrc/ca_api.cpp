@@ -42,6 +42,20 @@ ca_status fail(ca_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+ca_status ca::set_error(ca_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+namespace {
+
 ca_status hip_fail(hipError_t e, const char* what) {
   return fail(CA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }

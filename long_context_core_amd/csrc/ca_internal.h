@@ -132,4 +132,7 @@ hipError_t launch_f32_to_bf16(const float* src, __bf16* dst, int64_t n, hipStrea
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_zero_bf16(__bf16* p, int64_t n, hipStream_t s);
 
+// Records the thread's last-error text (ca_last_error) and returns st.
+ca_status set_error(ca_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 }  // namespace ca

@@ -59,7 +59,8 @@ class CostModel:
     time over the bracketing cell.  Beyond the grid in both coordinates (the
     saturated region): FLOPs / the maximum measured throughput.  Beyond it in
     one coordinate only: FLOPs / the throughput interpolated at the point
-    clamped into the grid."""
+    clamped into the grid.  FLOPs count min(n_q, n_kv) queries (a grid point
+    with more queries than context stands for the full causal block)."""
 
     def __init__(self, grid_q, grid_kv, times, flops_per_pair):
         self.q = [float(x) for x in grid_q]
@@ -75,7 +76,10 @@ class CostModel:
         self.peak = best
 
     def flops(self, n_q, n_kv):
-        return self.fpp * (n_q * n_kv - n_q * (n_q - 1) / 2.0)
+        """FLOPs of the block; a query block longer than its context is read
+        as one of n_kv queries (every query of a causal block has its key)."""
+        m = min(n_q, n_kv)
+        return self.fpp * (m * n_kv - m * (m - 1) / 2.0)
 
     @staticmethod
     def _bracket(axis, x):
