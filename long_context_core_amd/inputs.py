@@ -144,6 +144,62 @@ def shard_sweep_32k(shard, seed=106, total_q=32768, ctx_max=8192):
                     n * shard, ko, n * shard)
 
 
+# --------------------------------------------------------------------------
+# sparse-mask recipes ("Dynamic Context Parallelism", Section 2.4, Figure 6)
+# --------------------------------------------------------------------------
+
+def lambda_tasks(doc_lens, window=4096, sink=64):
+    """Lambda mask per packed document: every token sees the first ``sink``
+    tokens of its document and its ``window`` latest tokens (itself
+    included).  (n, 9) table: the varlen tasks plus window / sink columns."""
+    t = varlen_tasks(doc_lens)
+    w = np.zeros((len(t), 2), dtype=np.int64)
+    w[:, 0] = window
+    w[:, 1] = sink
+    return np.concatenate([t, w], axis=1)
+
+
+def blockwise_tasks(doc_lens, block=256, win_blocks=2):
+    """Causal-blockwise mask per packed document, as two partial slots to be
+    merged by Equation 4 (output rows o_off in slot s are s * T + row):
+    documents are cut into blocks of ``block`` tokens (in-context examples);
+    a token of block b sees block 0 (the sink block), blocks b - win_blocks + 1
+    .. b - 1 and its own block up to itself; the last block of a document (the
+    test example) sees everything before it.  Slot 0 holds the window part
+    (the causal context from the window's first block), slot 1 the sink block
+    when the window does not reach it."""
+    T = int(sum(doc_lens))
+    t = []
+    off = 0
+    for L in doc_lens:
+        nb = -(-L // block)
+        for b in range(nb):
+            q0, q1 = b * block, min(L, (b + 1) * block)
+            last = b == nb - 1
+            k0 = 0 if last else max(0, b - win_blocks + 1) * block
+            t.append((off + q0, off + k0, off + q0, q1 - q0, q1 - k0, q0, k0))
+            if not last and k0 > 0:
+                t.append((off + q0, off, T + off + q0, q1 - q0, block, q0, 0))
+        off += L
+    return np.array(t, dtype=np.int64).reshape(-1, 7), 2
+
+
+def shared_question_tasks(question, answers):
+    """Shared-question mask (one question, several answers packed after it):
+    the question is causal; each answer sees the whole question and itself
+    causally, never another answer.  Two partial slots to be merged by
+    Equation 4: slot 0 holds causal self-attention of every segment, slot 1
+    the answers' attention to the question."""
+    T = int(question + sum(answers))
+    t = [(0, 0, 0, question, question, 0, 0)]
+    off = question
+    for a in answers:
+        t.append((off, off, off, a, a, 0, 0))
+        t.append((off, 0, T + off, a, question, question, 0))
+        off += a
+    return np.array(t, dtype=np.int64).reshape(-1, 7), 2
+
+
 def ring_prefill_405b_tp8(total=131072, n=8):
     """One GPU's share of Llama3-405B under TP8 (16 query heads, 1 KV head,
     d = 128): one causal document of ``total`` tokens split into n contiguous

@@ -20,6 +20,7 @@ are pinned by ``tests/test_oracle_pins.py`` except where a docstring says
 
 from .attention import (  # noqa: F401
     TASK_FIELDS,
+    MASK_FIELDS,
     bf16_bits_to_f64,
     visible_mask,
     forward,
@@ -29,6 +30,7 @@ from .attention import (  # noqa: F401
 )
 from .counting import (  # noqa: F401
     visible_pairs_task,
+    visible_pairs_masked,
     visible_pairs,
     forward_flops,
     backward_flops,

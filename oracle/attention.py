@@ -39,6 +39,15 @@ An ``(n, 7)`` int64 array, one row per CA-task, columns ``TASK_FIELDS``:
   kv_pos0 document position of the first context row
 
 Key j of a task is visible to its query i  iff  kv_pos0 + j <= q_pos0 + i.
+
+Two optional columns after these, ``MASK_FIELDS`` (0 when absent), narrow the
+causal mask to the lambda shape of the sparse masks ("Dynamic Context
+Parallelism", Section 2.4 / Figure 6b): an attention sink plus a sliding
+window.  With kp = kv_pos0 + j and qp = q_pos0 + i, the key is visible iff
+kp <= qp and (window == 0 or kp > qp - window or kp < sink): every query sees
+the first ``sink`` positions and its ``window`` latest positions (itself
+included).  Causal-blockwise and shared-question masks are unions of causal
+task contexts and are written as several tasks merged by Equation 4.
 A row with no visible key has O = 0 and LSE = -inf (a reading: the pages do
 not discuss empty rows; this is the value that gives the row zero weight in
 Equation 4).
@@ -50,6 +59,7 @@ LSE [To, Hq].  bf16 inputs are widened exactly by ``bf16_bits_to_f64``.
 import numpy as np
 
 TASK_FIELDS = ("q_off", "kv_off", "o_off", "q_len", "kv_len", "q_pos0", "kv_pos0")
+MASK_FIELDS = ("window", "sink")
 
 # Row-chunk budget for materialised score blocks (elements of float64).
 _CHUNK_ELEMS = 1 << 24
@@ -67,11 +77,15 @@ def bf16_bits_to_f64(bits):
 
 
 def _as_tasks(tasks):
+    """(n, 7) or (n, 9) int table -> (n, 9) with zero window / sink columns
+    where absent."""
     t = np.asarray(tasks, dtype=np.int64)
     if t.ndim == 1:
         t = t.reshape(1, -1)
-    if t.shape[1] != len(TASK_FIELDS):
-        raise ValueError("task table must have columns %s" % (TASK_FIELDS,))
+    if t.shape[1] == len(TASK_FIELDS):
+        t = np.concatenate([t, np.zeros((len(t), len(MASK_FIELDS)), dtype=np.int64)], axis=1)
+    if t.shape[1] != len(TASK_FIELDS) + len(MASK_FIELDS):
+        raise ValueError("task table must have columns %s (+ %s)" % (TASK_FIELDS, MASK_FIELDS))
     return t
 
 
@@ -85,18 +99,24 @@ def visible_mask(task, rows, n_keys):
 
     The definition of the causal CA-task mask: document position of key j is
     kv_pos0 + j, of query i is q_pos0 + i; a key is visible iff its position
-    does not exceed the query's (diagonal included).
+    does not exceed the query's (diagonal included).  With a window (column 8)
+    it must also lie within the query's ``window`` latest positions or below
+    ``sink`` (column 9).
     """
-    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task)
+    t = _as_tasks(task)[0]
+    q_pos0, kv_pos0, window, sink = int(t[5]), int(t[6]), int(t[7]), int(t[8])
     qpos = q_pos0 + np.asarray(rows, dtype=np.int64)
     kpos = kv_pos0 + np.arange(n_keys, dtype=np.int64)
-    return kpos[None, :] <= qpos[:, None]
+    vis = kpos[None, :] <= qpos[:, None]
+    if window > 0:
+        vis &= (kpos[None, :] > qpos[:, None] - window) | (kpos[None, :] < sink)
+    return vis
 
 
 def _context_len(task, rows):
     """How many leading context rows any of ``rows`` can see (keys past this
     are invisible to every row in the set)."""
-    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task)
+    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task[:7])
     if len(rows) == 0:
         return 0
     last = q_pos0 + int(np.max(rows)) - kv_pos0 + 1
@@ -119,7 +139,7 @@ def _head_rows(task, rows, h, Q, K, V, scale, hq, hkv):
     keys, m = max s, w = exp(s - m), l = sum w, O = sum w v / l,
     LSE = m + ln l.  No online rescaling, no blocking of the key axis.
     """
-    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task)
+    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task[:7])
     g = _group_of(h, hq, hkv)
     n = _context_len(task, rows)
     d = Q.shape[2]

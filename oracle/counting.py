@@ -24,10 +24,32 @@ def visible_pairs_task(q_len, kv_len, q_pos0, kv_pos0):
     return int(per_row.sum())
 
 
+def visible_pairs_masked(q_len, kv_len, q_pos0, kv_pos0, window, sink):
+    """Pairs under the sink + sliding-window mask, row by row: the causal
+    context of row i is positions [kv_pos0, kv_pos0 + c_i); of those it sees
+    the ones above qp - window and the ones below sink (window 0: all)."""
+    if int(window) <= 0:
+        return visible_pairs_task(q_len, kv_len, q_pos0, kv_pos0)
+    total = 0
+    for i in range(int(q_len)):
+        qp = int(q_pos0) + i
+        hi = int(kv_pos0) + min(int(kv_len), max(0, qp - int(kv_pos0) + 1))   # end of the causal context
+        lo = int(kv_pos0)
+        win_lo = max(lo, qp - int(window) + 1)
+        n_win = max(0, hi - win_lo)
+        n_sink = max(0, min(int(sink), hi, win_lo) - lo)
+        total += n_win + n_sink
+    return total
+
+
 def visible_pairs(tasks):
-    """Unmasked pairs of a whole task table (columns as oracle.TASK_FIELDS)."""
-    t = np.asarray(tasks, dtype=np.int64).reshape(-1, 7)
-    return int(sum(visible_pairs_task(r[3], r[4], r[5], r[6]) for r in t))
+    """Unmasked pairs of a whole task table (columns as oracle.TASK_FIELDS,
+    optionally followed by window and sink)."""
+    t = np.asarray(tasks, dtype=np.int64)
+    t = t.reshape(-1, t.shape[-1]) if t.size else t.reshape(0, 7)
+    if t.shape[1] == 7:
+        return int(sum(visible_pairs_task(r[3], r[4], r[5], r[6]) for r in t))
+    return int(sum(visible_pairs_masked(r[3], r[4], r[5], r[6], r[7], r[8]) for r in t))
 
 
 def forward_flops(pairs, hq, d):
