@@ -84,6 +84,23 @@ typedef struct {
   int64_t kv_pos0; /* document position of context row 0                   */
 } ca_task;
 
+/*
+ * Optional per-task narrowing of the causal mask to the lambda shape of the
+ * sparse masks of "Dynamic Context Parallelism" (Section 2.4, Figure 6b): an
+ * attention sink plus a sliding window.  With kp = kv_pos0 + j and
+ * qp = q_pos0 + i, key j is visible to query i iff
+ *     kp <= qp  and  (window == 0  or  kp > qp - window  or  kp < sink):
+ * the query sees its `window` latest positions (itself included) and every
+ * position below `sink`.  window == 0 is the plain causal task (sink unused).
+ * Causal-blockwise and shared-question masks are unions of causal task
+ * contexts: write them as tasks into separate partial slots and combine the
+ * slots with ca_merge.
+ */
+typedef struct {
+  int32_t window;  /* >= 0                                                 */
+  int32_t sink;    /* >= 0                                                 */
+} ca_task_mask;
+
 enum {
   CA_OUT_F32 = 1u << 0 /* forward/merge: write O as fp32 (partials for a later merge) */
 };
@@ -116,6 +133,16 @@ size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, in
 ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks,
                      const void* Q, const void* K, const void* V, void* O, float* LSE,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* ca_forward with a ca_task_mask per task (masks_host may be NULL: all
+ * causal).  Single-row tasks with a window run in the tiled kernel instead
+ * of the split-KV decode kernel.  Errors as ca_forward, plus CA_ERR_INVALID
+ * for a negative window or sink. */
+size_t ca_forward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host,
+                                   const ca_task_mask* masks_host, int32_t n_tasks);
+ca_status ca_forward_masked(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                            int32_t n_tasks, const void* Q, const void* K, const void* V, void* O,
+                            float* LSE, void* ws, size_t ws_bytes, void* stream);
 
 /* Packed causal documents: document i occupies rows [cu[i], cu[i+1]) of Q,
  * K, V, O and LSE (the task {cu[i], cu[i], cu[i], l, l, 0, 0}).
@@ -236,6 +263,8 @@ ca_status ca_sched_tasks(const ca_sched_item* items_host, int32_t n_items, const
  * (FLOPs = 4 d pairs hq forward, 10 d pairs hq backward).  -1 on an invalid
  * table. */
 int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks);
+/* The same under per-task masks (masks_host may be NULL). */
+int64_t ca_visible_pairs_masked(const ca_task* tasks_host, const ca_task_mask* masks_host, int32_t n_tasks);
 
 const char* ca_status_string(ca_status status);
 const char* ca_last_error(void);

@@ -31,6 +31,9 @@ EXPORTS = (
     "ca_backward_workspace",
     "ca_backward",
     "ca_visible_pairs",
+    "ca_visible_pairs_masked",
+    "ca_forward_masked_workspace",
+    "ca_forward_masked",
     "ca_cost_time",
     "ca_schedule_max_items",
     "ca_schedule",
@@ -44,6 +47,10 @@ TASK_DTYPE = np.dtype([("q_off", "<i8"), ("kv_off", "<i8"), ("o_off", "<i8"),
                        ("q_len", "<i4"), ("kv_len", "<i4"),
                        ("q_pos0", "<i8"), ("kv_pos0", "<i8")])
 assert TASK_DTYPE.itemsize == 48
+
+# numpy view of the C struct ca_task_mask (8 bytes)
+MASK_DTYPE = np.dtype([("window", "<i4"), ("sink", "<i4")])
+assert MASK_DTYPE.itemsize == 8
 
 
 class Shape(ctypes.Structure):
@@ -98,6 +105,12 @@ def lib():
         L.ca_backward.restype = ctypes.c_int
         L.ca_visible_pairs.argtypes = [vp, i32]
         L.ca_visible_pairs.restype = i64
+        L.ca_visible_pairs_masked.argtypes = [vp, vp, i32]
+        L.ca_visible_pairs_masked.restype = i64
+        L.ca_forward_masked_workspace.argtypes = [sp, vp, vp, i32]
+        L.ca_forward_masked_workspace.restype = sz
+        L.ca_forward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_forward_masked.restype = ctypes.c_int
         dbl = ctypes.c_double
         L.ca_cost_time.argtypes = [vp, i32, vp, i32, vp, dbl, i64, i64]
         L.ca_cost_time.restype = dbl
@@ -163,17 +176,47 @@ def _tasks_ptr(ta):
     return ta.ctypes.data_as(ctypes.c_void_p) if len(ta) else None
 
 
-def visible_pairs(tasks):
+def split_tasks(tasks, masks=None):
+    """(ca_task records, ca_task_mask records or None) from an (n, 7) table
+    plus optional masks, or an (n, 9) table whose last two columns are
+    window and sink."""
+    if not (isinstance(tasks, np.ndarray) and tasks.dtype == TASK_DTYPE):
+        t = np.asarray(tasks, dtype=np.int64)
+        t = t.reshape(-1, t.shape[-1]) if t.size else t.reshape(0, 7)
+        if t.shape[1] == 9:
+            if masks is None:
+                masks = t[:, 7:9]
+            t = t[:, :7]
+        tasks = t
     ta = task_array(tasks)
-    n = lib().ca_visible_pairs(_tasks_ptr(ta), len(ta))
+    if masks is None:
+        return ta, None
+    if isinstance(masks, np.ndarray) and masks.dtype == MASK_DTYPE:
+        ma = np.ascontiguousarray(masks)
+    else:
+        mm = np.asarray(masks, dtype=np.int64).reshape(-1, 2)
+        ma = np.zeros(len(mm), dtype=MASK_DTYPE)
+        ma["window"], ma["sink"] = mm[:, 0], mm[:, 1]
+    if len(ma) != len(ta):
+        raise CAError(CA_ERR_INVALID, "one mask per task required")
+    return ta, ma
+
+
+def _mask_ptr(ma):
+    return None if ma is None else ma.ctypes.data_as(ctypes.c_void_p)
+
+
+def visible_pairs(tasks, masks=None):
+    ta, ma = split_tasks(tasks, masks)
+    n = lib().ca_visible_pairs_masked(_tasks_ptr(ta), _mask_ptr(ma), len(ta))
     if n < 0:
         raise CAError(CA_ERR_INVALID, "invalid task table")
     return int(n)
 
 
-def forward_workspace(shape, tasks):
-    ta = task_array(tasks)
-    return int(lib().ca_forward_workspace(ctypes.byref(shape), _tasks_ptr(ta), len(ta)))
+def forward_workspace(shape, tasks, masks=None):
+    ta, ma = split_tasks(tasks, masks)
+    return int(lib().ca_forward_masked_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta)))
 
 
 def workspace_tensor(nbytes, device):
@@ -181,14 +224,20 @@ def workspace_tensor(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None):
+def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None):
     """ca_forward on torch tensors: Q [q_rows, hq, d] bf16, K/V [kv_rows, hkv, d]
-    bf16, O [o_rows, hq, d] bf16 (fp32 with out_f32), LSE [o_rows, hq] fp32."""
-    ta = task_array(tasks)
+    bf16, O [o_rows, hq, d] bf16 (fp32 with out_f32), LSE [o_rows, hq] fp32.
+    With masks (or a 9-column table) it calls ca_forward_masked."""
+    ta, ma = split_tasks(tasks, masks)
     if ws is None:
-        ws = workspace_tensor(forward_workspace(shape, ta), Q.device)
-    st = lib().ca_forward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
-                          _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
+        ws = workspace_tensor(forward_workspace(shape, ta, ma), Q.device)
+    if ma is None:
+        st = lib().ca_forward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
+                              _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    else:
+        st = lib().ca_forward_masked(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta), _ptr(Q),
+                                     _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(),
+                                     _stream_ptr(stream))
     _check(st)
     return O, LSE
 

@@ -81,6 +81,34 @@ int64_t range_pairs(int64_t a, int64_t b, int64_t delta, int64_t kv_len) {
   return total;
 }
 
+// Window and sink of task i (no mask array: causal, window 0).  The sink is
+// only meaningful with a window; it is returned as a task-relative key count.
+int32_t task_window(const ca_task_mask* m, int32_t i) { return m ? m[i].window : 0; }
+int64_t task_sink_keys(const ca_task* t, const ca_task_mask* m, int32_t i) {
+  if (!m || m[i].window <= 0) return 0;
+  return std::min<int64_t>(t[i].kv_len, std::max<int64_t>(0, (int64_t)m[i].sink - t[i].kv_pos0));
+}
+
+// range_pairs under the sink + sliding-window mask: row i sees the keys of
+// its causal context [0, c_i) that are >= i + delta - win + 1 or < sj.
+int64_t range_pairs_masked(int64_t a, int64_t b, int64_t delta, int64_t kv_len, int64_t win, int64_t sj) {
+  if (win <= 0) return range_pairs(a, b, delta, kv_len);
+  int64_t total = 0;
+  for (int64_t i = a; i <= b; ++i) {
+    const int64_t c = std::min(kv_len, std::max<int64_t>(0, i + delta + 1));
+    const int64_t wlo = std::max<int64_t>(0, i + delta - win + 1);
+    total += std::max<int64_t>(0, c - wlo) + std::max<int64_t>(0, std::min(std::min(sj, c), wlo));
+  }
+  return total;
+}
+
+ca_status check_masks(const ca_task_mask* m, int32_t n) {
+  if (!m) return CA_OK;
+  for (int32_t i = 0; i < n; ++i)
+    if (m[i].window < 0 || m[i].sink < 0) return fail(CA_ERR_INVALID, "task %d: negative window or sink", i);
+  return CA_OK;
+}
+
 ca_status check_shape(const ca_shape* s) {
   if (!s) return fail(CA_ERR_INVALID, "shape is NULL");
   if (s->hq < 1 || s->hkv < 1) return fail(CA_ERR_INVALID, "hq=%d hkv=%d must be >= 1", s->hq, s->hkv);
@@ -180,7 +208,9 @@ constexpr int kDecTargetItems = 1024;      // two rounds of two 4-wave items per
 constexpr int kDecMinChunk = 512;
 constexpr int kDecMaxGroup = 16;
 
-bool is_decode_task(const ca_task& k, int group) { return k.q_len == 1 && group <= kDecMaxGroup; }
+bool is_decode_task(const ca_task& k, int group, int32_t window) {
+  return k.q_len == 1 && group <= kDecMaxGroup && window == 0;
+}
 
 // keys of a decode task that its single row can see: [0, vis)
 int64_t decode_visible(const ca_task& k) {
@@ -194,10 +224,11 @@ struct FwdPlan {
   size_t n_split = 0;        // decode (task, kv head) pairs cut into > 1 chunk
   size_t n_parts = 0;        // staging slots for those chunks
   int64_t dec_chunk = 0;
-  size_t off_tasks = 0, off_items = 0, off_dec = 0, off_split = 0, off_part_o = 0, off_part_l = 0, bytes = 0;
+  size_t off_tasks = 0, off_masks = 0, off_items = 0, off_dec = 0, off_split = 0, off_part_o = 0, off_part_l = 0,
+         bytes = 0;
 };
 
-FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
+FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n) {
   FwdPlan p;
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, kFwdWaves);
@@ -205,7 +236,7 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
   int64_t dec_keys = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (t[i].q_len <= 0) continue;
-    if (is_decode_task(t[i], p.group)) {
+    if (is_decode_task(t[i], p.group, task_window(m, i))) {
       dec_keys += decode_visible(t[i]) * s->hkv;
       continue;
     }
@@ -215,7 +246,7 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
   const int64_t per_item = (dec_keys + kDecTargetItems - 1) / kDecTargetItems;
   p.dec_chunk = std::max<int64_t>(kDecMinChunk, (per_item + 127) / 128 * 128);
   for (int32_t i = 0; i < n; ++i) {
-    if (t[i].q_len <= 0 || !is_decode_task(t[i], p.group)) continue;
+    if (t[i].q_len <= 0 || !is_decode_task(t[i], p.group, task_window(m, i))) continue;
     const int64_t vis = decode_visible(t[i]);
     const int64_t chunks = std::max<int64_t>(1, (vis + p.dec_chunk - 1) / p.dec_chunk);
     p.n_dec_items += (size_t)chunks * s->hkv;
@@ -225,7 +256,8 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
     }
   }
   p.off_tasks = 0;
-  p.off_items = align_up(sizeof(ca_task) * (size_t)n);
+  p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
+  p.off_items = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
   p.off_dec = p.off_items + align_up(sizeof(ca::FwdItem) * p.n_items);
   p.off_split = p.off_dec + align_up(sizeof(ca::DecItem) * p.n_dec_items);
   p.off_part_o = p.off_split + align_up(4 * sizeof(int32_t) * p.n_split);
@@ -234,8 +266,8 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, int32_t n) {
   return p;
 }
 
-void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const FwdPlan& p,
-                         std::vector<ca::FwdItem>& items) {
+void build_forward_items(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                         const FwdPlan& p, std::vector<ca::FwdItem>& items) {
   struct Keyed {
     int64_t cost;
     ca::FwdItem it;
@@ -244,12 +276,14 @@ void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const F
   tmp.reserve(p.n_items);
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& k = t[i];
-    if (k.q_len <= 0 || is_decode_task(k, p.group)) continue;
+    const int32_t win = task_window(m, i);
+    if (k.q_len <= 0 || is_decode_task(k, p.group, win)) continue;
     const int64_t delta = k.q_pos0 - k.kv_pos0;
+    const int64_t sj = task_sink_keys(t, m, i);
     for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
       const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
       // pairs of the tile (per head) plus a per-row epilogue term
-      const int64_t cost = range_pairs(r0, r1, delta, k.kv_len) * p.hpw + (r1 - r0 + 1) * 64;
+      const int64_t cost = range_pairs_masked(r0, r1, delta, k.kv_len, win, sj) * p.hpw + (r1 - r0 + 1) * 64;
       for (int32_t g = 0; g < s->hkv; ++g)
         for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
     }
@@ -265,15 +299,15 @@ void build_forward_items(const ca_shape* s, const ca_task* t, int32_t n, const F
 // Decode items (longest chunk first) and the merge records of split tasks:
 // split[0..n) first staging slot, [n..2n) chunk count, [2n..3n) task,
 // [3n..4n) KV head.
-void build_decode_items(const ca_shape* s, const ca_task* t, int32_t n, const FwdPlan& p,
-                        std::vector<ca::DecItem>& items, std::vector<int32_t>& split) {
+void build_decode_items(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                        const FwdPlan& p, std::vector<ca::DecItem>& items, std::vector<int32_t>& split) {
   items.clear();
   split.assign(4 * p.n_split, 0);
   size_t rec = 0;
   int32_t part = 0;
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& k = t[i];
-    if (k.q_len <= 0 || !is_decode_task(k, p.group)) continue;
+    if (k.q_len <= 0 || !is_decode_task(k, p.group, task_window(m, i))) continue;
     const int64_t vis = decode_visible(k);
     const int64_t chunks = std::max<int64_t>(1, (vis + p.dec_chunk - 1) / p.dec_chunk);
     for (int32_t g = 0; g < s->hkv; ++g) {
@@ -300,13 +334,16 @@ void build_decode_items(const ca_shape* s, const ca_task* t, int32_t n, const Fw
   });
 }
 
-ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const void* Q, const void* K,
-                       const void* V, void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
+ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const void* Q,
+                       const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
+                       void* stream) {
   ca_status st = check_shape(s);
   if (st != CA_OK) return st;
   st = check_tasks(s, t, n);
   if (st != CA_OK) return st;
-  const FwdPlan p = plan_forward(s, t, n);
+  st = check_masks(m, n);
+  if (st != CA_OK) return st;
+  const FwdPlan p = plan_forward(s, t, m, n);
   if (p.n_items == 0 && p.n_dec_items == 0) return CA_OK;
   if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
   if (!ws || ws_bytes < p.bytes)
@@ -318,12 +355,13 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const voi
     if ((int64_t)t[i].kv_len * s->hkv * s->d * 2 >= (int64_t(1) << 31))
       return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
   std::vector<ca::FwdItem> items;
-  build_forward_items(s, t, n, p, items);
+  build_forward_items(s, t, m, n, p, items);
   std::vector<ca::DecItem> ditems;
   std::vector<int32_t> split;
-  build_decode_items(s, t, n, p, ditems, split);
+  build_decode_items(s, t, m, n, p, ditems, split);
   std::vector<char> host(p.off_part_o, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
+  if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
   if (!items.empty()) std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
   if (!ditems.empty()) std::memcpy(host.data() + p.off_dec, ditems.data(), sizeof(ca::DecItem) * ditems.size());
   if (!split.empty()) std::memcpy(host.data() + p.off_split, split.data(), sizeof(int32_t) * split.size());
@@ -341,6 +379,7 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, int32_t n, const voi
     fp.O = O;
     fp.LSE = LSE;
     fp.tasks = (const ca_task*)(w + p.off_tasks);
+    fp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
     fp.items = (const ca::FwdItem*)(w + p.off_items);
     fp.n_items = (int32_t)items.size();
     fp.hq = s->hq;
@@ -540,14 +579,27 @@ bool varlen_to_tasks(const int32_t* cu, int32_t n_docs, std::vector<ca_task>& ou
 extern "C" {
 
 size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks) {
-  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK) return 0;
-  return plan_forward(shape, tasks_host, n_tasks).bytes;
+  return ca_forward_masked_workspace(shape, tasks_host, nullptr, n_tasks);
 }
 
 ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks, const void* Q,
                      const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
                      void* stream) {
-  return forward_impl(shape, tasks_host, n_tasks, Q, K, V, O, LSE, ws, ws_bytes, stream);
+  return forward_impl(shape, tasks_host, nullptr, n_tasks, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+size_t ca_forward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                   int32_t n_tasks) {
+  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK ||
+      check_masks(masks_host, n_tasks) != CA_OK)
+    return 0;
+  return plan_forward(shape, tasks_host, masks_host, n_tasks).bytes;
+}
+
+ca_status ca_forward_masked(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                            int32_t n_tasks, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(shape, tasks_host, masks_host, n_tasks, Q, K, V, O, LSE, ws, ws_bytes, stream);
 }
 
 size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu, int32_t n_docs) {
@@ -562,7 +614,7 @@ ca_status ca_forward_varlen(const ca_shape* shape, const int32_t* cu, int32_t n_
   std::vector<ca_task> t;
   if (!varlen_to_tasks(cu, n_docs, t))
     return fail(CA_ERR_INVALID, "cu_seqlens must start at 0 and be non-decreasing");
-  return forward_impl(shape, t.data(), n_docs, Q, K, V, O, LSE, ws, ws_bytes, stream);
+  return forward_impl(shape, t.data(), nullptr, n_docs, Q, K, V, O, LSE, ws, ws_bytes, stream);
 }
 
 ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows, const float* O_parts,
@@ -697,12 +749,20 @@ ca_status ca_backward(const ca_shape* s, const ca_task* t, int32_t n, const void
 }
 
 int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks) {
+  return ca_visible_pairs_masked(tasks_host, nullptr, n_tasks);
+}
+
+int64_t ca_visible_pairs_masked(const ca_task* tasks_host, const ca_task_mask* masks_host, int32_t n_tasks) {
   if (n_tasks < 0 || (n_tasks > 0 && !tasks_host)) return -1;
+  if (masks_host)
+    for (int32_t i = 0; i < n_tasks; ++i)
+      if (masks_host[i].window < 0 || masks_host[i].sink < 0) return -1;
   int64_t total = 0;
   for (int32_t i = 0; i < n_tasks; ++i) {
     const ca_task& k = tasks_host[i];
     if (k.q_len < 0 || k.kv_len < 0) return -1;
-    total += range_pairs(0, (int64_t)k.q_len - 1, k.q_pos0 - k.kv_pos0, k.kv_len);
+    total += range_pairs_masked(0, (int64_t)k.q_len - 1, k.q_pos0 - k.kv_pos0, k.kv_len,
+                                task_window(masks_host, i), task_sink_keys(tasks_host, masks_host, i));
   }
   return total;
 }

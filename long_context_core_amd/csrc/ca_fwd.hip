@@ -79,6 +79,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // Tiles [0, w_full) are visible to every row of the wave: no mask.
   const int w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
 
+  // Sink + sliding-window mask (win > 0): besides being causal, key j must lie
+  // within the row's win latest positions (j > i + delta - win) or be one of
+  // the sink keys [0, sj).  The workgroup visits the sink tiles [0, t_a) and
+  // the window tiles [t_b, n_tiles); win == 0 visits [0, n_tiles).
+  int win = 0, sj = 0;
+  if (p.masks) {
+    win = p.masks[it.task].window;
+    if (win > 0) sj = (int)clamp64((int64_t)p.masks[it.task].sink - t.kv_pos0, 0, kv_len);
+  }
+  // window starts (first visible window key) of the wave's first and last rows
+  const int64_t w_lo_first = (int64_t)wrow0 + delta - win + 1;
+  const int64_t w_lo_last = (int64_t)w_last + delta - win + 1;
+
   // Q^T operand: this lane's query row, channels 16 s + 8 hh .. + 7.
   const int qrow = wrow0 + l32;
   const bool qvalid = qrow < t.q_len;
@@ -96,6 +109,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   float lsum = 0.f;       // sum of exp2(s * c - m2)
 
   const int n_tiles = (kv_hi + BN - 1) / BN;
+  int t_a = 0, t_b = 0;
+  if (win > 0) {
+    t_a = min((sj + BN - 1) / BN, n_tiles);
+    t_b = max(t_a, (int)(clamp64((int64_t)it.row0 + delta - win + 1, 0, kv_len) / BN));
+    t_b = min(t_b, n_tiles);
+  }
+  const int n_visit = t_a + (n_tiles - t_b);
+  auto tile_of = [&](int k) { return k < t_a ? k : t_b + (k - t_a); };
+  // Does this wave see any key of the tile, and does every row see all of it?
+  auto wave_sees = [&](int tile) {
+    if (tile * BN >= w_kv_hi) return false;
+    return win == 0 || tile * BN < sj || (int64_t)(tile + 1) * BN > w_lo_first;
+  };
+  auto needs_mask = [&](int tile) {
+    if (tile >= w_full) return true;
+    return win > 0 && !((tile + 1) * BN <= sj || (int64_t)tile * BN >= w_lo_last);
+  };
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
   const __bf16* kbase = p.K + t.kv_off * kv_stride + it.kv_head * D;
@@ -162,17 +192,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Mask only where the tile straddles the diagonal or the context end:
-    // key k0 + r (r in [0, 64)) is visible iff r <= lim.
-    if (tile >= w_full) {
+    // Mask only where the tile straddles the diagonal, the context end or a
+    // window / sink edge: key k0 + r (r in [0, 64)) is visible iff r <= lim
+    // and (no window, or r >= wlo, or r < slim).
+    if (needs_mask(tile)) {
       keep_branch();
       const int lim = (int)clamp64(min((int64_t)qrow + delta, (int64_t)kv_len - 1) - k0, -1, BN);
+      const int wlo = win > 0 ? (int)clamp64((int64_t)qrow + delta - win + 1 - k0, -1, BN + 1) : -1;
+      const int slim = (int)clamp64((int64_t)sj - k0, 0, BN);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int r = mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          s_acc[mb][j] = (r <= lim) ? s_acc[mb][j] : -INFINITY;
+          s_acc[mb][j] = (r <= lim && (r >= wlo || r < slim)) ? s_acc[mb][j] : -INFINITY;
         }
     }
     // Tile max of this row, both half-waves.
@@ -228,13 +261,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     }
   };
 
-  if (n_tiles > 0) gload(0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
+  if (n_visit > 0) gload(tile_of(0));
+  for (int k = 0; k < n_visit; ++k) {
+    const int buf = k & 1;
+    const int tile = tile_of(k);
     swrite(buf);
     __syncthreads();
-    if (tile + 1 < n_tiles) gload(tile + 1);
-    if (tile * BN < w_kv_hi) do_tile(tile, buf);
+    if (k + 1 < n_visit) gload(tile_of(k + 1));
+    if (wave_sees(tile)) do_tile(tile, buf);
   }
 
   // Epilogue: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty rows: 0, -inf.

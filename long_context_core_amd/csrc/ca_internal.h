@@ -46,6 +46,7 @@ struct FwdParams {
   void* O;
   float* LSE;
   const ca_task* tasks;
+  const ca_task_mask* masks;   // per task, or nullptr: causal only
   const FwdItem* items;
   int32_t n_items;
   int32_t hq, hkv, group, hpw;

@@ -102,3 +102,19 @@ def test_varlen_rejects_bad_cu_seqlens():
         st = L.ca_forward_varlen(ctypes.byref(s), a.ctypes.data_as(ctypes.c_void_p), len(a) - 1,
                                  FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
         assert st == ca.CA_ERR_INVALID
+
+
+def test_masked_visible_pairs_match_the_oracle():
+    """ca_visible_pairs_masked (host code) counts the sink + window mask's
+    pairs exactly as the oracle does."""
+    import numpy as np
+    import oracle
+    from long_context_core_amd import ca, inputs as I
+    rng = np.random.default_rng(4)
+    for _ in range(30):
+        docs = [int(x) for x in rng.integers(1, 3000, size=rng.integers(1, 6))]
+        t = I.lambda_tasks(docs, window=int(rng.integers(1, 5000)), sink=int(rng.integers(0, 300)))
+        if rng.random() < 0.5:        # shifted positions, partial contexts
+            t[:, 5] += rng.integers(0, 50, size=len(t))
+        assert ca.visible_pairs(t) == oracle.visible_pairs(t)
+    assert ca.visible_pairs(I.varlen_tasks([5, 7])) == oracle.visible_pairs(I.varlen_tasks([5, 7]))

@@ -1,0 +1,90 @@
+"""GPU parity of the sparse masks ("Dynamic Context Parallelism", Section
+2.4, Figure 6) against the fp64 oracle: the lambda mask (sink + sliding
+window) through ca_forward_masked, and the causal-blockwise and
+shared-question masks as partial slots combined by ca_merge."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_core_amd import ca
+from long_context_core_amd import inputs as I
+from tests.gpu_util import announce, check_forward, torch_cuda, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def run_forward(tasks, hq, hkv, d, T, seed, o_rows=None, out_f32=False):
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    o_rows = T if o_rows is None else o_rows
+    Q = I.randn_bf16((T, hq, d), seed)
+    K = I.randn_bf16((T, hkv, d), seed + 1)
+    V = I.randn_bf16((T, hkv, d), seed + 2)
+    shape = ca.make_shape(hq, hkv, d, T, T, o_rows, out_f32=out_f32)
+    O = torch.zeros((o_rows, hq, d), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
+    LSE = torch.full((o_rows, hq), -float("inf"), device=dev)
+    ca.forward(shape, tasks, Q.to(dev), K.to(dev), V.to(dev), O, LSE)
+    torch.cuda.synchronize()
+    return O, LSE, Q, K, V
+
+
+@pytest.mark.parametrize("window,sink,hq,hkv,d", [
+    (4096, 64, 8, 2, 128), (100, 0, 8, 2, 128), (37, 5, 4, 4, 64), (1, 0, 8, 2, 128),
+    (64, 64, 16, 1, 128), (200, 300, 6, 2, 64), (130, 1, 8, 8, 128)])
+def test_lambda_mask_forward(window, sink, hq, hkv, d):
+    announce("lambda forward window=%d sink=%d hq%d hkv%d d%d" % (window, sink, hq, hkv, d))
+    docs = [1500, 1, 70, 700, 333]
+    T = sum(docs)
+    tasks = I.lambda_tasks(docs, window=window, sink=sink)
+    O, LSE, Q, K, V = run_forward(tasks, hq, hkv, d, T, 1400 + window)
+    O_ref, LSE_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
+    check_forward(O, LSE, O_ref, LSE_ref, "lambda")
+
+
+def test_lambda_mask_single_rows_and_shards():
+    """Windowed single-row tasks (they take the tiled kernel) and mid-document
+    shards whose window starts inside the shard's context."""
+    announce("lambda forward: single rows and shards")
+    rows = [(0, 0, 0, 1, 900, 899, 0, 128, 16),         # last token of a 900-token document
+            (1, 900, 1, 1, 50, 49, 0, 4096, 4),
+            (2, 950, 2, 300, 1000, 700, 0, 257, 33),     # shard [700, 1000) of a 1000-token document
+            (302, 1950, 302, 64, 2000, 1936, 0, 64, 0)]
+    T = 2000 + 1950
+    tasks = np.array(rows, dtype=np.int64)
+    O, LSE, Q, K, V = run_forward(tasks, 8, 2, 128, T, 1450, o_rows=366)
+    O_ref, LSE_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(128), o_rows=366)
+    check_forward(O, LSE, O_ref, LSE_ref, "lambda rows")
+
+
+def merged_gpu(tasks, parts, T, hq, hkv, d, seed):
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    O, LSE, Q, K, V = run_forward(tasks, hq, hkv, d, T, seed, o_rows=parts * T, out_f32=True)
+    Om = torch.empty((T, hq, d), dtype=torch.bfloat16, device=dev)
+    Lm = torch.empty((T, hq), device=dev)
+    ca.merge(ca.make_shape(hq, hkv, d, T, T, T), O.view(parts, T, hq, d), LSE.view(parts, T, hq), Om, Lm)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(d), o_rows=parts * T)
+    Lo = np.where(np.isnan(Lo), -np.inf, Lo)
+    Oo = np.where(np.isnan(Oo), 0.0, Oo)
+    O_ref, LSE_ref = oracle.merge(Oo.reshape(parts, T, hq, d), Lo.reshape(parts, T, hq))
+    return Om, Lm, O_ref, LSE_ref
+
+
+def test_blockwise_mask_forward():
+    announce("causal-blockwise forward (2 slots + merge)")
+    docs = [2100, 300, 1024]
+    tasks, parts = I.blockwise_tasks(docs, block=256, win_blocks=2)
+    Om, Lm, O_ref, LSE_ref = merged_gpu(tasks, parts, sum(docs), 8, 2, 128, 1460)
+    check_forward(Om, Lm, O_ref, LSE_ref, "blockwise")
+
+
+def test_shared_question_mask_forward():
+    announce("shared-question forward (2 slots + merge)")
+    question, answers = 700, [300, 129, 1000, 64]
+    tasks, parts = I.shared_question_tasks(question, answers)
+    Om, Lm, O_ref, LSE_ref = merged_gpu(tasks, parts, question + sum(answers), 8, 2, 128, 1470)
+    check_forward(Om, Lm, O_ref, LSE_ref, "shared question")
