@@ -188,6 +188,16 @@ ca_status ca_backward(const ca_shape* shape, const ca_task* tasks_host, int32_t 
                       const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* ca_backward with a ca_task_mask per task (masks_host may be NULL: all
+ * causal); the same mask as the forward that produced O and LSE.  Errors as
+ * ca_backward, plus CA_ERR_INVALID for a negative window or sink. */
+size_t ca_backward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host,
+                                    const ca_task_mask* masks_host, int32_t n_tasks);
+ca_status ca_backward_masked(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                             int32_t n_tasks, const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* CA-task scheduling (host only; no device memory, no HIP calls)          */
 /* ---------------------------------------------------------------------- */

@@ -34,6 +34,8 @@ EXPORTS = (
     "ca_visible_pairs_masked",
     "ca_forward_masked_workspace",
     "ca_forward_masked",
+    "ca_backward_masked_workspace",
+    "ca_backward_masked",
     "ca_cost_time",
     "ca_schedule_max_items",
     "ca_schedule",
@@ -111,6 +113,10 @@ def lib():
         L.ca_forward_masked_workspace.restype = sz
         L.ca_forward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ca_forward_masked.restype = ctypes.c_int
+        L.ca_backward_masked_workspace.argtypes = [sp, vp, vp, i32]
+        L.ca_backward_masked_workspace.restype = sz
+        L.ca_backward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_backward_masked.restype = ctypes.c_int
         dbl = ctypes.c_double
         L.ca_cost_time.argtypes = [vp, i32, vp, i32, vp, dbl, i64, i64]
         L.ca_cost_time.restype = dbl
@@ -263,18 +269,24 @@ def merge(shape, O_parts, LSE_parts, O, LSE, stream=None):
     return O, LSE
 
 
-def backward_workspace(shape, tasks):
-    ta = task_array(tasks)
-    return int(lib().ca_backward_workspace(ctypes.byref(shape), _tasks_ptr(ta), len(ta)))
+def backward_workspace(shape, tasks, masks=None):
+    ta, ma = split_tasks(tasks, masks)
+    return int(lib().ca_backward_masked_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta)))
 
 
-def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None):
-    ta = task_array(tasks)
+def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None, masks=None):
+    """ca_backward (ca_backward_masked with masks or a 9-column table)."""
+    ta, ma = split_tasks(tasks, masks)
     if ws is None:
-        ws = workspace_tensor(backward_workspace(shape, ta), Q.device)
-    st = lib().ca_backward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
-                           _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
-                           ws.numel(), _stream_ptr(stream))
+        ws = workspace_tensor(backward_workspace(shape, ta, ma), Q.device)
+    if ma is None:
+        st = lib().ca_backward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
+                               _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
+                               ws.numel(), _stream_ptr(stream))
+    else:
+        st = lib().ca_backward_masked(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta), _ptr(Q),
+                                      _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK),
+                                      _ptr(dV), _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st)
     return dQ, dK, dV
 

@@ -477,10 +477,11 @@ struct BwdPlan {
   std::vector<int> q_pass_of, kv_pass_of;
   bool q_full = false, kv_full = false;          // every row covered by some task
   size_t n_qitems = 0, n_kvitems = 0;
-  size_t off_tasks = 0, off_qitems = 0, off_kvitems = 0, off_d = 0, off_dq = 0, off_dk = 0, off_dv = 0, bytes = 0;
+  size_t off_tasks = 0, off_masks = 0, off_qitems = 0, off_kvitems = 0, off_d = 0, off_dq = 0, off_dk = 0,
+         off_dv = 0, bytes = 0;
 };
 
-BwdPlan plan_backward(const ca_shape* s, const ca_task* t, int32_t n) {
+BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n) {
   BwdPlan p;
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, 4);
@@ -503,7 +504,8 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, int32_t n) {
   p.q_full = p.q_passes == 1 && q_cover == s->q_rows;
   p.kv_full = p.kv_passes == 1 && kv_cover == s->kv_rows;
   p.off_tasks = 0;
-  p.off_qitems = align_up(sizeof(ca_task) * (size_t)n);
+  p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
+  p.off_qitems = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
   p.off_kvitems = p.off_qitems + align_up(sizeof(ca::FwdItem) * p.n_qitems);
   p.off_d = p.off_kvitems + align_up(sizeof(ca::BwdItem) * p.n_kvitems);
   p.off_dq = p.off_d + align_up(sizeof(float) * (size_t)s->o_rows * s->hq);
@@ -517,7 +519,7 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, int32_t n) {
 
 // Items of every pass, pass-major, each pass longest first; pass_begin has
 // passes + 1 entries.
-void build_backward_items(const ca_shape* s, const ca_task* t, int32_t n, const BwdPlan& p,
+void build_backward_items(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const BwdPlan& p,
                           std::vector<ca::FwdItem>& qitems, std::vector<size_t>& q_begin,
                           std::vector<ca::BwdItem>& kvitems, std::vector<size_t>& kv_begin) {
   qitems.clear();
@@ -531,9 +533,11 @@ void build_backward_items(const ca_shape* s, const ca_task* t, int32_t n, const 
       const ca_task& k = t[i];
       if (k.q_len <= 0 || p.q_pass_of[i] != pass) continue;
       const int64_t delta = k.q_pos0 - k.kv_pos0;
+      const int32_t win = task_window(m, i);
+      const int64_t sj = task_sink_keys(t, m, i);
       for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
         const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
-        const int64_t cost = range_pairs(r0, r1, delta, k.kv_len) * p.hpw + (r1 - r0 + 1) * 64;
+        const int64_t cost = range_pairs_masked(r0, r1, delta, k.kv_len, win, sj) * p.hpw + (r1 - r0 + 1) * 64;
         for (int32_t g = 0; g < s->hkv; ++g)
           for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
       }
@@ -549,10 +553,18 @@ void build_backward_items(const ca_shape* s, const ca_task* t, int32_t n, const 
       const ca_task& k = t[i];
       if (k.q_len <= 0 || p.kv_pass_of[i] != pass) continue;
       const int64_t delta = k.q_pos0 - k.kv_pos0;
+      const int32_t win = task_window(m, i);
+      const int64_t sj = task_sink_keys(t, m, i);
       for (int32_t k0 = 0; k0 < k.kv_len; k0 += kBwdKeyTile) {
-        // rows that see key k0: i >= k0 - delta
+        // rows that see the block: i >= k0 - delta, and (window, no sink key)
+        // i < last key - delta + win
         const int64_t r_lo = std::min<int64_t>(k.q_len, std::max<int64_t>(0, k0 - delta));
-        const int64_t cost = (k.q_len - r_lo) * p.group * kBwdKeyTile + 64 * kBwdKeyTile;
+        int64_t r_end = k.q_len;
+        if (win > 0 && k0 >= sj) {
+          const int64_t last = std::min<int64_t>(k0 + kBwdKeyTile, k.kv_len) - 1;
+          r_end = std::min<int64_t>(k.q_len, std::max<int64_t>(r_lo, last - delta + win));
+        }
+        const int64_t cost = (r_end - r_lo) * p.group * kBwdKeyTile + 64 * kBwdKeyTile;
         for (int32_t g = 0; g < s->hkv; ++g) tmp.push_back({cost, {i, g, k0, 0}});
       }
     }
@@ -572,6 +584,111 @@ bool varlen_to_tasks(const int32_t* cu, int32_t n_docs, std::vector<ca_task>& ou
     out[(size_t)i] = ca_task{cu[i], cu[i], cu[i], l, l, 0, 0};
   }
   return true;
+}
+
+ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const void* Q,
+                        const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+                        void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  ca_status st = check_shape(s);
+  if (st != CA_OK) return st;
+  if (s->flags & CA_OUT_F32) return fail(CA_ERR_INVALID, "CA_OUT_F32 is a forward/merge flag");
+  st = check_tasks(s, t, n);
+  if (st != CA_OK) return st;
+  st = check_masks(m, n);
+  if (st != CA_OK) return st;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return fail(CA_ERR_INVALID, "NULL tensor pointer");
+  const BwdPlan p = plan_backward(s, t, m, n);
+  if (!ws || ws_bytes < p.bytes)
+    return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
+  if (p.n_qitems > 0x7fffffffu || p.n_kvitems > 0x7fffffffu) return fail(CA_ERR_UNSUPPORTED, "too many work items");
+  for (int32_t i = 0; i < n; ++i)
+    if ((int64_t)t[i].kv_len * s->hkv * s->d * 2 >= (int64_t(1) << 31))
+      return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
+  std::vector<ca::FwdItem> qitems;
+  std::vector<ca::BwdItem> kvitems;
+  std::vector<size_t> q_begin, kv_begin;
+  build_backward_items(s, t, m, n, p, qitems, q_begin, kvitems, kv_begin);
+  std::vector<char> host(p.off_d, 0);
+  std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
+  if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+  if (!qitems.empty()) std::memcpy(host.data() + p.off_qitems, qitems.data(), sizeof(ca::FwdItem) * qitems.size());
+  if (!kvitems.empty()) std::memcpy(host.data() + p.off_kvitems, kvitems.data(), sizeof(ca::BwdItem) * kvitems.size());
+  hipStream_t hs = (hipStream_t)stream;
+  st = upload(ws, host, hs);
+  if (st != CA_OK) return st;
+  char* w = (char*)ws;
+  float* Dv = (float*)(w + p.off_d);
+  const int64_t q_elems = s->q_rows * s->hq * (int64_t)s->d;
+  const int64_t kv_elems = s->kv_rows * s->hkv * (int64_t)s->d;
+  hipError_t e = ca::launch_bwd_prep((const __bf16*)O, (const __bf16*)dO, Dv, s->o_rows * (int64_t)s->hq, s->d, hs);
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  const bool acc_q = p.q_passes > 1, acc_kv = p.kv_passes > 1;
+  // rows no kernel writes must read as zero
+  if (acc_q) e = ca::launch_zero_f32((float*)(w + p.off_dq), q_elems, hs);
+  else if (!p.q_full) e = ca::launch_zero_bf16((__bf16*)dQ, q_elems, hs);
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+  if (acc_kv) {
+    e = ca::launch_zero_f32((float*)(w + p.off_dk), kv_elems, hs);
+    if (e == hipSuccess) e = ca::launch_zero_f32((float*)(w + p.off_dv), kv_elems, hs);
+  } else if (!p.kv_full) {
+    e = ca::launch_zero_bf16((__bf16*)dK, kv_elems, hs);
+    if (e == hipSuccess) e = ca::launch_zero_bf16((__bf16*)dV, kv_elems, hs);
+  }
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+
+  ca::BwdParams bp;
+  bp.Q = (const __bf16*)Q;
+  bp.K = (const __bf16*)K;
+  bp.V = (const __bf16*)V;
+  bp.dO = (const __bf16*)dO;
+  bp.LSE = LSE;
+  bp.Dvec = Dv;
+  bp.dQ = (__bf16*)dQ;
+  bp.dK = (__bf16*)dK;
+  bp.dV = (__bf16*)dV;
+  bp.dQacc = (float*)(w + p.off_dq);
+  bp.dKacc = (float*)(w + p.off_dk);
+  bp.dVacc = (float*)(w + p.off_dv);
+  bp.tasks = (const ca_task*)(w + p.off_tasks);
+  bp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
+  bp.hq = s->hq;
+  bp.hkv = s->hkv;
+  bp.group = p.group;
+  bp.hpw = p.hpw;
+  bp.scale = s->scale;
+  bp.scale_log2 = s->scale * 1.4426950408889634f;
+  const ca::FwdItem* qi = (const ca::FwdItem*)(w + p.off_qitems);
+  const ca::BwdItem* ki = (const ca::BwdItem*)(w + p.off_kvitems);
+  for (int pass = 0; pass < p.q_passes; ++pass) {
+    ca::BwdParams pp = bp;
+    pp.accumulate = acc_q ? 1 : 0;
+    pp.qitems = qi + q_begin[pass];
+    pp.n_qitems = (int32_t)(q_begin[pass + 1] - q_begin[pass]);
+    pp.items = nullptr;
+    pp.n_items = 0;
+    e = ca::launch_bwd_q(pp, s->d, hs);
+    if (e != hipSuccess) return hip_fail(e, "dQ launch");
+  }
+  for (int pass = 0; pass < p.kv_passes; ++pass) {
+    ca::BwdParams pp = bp;
+    pp.accumulate = acc_kv ? 1 : 0;
+    pp.items = ki + kv_begin[pass];
+    pp.n_items = (int32_t)(kv_begin[pass + 1] - kv_begin[pass]);
+    pp.qitems = nullptr;
+    pp.n_qitems = 0;
+    e = ca::launch_bwd_kv(pp, s->d, hs);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  }
+  if (acc_q) {
+    e = ca::launch_f32_to_bf16(bp.dQacc, (__bf16*)dQ, q_elems, hs);
+    if (e != hipSuccess) return hip_fail(e, "dQ conversion");
+  }
+  if (acc_kv) {
+    e = ca::launch_f32_to_bf16(bp.dKacc, (__bf16*)dK, kv_elems, hs);
+    if (e == hipSuccess) e = ca::launch_f32_to_bf16(bp.dVacc, (__bf16*)dV, kv_elems, hs);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV conversion");
+  }
+  return CA_OK;
 }
 
 }  // namespace
@@ -643,110 +760,29 @@ ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows, const
 }
 
 size_t ca_backward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks) {
-  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK) return 0;
-  return plan_backward(shape, tasks_host, n_tasks).bytes;
+  return ca_backward_masked_workspace(shape, tasks_host, nullptr, n_tasks);
+}
+
+size_t ca_backward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                    int32_t n_tasks) {
+  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK ||
+      check_masks(masks_host, n_tasks) != CA_OK)
+    return 0;
+  return plan_backward(shape, tasks_host, masks_host, n_tasks).bytes;
 }
 
 ca_status ca_backward(const ca_shape* s, const ca_task* t, int32_t n, const void* Q, const void* K,
                       const void* V, const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
                       void* dV, void* ws, size_t ws_bytes, void* stream) {
-  ca_status st = check_shape(s);
-  if (st != CA_OK) return st;
-  if (s->flags & CA_OUT_F32) return fail(CA_ERR_INVALID, "CA_OUT_F32 is a forward/merge flag");
-  st = check_tasks(s, t, n);
-  if (st != CA_OK) return st;
-  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return fail(CA_ERR_INVALID, "NULL tensor pointer");
-  const BwdPlan p = plan_backward(s, t, n);
-  if (!ws || ws_bytes < p.bytes)
-    return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
-  if (p.n_qitems > 0x7fffffffu || p.n_kvitems > 0x7fffffffu) return fail(CA_ERR_UNSUPPORTED, "too many work items");
-  for (int32_t i = 0; i < n; ++i)
-    if ((int64_t)t[i].kv_len * s->hkv * s->d * 2 >= (int64_t(1) << 31))
-      return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
-  std::vector<ca::FwdItem> qitems;
-  std::vector<ca::BwdItem> kvitems;
-  std::vector<size_t> q_begin, kv_begin;
-  build_backward_items(s, t, n, p, qitems, q_begin, kvitems, kv_begin);
-  std::vector<char> host(p.off_d, 0);
-  std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
-  if (!qitems.empty()) std::memcpy(host.data() + p.off_qitems, qitems.data(), sizeof(ca::FwdItem) * qitems.size());
-  if (!kvitems.empty()) std::memcpy(host.data() + p.off_kvitems, kvitems.data(), sizeof(ca::BwdItem) * kvitems.size());
-  hipStream_t hs = (hipStream_t)stream;
-  st = upload(ws, host, hs);
-  if (st != CA_OK) return st;
-  char* w = (char*)ws;
-  float* Dv = (float*)(w + p.off_d);
-  const int64_t q_elems = s->q_rows * s->hq * (int64_t)s->d;
-  const int64_t kv_elems = s->kv_rows * s->hkv * (int64_t)s->d;
-  hipError_t e = ca::launch_bwd_prep((const __bf16*)O, (const __bf16*)dO, Dv, s->o_rows * (int64_t)s->hq, s->d, hs);
-  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  const bool acc_q = p.q_passes > 1, acc_kv = p.kv_passes > 1;
-  // rows no kernel writes must read as zero
-  if (acc_q) e = ca::launch_zero_f32((float*)(w + p.off_dq), q_elems, hs);
-  else if (!p.q_full) e = ca::launch_zero_bf16((__bf16*)dQ, q_elems, hs);
-  if (e != hipSuccess) return hip_fail(e, "zero fill");
-  if (acc_kv) {
-    e = ca::launch_zero_f32((float*)(w + p.off_dk), kv_elems, hs);
-    if (e == hipSuccess) e = ca::launch_zero_f32((float*)(w + p.off_dv), kv_elems, hs);
-  } else if (!p.kv_full) {
-    e = ca::launch_zero_bf16((__bf16*)dK, kv_elems, hs);
-    if (e == hipSuccess) e = ca::launch_zero_bf16((__bf16*)dV, kv_elems, hs);
-  }
-  if (e != hipSuccess) return hip_fail(e, "zero fill");
-
-  ca::BwdParams bp;
-  bp.Q = (const __bf16*)Q;
-  bp.K = (const __bf16*)K;
-  bp.V = (const __bf16*)V;
-  bp.dO = (const __bf16*)dO;
-  bp.LSE = LSE;
-  bp.Dvec = Dv;
-  bp.dQ = (__bf16*)dQ;
-  bp.dK = (__bf16*)dK;
-  bp.dV = (__bf16*)dV;
-  bp.dQacc = (float*)(w + p.off_dq);
-  bp.dKacc = (float*)(w + p.off_dk);
-  bp.dVacc = (float*)(w + p.off_dv);
-  bp.tasks = (const ca_task*)(w + p.off_tasks);
-  bp.hq = s->hq;
-  bp.hkv = s->hkv;
-  bp.group = p.group;
-  bp.hpw = p.hpw;
-  bp.scale = s->scale;
-  bp.scale_log2 = s->scale * 1.4426950408889634f;
-  const ca::FwdItem* qi = (const ca::FwdItem*)(w + p.off_qitems);
-  const ca::BwdItem* ki = (const ca::BwdItem*)(w + p.off_kvitems);
-  for (int pass = 0; pass < p.q_passes; ++pass) {
-    ca::BwdParams pp = bp;
-    pp.accumulate = acc_q ? 1 : 0;
-    pp.qitems = qi + q_begin[pass];
-    pp.n_qitems = (int32_t)(q_begin[pass + 1] - q_begin[pass]);
-    pp.items = nullptr;
-    pp.n_items = 0;
-    e = ca::launch_bwd_q(pp, s->d, hs);
-    if (e != hipSuccess) return hip_fail(e, "dQ launch");
-  }
-  for (int pass = 0; pass < p.kv_passes; ++pass) {
-    ca::BwdParams pp = bp;
-    pp.accumulate = acc_kv ? 1 : 0;
-    pp.items = ki + kv_begin[pass];
-    pp.n_items = (int32_t)(kv_begin[pass + 1] - kv_begin[pass]);
-    pp.qitems = nullptr;
-    pp.n_qitems = 0;
-    e = ca::launch_bwd_kv(pp, s->d, hs);
-    if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
-  }
-  if (acc_q) {
-    e = ca::launch_f32_to_bf16(bp.dQacc, (__bf16*)dQ, q_elems, hs);
-    if (e != hipSuccess) return hip_fail(e, "dQ conversion");
-  }
-  if (acc_kv) {
-    e = ca::launch_f32_to_bf16(bp.dKacc, (__bf16*)dK, kv_elems, hs);
-    if (e == hipSuccess) e = ca::launch_f32_to_bf16(bp.dVacc, (__bf16*)dV, kv_elems, hs);
-    if (e != hipSuccess) return hip_fail(e, "dK/dV conversion");
-  }
-  return CA_OK;
+  return backward_impl(s, t, nullptr, n, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
 }
+
+ca_status ca_backward_masked(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const void* Q,
+                             const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                             void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl(s, t, m, n, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
+}
+
 
 int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks) {
   return ca_visible_pairs_masked(tasks_host, nullptr, n_tasks);

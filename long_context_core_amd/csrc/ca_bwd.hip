@@ -132,10 +132,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 
   // Query rows that see at least one key of the workgroup: i + delta >= key0.
   const int wg_keys = min(128, t.kv_len - it.key0);
+  // Sink + sliding-window mask (win > 0): key j is also required to lie in
+  // the row's win latest positions (j > i + delta - win) or among the sink
+  // keys [0, sj).
+  int win = 0, sj = 0;
+  if (p.masks) {
+    win = p.masks[it.task].window;
+    if (win > 0) sj = (int)clamp64((int64_t)p.masks[it.task].sink - t.kv_pos0, 0, t.kv_len);
+  }
   const int r_lo = (int)clamp64((int64_t)it.key0 - delta, 0, t.q_len);
+  // Rows past the window of the workgroup's last key see none of its keys,
+  // unless it holds sink keys.
+  const int r_end = (win > 0 && it.key0 >= sj)
+                        ? (int)clamp64((int64_t)it.key0 + wg_keys - 1 - delta + win, r_lo, t.q_len)
+                        : t.q_len;
   const int r_first = (r_lo / BQ) * BQ;
-  const int n_rt = (t.q_len - r_first + BQ - 1) / BQ;
-  const int n_steps = (wg_keys > 0 && t.q_len > r_lo) ? n_rt * G : 0;
+  const int n_rt = (r_end - r_first + BQ - 1) / BQ;
+  const int n_steps = (wg_keys > 0 && r_end > r_lo) ? n_rt * G : 0;
 
   // Tile loads through range-checked buffers based at the tile's first row:
   // rows past the task read as 0 (Q = dO = 0 there, so such rows add nothing
@@ -247,13 +260,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) pv[4 * q4 + j] = exp2_fast(fmaf(s_acc[4 * q4 + j], p.scale_log2, -lv[j]));
     }
-    if ((int64_t)r0 + delta < (int64_t)kw0 + 31) {
+    // With a window, row m also needs m < (l32 - 4 hh) - (r0 + delta - kw0) + win
+    // unless key l32 is a sink key.
+    const int64_t dd = (int64_t)r0 + delta - kw0;
+    const bool win_edge = win > 0 && !(kw0 + 31 < sj || dd + 31 - win < 0);
+    if (dd < 31 || win_edge) {
       keep_branch();
-      const int x = l32 - 4 * hh - (int)clamp64((int64_t)r0 + delta - kw0, -64, 64);
+      const int x = l32 - 4 * hh - (int)clamp64(dd, -64, 64);
+      const int wthr = win > 0 ? (int)clamp64((int64_t)(l32 - 4 * hh) - dd + win, -1, 64) : 64;
+      const bool sink_key = kw0 + l32 < sj;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pv[4 * q4 + j] = (x <= 8 * q4 + j) ? pv[4 * q4 + j] : 0.f;
+        for (int j = 0; j < 4; ++j)
+          pv[4 * q4 + j] = (x <= 8 * q4 + j && (8 * q4 + j < wthr || sink_key)) ? pv[4 * q4 + j] : 0.f;
     }
     bf16x8 pf[2];
 #pragma unroll
@@ -378,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // address is a lane constant plus an immediate; the band is rounded up to an
   // even number of steps (its body is correct for any step).
   const int n_diag_rt = (int)clamp64(((int64_t)it.key0 + 127 - delta - r_first + BQ - 1) / BQ, 0, n_rt);
-  const int n_diag = min(n_steps, (n_diag_rt * G + 1) & ~1);
+  const int n_diag = win > 0 ? n_steps : min(n_steps, (n_diag_rt * G + 1) & ~1);   // windowed: all masked
   int cur_g = 0, cur_r0 = r_first;
   auto do_step = [&](auto buf_tag, auto diag_tag, int step) {
     constexpr int BUF = decltype(buf_tag)::value;
@@ -392,8 +412,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     }
     if (step + 1 < n_steps) gload();
     if constexpr (DIAG) {
-      // Skip blocks where no row of the step sees any key of this wave.
+      // Skip blocks where no row of the step sees any key of this wave: all
+      // keys after the last row, or (window) all before the first row's
+      // window and none of them a sink key.
       if ((int64_t)r0 + BQ - 1 + delta < kw0) return;
+      if (win > 0 && kw0 >= sj && (int64_t)r0 + delta - win + 1 > (int64_t)kw0 + 31) return;
       diag_body(BUF, r0);
     } else {
       full_body(BUF);
@@ -540,11 +563,37 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   // Key tiles [0, n_full) are visible to every row of the workgroup (no mask,
   // no skip); the rest go through the general body.  Tiles run in LDS-buffer
   // pairs so that every LDS address is a lane constant plus an immediate.
-  const int n_full = min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN)) & ~1;
+  // Sink + sliding-window mask (win > 0): as in the forward, the workgroup
+  // visits the sink tiles [0, t_a) and the window tiles [t_b, n_tiles), and
+  // every tile goes through the general body.
+  int win = 0, sj = 0;
+  if (p.masks) {
+    win = p.masks[it.task].window;
+    if (win > 0) sj = (int)clamp64((int64_t)p.masks[it.task].sink - t.kv_pos0, 0, kv_len);
+  }
+  const int64_t w_lo_first = (int64_t)wrow0 + delta - win + 1;
+  const int64_t w_lo_last = (int64_t)w_last + delta - win + 1;
+  int t_a = 0, t_b = 0;
+  if (win > 0) {
+    t_a = min((sj + BN - 1) / BN, n_tiles);
+    t_b = min(max(t_a, (int)(clamp64((int64_t)it.row0 + delta - win + 1, 0, kv_len) / BN)), n_tiles);
+  }
+  const int n_visit = t_a + (n_tiles - t_b);
+  auto tile_of = [&](int k) { return k < t_a ? k : t_b + (k - t_a); };
+  auto wave_sees = [&](int tile) {
+    if (tile * BN >= w_kv_hi) return false;
+    return win == 0 || tile * BN < sj || (int64_t)(tile + 1) * BN > w_lo_first;
+  };
+  auto needs_mask = [&](int tile) {
+    if (tile >= w_full) return true;
+    return win > 0 && !((tile + 1) * BN <= sj || (int64_t)tile * BN >= w_lo_last);
+  };
+  const int n_full = win > 0 ? 0
+                             : min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN)) & ~1;
 
   auto diag_body = [&](int buf, int tile) {
     const int k0 = tile * BN;
-    if (k0 >= w_kv_hi) return;
+    if (!wave_sees(tile)) return;
     f32x16 s_acc[2], dp_acc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -566,15 +615,17 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) pv[mb][j] = exp2_fast(fmaf(s_acc[mb][j], p.scale_log2, -lse2));
-    if (tile >= w_full) {
+    if (needs_mask(tile)) {
       keep_branch();
       const int lim = (int)clamp64(min((int64_t)qrow + delta, (int64_t)kv_len - 1) - k0, -1, BN);
+      const int wlo = win > 0 ? (int)clamp64((int64_t)qrow + delta - win + 1 - k0, -1, BN + 1) : -1;
+      const int slim = (int)clamp64((int64_t)sj - k0, 0, BN);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int r = mb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          pv[mb][j] = (r <= lim) ? pv[mb][j] : 0.f;
+          pv[mb][j] = (r <= lim && (r >= wlo || r < slim)) ? pv[mb][j] : 0.f;
         }
     }
     bf16x8 dsf[2][2];
@@ -692,29 +743,31 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     }
   };
 
-  auto do_tile = [&](auto buf_tag, auto full_tag, int tile) {
+  // k indexes the visited tiles (tile_of(k) == k without a window, so the
+  // fully visible tiles [0, n_full) come first).
+  auto do_tile = [&](auto buf_tag, auto full_tag, int k) {
     constexpr int BUF = decltype(buf_tag)::value;
     swrite(BUF);
     __syncthreads();
-    if (tile + 1 < n_tiles) gload(tile + 1);
+    if (k + 1 < n_visit) gload(tile_of(k + 1));
     if constexpr (decltype(full_tag)::value)
       full_body(BUF);
     else
-      diag_body(BUF, tile);
+      diag_body(BUF, tile_of(k));
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  int tile = 0;
-  if (n_tiles > 0) gload(0);
-  for (; tile < n_full; tile += 2) {
-    do_tile(B0{}, std::true_type{}, tile);
-    do_tile(B1{}, std::true_type{}, tile + 1);
+  int k = 0;
+  if (n_visit > 0) gload(tile_of(0));
+  for (; k < n_full; k += 2) {
+    do_tile(B0{}, std::true_type{}, k);
+    do_tile(B1{}, std::true_type{}, k + 1);
   }
-  for (; tile + 1 < n_tiles; tile += 2) {
-    do_tile(B0{}, std::false_type{}, tile);
-    do_tile(B1{}, std::false_type{}, tile + 1);
+  for (; k + 1 < n_visit; k += 2) {
+    do_tile(B0{}, std::false_type{}, k);
+    do_tile(B1{}, std::false_type{}, k + 1);
   }
-  if (tile < n_tiles) do_tile(B0{}, std::false_type{}, tile);
+  if (k < n_visit) do_tile(B0{}, std::false_type{}, k);
 
   if (!qvalid) return;
   const int64_t base = (t.q_off + qrow) * q_stride + head * D;

@@ -111,6 +111,7 @@ struct BwdParams {
   float* dKacc;       // [kv_rows][hkv][d] fp32, used when accumulate != 0 (dK/dV kernel)
   float* dVacc;
   const ca_task* tasks;
+  const ca_task_mask* masks;   // per task, or nullptr: causal only
   const BwdItem* items;   // dK/dV kernel
   int32_t n_items;
   const FwdItem* qitems;  // dQ kernel

@@ -88,3 +88,123 @@ def test_shared_question_mask_forward():
     tasks, parts = I.shared_question_tasks(question, answers)
     Om, Lm, O_ref, LSE_ref = merged_gpu(tasks, parts, question + sum(answers), 8, 2, 128, 1470)
     check_forward(Om, Lm, O_ref, LSE_ref, "shared question")
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+from tests.gpu_util import GRAD_REL_FRO, rel_fro   # noqa: E402
+
+
+def gpu_grads(fwd_tasks, bwd_tasks, parts, T, hq, hkv, d, seed):
+    """Forward (into partial slots, merged when parts > 1) then the backward
+    over bwd_tasks, whose output rows are the merged rows."""
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((T, hq, d), seed)
+    K = I.randn_bf16((T, hkv, d), seed + 1)
+    V = I.randn_bf16((T, hkv, d), seed + 2)
+    dO = I.randn_bf16((T, hq, d), seed + 3)
+    Qd, Kd, Vd, dOd = Q.to(dev), K.to(dev), V.to(dev), dO.to(dev)
+    shape = ca.make_shape(hq, hkv, d, T, T, T)
+    O = torch.empty((T, hq, d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((T, hq), device=dev)
+    if parts == 1:
+        ca.forward(shape, fwd_tasks, Qd, Kd, Vd, O, LSE)
+    else:
+        sp = ca.make_shape(hq, hkv, d, T, T, parts * T, out_f32=True)
+        Op = torch.zeros((parts * T, hq, d), device=dev)
+        Lp = torch.full((parts * T, hq), -float("inf"), device=dev)
+        ca.forward(sp, fwd_tasks, Qd, Kd, Vd, Op, Lp)
+        ca.merge(shape, Op.view(parts, T, hq, d), Lp.view(parts, T, hq), O, LSE)
+    dQ, dK, dV = torch.empty_like(Qd), torch.empty_like(Kd), torch.empty_like(Vd)
+    ca.backward(shape, bwd_tasks, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV)
+    torch.cuda.synchronize()
+    return (dQ, dK, dV), Q, K, V, dO
+
+
+def brute_grads(Q, K, V, dO, scale, rows_keys, hq, hkv):
+    """Gradient of sum(O * dO) for O defined row by row as the softmax over
+    the listed keys (float64 numpy, one row at a time)."""
+    Q, K, V, dO = widen(Q), widen(K), widen(V), widen(dO)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for r, keys in enumerate(rows_keys):
+        if not keys:
+            continue
+        ks = np.asarray(keys)
+        for h in range(hq):
+            g = (h * hkv) // hq
+            s = scale * (K[ks, g] @ Q[r, h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = p @ V[ks, g]
+            dp = V[ks, g] @ dO[r, h]
+            ds = p * (dp - dO[r, h] @ o)
+            dV[ks, g] += p[:, None] * dO[r, h][None]
+            dQ[r, h] += scale * (ds @ K[ks, g])
+            dK[ks, g] += scale * ds[:, None] * Q[r, h][None]
+    return dQ, dK, dV
+
+
+def check_grads(got, ref, label):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        e = rel_fro(widen(g), r)
+        print("%s %s relF=%.3e" % (label, name, e), flush=True)
+        assert e <= GRAD_REL_FRO, label + " " + name
+
+
+@pytest.mark.parametrize("window,sink,hq,hkv,d", [
+    (300, 16, 8, 2, 128), (37, 0, 4, 4, 64), (1, 0, 8, 2, 128), (130, 129, 16, 1, 128), (64, 0, 6, 2, 64)])
+def test_lambda_mask_backward(window, sink, hq, hkv, d):
+    announce("lambda backward window=%d sink=%d hq%d hkv%d d%d" % (window, sink, hq, hkv, d))
+    docs = [900, 1, 257, 400]
+    T = sum(docs)
+    tasks = I.lambda_tasks(docs, window=window, sink=sink)
+    got, Q, K, V, dO = gpu_grads(tasks, tasks, 1, T, hq, hkv, d, 1500 + window)
+    ref = oracle.backward(tasks, widen(Q), widen(K), widen(V), widen(dO), 1 / math.sqrt(d))
+    check_grads(got, ref, "lambda bwd")
+
+
+def merged_row_tasks(tasks):
+    """The same tasks writing (and, in the backward, reading) the merged rows."""
+    t = np.array(tasks, dtype=np.int64).copy()
+    t[:, 2] = t[:, 0]
+    return t
+
+
+def test_blockwise_mask_backward():
+    announce("causal-blockwise backward (merged partials)")
+    docs = [700, 200, 333]
+    block, w = 128, 2
+    hq, hkv, d = 4, 2, 64
+    T = sum(docs)
+    tasks, parts = I.blockwise_tasks(docs, block=block, win_blocks=w)
+    got, Q, K, V, dO = gpu_grads(tasks, merged_row_tasks(tasks), parts, T, hq, hkv, d, 1520)
+    rows_keys, start = [], 0
+    for L in docs:
+        nb = -(-L // block)
+        for p in range(L):
+            b = p // block
+            if b == nb - 1:
+                keys = list(range(p + 1))
+            else:
+                keys = sorted(set(range(min(block, p + 1))) | set(range(max(0, b - w + 1) * block, p + 1)))
+            rows_keys.append([start + k for k in keys])
+        start += L
+    check_grads(got, brute_grads(Q, K, V, dO, 1 / math.sqrt(d), rows_keys, hq, hkv), "blockwise bwd")
+
+
+def test_shared_question_mask_backward():
+    announce("shared-question backward (merged partials)")
+    question, answers = 300, [150, 7, 260]
+    hq, hkv, d = 4, 2, 64
+    T = question + sum(answers)
+    tasks, parts = I.shared_question_tasks(question, answers)
+    got, Q, K, V, dO = gpu_grads(tasks, merged_row_tasks(tasks), parts, T, hq, hkv, d, 1530)
+    rows_keys = [list(range(p + 1)) for p in range(question)]
+    off = question
+    for a in answers:
+        rows_keys += [list(range(question)) + [off + j for j in range(i + 1)] for i in range(a)]
+        off += a
+    check_grads(got, brute_grads(Q, K, V, dO, 1 / math.sqrt(d), rows_keys, hq, hkv), "shared-question bwd")
