@@ -238,6 +238,48 @@ def secondary(steps=3, warmup=1):
     del Q, K, V, O, LSE
     torch.cuda.empty_cache()
 
+    # Lambda mask (sink 64 + sliding window 4096) on the 512K training batch
+    w = I.train_8b_prolong_512k()
+    lt = I.lambda_tasks(w.doc_lens, window=4096, sink=64)
+    Q = I.randn_bf16((w.q_rows, w.hq, w.d), 210, device=dev)
+    K = I.randn_bf16((w.kv_rows, w.hkv, w.d), 211, device=dev)
+    V = I.randn_bf16((w.kv_rows, w.hkv, w.d), 212, device=dev)
+    dO = I.randn_bf16((w.o_rows, w.hq, w.d), 213, device=dev)
+    O = torch.empty((w.o_rows, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((w.o_rows, w.hq), device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    shape = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
+    ws = ca.workspace_tensor(ca.forward_workspace(shape, lt), dev)
+    bws = ca.workspace_tensor(ca.backward_workspace(shape, lt), dev)
+    pairs = ca.visible_pairs(lt)
+    ms_f = timed(lambda: ca.forward(shape, lt, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
+    ms_b = timed(lambda: ca.backward(shape, lt, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
+                 steps, warmup, stream)
+    ff, bf = oracle.forward_flops(pairs, w.hq, w.d), oracle.backward_flops(pairs, w.hq, w.d)
+    out["lambda_mask_512k"] = {"workload": w.name + ", lambda mask sink 64 + window 4096",
+                               "visible_pairs_per_head": pairs, "fwd_ms": round(ms_f, 2),
+                               "fwd_tflops": round(ff / ms_f / 1e9, 1), "bwd_ms": round(ms_b, 2),
+                               "bwd_tflops_10d": round(bf / ms_b / 1e9, 1)}
+    log("lambda mask 512k: fwd %.1f ms (%.1f TFLOP/s), bwd %.1f ms (%.1f TFLOP/s at 10d)"
+        % (ms_f, ff / ms_f / 1e9, ms_b, bf / ms_b / 1e9))
+    del Q, K, V, dO, O, LSE, dQ, dK, dV, ws, bws
+    torch.cuda.empty_cache()
+
+    # CA-tasks backward (34B shape: each re-batched task carries its own context)
+    w = I.ca_tasks_34b()
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 214)
+    ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
+    dO = I.randn_bf16((w.o_rows, w.hq, w.d), 215, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    bws = ca.workspace_tensor(ca.backward_workspace(shape, tasks), dev)
+    ms_b = timed(lambda: ca.backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
+                 steps, warmup, stream)
+    bf = oracle.backward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    out["ca_tasks_34b_bwd"] = {"workload": w.name, "ms": round(ms_b, 2), "tflops_10d": round(bf / ms_b / 1e9, 1)}
+    log("CA-tasks bwd: %.1f ms, %.1f TFLOP/s at 10d" % (ms_b, bf / ms_b / 1e9))
+    del Q, K, V, O, LSE, ws, dO, dQ, dK, dV, bws
+    torch.cuda.empty_cache()
+
     # Training forward + backward (Llama-3-8B shape, 512K ProLong-like)
     w = I.train_8b_prolong_512k()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 205)
