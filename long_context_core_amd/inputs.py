@@ -260,6 +260,55 @@ def train_8b_prolong_512k(seed=105, total=524288, div=1):
 
 
 # --------------------------------------------------------------------------
+# paged K/V layouts (block tables)
+# --------------------------------------------------------------------------
+
+def page_table(n_virtual, n_physical, seed):
+    """Block table: each of n_virtual virtual pages gets a distinct physical
+    page, drawn at random from n_physical >= n_virtual."""
+    rng = np.random.default_rng(seed)
+    return rng.permutation(int(n_physical))[:int(n_virtual)].astype(np.int32)
+
+
+def page_store(X, table, page_rows, n_physical, fill=float("nan")):
+    """Physical page store (torch tensor) of the virtual tensor X: virtual page
+    v is copied to physical page table[v]; pages no entry names hold
+    ``fill``.  X has len(table) * page_rows rows."""
+    import torch
+    P = int(page_rows)
+    store = torch.full((int(n_physical) * P,) + tuple(X.shape[1:]), fill, dtype=X.dtype, device=X.device)
+    for v, pp in enumerate(np.asarray(table).tolist()):
+        store[pp * P:(pp + 1) * P] = X[v * P:(v + 1) * P]
+    return store
+
+
+def paged_varlen_tasks(doc_lens, page_rows):
+    """Packed causal documents whose K/V live in pages: queries packed as in
+    varlen_tasks, document i's context starting at its own virtual page.
+    Returns (tasks, number of virtual pages)."""
+    P = int(page_rows)
+    t = []
+    q = 0
+    vp = 0
+    for l in doc_lens:
+        l = int(l)
+        t.append((q, vp * P, q, l, l, 0, 0))
+        q += l
+        vp += -(-l // P)
+    return np.array(t, dtype=np.int64).reshape(-1, 7), vp
+
+
+def llama8b_packed_131k_paged(page_rows=512, seed=102):
+    """The 131K packed Llama-3-8B batch with K/V in pages of page_rows rows
+    (the data-block sizes 512 ... 4096 of the DCP page, Block Generation);
+    tasks address virtual rows.  kv_rows counts the virtual rows."""
+    w = llama8b_packed_131k(seed=seed)
+    tasks, n_vp = paged_varlen_tasks(w.doc_lens, page_rows)
+    return Workload("llama3-8b-packed-128k-lognormal-paged%d" % page_rows, w.hq, w.hkv, w.d, tasks,
+                    w.q_rows, n_vp * page_rows, w.o_rows, doc_lens=w.doc_lens)
+
+
+# --------------------------------------------------------------------------
 # tensors
 # --------------------------------------------------------------------------
 

@@ -12,6 +12,8 @@ attention  forward / merge / backward / decode written as the plain definition
 counting   unmasked (query, key) pair counts and the FLOP convention.
 scheduler  the profiler cost model, Appendix-B shard sizing and the
            communication-aware greedy placement of CA-tasks on servers.
+paging     attention over paged K/V (block tables): the virtual K/V a table
+           describes, then the plain forward.
 
 Parity status of every function is stated in its own docstring; all of them
 are pinned by ``tests/test_oracle_pins.py`` except where a docstring says
@@ -28,6 +30,7 @@ from .attention import (  # noqa: F401
     merge,
     backward,
 )
+from .paging import virtual_rows, forward_paged  # noqa: F401
 from .counting import (  # noqa: F401
     visible_pairs_task,
     visible_pairs_masked,

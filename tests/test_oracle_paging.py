@@ -1,0 +1,85 @@
+"""Pins of the oracle's paged K/V (block tables: "DCP: Addressing Input
+Dynamism In Long-Context Training via Dynamic Context Parallelism", Executor
+Design, Blockwise Attention).  Paging moves rows and nothing else, so the
+pins build page stores by hand, page by page, and require attention over
+them to equal attention over the unpaged tensors bit for bit."""
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_core_amd import inputs as I
+
+
+def test_virtual_rows_hand_example():
+    # 3 physical pages of 2 rows: rows 0..5 hold 10..15; table [2, 0] reads
+    # physical page 2 then page 0
+    X = np.arange(10, 16, dtype=np.float64).reshape(6, 1)
+    V = oracle.virtual_rows(X, [2, 0], 2)
+    assert V[:, 0].tolist() == [14, 15, 10, 11]
+    # a page named twice (a shared prefix) appears twice
+    assert oracle.virtual_rows(X, [1, 1, 0], 2)[:, 0].tolist() == [12, 13, 12, 13, 10, 11]
+
+
+def hand_store(Xv, table, P, n_phys):
+    """Scatter the virtual rows into physical pages; unused pages are NaN."""
+    store = np.full((n_phys * P,) + Xv.shape[1:], np.nan)
+    for v, pp in enumerate(table):
+        store[pp * P:(pp + 1) * P] = Xv[v * P:(v + 1) * P]
+    return store
+
+
+@pytest.mark.parametrize("P", [2, 4, 16])
+def test_paged_forward_equals_unpaged(P):
+    docs = [13, 1, 40, 7]
+    tasks, n_vp = I.paged_varlen_tasks(docs, P)
+    hq, hkv, d = 4, 2, 8
+    rng = np.random.default_rng(90 + P)
+    T = sum(docs)
+    Q = rng.standard_normal((T, hq, d))
+    Kv = rng.standard_normal((n_vp * P, hkv, d))
+    Vv = rng.standard_normal((n_vp * P, hkv, d))
+    n_phys = n_vp + 5
+    table = rng.permutation(n_phys)[:n_vp]
+    Ks, Vs = hand_store(Kv, table, P, n_phys), hand_store(Vv, table, P, n_phys)
+    O, L = oracle.forward_paged(tasks, Q, Ks, Vs, table, P, 0.4)
+    O0, L0 = oracle.forward(tasks, Q, Kv, Vv, 0.4)
+    assert np.isfinite(O).all() and np.array_equal(O, O0) and np.array_equal(L, L0)
+    # and the unpaged reading of the same packing: documents back to back
+    Kp = np.concatenate([Kv[t[1]:t[1] + t[4]] for t in tasks])
+    Vp = np.concatenate([Vv[t[1]:t[1] + t[4]] for t in tasks])
+    O1, L1 = oracle.forward(I.varlen_tasks(docs), Q, Kp, Vp, 0.4)
+    assert np.array_equal(O, O1) and np.array_equal(L, L1)
+
+
+def test_shared_prefix_pages():
+    """Two tasks whose tables share their first pages read the same rows."""
+    P = 4
+    rng = np.random.default_rng(95)
+    hq, hkv, d = 2, 1, 8
+    prefix = rng.standard_normal((2 * P, hkv, d))
+    tail_a = rng.standard_normal((P, hkv, d))
+    tail_b = rng.standard_normal((P, hkv, d))
+    store = np.concatenate([tail_b, prefix, tail_a])          # physical pages: b, p0, p1, a
+    table = [1, 2, 3, 1, 2, 0]                                 # task a: p0 p1 a, task b: p0 p1 b
+    Q = rng.standard_normal((2, hq, d))
+    tasks = np.array([[0, 0, 0, 1, 3 * P, 3 * P - 1, 0],
+                      [1, 3 * P, 1, 1, 3 * P, 3 * P - 1, 0]], dtype=np.int64)
+    O, L = oracle.forward_paged(tasks, Q, store, store, table, P, 0.5)
+    for r, tail in ((0, tail_a), (1, tail_b)):
+        K = np.concatenate([prefix, tail])
+        Or, Lr = oracle.forward(np.array([[0, 0, 0, 1, 3 * P, 3 * P - 1, 0]]), Q[r:r + 1], K, K, 0.5)
+        assert np.array_equal(O[r], Or[0]) and np.array_equal(L[r], Lr[0])
+
+
+def test_planted_page_formula_mistake_is_caught():
+    """Reading pages with the row-in-page and page index swapped fails the
+    equality the tests above rely on."""
+    P, n_vp = 4, 3
+    rng = np.random.default_rng(96)
+    Xv = rng.standard_normal((n_vp * P, 1, 2))
+    table = np.array([2, 0, 1])
+    store = hand_store(Xv, table, P, 3)
+    wrong = np.stack([store[table[v % n_vp] * P + v // n_vp] for v in range(n_vp * P)])
+    assert not np.array_equal(wrong, Xv)
+    assert np.array_equal(oracle.virtual_rows(store, table, P), Xv)
