@@ -177,7 +177,50 @@ def secondary(steps=3, warmup=1):
                                    "gbs": round(kv_bytes / ms / 1e6, 1),
                                    "pct_of_hbm_peak": round(100 * kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 2)}
     log("decode: %.3f ms, %.0f GB/s of K+V" % (ms, kv_bytes / ms / 1e6))
-    del Q, K, V, O, LSE, ws, Om, Lm
+
+    # The same decode step over paged caches: 256-row pages in a random
+    # physical order (block tables)
+    P = 256
+    n_vp = w.kv_rows // P
+    table = I.page_table(n_vp, n_vp, 206)
+    idx = torch.from_numpy(table.astype(np.int64)).to(dev)
+    Ks, Vs = torch.empty_like(K), torch.empty_like(V)
+    Ks.view(n_vp, -1)[idx] = K.view(n_vp, -1)
+    Vs.view(n_vp, -1)[idx] = V.view(n_vp, -1)
+    pages = ca.kv_pages(table, P)
+    pws = ca.workspace_tensor(ca.forward_workspace(shape, tasks, pages=pages), dev)
+
+    def dec_step_paged():
+        ca.forward(shape, tasks, Q, Ks, Vs, O, LSE, ws=pws, stream=stream, pages=pages)
+        ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream)
+
+    ms = timed(dec_step_paged, max(steps, 10), warmup, stream)
+    out["ring_decode_405b_tp8_paged256"] = {"workload": w.name + ", K/V in shuffled 256-row pages",
+                                            "ms": round(ms, 4), "gbs": round(kv_bytes / ms / 1e6, 1)}
+    log("decode, paged K/V (256-row pages): %.3f ms, %.0f GB/s of K+V" % (ms, kv_bytes / ms / 1e6))
+    del Q, K, V, O, LSE, ws, Om, Lm, Ks, Vs, pws
+    torch.cuda.empty_cache()
+
+    # Headline forward over paged K/V: documents start on their own 512-row
+    # page, pages in a random physical order
+    w = I.llama8b_packed_131k_paged(512)
+    Q, K, V, O, LSE, shape, tasks, _ = fwd_setup(w, 207)
+    n_vp = w.kv_rows // 512
+    table = I.page_table(n_vp, n_vp, 208)
+    idx = torch.from_numpy(table.astype(np.int64)).to(dev)
+    Ks, Vs = torch.empty_like(K), torch.empty_like(V)
+    Ks.view(n_vp, -1)[idx] = K.view(n_vp, -1)
+    Vs.view(n_vp, -1)[idx] = V.view(n_vp, -1)
+    del K, V
+    pages = ca.kv_pages(table, 512)
+    pws = ca.workspace_tensor(ca.forward_workspace(shape, tasks, pages=pages), dev)
+    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    ms = timed(lambda: ca.forward(shape, tasks, Q, Ks, Vs, O, LSE, ws=pws, stream=stream, pages=pages),
+               steps, warmup, stream)
+    out["llama3_8b_packed_128k_paged512"] = {"workload": w.name, "ms": round(ms, 3),
+                                             "tflops": round(fl / ms / 1e9, 1)}
+    log("headline forward, paged K/V (512-row pages): %.2f ms, %.1f TFLOP/s" % (ms, fl / ms / 1e9))
+    del Q, Ks, Vs, O, LSE, pws
     torch.cuda.empty_cache()
 
     # Throughput vs shard length in one fused 32K-token chunk

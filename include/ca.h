@@ -144,6 +144,38 @@ ca_status ca_forward_masked(const ca_shape* shape, const ca_task* tasks_host, co
                             int32_t n_tasks, const void* Q, const void* K, const void* V, void* O,
                             float* LSE, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Paged K/V: block tables as in the Blockwise Attention instruction of "DCP:
+ * Addressing Input Dynamism In Long-Context Training via Dynamic Context
+ * Parallelism" (Executor Design; its data blocks are per-head runs of B
+ * tokens, Block Generation).  K and V are stores of physical pages of
+ * page_rows rows: physical page p is rows [p * page_rows, (p + 1) * page_rows)
+ * of K and of V.  Every task's kv_off and kv_len then address a virtual row
+ * space of n_pages * page_rows rows, whose row v is the physical row
+ *     table_host[v / page_rows] * page_rows + v % page_rows.
+ * Pages may be shared by several virtual pages and tasks (a shared prefix).
+ * Requirements, else CA_ERR_INVALID: page_rows a power of two in
+ * [128, 1 << 20]; n_pages >= 0; every entry in [0, kv_rows / page_rows);
+ * every task's [kv_off, kv_off + kv_len) inside the virtual space, with
+ * kv_off a multiple of 128.  The call copies the table into the workspace;
+ * the host array may be reused once the call has returned.
+ */
+typedef struct {
+  const int32_t* table_host;  /* [n_pages] physical page of each virtual page */
+  int64_t n_pages;            /* virtual pages                                 */
+  int32_t page_rows;          /* rows per page                                 */
+  int32_t reserved;           /* must be 0                                     */
+} ca_kv_pages;
+
+/* ca_forward_masked over paged K/V (pages must not be NULL; masks_host may
+ * be).  Errors as ca_forward_masked, with the context ranges checked against
+ * the virtual space instead of kv_rows, plus the page requirements above. */
+size_t ca_forward_paged_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                  int32_t n_tasks, const ca_kv_pages* pages);
+ca_status ca_forward_paged(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                           int32_t n_tasks, const ca_kv_pages* pages, const void* Q, const void* K,
+                           const void* V, void* O, float* LSE, void* ws, size_t ws_bytes, void* stream);
+
 /* Packed causal documents: document i occupies rows [cu[i], cu[i+1]) of Q,
  * K, V, O and LSE (the task {cu[i], cu[i], cu[i], l, l, 0, 0}).
  * cu_seqlens_host has n_docs + 1 non-decreasing entries starting at 0. */

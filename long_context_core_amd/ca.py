@@ -34,6 +34,8 @@ EXPORTS = (
     "ca_visible_pairs_masked",
     "ca_forward_masked_workspace",
     "ca_forward_masked",
+    "ca_forward_paged_workspace",
+    "ca_forward_paged",
     "ca_backward_masked_workspace",
     "ca_backward_masked",
     "ca_cost_time",
@@ -59,6 +61,20 @@ class Shape(ctypes.Structure):
     _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
                 ("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64), ("o_rows", ctypes.c_int64)]
+
+
+class KVPages(ctypes.Structure):
+    """ca_kv_pages: block table of paged K/V (physical page of each virtual page)."""
+    _fields_ = [("table_host", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("page_rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def kv_pages(table, page_rows):
+    """KVPages over an int32 copy of ``table``; the struct keeps that copy alive."""
+    tb = np.ascontiguousarray(np.asarray(table, dtype=np.int32).reshape(-1))
+    pg = KVPages(tb.ctypes.data_as(ctypes.c_void_p) if tb.size else None, len(tb), int(page_rows), 0)
+    pg._table = tb
+    return pg
 
 
 class SchedParams(ctypes.Structure):
@@ -113,6 +129,10 @@ def lib():
         L.ca_forward_masked_workspace.restype = sz
         L.ca_forward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ca_forward_masked.restype = ctypes.c_int
+        L.ca_forward_paged_workspace.argtypes = [sp, vp, vp, i32, vp]
+        L.ca_forward_paged_workspace.restype = sz
+        L.ca_forward_paged.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_forward_paged.restype = ctypes.c_int
         L.ca_backward_masked_workspace.argtypes = [sp, vp, vp, i32]
         L.ca_backward_masked_workspace.restype = sz
         L.ca_backward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -220,8 +240,11 @@ def visible_pairs(tasks, masks=None):
     return int(n)
 
 
-def forward_workspace(shape, tasks, masks=None):
+def forward_workspace(shape, tasks, masks=None, pages=None):
     ta, ma = split_tasks(tasks, masks)
+    if pages is not None:
+        return int(lib().ca_forward_paged_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
+                                                    ctypes.byref(pages)))
     return int(lib().ca_forward_masked_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta)))
 
 
@@ -230,14 +253,19 @@ def workspace_tensor(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None):
+def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None, pages=None):
     """ca_forward on torch tensors: Q [q_rows, hq, d] bf16, K/V [kv_rows, hkv, d]
     bf16, O [o_rows, hq, d] bf16 (fp32 with out_f32), LSE [o_rows, hq] fp32.
-    With masks (or a 9-column table) it calls ca_forward_masked."""
+    With masks (or a 9-column table) it calls ca_forward_masked; with pages
+    (a KVPages from kv_pages) ca_forward_paged, K/V then being page stores."""
     ta, ma = split_tasks(tasks, masks)
     if ws is None:
-        ws = workspace_tensor(forward_workspace(shape, ta, ma), Q.device)
-    if ma is None:
+        ws = workspace_tensor(forward_workspace(shape, ta, ma, pages), Q.device)
+    if pages is not None:
+        st = lib().ca_forward_paged(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
+                                    ctypes.byref(pages), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE),
+                                    _ptr(ws), ws.numel(), _stream_ptr(stream))
+    elif ma is None:
         st = lib().ca_forward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
                               _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
     else:

@@ -121,7 +121,9 @@ ca_status check_shape(const ca_shape* s) {
   return CA_OK;
 }
 
-ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n) {
+// kv_limit: rows of the space that kv_off / kv_len address (kv_rows, or the
+// virtual rows of a page table).
+ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n, int64_t kv_limit) {
   if (n < 0) return fail(CA_ERR_INVALID, "n_tasks=%d < 0", n);
   if (n > 0 && !t) return fail(CA_ERR_INVALID, "tasks_host is NULL");
   for (int32_t i = 0; i < n; ++i) {
@@ -131,9 +133,9 @@ ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n) {
     if (k.q_off + k.q_len > s->q_rows)
       return fail(CA_ERR_INVALID, "task %d: query rows [%lld, %lld) past q_rows=%lld", i,
                   (long long)k.q_off, (long long)(k.q_off + k.q_len), (long long)s->q_rows);
-    if (k.kv_off + k.kv_len > s->kv_rows)
-      return fail(CA_ERR_INVALID, "task %d: context rows [%lld, %lld) past kv_rows=%lld", i,
-                  (long long)k.kv_off, (long long)(k.kv_off + k.kv_len), (long long)s->kv_rows);
+    if (k.kv_off + k.kv_len > kv_limit)
+      return fail(CA_ERR_INVALID, "task %d: context rows [%lld, %lld) past %lld", i,
+                  (long long)k.kv_off, (long long)(k.kv_off + k.kv_len), (long long)kv_limit);
     if (k.o_off + k.q_len > s->o_rows)
       return fail(CA_ERR_INVALID, "task %d: output rows [%lld, %lld) past o_rows=%lld", i,
                   (long long)k.o_off, (long long)(k.o_off + k.q_len), (long long)s->o_rows);
@@ -142,6 +144,61 @@ ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n) {
       return fail(CA_ERR_INVALID, "task %d: positions out of range", i);
   }
   return CA_OK;
+}
+
+ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n) { return check_tasks(s, t, n, s->kv_rows); }
+
+constexpr int kPageAlign = 128;   // task starts and page sizes: whole 128-row tiles
+
+// Page table checks; see ca_kv_pages.
+ca_status check_page_table(const ca_shape* s, const ca_kv_pages* pg) {
+  if (!pg) return fail(CA_ERR_INVALID, "pages is NULL");
+  const int32_t pr = pg->page_rows;
+  if (pr < kPageAlign || pr > (1 << 20) || (pr & (pr - 1)) != 0)
+    return fail(CA_ERR_INVALID, "page_rows=%d must be a power of two in [128, 1 << 20]", pr);
+  if (pg->n_pages < 0 || pg->n_pages > (int64_t(1) << 31) / 4)
+    return fail(CA_ERR_INVALID, "n_pages=%lld out of range", (long long)pg->n_pages);
+  if (pg->reserved != 0) return fail(CA_ERR_INVALID, "reserved field must be 0");
+  if (pg->n_pages > 0 && !pg->table_host) return fail(CA_ERR_INVALID, "table_host is NULL");
+  const int64_t phys = s->kv_rows / pr;
+  for (int64_t v = 0; v < pg->n_pages; ++v)
+    if (pg->table_host[v] < 0 || pg->table_host[v] >= phys)
+      return fail(CA_ERR_INVALID, "page table entry %lld = %d not in [0, %lld)", (long long)v, pg->table_host[v],
+                  (long long)phys);
+  return CA_OK;
+}
+
+// Paged tasks start on a 128-row boundary of the virtual space.
+ca_status check_paged_tasks(const ca_task* t, int32_t n) {
+  for (int32_t i = 0; i < n; ++i)
+    if (t[i].kv_len > 0 && t[i].kv_off % kPageAlign != 0)
+      return fail(CA_ERR_INVALID, "task %d: kv_off=%lld is not a multiple of 128 (paged K/V)", i,
+                  (long long)t[i].kv_off);
+  return CA_OK;
+}
+
+int page_shift_of(const ca_kv_pages* pg) {
+  int sh = 0;
+  while ((1 << sh) < pg->page_rows) ++sh;
+  return sh;
+}
+
+// Argument checks shared by the forward entry points and their workspace queries.
+ca_status check_forward_args(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                             const ca_kv_pages* pg) {
+  ca_status st = check_shape(s);
+  if (st != CA_OK) return st;
+  if (pg) {
+    st = check_page_table(s, pg);
+    if (st != CA_OK) return st;
+    st = check_tasks(s, t, n, pg->n_pages * pg->page_rows);
+    if (st != CA_OK) return st;
+    st = check_paged_tasks(t, n);
+  } else {
+    st = check_tasks(s, t, n);
+  }
+  if (st != CA_OK) return st;
+  return check_masks(m, n);
 }
 
 int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
@@ -224,11 +281,12 @@ struct FwdPlan {
   size_t n_split = 0;        // decode (task, kv head) pairs cut into > 1 chunk
   size_t n_parts = 0;        // staging slots for those chunks
   int64_t dec_chunk = 0;
-  size_t off_tasks = 0, off_masks = 0, off_items = 0, off_dec = 0, off_split = 0, off_part_o = 0, off_part_l = 0,
-         bytes = 0;
+  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_items = 0, off_dec = 0, off_split = 0, off_part_o = 0,
+         off_part_l = 0, bytes = 0;
 };
 
-FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n) {
+FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                     const ca_kv_pages* pg = nullptr) {
   FwdPlan p;
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, kFwdWaves);
@@ -257,7 +315,8 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m,
   }
   p.off_tasks = 0;
   p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
-  p.off_items = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
+  p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
+  p.off_items = p.off_pages + (pg ? align_up(sizeof(int32_t) * (size_t)pg->n_pages) : 0);
   p.off_dec = p.off_items + align_up(sizeof(ca::FwdItem) * p.n_items);
   p.off_split = p.off_dec + align_up(sizeof(ca::DecItem) * p.n_dec_items);
   p.off_part_o = p.off_split + align_up(4 * sizeof(int32_t) * p.n_split);
@@ -334,26 +393,18 @@ void build_decode_items(const ca_shape* s, const ca_task* t, const ca_task_mask*
   });
 }
 
-ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const void* Q,
-                       const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
-                       void* stream) {
-  ca_status st = check_shape(s);
+ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                       const ca_kv_pages* pg, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       void* ws, size_t ws_bytes, void* stream) {
+  ca_status st = check_forward_args(s, t, m, n, pg);
   if (st != CA_OK) return st;
-  st = check_tasks(s, t, n);
-  if (st != CA_OK) return st;
-  st = check_masks(m, n);
-  if (st != CA_OK) return st;
-  const FwdPlan p = plan_forward(s, t, m, n);
+  const FwdPlan p = plan_forward(s, t, m, n, pg);
   if (p.n_items == 0 && p.n_dec_items == 0) return CA_OK;
   if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
   if (!ws || ws_bytes < p.bytes)
     return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
   if (p.n_items > 0x7fffffffu || p.n_dec_items > 0x7fffffffu || p.n_parts > 0x7fffffffu)
     return fail(CA_ERR_UNSUPPORTED, "too many work items");
-  // 32-bit buffer offsets inside one task's context
-  for (int32_t i = 0; i < n; ++i)
-    if ((int64_t)t[i].kv_len * s->hkv * s->d * 2 >= (int64_t(1) << 31))
-      return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
   std::vector<ca::FwdItem> items;
   build_forward_items(s, t, m, n, p, items);
   std::vector<ca::DecItem> ditems;
@@ -362,6 +413,8 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
   std::vector<char> host(p.off_part_o, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
   if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+  if (pg && pg->n_pages > 0)
+    std::memcpy(host.data() + p.off_pages, pg->table_host, sizeof(int32_t) * (size_t)pg->n_pages);
   if (!items.empty()) std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
   if (!ditems.empty()) std::memcpy(host.data() + p.off_dec, ditems.data(), sizeof(ca::DecItem) * ditems.size());
   if (!split.empty()) std::memcpy(host.data() + p.off_split, split.data(), sizeof(int32_t) * split.size());
@@ -371,6 +424,8 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
   char* w = (char*)ws;
   const float scale_log2 = s->scale * 1.4426950408889634f;
   const int out_f32 = (s->flags & CA_OUT_F32) ? 1 : 0;
+  const int32_t* pages = pg ? (const int32_t*)(w + p.off_pages) : nullptr;
+  const int page_shift = pg ? page_shift_of(pg) : 0;
   if (!items.empty()) {
     ca::FwdParams fp;
     fp.Q = (const __bf16*)Q;
@@ -381,6 +436,8 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
     fp.tasks = (const ca_task*)(w + p.off_tasks);
     fp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
     fp.items = (const ca::FwdItem*)(w + p.off_items);
+    fp.pages = pages;
+    fp.page_shift = page_shift;
     fp.n_items = (int32_t)items.size();
     fp.hq = s->hq;
     fp.hkv = s->hkv;
@@ -403,6 +460,8 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
     dp.part_LSE = (float*)(w + p.off_part_l);
     dp.tasks = (const ca_task*)(w + p.off_tasks);
     dp.items = (const ca::DecItem*)(w + p.off_dec);
+    dp.pages = pages;
+    dp.page_shift = page_shift;
     dp.n_items = (int32_t)ditems.size();
     dp.hq = s->hq;
     dp.hkv = s->hkv;
@@ -702,21 +761,32 @@ size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, in
 ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks, const void* Q,
                      const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
                      void* stream) {
-  return forward_impl(shape, tasks_host, nullptr, n_tasks, Q, K, V, O, LSE, ws, ws_bytes, stream);
+  return forward_impl(shape, tasks_host, nullptr, n_tasks, nullptr, Q, K, V, O, LSE, ws, ws_bytes, stream);
 }
 
 size_t ca_forward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
                                    int32_t n_tasks) {
-  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK ||
-      check_masks(masks_host, n_tasks) != CA_OK)
-    return 0;
+  if (check_forward_args(shape, tasks_host, masks_host, n_tasks, nullptr) != CA_OK) return 0;
   return plan_forward(shape, tasks_host, masks_host, n_tasks).bytes;
 }
 
 ca_status ca_forward_masked(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
                             int32_t n_tasks, const void* Q, const void* K, const void* V, void* O, float* LSE,
                             void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(shape, tasks_host, masks_host, n_tasks, Q, K, V, O, LSE, ws, ws_bytes, stream);
+  return forward_impl(shape, tasks_host, masks_host, n_tasks, nullptr, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+size_t ca_forward_paged_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                  int32_t n_tasks, const ca_kv_pages* pages) {
+  if (!pages || check_forward_args(shape, tasks_host, masks_host, n_tasks, pages) != CA_OK) return 0;
+  return plan_forward(shape, tasks_host, masks_host, n_tasks, pages).bytes;
+}
+
+ca_status ca_forward_paged(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                           int32_t n_tasks, const ca_kv_pages* pages, const void* Q, const void* K, const void* V,
+                           void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
+  if (!pages) return fail(CA_ERR_INVALID, "pages is NULL");
+  return forward_impl(shape, tasks_host, masks_host, n_tasks, pages, Q, K, V, O, LSE, ws, ws_bytes, stream);
 }
 
 size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu, int32_t n_docs) {
@@ -731,7 +801,7 @@ ca_status ca_forward_varlen(const ca_shape* shape, const int32_t* cu, int32_t n_
   std::vector<ca_task> t;
   if (!varlen_to_tasks(cu, n_docs, t))
     return fail(CA_ERR_INVALID, "cu_seqlens must start at 0 and be non-decreasing");
-  return forward_impl(shape, t.data(), nullptr, n_docs, Q, K, V, O, LSE, ws, ws_bytes, stream);
+  return forward_impl(shape, t.data(), nullptr, n_docs, nullptr, Q, K, V, O, LSE, ws, ws_bytes, stream);
 }
 
 ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows, const float* O_parts,

@@ -171,18 +171,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   uint4 qreg[PASSES], oreg[PASSES];
   float lse_reg = 0.f, d_reg = 0.f;
   auto gload = [&]() {
-    const uint32_t nvalid = (uint32_t)min(BQ, nx_left);
-    const uint32_t qbytes = nvalid * row_bytes;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(nq + nx_g * D, qbytes);
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(no + nx_g * D, qbytes);
+    const int nvalid = max(0, min(BQ, nx_left));
+    const __amdgpu_buffer_rsrc_t qr = rows_rsrc(nq + nx_g * D, nvalid, row_bytes);
+    const __amdgpu_buffer_rsrc_t orr = rows_rsrc(no + nx_g * D, nvalid, row_bytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       qreg[r] = buffer_load_16(qr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
       oreg[r] = buffer_load_16(orr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
-    const uint32_t lbytes = nvalid * (uint32_t)p.hq * 4;
-    const __amdgpu_buffer_rsrc_t lr = make_rsrc(nl + nx_g, lbytes);
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(nd + nx_g, lbytes);
+    const __amdgpu_buffer_rsrc_t lr = rows_rsrc(nl + nx_g, nvalid, (uint32_t)p.hq * 4);
+    const __amdgpu_buffer_rsrc_t dr = rows_rsrc(nd + nx_g, nvalid, (uint32_t)p.hq * 4);
     if (tid < BQ) {
       lse_reg = buffer_load_f32(lr, lse_voff, 0);
       d_reg = buffer_load_f32(dr, lse_voff, 0);
@@ -532,18 +530,22 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int n_tiles = (kv_hi + BN - 1) / BN;
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.K + t.kv_off * kv_stride + it.kv_head * D, (uint32_t)kv_hi * row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.V + t.kv_off * kv_stride + it.kv_head * D, (uint32_t)kv_hi * row_bytes);
+  const __bf16* kbase = p.K + t.kv_off * kv_stride + it.kv_head * D;
+  const __bf16* vbase = p.V + t.kv_off * kv_stride + it.kv_head * D;
   const int ld_row = tid / CH;
   const int ld_chunk = tid % CH;
   const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
   uint4 kreg[PASSES], vreg[PASSES];
+  // rows >= kv_hi read as zeros; nothing past the context is read
   auto gload = [&](int tile) {
-    const uint32_t soff = (uint32_t)tile * BN * row_bytes;
+    const int64_t r0 = (int64_t)tile * BN;
+    const int n = min(BN, kv_hi - tile * BN);
+    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
-      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
+      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
+      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
   };
   auto swrite = [&](int buf) {

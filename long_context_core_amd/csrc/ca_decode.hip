@@ -29,7 +29,7 @@ __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shf
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
 }  // namespace
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
   constexpr int TK = 128;            // keys per tile, 32 per wave
   constexpr int NT = D / 32;         // 32-channel reduction steps of Q.K
@@ -63,9 +63,9 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
   const int nkeys = it.k_end - it.k_begin;
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
-  const int64_t row0 = t.kv_off + it.k_begin;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.K + row0 * kv_stride + it.kv_head * D, (uint32_t)nkeys * row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.V + row0 * kv_stride + it.kv_head * D, (uint32_t)nkeys * row_bytes);
+  const int64_t row0 = t.kv_off + it.k_begin;   // virtual row of the chunk's first key
+  const __bf16* kbase = p.K + it.kv_head * D;
+  const __bf16* vbase = p.V + it.kv_head * D;
 
   // K operand loads: key 32 w + 16 b + l16, channels 32 s + 8 g4.
   uint32_t k_voff[2];
@@ -79,14 +79,21 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
   const int v_rd = (4 * g4 + (l16 >> 2)) * VS + 4 * (l16 & 3);
 
   uint4 kr[2][NT], vr[VPASS];
+  // Tile loads over the tile's own rows: keys >= nkeys read as zeros and
+  // nothing past the chunk is read.  Paged K/V: chunks start at multiples of
+  // 128 keys, tasks at multiples of 128 virtual rows, and pages hold a
+  // multiple of 128 rows, so each tile lies inside one page.
   auto gload = [&](int tile) {
-    const uint32_t soff = (uint32_t)tile * TK * row_bytes;
+    const int64_t r0 = kv_phys_row<PAGED>(p.pages, p.page_shift, row0 + (int64_t)tile * TK);
+    const int n = min(TK, nkeys - tile * TK);
+    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int s = 0; s < NT; ++s) kr[b][s] = buffer_load_16(krs, k_voff[b] + 64 * s, soff);
+      for (int s = 0; s < NT; ++s) kr[b][s] = buffer_load_16(krs, k_voff[b] + 64 * s, 0);
 #pragma unroll
-    for (int r = 0; r < VPASS; ++r) vr[r] = buffer_load_16(vrs, v_voff + (uint32_t)(r * VROWS) * row_bytes, soff);
+    for (int r = 0; r < VPASS; ++r) vr[r] = buffer_load_16(vrs, v_voff + (uint32_t)(r * VROWS) * row_bytes, 0);
   };
 
   f32x4 o_acc[NCB];
@@ -247,13 +254,18 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecMergeParams p) {
   if (sub == 0) p.LSE[t.o_off * p.hq + head] = lse;
 }
 
+template <int D>
+hipError_t launch_decode_d(const DecParams& p, hipStream_t s) {
+  if (p.pages)
+    hipLaunchKernelGGL((dec_kernel<D, true>), dim3(p.n_items), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((dec_kernel<D, false>), dim3(p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecParams& p, int d, hipStream_t s) {
   if (p.n_items <= 0) return hipSuccess;
-  if (d == 128)
-    hipLaunchKernelGGL(dec_kernel<128>, dim3(p.n_items), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(dec_kernel<64>, dim3(p.n_items), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return d == 128 ? launch_decode_d<128>(p, s) : launch_decode_d<64>(p, s);
 }
 
 hipError_t launch_decode_merge(const DecMergeParams& p, int d, hipStream_t s) {

@@ -39,7 +39,7 @@ namespace ca {
 // regardless of when the reference moved.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int NW>
+template <int D, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   constexpr int NT = 64 * NW;     // threads
   constexpr int BN = 64;          // keys per tile
@@ -128,22 +128,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   };
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
-  const __bf16* kbase = p.K + t.kv_off * kv_stride + it.kv_head * D;
-  const __bf16* vbase = p.V + t.kv_off * kv_stride + it.kv_head * D;
-  // Rows >= kv_hi read as zeros (range-checked buffer loads).
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)kv_hi * row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)kv_hi * row_bytes);
+  const __bf16* kbase = p.K + it.kv_head * D;
+  const __bf16* vbase = p.V + it.kv_head * D;
   const int ld_row = tid / CH;
   const int ld_chunk = tid % CH;
   const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
 
+  // Tile loads: rows >= kv_hi read as zeros (range-checked buffer loads over
+  // the tile's own rows, so nothing past the context is ever read).  Paged
+  // K/V: a tile starts at a multiple of 64 virtual rows and pages hold a
+  // multiple of 128 rows, so each tile lies inside one page.
   uint4 kreg[PASSES], vreg[PASSES];
   auto gload = [&](int tile) {
-    const uint32_t soff = (uint32_t)tile * BN * row_bytes;
+    const int64_t r0 = kv_phys_row<PAGED>(p.pages, p.page_shift, t.kv_off + (int64_t)tile * BN);
+    const int n = min(BN, kv_hi - tile * BN);
+    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
-      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, soff);
+      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
+      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
   };
   auto swrite = [&](int buf) {
@@ -302,20 +306,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   }
 }
 
+template <int D, int NW>
+hipError_t launch_forward_d(const FwdParams& p, hipStream_t s) {
+  if (p.pages)
+    hipLaunchKernelGGL((fwd_kernel<D, NW, true>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, NW, false>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s) {
   if (p.n_items <= 0) return hipSuccess;
-  if (p.waves == 8) {
-    if (d == 128)
-      hipLaunchKernelGGL((fwd_kernel<128, 8>), dim3(p.n_items), dim3(512), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<64, 8>), dim3(p.n_items), dim3(512), 0, s, p);
-  } else {
-    if (d == 128)
-      hipLaunchKernelGGL((fwd_kernel<128, 4>), dim3(p.n_items), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<64, 4>), dim3(p.n_items), dim3(256), 0, s, p);
-  }
-  return hipGetLastError();
+  if (p.waves == 8) return d == 128 ? launch_forward_d<128, 8>(p, s) : launch_forward_d<64, 8>(p, s);
+  return d == 128 ? launch_forward_d<128, 4>(p, s) : launch_forward_d<64, 4>(p, s);
 }
 
 }  // namespace ca

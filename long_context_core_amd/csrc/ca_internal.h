@@ -48,6 +48,8 @@ struct FwdParams {
   const ca_task* tasks;
   const ca_task_mask* masks;   // per task, or nullptr: causal only
   const FwdItem* items;
+  const int32_t* pages;   // K/V block table (virtual page -> physical page), or nullptr: rows are physical
+  int32_t page_shift;     // log2 of the rows per page
   int32_t n_items;
   int32_t hq, hkv, group, hpw;
   float scale_log2;   // softmax scale * log2(e)
@@ -65,6 +67,8 @@ struct DecParams {
   float* part_LSE;    // [n_parts][group]
   const ca_task* tasks;
   const DecItem* items;
+  const int32_t* pages;   // as in FwdParams
+  int32_t page_shift;
   int32_t n_items;
   int32_t hq, hkv, group;
   float scale_log2;

@@ -57,8 +57,32 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // (hardware range check), which zero-fills ragged tiles without branches.
+// Only the per-lane offset is relied on for that check: a tile is addressed
+// by moving the base, and the scalar offset of the loads stays 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Resource over n rows (n <= 0: none) that start at row0_ptr and lie
+// row_bytes apart; loads of rows >= n return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* row0_ptr, int n, uint32_t row_bytes) {
+  return make_rsrc(row0_ptr, n > 0 ? (uint32_t)n * row_bytes : 0u);
+}
+
+// Physical K/V row of virtual row v.  Paged: pages of 2^shift rows, virtual
+// page v >> shift stored at physical page pages[v >> shift] (a block table:
+// "DCP: Addressing Input Dynamism In Long-Context Training via Dynamic
+// Context Parallelism", Executor Design, the Blockwise Attention
+// instruction).  Callers only translate the first row of a tile that lies
+// inside one page.
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_phys_row(const int32_t* pages, int shift, int64_t v) {
+  if constexpr (!PAGED) {
+    return v;
+  } else {
+    const int64_t page = pages[v >> shift];
+    return (page << shift) | (v & ((int64_t(1) << shift) - 1));
+  }
 }
 
 __device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

@@ -118,3 +118,32 @@ def test_masked_visible_pairs_match_the_oracle():
             t[:, 5] += rng.integers(0, 50, size=len(t))
         assert ca.visible_pairs(t) == oracle.visible_pairs(t)
     assert ca.visible_pairs(I.varlen_tasks([5, 7])) == oracle.visible_pairs(I.varlen_tasks([5, 7]))
+
+
+def call_paged(shape, tasks, table, page_rows, reserved=0, ws_bytes=1 << 20):
+    ta = ca.task_array(tasks)
+    pg = ca.kv_pages(table, page_rows)
+    pg.reserved = reserved
+    return ca.lib().ca_forward_paged(ctypes.byref(shape), ta.ctypes.data_as(ctypes.c_void_p), None, len(ta),
+                                     ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_paged_forward_rejects_bad_page_tables():
+    s = ca.make_shape(8, 2, 128, 300, 4 * 256, 300)        # 4 physical pages of 256 rows
+    good = [(0, 256, 0, 300, 300, 0, 0)]                    # virtual rows [256, 556)
+    table = [3, 1, 0]                                       # 3 virtual pages
+    for bad_rows in (0, 64, 192, 3 << 20):
+        assert call_paged(ca.make_shape(8, 2, 128, 300, 4 * 1024, 300), good, table, bad_rows) == \
+            ca.CA_ERR_INVALID, bad_rows
+    assert call_paged(s, good, [3, 4, 0], 256) == ca.CA_ERR_INVALID            # physical page 4 of 4
+    assert call_paged(s, good, [3, -1, 0], 256) == ca.CA_ERR_INVALID
+    assert call_paged(s, good, table, 256, reserved=1) == ca.CA_ERR_INVALID
+    assert call_paged(s, [(0, 256, 0, 300, 600, 0, 0)], table, 256) == ca.CA_ERR_INVALID   # past 768 rows
+    assert call_paged(s, [(0, 64, 0, 300, 300, 0, 0)], table, 256) == ca.CA_ERR_INVALID    # kv_off % 128
+    assert "multiple of 128" in ca.lib().ca_last_error().decode()
+    need = ca.forward_workspace(s, good, pages=ca.kv_pages(table, 256))
+    assert need > ca.forward_workspace(s, [(0, 0, 0, 300, 300, 0, 0)])          # the table travels too
+    assert call_paged(s, good, table, 256, ws_bytes=need - 1) == ca.CA_ERR_WORKSPACE
+    assert ca.forward_workspace(s, good, pages=ca.kv_pages([3, 9, 0], 256)) == 0
+    # a context that is empty needs no alignment; nothing to do: OK
+    assert call_paged(s, [(0, 5, 0, 0, 0, 0, 0)], table, 256) == ca.CA_OK

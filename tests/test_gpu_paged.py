@@ -1,0 +1,242 @@
+"""GPU parity of paged K/V (ca_forward_paged: block tables as in the
+Blockwise Attention instruction of "DCP: Addressing Input Dynamism In
+Long-Context Training via Dynamic Context Parallelism", Executor Design)
+against the fp64 oracle, and bit-for-bit against the unpaged forward over the
+virtual K/V; plus the guarantee that no kernel reads K/V rows outside a
+task's context (rows there hold NaN)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_core_amd import ca
+from long_context_core_amd import inputs as I
+from tests.gpu_util import GRAD_REL_FRO, announce, check_forward, rel_fro, torch_cuda, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def run_paged(tasks, masks, hq, hkv, d, q_rows, n_vp, P, seed, extra_pages=7):
+    """Paged and unpaged forward of the same virtual K/V; returns both GPU
+    results and the oracle's."""
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((q_rows, hq, d), seed)
+    Kv = I.randn_bf16((n_vp * P, hkv, d), seed + 1)
+    Vv = I.randn_bf16((n_vp * P, hkv, d), seed + 2)
+    n_phys = n_vp + extra_pages
+    table = I.page_table(n_vp, n_phys, seed + 3)
+    Ks = I.page_store(Kv, table, P, n_phys).to(dev)
+    Vs = I.page_store(Vv, table, P, n_phys).to(dev)
+    Qd = Q.to(dev)
+    outs = []
+    for paged in (True, False):
+        O = torch.full((q_rows, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        LSE = torch.full((q_rows, hq), float("nan"), device=dev)
+        if paged:
+            shape = ca.make_shape(hq, hkv, d, q_rows, n_phys * P, q_rows)
+            ca.forward(shape, tasks, Qd, Ks, Vs, O, LSE, masks=masks, pages=ca.kv_pages(table, P))
+        else:
+            shape = ca.make_shape(hq, hkv, d, q_rows, n_vp * P, q_rows)
+            ca.forward(shape, tasks, Qd, Kv.to(dev), Vv.to(dev), O, LSE, masks=masks)
+        outs.append((O, LSE))
+    torch.cuda.synchronize()
+    t9 = tasks if masks is None else np.concatenate([tasks, np.asarray(masks)], axis=1)
+    Ks_np = widen(Ks)
+    Vs_np = widen(Vs)
+    O_ref, L_ref = oracle.forward_paged(t9, widen(Q), Ks_np, Vs_np, table, P, 1 / math.sqrt(d), o_rows=q_rows)
+    return outs, O_ref, L_ref
+
+
+def check_paged(outs, O_ref, L_ref, label):
+    torch = torch_cuda()
+    (Op, Lp), (Ou, Lu) = outs
+    check_forward(Op, Lp, O_ref, L_ref, label)
+    rows = torch.from_numpy(np.flatnonzero(~np.isnan(L_ref).any(1)))
+    # identical work items and arithmetic: identical bits
+    assert torch.equal(Op.cpu()[rows].view(torch.int16), Ou.cpu()[rows].view(torch.int16)), label
+    assert torch.equal(Lp.cpu()[rows], Lu.cpu()[rows]), label
+
+
+@pytest.mark.parametrize("P", [128, 256, 1024])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (4, 4, 64), (16, 1, 128)])
+def test_paged_varlen(P, hq, hkv, d):
+    announce("paged forward varlen P%d hq%d hkv%d d%d" % (P, hq, hkv, d))
+    docs = [1, 127, 129, 300, 64, 1000, 65, 700]
+    tasks, n_vp = I.paged_varlen_tasks(docs, P)
+    outs, Or, Lr = run_paged(tasks, None, hq, hkv, d, sum(docs), n_vp, P, 1500 + P + d)
+    check_paged(outs, Or, Lr, "paged varlen P%d" % P)
+
+
+def test_paged_ca_task_shards_and_shared_prefix():
+    """Query shards of long documents (CA-tasks) over paged contexts, two
+    documents sharing their first pages (a common prefix)."""
+    announce("paged CA-task shards with a shared prefix")
+    P = 256
+    hq, hkv, d = 8, 2, 128
+    # virtual pages: doc A = pages 0..11, doc B = pages 12..21; B's first 4
+    # pages are A's first 4 in the table below
+    tasks = np.array([
+        [0, 0, 0, 300, 2500, 2200, 0],          # A: queries 2200..2499 over A[0, 2500)
+        [300, 0, 300, 100, 3000, 2900, 0],      # A: queries 2900..2999 over A[0, 3000)
+        [400, 12 * P, 400, 257, 2001, 1744, 0],  # B: queries 1744..2000 over B[0, 2001)
+        [657, 12 * P, 657, 64, 64, 0, 0],       # B: its first 64 tokens
+    ], dtype=np.int64)
+    q_rows, n_vp = 721, 22
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((q_rows, hq, d), 1601)
+    Kv = I.randn_bf16((n_vp * P, hkv, d), 1602)
+    Vv = I.randn_bf16((n_vp * P, hkv, d), 1603)
+    table = I.page_table(n_vp, n_vp + 3, 1604)
+    table[12:16] = table[0:4]                   # shared prefix pages
+    Kv[12 * P:16 * P] = Kv[0:4 * P]             # the virtual view of B repeats them
+    Vv[12 * P:16 * P] = Vv[0:4 * P]
+    used = np.unique(table)
+    n_phys = n_vp + 3
+    Ks = torch.full((n_phys * P, hkv, d), float("nan"), dtype=torch.bfloat16)
+    Vs = torch.full((n_phys * P, hkv, d), float("nan"), dtype=torch.bfloat16)
+    for v, pp in enumerate(table.tolist()):
+        Ks[pp * P:(pp + 1) * P] = Kv[v * P:(v + 1) * P]
+        Vs[pp * P:(pp + 1) * P] = Vv[v * P:(v + 1) * P]
+    assert len(used) == n_vp - 4
+    O = torch.full((q_rows, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((q_rows, hq), float("nan"), device=dev)
+    shape = ca.make_shape(hq, hkv, d, q_rows, n_phys * P, q_rows)
+    ca.forward(shape, tasks, Q.to(dev), Ks.to(dev), Vs.to(dev), O, LSE, pages=ca.kv_pages(table, P))
+    torch.cuda.synchronize()
+    Or, Lr = oracle.forward(tasks, widen(Q), widen(Kv), widen(Vv), 1 / math.sqrt(d), o_rows=q_rows)
+    check_forward(O, LSE, Or, Lr, "paged CA-tasks shared prefix")
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 1), (8, 2)])
+def test_paged_decode(hq, hkv):
+    """Single-token queries over paged caches (the split-KV decode kernel),
+    caches of ragged length, split into several key chunks."""
+    announce("paged decode hq%d hkv%d" % (hq, hkv))
+    P, d = 256, 128
+    ctx = [5000, 131, 2048, 777, 9000, 1]
+    t = []
+    vp = 0
+    for b, c in enumerate(ctx):
+        t.append((b, vp * P, b, 1, c, c - 1, 0))
+        vp += -(-c // P)
+    tasks = np.array(t, dtype=np.int64)
+    outs, Or, Lr = run_paged(tasks, None, hq, hkv, d, len(ctx), vp, P, 1700 + hq)
+    check_paged(outs, Or, Lr, "paged decode")
+
+
+def test_paged_lambda_mask():
+    announce("paged forward with sink + sliding-window masks")
+    P = 128
+    docs = [3000, 130, 1500]
+    tasks, n_vp = I.paged_varlen_tasks(docs, P)
+    masks = np.array([[512, 64], [0, 0], [100, 3]], dtype=np.int64)
+    outs, Or, Lr = run_paged(tasks, masks, 8, 2, 128, sum(docs), n_vp, P, 1800)
+    check_paged(outs, Or, Lr, "paged lambda")
+
+
+# ---------------------------------------------------------------------------
+# No kernel reads K/V rows outside a task's context
+# ---------------------------------------------------------------------------
+
+def gapped_layout(ctx_lens, gap):
+    """Contexts placed back to back with `gap` rows between them (and after
+    the last one): (kv_off of each context, total rows)."""
+    offs, r = [], 0
+    for c in ctx_lens:
+        offs.append(r)
+        r += c + gap
+    return offs, r
+
+
+def poisoned_kv(ctx_lens, offs, rows, hkv, d, seed):
+    """K, V with N(0,1) rows inside the contexts and NaN everywhere else."""
+    torch = torch_cuda()
+    K = torch.full((rows, hkv, d), float("nan"), dtype=torch.bfloat16)
+    V = torch.full((rows, hkv, d), float("nan"), dtype=torch.bfloat16)
+    Kc = I.randn_bf16((rows, hkv, d), seed)
+    Vc = I.randn_bf16((rows, hkv, d), seed + 1)
+    for o, c in zip(offs, ctx_lens):
+        K[o:o + c] = Kc[o:o + c]
+        V[o:o + c] = Vc[o:o + c]
+    return K, V
+
+
+def test_forward_reads_nothing_past_the_context():
+    announce("forward with NaN rows around every context")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    hq, hkv, d = 8, 2, 128
+    ctx = [1, 63, 65, 100, 127, 129, 1000]
+    offs, rows = gapped_layout(ctx, 77)
+    tasks = np.array([(sum(ctx[:i]), offs[i], sum(ctx[:i]), c, c, 0, 0) for i, c in enumerate(ctx)],
+                     dtype=np.int64)
+    q_rows = sum(ctx)
+    Q = I.randn_bf16((q_rows, hq, d), 1900)
+    K, V = poisoned_kv(ctx, offs, rows, hkv, d, 1901)
+    O = torch.full((q_rows, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((q_rows, hq), float("nan"), device=dev)
+    ca.forward(ca.make_shape(hq, hkv, d, q_rows, rows, q_rows), tasks, Q.to(dev), K.to(dev), V.to(dev), O, LSE)
+    torch.cuda.synchronize()
+    Kz, Vz = torch.nan_to_num(K.float()), torch.nan_to_num(V.float())
+    Or, Lr = oracle.forward(tasks, widen(Q), widen(Kz), widen(Vz), 1 / math.sqrt(d))
+    check_forward(O, LSE, Or, Lr, "forward NaN-fenced contexts")
+
+
+def test_decode_reads_nothing_past_the_context():
+    announce("decode with NaN rows around every cache")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    hq, hkv, d = 16, 1, 128
+    ctx = [5000, 1, 129, 4097, 700]
+    offs, rows = gapped_layout(ctx, 200)
+    tasks = np.array([(b, offs[b], b, 1, c, c - 1, 0) for b, c in enumerate(ctx)], dtype=np.int64)
+    Q = I.randn_bf16((len(ctx), hq, d), 1910)
+    K, V = poisoned_kv(ctx, offs, rows, hkv, d, 1911)
+    O = torch.full((len(ctx), hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((len(ctx), hq), float("nan"), device=dev)
+    ca.forward(ca.make_shape(hq, hkv, d, len(ctx), rows, len(ctx)), tasks, Q.to(dev), K.to(dev), V.to(dev),
+               O, LSE)
+    torch.cuda.synchronize()
+    Kz, Vz = torch.nan_to_num(K.float()), torch.nan_to_num(V.float())
+    Or, Lr = oracle.forward(tasks, widen(Q), widen(Kz), widen(Vz), 1 / math.sqrt(d))
+    check_forward(O, LSE, Or, Lr, "decode NaN-fenced caches")
+
+
+def test_backward_reads_nothing_past_the_context():
+    announce("backward with NaN rows around every context")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    hq, hkv, d = 8, 2, 128
+    ctx = [1, 65, 127, 300, 129]
+    offs, rows = gapped_layout(ctx, 90)
+    tasks = np.array([(sum(ctx[:i]), offs[i], sum(ctx[:i]), c, c, 0, 0) for i, c in enumerate(ctx)],
+                     dtype=np.int64)
+    q_rows = sum(ctx)
+    Q = I.randn_bf16((q_rows, hq, d), 1920)
+    dO = I.randn_bf16((q_rows, hq, d), 1921)
+    K, V = poisoned_kv(ctx, offs, rows, hkv, d, 1922)
+    shape = ca.make_shape(hq, hkv, d, q_rows, rows, q_rows)
+    Qd, Kd, Vd, dOd = Q.to(dev), K.to(dev), V.to(dev), dO.to(dev)
+    O = torch.empty((q_rows, hq, d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((q_rows, hq), device=dev)
+    ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE)
+    dQ = torch.full_like(Qd, float("nan"))
+    dK = torch.full_like(Kd, float("nan"))
+    dV = torch.full_like(Vd, float("nan"))
+    ca.backward(shape, tasks, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV)
+    torch.cuda.synchronize()
+    Kz, Vz = torch.nan_to_num(K.float()), torch.nan_to_num(V.float())
+    ref = oracle.backward(tasks, widen(Q), widen(Kz), widen(Vz), widen(dO), 1 / math.sqrt(d))
+    inside = np.zeros(rows, dtype=bool)
+    for o, c in zip(offs, ctx):
+        inside[o:o + c] = True
+    for name, g, r, sel in (("dQ", dQ, ref[0], slice(None)), ("dK", dK, ref[1], inside), ("dV", dV, ref[2], inside)):
+        gw = widen(g)[sel]
+        assert np.isfinite(gw).all(), name
+        e = rel_fro(gw, r[sel])
+        print("NaN-fenced backward %s relF=%.3e" % (name, e), flush=True)
+        assert e <= GRAD_REL_FRO, name
