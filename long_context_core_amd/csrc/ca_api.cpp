@@ -437,6 +437,7 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
     fp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
     fp.items = (const ca::FwdItem*)(w + p.off_items);
     fp.pages = pages;
+    fp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
     fp.page_shift = page_shift;
     fp.n_items = (int32_t)items.size();
     fp.hq = s->hq;
@@ -461,6 +462,7 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
     dp.tasks = (const ca_task*)(w + p.off_tasks);
     dp.items = (const ca::DecItem*)(w + p.off_dec);
     dp.pages = pages;
+    dp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
     dp.page_shift = page_shift;
     dp.n_items = (int32_t)ditems.size();
     dp.hq = s->hq;

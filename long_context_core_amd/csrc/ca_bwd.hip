@@ -171,16 +171,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   uint4 qreg[PASSES], oreg[PASSES];
   float lse_reg = 0.f, d_reg = 0.f;
   auto gload = [&]() {
-    const int nvalid = max(0, min(BQ, nx_left));
-    const __amdgpu_buffer_rsrc_t qr = rows_rsrc(nq + nx_g * D, nvalid, row_bytes);
-    const __amdgpu_buffer_rsrc_t orr = rows_rsrc(no + nx_g * D, nvalid, row_bytes);
+    // nx_left >= 1 here: the last row tile starts below r_end <= q_len
+    const uint32_t nvalid = (uint32_t)min(BQ, nx_left);
+    const uint32_t qbytes = nvalid * row_bytes;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(nq + nx_g * D, qbytes);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(no + nx_g * D, qbytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       qreg[r] = buffer_load_16(qr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
       oreg[r] = buffer_load_16(orr, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
-    const __amdgpu_buffer_rsrc_t lr = rows_rsrc(nl + nx_g, nvalid, (uint32_t)p.hq * 4);
-    const __amdgpu_buffer_rsrc_t dr = rows_rsrc(nd + nx_g, nvalid, (uint32_t)p.hq * 4);
+    const uint32_t lbytes = nvalid * (uint32_t)p.hq * 4;
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(nl + nx_g, lbytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(nd + nx_g, lbytes);
     if (tid < BQ) {
       lse_reg = buffer_load_f32(lr, lse_voff, 0);
       d_reg = buffer_load_f32(dr, lse_voff, 0);

@@ -83,8 +83,24 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
   // nothing past the chunk is read.  Paged K/V: chunks start at multiples of
   // 128 keys, tasks at multiples of 128 virtual rows, and pages hold a
   // multiple of 128 rows, so each tile lies inside one page.
-  auto gload = [&](int tile) {
-    const int64_t r0 = kv_phys_row<PAGED>(p.pages, p.page_shift, row0 + (int64_t)tile * TK);
+  // Paged K/V: a tile's physical page is read one tile ahead (vector load,
+  // in order with the tile loads) and moved to a scalar register where used.
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(p.pages, p.page_bytes);
+  auto tile_page = [&](int tile) -> int {
+    if constexpr (PAGED) {
+      const int64_t v = row0 + (int64_t)tile * TK;
+      return __builtin_amdgcn_raw_buffer_load_b32(prs, (uint32_t)(v >> p.page_shift) * 4u, 0, 0);
+    } else {
+      return 0;
+    }
+  };
+  auto gload = [&](int tile, int page) {
+    const int64_t v = row0 + (int64_t)tile * TK;
+    int64_t r0 = v;
+    if constexpr (PAGED) {
+      const int64_t pg = __builtin_amdgcn_readfirstlane(page);
+      r0 = (pg << p.page_shift) | (v & ((int64_t(1) << p.page_shift) - 1));
+    }
     const int n = min(TK, nkeys - tile * TK);
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
     const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
@@ -102,7 +118,9 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
   float m2 = -INFINITY, lsum = 0.f;
 
   const int n_tiles = (nkeys + TK - 1) / TK;
-  if (n_tiles > 0) gload(0);
+  int next_page = 0;
+  if (n_tiles > 0) gload(0, tile_page(0));
+  if (n_tiles > 1) next_page = tile_page(1);
   for (int tile = 0; tile < n_tiles; ++tile) {
     uint4 kc[2][NT];
 #pragma unroll
@@ -112,7 +130,10 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
     // stage this wave's 32 V rows (wave-private LDS region)
 #pragma unroll
     for (int r = 0; r < VPASS; ++r) *(uint4*)(vw + v_st + r * VROWS * VS) = vr[r];
-    if (tile + 1 < n_tiles) gload(tile + 1);
+    if (tile + 1 < n_tiles) {
+      gload(tile + 1, next_page);
+      if (tile + 2 < n_tiles) next_page = tile_page(tile + 2);
+    }
 
     f32x4 s_acc[2];
 #pragma unroll

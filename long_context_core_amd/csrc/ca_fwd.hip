@@ -22,6 +22,14 @@
 // workgroup are never visited; only tiles that straddle the diagonal or the
 // end of the context apply the per-element mask.
 //
+// Paged K/V (PAGED): K and V are stores of pages of 2^page_shift rows and a
+// task's context rows are virtual; virtual row v lives in physical page
+// pages[v >> page_shift] at the same row within the page (block tables:
+// "DCP: Addressing Input Dynamism In Long-Context Training via Dynamic
+// Context Parallelism", Executor Design, the Blockwise Attention
+// instruction).  Pages hold a multiple of 128 rows and contexts start on a
+// 128-row boundary, so every 64-key tile lies inside one page.
+//
 // Outputs: O (bf16, or fp32 partials) and LSE = ln sum exp(scale q.k), the
 // statistic that makes partials mergeable by Equation 4 ("Context Parallelism
 // for Scalable Million-Token Inference", Section 3.4 Merge Attention).
@@ -139,8 +147,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // K/V: a tile starts at a multiple of 64 virtual rows and pages hold a
   // multiple of 128 rows, so each tile lies inside one page.
   uint4 kreg[PASSES], vreg[PASSES];
-  auto gload = [&](int tile) {
-    const int64_t r0 = kv_phys_row<PAGED>(p.pages, p.page_shift, t.kv_off + (int64_t)tile * BN);
+  // Paged K/V: the physical page of a tile is read one tile ahead of its
+  // loads, through a vector load (waited on in order with the tile loads; a
+  // load that had to complete at once would stall on the tile in flight),
+  // and moved to a scalar register only where the loads need it.
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(p.pages, p.page_bytes);
+  auto tile_page = [&](int tile) -> int {
+    if constexpr (PAGED) {
+      const int64_t v = t.kv_off + (int64_t)tile * BN;
+      return __builtin_amdgcn_raw_buffer_load_b32(prs, (uint32_t)(v >> p.page_shift) * 4u, 0, 0);
+    } else {
+      return 0;
+    }
+  };
+  auto tile_row = [&](int tile, int page) -> int64_t {
+    const int64_t v = t.kv_off + (int64_t)tile * BN;
+    if constexpr (PAGED) {
+      const int64_t pg = __builtin_amdgcn_readfirstlane(page);
+      return (pg << p.page_shift) | (v & ((int64_t(1) << p.page_shift) - 1));
+    } else {
+      return v;
+    }
+  };
+  auto gload = [&](int tile, int64_t r0) {
     const int n = min(BN, kv_hi - tile * BN);
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
     const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
@@ -265,13 +294,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     }
   };
 
-  if (n_visit > 0) gload(tile_of(0));
+  int next_page = 0;
+  if (n_visit > 0) gload(tile_of(0), tile_row(tile_of(0), tile_page(tile_of(0))));
+  if (n_visit > 1) next_page = tile_page(tile_of(1));
   for (int k = 0; k < n_visit; ++k) {
     const int buf = k & 1;
     const int tile = tile_of(k);
     swrite(buf);
     __syncthreads();
-    if (k + 1 < n_visit) gload(tile_of(k + 1));
+    if (k + 1 < n_visit) {
+      gload(tile_of(k + 1), tile_row(tile_of(k + 1), next_page));
+      if (k + 2 < n_visit) next_page = tile_page(tile_of(k + 2));
+    }
     if (wave_sees(tile)) do_tile(tile, buf);
   }
 

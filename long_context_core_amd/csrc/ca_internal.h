@@ -49,6 +49,7 @@ struct FwdParams {
   const ca_task_mask* masks;   // per task, or nullptr: causal only
   const FwdItem* items;
   const int32_t* pages;   // K/V block table (virtual page -> physical page), or nullptr: rows are physical
+  uint32_t page_bytes;    // bytes of the table
   int32_t page_shift;     // log2 of the rows per page
   int32_t n_items;
   int32_t hq, hkv, group, hpw;
@@ -68,6 +69,7 @@ struct DecParams {
   const ca_task* tasks;
   const DecItem* items;
   const int32_t* pages;   // as in FwdParams
+  uint32_t page_bytes;
   int32_t page_shift;
   int32_t n_items;
   int32_t hq, hkv, group;

@@ -69,22 +69,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* row0_ptr
   return make_rsrc(row0_ptr, n > 0 ? (uint32_t)n * row_bytes : 0u);
 }
 
-// Physical K/V row of virtual row v.  Paged: pages of 2^shift rows, virtual
-// page v >> shift stored at physical page pages[v >> shift] (a block table:
-// "DCP: Addressing Input Dynamism In Long-Context Training via Dynamic
-// Context Parallelism", Executor Design, the Blockwise Attention
-// instruction).  Callers only translate the first row of a tile that lies
-// inside one page.
-template <bool PAGED>
-__device__ __forceinline__ int64_t kv_phys_row(const int32_t* pages, int shift, int64_t v) {
-  if constexpr (!PAGED) {
-    return v;
-  } else {
-    const int64_t page = pages[v >> shift];
-    return (page << shift) | (v & ((int64_t(1) << shift) - 1));
-  }
-}
-
 __device__ __forceinline__ uint4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
