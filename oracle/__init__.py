@@ -30,7 +30,7 @@ from .attention import (  # noqa: F401
     merge,
     backward,
 )
-from .paging import virtual_rows, forward_paged  # noqa: F401
+from .paging import virtual_rows, forward_paged, backward_paged  # noqa: F401
 from .counting import (  # noqa: F401
     visible_pairs_task,
     visible_pairs_masked,

@@ -37,3 +37,22 @@ def forward_paged(tasks, Q, K_pages, V_pages, table, page_rows, scale, o_rows=No
     K = virtual_rows(K_pages, table, page_rows)
     V = virtual_rows(V_pages, table, page_rows)
     return forward(tasks, Q, K, V, scale, o_rows=o_rows)
+
+
+def backward_paged(tasks, Q, K_pages, V_pages, dO, table, page_rows, scale):
+    """Gradients of L = sum(O * dO) for the paged forward: dQ, and dK, dV as
+    page stores shaped like K_pages / V_pages.  The gradient of virtual row v
+    is added to its physical row, so a page that several virtual pages name
+    collects all their contributions; rows of pages no entry names are 0."""
+    from .attention import backward
+    P = int(page_rows)
+    table = np.asarray(table, dtype=np.int64).reshape(-1)
+    K = virtual_rows(K_pages, table, P)
+    V = virtual_rows(V_pages, table, P)
+    dQ, dKv, dVv = backward(tasks, Q, K, V, dO, scale)
+    rows = (table[:, None] * P + np.arange(P)[None, :]).reshape(-1)
+    dK = np.zeros(K_pages.shape)
+    dV = np.zeros(V_pages.shape)
+    np.add.at(dK, rows, dKv)
+    np.add.at(dV, rows, dVv)
+    return dQ, dK, dV

@@ -83,3 +83,37 @@ def test_planted_page_formula_mistake_is_caught():
     wrong = np.stack([store[table[v % n_vp] * P + v // n_vp] for v in range(n_vp * P)])
     assert not np.array_equal(wrong, Xv)
     assert np.array_equal(oracle.virtual_rows(store, table, P), Xv)
+
+
+def test_paged_backward_matches_finite_differences_on_a_shared_page():
+    """Central differences of L = sum(O * dO) with respect to entries of the
+    physical stores; physical page 0 is read by both tasks, so its gradient
+    sums two contributions (a dropped contribution fails this)."""
+    P = 2
+    rng = np.random.default_rng(97)
+    hq, hkv, d = 2, 1, 3
+    table = np.array([0, 1, 0, 2])
+    tasks = np.array([[0, 0, 0, 4, 4, 0, 0],          # A: virtual rows 0..3 = pages 0, 1
+                      [4, 4, 4, 3, 4, 1, 0]], dtype=np.int64)   # B: queries 1..3 over pages 0, 2
+    Q = rng.standard_normal((7, hq, d))
+    dO = rng.standard_normal((7, hq, d))
+    Kp = rng.standard_normal((3 * P, hkv, d))
+    Vp = rng.standard_normal((3 * P, hkv, d))
+    dQ, dK, dV = oracle.backward_paged(tasks, Q, Kp, Vp, dO, table, P, 0.7)
+
+    def loss(K, V, Qx=Q):
+        O, _ = oracle.forward_paged(tasks, Qx, K, V, table, P, 0.7)
+        return float(np.sum(O * dO))
+
+    h = 1e-6
+    for (r, c) in [(0, 1), (1, 2), (3, 0), (5, 1)]:       # page 0 (shared), page 1, page 2
+        for X, G in ((Kp, dK), (Vp, dV)):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[r, 0, c] += h
+            Xm[r, 0, c] -= h
+            fd = (loss(Xp, Vp) - loss(Xm, Vp)) / (2 * h) if X is Kp else (loss(Kp, Xp) - loss(Kp, Xm)) / (2 * h)
+            assert abs(fd - G[r, 0, c]) < 1e-7 * max(1.0, abs(fd)), (r, c)
+    Qp, Qm = Q.copy(), Q.copy()
+    Qp[5, 1, 2] += h
+    Qm[5, 1, 2] -= h
+    assert abs((loss(Kp, Vp, Qp) - loss(Kp, Vp, Qm)) / (2 * h) - dQ[5, 1, 2]) < 1e-7
