@@ -230,6 +230,19 @@ ca_status ca_backward_masked(const ca_shape* shape, const ca_task* tasks_host, c
                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ca_backward_masked over paged K/V (see ca_kv_pages; pages must not be
+ * NULL).  dK and dV are page stores laid out like K and V: the gradient of
+ * virtual row v lands in its physical row.  Rows of pages no task reads are
+ * zero.  Tasks may share physical pages (their contributions are summed);
+ * one task must not read the same physical page twice (CA_ERR_INVALID).
+ * Errors otherwise as ca_backward_masked and ca_forward_paged. */
+size_t ca_backward_paged_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                   int32_t n_tasks, const ca_kv_pages* pages);
+ca_status ca_backward_paged(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                            int32_t n_tasks, const ca_kv_pages* pages, const void* Q, const void* K,
+                            const void* V, const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
+                            void* dV, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* CA-task scheduling (host only; no device memory, no HIP calls)          */
 /* ---------------------------------------------------------------------- */

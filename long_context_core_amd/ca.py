@@ -38,6 +38,8 @@ EXPORTS = (
     "ca_forward_paged",
     "ca_backward_masked_workspace",
     "ca_backward_masked",
+    "ca_backward_paged_workspace",
+    "ca_backward_paged",
     "ca_cost_time",
     "ca_schedule_max_items",
     "ca_schedule",
@@ -133,6 +135,10 @@ def lib():
         L.ca_forward_paged_workspace.restype = sz
         L.ca_forward_paged.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ca_forward_paged.restype = ctypes.c_int
+        L.ca_backward_paged_workspace.argtypes = [sp, vp, vp, i32, vp]
+        L.ca_backward_paged_workspace.restype = sz
+        L.ca_backward_paged.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.ca_backward_paged.restype = ctypes.c_int
         L.ca_backward_masked_workspace.argtypes = [sp, vp, vp, i32]
         L.ca_backward_masked_workspace.restype = sz
         L.ca_backward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -297,17 +303,26 @@ def merge(shape, O_parts, LSE_parts, O, LSE, stream=None):
     return O, LSE
 
 
-def backward_workspace(shape, tasks, masks=None):
+def backward_workspace(shape, tasks, masks=None, pages=None):
     ta, ma = split_tasks(tasks, masks)
+    if pages is not None:
+        return int(lib().ca_backward_paged_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
+                                                     ctypes.byref(pages)))
     return int(lib().ca_backward_masked_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta)))
 
 
-def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None, masks=None):
-    """ca_backward (ca_backward_masked with masks or a 9-column table)."""
+def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None, masks=None, pages=None):
+    """ca_backward (ca_backward_masked with masks or a 9-column table,
+    ca_backward_paged with pages: K, V, dK, dV are then page stores)."""
     ta, ma = split_tasks(tasks, masks)
     if ws is None:
-        ws = workspace_tensor(backward_workspace(shape, ta, ma), Q.device)
-    if ma is None:
+        ws = workspace_tensor(backward_workspace(shape, ta, ma, pages), Q.device)
+    if pages is not None:
+        st = lib().ca_backward_paged(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
+                                     ctypes.byref(pages), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
+                                     _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws), ws.numel(),
+                                     _stream_ptr(stream))
+    elif ma is None:
         st = lib().ca_backward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
                                _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
                                ws.numel(), _stream_ptr(stream))

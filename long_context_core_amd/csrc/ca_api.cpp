@@ -532,17 +532,51 @@ int partition_passes(const std::vector<std::pair<int64_t, int64_t>>& iv, std::ve
   return std::max<int>(1, (int)pass_end.size());
 }
 
+// Physical pages read by task i of a paged table (in virtual order).
+std::vector<int32_t> task_pages(const ca_task& k, const ca_kv_pages* pg) {
+  std::vector<int32_t> out;
+  if (k.kv_len <= 0) return out;
+  const int64_t first = k.kv_off / pg->page_rows, last = (k.kv_off + k.kv_len - 1) / pg->page_rows;
+  for (int64_t v = first; v <= last; ++v) out.push_back(pg->table_host[v]);
+  return out;
+}
+
+// Paged K/V: dK/dV rows are physical, so tasks conflict when they share a
+// physical page.  Greedy: each task (in table order) takes the first pass
+// none of whose tasks uses any of its pages.  Returns the number of passes.
+int partition_page_passes(const ca_task* t, int32_t n, const ca_kv_pages* pg, int64_t n_phys,
+                          std::vector<int>& pass_of) {
+  pass_of.assign((size_t)n, 0);
+  std::vector<std::vector<uint8_t>> used;
+  for (int32_t i = 0; i < n; ++i) {
+    if (t[i].q_len <= 0 || t[i].kv_len <= 0) continue;
+    const std::vector<int32_t> pages = task_pages(t[i], pg);
+    size_t q = 0;
+    for (; q < used.size(); ++q) {
+      bool free = true;
+      for (int32_t pp : pages)
+        if (used[q][(size_t)pp]) { free = false; break; }
+      if (free) break;
+    }
+    if (q == used.size()) used.emplace_back((size_t)n_phys, 0);
+    for (int32_t pp : pages) used[q][(size_t)pp] = 1;
+    pass_of[(size_t)i] = (int)q;
+  }
+  return std::max<int>(1, (int)used.size());
+}
+
 struct BwdPlan {
   int group = 1, hpw = 1, rt = 128;
   int q_passes = 1, kv_passes = 1;
   std::vector<int> q_pass_of, kv_pass_of;
   bool q_full = false, kv_full = false;          // every row covered by some task
   size_t n_qitems = 0, n_kvitems = 0;
-  size_t off_tasks = 0, off_masks = 0, off_qitems = 0, off_kvitems = 0, off_d = 0, off_dq = 0, off_dk = 0,
-         off_dv = 0, bytes = 0;
+  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_qitems = 0, off_kvitems = 0, off_d = 0, off_dq = 0,
+         off_dk = 0, off_dv = 0, bytes = 0;
 };
 
-BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n) {
+BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                      const ca_kv_pages* pg = nullptr) {
   BwdPlan p;
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, 4);
@@ -561,12 +595,14 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
     }
   }
   p.q_passes = partition_passes(qiv, p.q_pass_of);
-  p.kv_passes = partition_passes(kviv, p.kv_pass_of);
+  p.kv_passes = pg ? partition_page_passes(t, n, pg, s->kv_rows / pg->page_rows, p.kv_pass_of)
+                   : partition_passes(kviv, p.kv_pass_of);
   p.q_full = p.q_passes == 1 && q_cover == s->q_rows;
-  p.kv_full = p.kv_passes == 1 && kv_cover == s->kv_rows;
+  p.kv_full = !pg && p.kv_passes == 1 && kv_cover == s->kv_rows;   // paged: unread page rows stay zero
   p.off_tasks = 0;
   p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
-  p.off_qitems = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
+  p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
+  p.off_qitems = p.off_pages + (pg ? align_up(sizeof(int32_t) * (size_t)pg->n_pages) : 0);
   p.off_kvitems = p.off_qitems + align_up(sizeof(ca::FwdItem) * p.n_qitems);
   p.off_d = p.off_kvitems + align_up(sizeof(ca::BwdItem) * p.n_kvitems);
   p.off_dq = p.off_d + align_up(sizeof(float) * (size_t)s->o_rows * s->hq);
@@ -647,18 +683,39 @@ bool varlen_to_tasks(const int32_t* cu, int32_t n_docs, std::vector<ca_task>& ou
   return true;
 }
 
-ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const void* Q,
-                        const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
-                        void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
-  ca_status st = check_shape(s);
+// Argument checks of the backward entry points and their workspace queries:
+// those of the forward, plus (paged) no task reading one physical page twice,
+// since its dK/dV rows would then be written by two work items of one pass.
+ca_status check_backward_args(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                              const ca_kv_pages* pg) {
+  ca_status st = check_forward_args(s, t, m, n, pg);
   if (st != CA_OK) return st;
   if (s->flags & CA_OUT_F32) return fail(CA_ERR_INVALID, "CA_OUT_F32 is a forward/merge flag");
-  st = check_tasks(s, t, n);
-  if (st != CA_OK) return st;
-  st = check_masks(m, n);
+  if (pg) {
+    std::vector<uint8_t> seen((size_t)(s->kv_rows / pg->page_rows), 0);
+    for (int32_t i = 0; i < n; ++i) {
+      const std::vector<int32_t> pages = task_pages(t[i], pg);
+      for (int32_t pp : pages) {
+        if (seen[(size_t)pp]) {
+          for (int32_t q : pages) seen[(size_t)q] = 0;
+          return fail(CA_ERR_INVALID, "task %d reads physical page %d twice (paged backward)", i, pp);
+        }
+        seen[(size_t)pp] = 1;
+      }
+      for (int32_t pp : pages) seen[(size_t)pp] = 0;
+    }
+  }
+  return CA_OK;
+}
+
+ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                        const ca_kv_pages* pg, const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                        void* stream) {
+  ca_status st = check_backward_args(s, t, m, n, pg);
   if (st != CA_OK) return st;
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return fail(CA_ERR_INVALID, "NULL tensor pointer");
-  const BwdPlan p = plan_backward(s, t, m, n);
+  const BwdPlan p = plan_backward(s, t, m, n, pg);
   if (!ws || ws_bytes < p.bytes)
     return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
   if (p.n_qitems > 0x7fffffffu || p.n_kvitems > 0x7fffffffu) return fail(CA_ERR_UNSUPPORTED, "too many work items");
@@ -672,6 +729,8 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
   std::vector<char> host(p.off_d, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
   if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+  if (pg && pg->n_pages > 0)
+    std::memcpy(host.data() + p.off_pages, pg->table_host, sizeof(int32_t) * (size_t)pg->n_pages);
   if (!qitems.empty()) std::memcpy(host.data() + p.off_qitems, qitems.data(), sizeof(ca::FwdItem) * qitems.size());
   if (!kvitems.empty()) std::memcpy(host.data() + p.off_kvitems, kvitems.data(), sizeof(ca::BwdItem) * kvitems.size());
   hipStream_t hs = (hipStream_t)stream;
@@ -712,6 +771,9 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
   bp.dVacc = (float*)(w + p.off_dv);
   bp.tasks = (const ca_task*)(w + p.off_tasks);
   bp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
+  bp.pages = pg ? (const int32_t*)(w + p.off_pages) : nullptr;
+  bp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
+  bp.page_shift = pg ? page_shift_of(pg) : 0;
   bp.hq = s->hq;
   bp.hkv = s->hkv;
   bp.group = p.group;
@@ -837,24 +899,35 @@ size_t ca_backward_workspace(const ca_shape* shape, const ca_task* tasks_host, i
 
 size_t ca_backward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
                                     int32_t n_tasks) {
-  if (check_shape(shape) != CA_OK || check_tasks(shape, tasks_host, n_tasks) != CA_OK ||
-      check_masks(masks_host, n_tasks) != CA_OK)
-    return 0;
+  if (check_backward_args(shape, tasks_host, masks_host, n_tasks, nullptr) != CA_OK) return 0;
   return plan_backward(shape, tasks_host, masks_host, n_tasks).bytes;
 }
 
 ca_status ca_backward(const ca_shape* s, const ca_task* t, int32_t n, const void* Q, const void* K,
                       const void* V, const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
                       void* dV, void* ws, size_t ws_bytes, void* stream) {
-  return backward_impl(s, t, nullptr, n, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
+  return backward_impl(s, t, nullptr, n, nullptr, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
 }
 
 ca_status ca_backward_masked(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const void* Q,
                              const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                              void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
-  return backward_impl(s, t, m, n, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
+  return backward_impl(s, t, m, n, nullptr, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
 }
 
+size_t ca_backward_paged_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                   int32_t n_tasks, const ca_kv_pages* pages) {
+  if (!pages || check_backward_args(shape, tasks_host, masks_host, n_tasks, pages) != CA_OK) return 0;
+  return plan_backward(shape, tasks_host, masks_host, n_tasks, pages).bytes;
+}
+
+ca_status ca_backward_paged(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                            const ca_kv_pages* pages, const void* Q, const void* K, const void* V, const void* O,
+                            const void* dO, const float* LSE, void* dQ, void* dK, void* dV, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!pages) return fail(CA_ERR_INVALID, "pages is NULL");
+  return backward_impl(s, t, m, n, pages, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, ws_bytes, stream);
+}
 
 int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks) {
   return ca_visible_pairs_masked(tasks_host, nullptr, n_tasks);

@@ -85,7 +85,7 @@ struct QTile<128> {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (task, KV head, 128 context rows).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   using Tile = QTile<D>;
   constexpr int BQ = 32;            // query rows per step
@@ -112,11 +112,21 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int my_key = kw0 + l32;
   const bool key_ok = my_key < t.kv_len;
 
+  // Physical row of the item's first key: the 128 keys of an item lie in
+  // one page of paged K/V (pages hold a multiple of 128 rows and contexts
+  // start on a 128-row boundary).
+  // kv_row0 + key is the physical row of task-relative key `key` of the item.
+  int64_t kv_row0 = t.kv_off;
+  if constexpr (PAGED) {
+    const int64_t v = t.kv_off + it.key0;
+    const int64_t page = p.pages[v >> p.page_shift];
+    kv_row0 = ((page << p.page_shift) | (v & ((int64_t(1) << p.page_shift) - 1))) - it.key0;
+  }
   // Stationary operands: K and V rows of this lane's key (B of S = Q K^T and of dP = dO V^T).
   const int64_t kv_stride = (int64_t)p.hkv * D;
   bf16x8 kf[NKS], vf[NKS];
   {
-    const int64_t roff = (t.kv_off + (key_ok ? my_key : 0)) * kv_stride + it.kv_head * D + 8 * hh;
+    const int64_t roff = (kv_row0 + (key_ok ? my_key : 0)) * kv_stride + it.kv_head * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       kf[s] = key_ok ? *(const bf16x8*)(p.K + roff + 16 * s) : bf16x8_zero();
@@ -443,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 
   // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
   if (!key_ok) return;
-  const int64_t base = (t.kv_off + my_key) * kv_stride + it.kv_head * D;
+  const int64_t base = (kv_row0 + my_key) * kv_stride + it.kv_head * D;
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
 #pragma unroll
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: work items as in the forward (hpw heads x 4/hpw blocks of 32 rows).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   constexpr int BN = 64;
   constexpr int KS = D + 16;      // K is read row-wise and by transpose reads
@@ -533,15 +543,31 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int n_tiles = (kv_hi + BN - 1) / BN;
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
-  const __bf16* kbase = p.K + t.kv_off * kv_stride + it.kv_head * D;
-  const __bf16* vbase = p.V + t.kv_off * kv_stride + it.kv_head * D;
+  const __bf16* kbase = p.K + it.kv_head * D;
+  const __bf16* vbase = p.V + it.kv_head * D;
   const int ld_row = tid / CH;
   const int ld_chunk = tid % CH;
   const uint32_t ld_voff = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16;
   uint4 kreg[PASSES], vreg[PASSES];
+  // Paged K/V: a tile's physical page is read one tile ahead (vector load,
+  // waited on in order with the tile loads) and moved to a scalar register
+  // where the loads need it; 64-key tiles lie inside one page.
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(p.pages, p.page_bytes);
+  auto tile_page = [&](int tile) -> int {
+    if constexpr (PAGED) {
+      const int64_t v = t.kv_off + (int64_t)tile * BN;
+      return __builtin_amdgcn_raw_buffer_load_b32(prs, (uint32_t)(v >> p.page_shift) * 4u, 0, 0);
+    } else {
+      return 0;
+    }
+  };
   // rows >= kv_hi read as zeros; nothing past the context is read
-  auto gload = [&](int tile) {
-    const int64_t r0 = (int64_t)tile * BN;
+  auto gload = [&](int tile, int page) {
+    int64_t r0 = t.kv_off + (int64_t)tile * BN;
+    if constexpr (PAGED) {
+      const int64_t pg = __builtin_amdgcn_readfirstlane(page);
+      r0 = (pg << p.page_shift) | (r0 & ((int64_t(1) << p.page_shift) - 1));
+    }
     const int n = min(BN, kv_hi - tile * BN);
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
     const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
@@ -748,13 +774,17 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     }
   };
 
+  int next_page = 0;
   // k indexes the visited tiles (tile_of(k) == k without a window, so the
   // fully visible tiles [0, n_full) come first).
   auto do_tile = [&](auto buf_tag, auto full_tag, int k) {
     constexpr int BUF = decltype(buf_tag)::value;
     swrite(BUF);
     __syncthreads();
-    if (k + 1 < n_visit) gload(tile_of(k + 1));
+    if (k + 1 < n_visit) {
+      gload(tile_of(k + 1), next_page);
+      if (k + 2 < n_visit) next_page = tile_page(tile_of(k + 2));
+    }
     if constexpr (decltype(full_tag)::value)
       full_body(BUF);
     else
@@ -763,7 +793,8 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   int k = 0;
-  if (n_visit > 0) gload(tile_of(0));
+  if (n_visit > 0) gload(tile_of(0), tile_page(tile_of(0)));
+  if (n_visit > 1) next_page = tile_page(tile_of(1));
   for (; k < n_full; k += 2) {
     do_tile(B0{}, std::true_type{}, k);
     do_tile(B1{}, std::true_type{}, k + 1);
@@ -820,22 +851,32 @@ hipError_t launch_bwd_prep(const __bf16* O, const __bf16* dO, float* Dv, int64_t
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_bwd_kv_d(const BwdParams& p, hipStream_t s) {
+  if (p.pages)
+    hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3(p.n_items), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3(p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_q_d(const BwdParams& p, hipStream_t s) {
+  if (p.pages)
+    hipLaunchKernelGGL((bwd_q_kernel<D, true>), dim3(p.n_qitems), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<D, false>), dim3(p.n_qitems), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_kv(const BwdParams& p, int d, hipStream_t s) {
   if (p.n_items <= 0) return hipSuccess;
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_kv_kernel<128>, dim3(p.n_items), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(bwd_kv_kernel<64>, dim3(p.n_items), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return d == 128 ? launch_bwd_kv_d<128>(p, s) : launch_bwd_kv_d<64>(p, s);
 }
 
 hipError_t launch_bwd_q(const BwdParams& p, int d, hipStream_t s) {
   if (p.n_qitems <= 0) return hipSuccess;
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_q_kernel<128>, dim3(p.n_qitems), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(bwd_q_kernel<64>, dim3(p.n_qitems), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return d == 128 ? launch_bwd_q_d<128>(p, s) : launch_bwd_q_d<64>(p, s);
 }
 
 hipError_t launch_f32_to_bf16(const float* src, __bf16* dst, int64_t n, hipStream_t s) {

@@ -118,6 +118,9 @@ struct BwdParams {
   float* dVacc;
   const ca_task* tasks;
   const ca_task_mask* masks;   // per task, or nullptr: causal only
+  const int32_t* pages;   // as in FwdParams
+  uint32_t page_bytes;
+  int32_t page_shift;
   const BwdItem* items;   // dK/dV kernel
   int32_t n_items;
   const FwdItem* qitems;  // dQ kernel

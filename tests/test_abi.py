@@ -147,3 +147,18 @@ def test_paged_forward_rejects_bad_page_tables():
     assert ca.forward_workspace(s, good, pages=ca.kv_pages([3, 9, 0], 256)) == 0
     # a context that is empty needs no alignment; nothing to do: OK
     assert call_paged(s, [(0, 5, 0, 0, 0, 0, 0)], table, 256) == ca.CA_OK
+
+
+def test_paged_backward_rejects_a_task_reading_a_page_twice():
+    s = ca.make_shape(8, 2, 128, 300, 4 * 128, 300)
+    tasks = ca.task_array([(0, 0, 0, 300, 300, 0, 0)])            # virtual pages 0, 1, 2
+    for table, want in (([1, 2, 1], ca.CA_ERR_INVALID), ([1, 2, 3], ca.CA_OK)):
+        pg = ca.kv_pages(table, 128)
+        need = ca.lib().ca_backward_paged_workspace(ctypes.byref(s), tasks.ctypes.data_as(ctypes.c_void_p), None,
+                                                     1, ctypes.byref(pg))
+        assert (need == 0) == (want != ca.CA_OK)
+    pg = ca.kv_pages([1, 2, 1], 128)
+    st = ca.lib().ca_backward_paged(ctypes.byref(s), tasks.ctypes.data_as(ctypes.c_void_p), None, 1,
+                                    ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    1 << 30, None)
+    assert st == ca.CA_ERR_INVALID and "twice" in ca.lib().ca_last_error().decode()

@@ -240,3 +240,97 @@ def test_backward_reads_nothing_past_the_context():
         e = rel_fro(gw, r[sel])
         print("NaN-fenced backward %s relF=%.3e" % (name, e), flush=True)
         assert e <= GRAD_REL_FRO, name
+
+
+# ---------------------------------------------------------------------------
+# Paged backward
+# ---------------------------------------------------------------------------
+
+def run_paged_backward(tasks, table, P, n_phys, hq, hkv, d, q_rows, seed, masks=None):
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((q_rows, hq, d), seed)
+    dO = I.randn_bf16((q_rows, hq, d), seed + 1)
+    Ks = I.randn_bf16((n_phys * P, hkv, d), seed + 2)
+    Vs = I.randn_bf16((n_phys * P, hkv, d), seed + 3)
+    pages = ca.kv_pages(table, P)
+    shape = ca.make_shape(hq, hkv, d, q_rows, n_phys * P, q_rows)
+    Qd, dOd, Kd, Vd = Q.to(dev), dO.to(dev), Ks.to(dev), Vs.to(dev)
+    O = torch.empty((q_rows, hq, d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((q_rows, hq), device=dev)
+    ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE, masks=masks, pages=pages)
+    dQ = torch.full_like(Qd, float("nan"))
+    dK = torch.full_like(Kd, float("nan"))
+    dV = torch.full_like(Vd, float("nan"))
+    ca.backward(shape, tasks, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV, masks=masks, pages=pages)
+    torch.cuda.synchronize()
+    t9 = tasks if masks is None else np.concatenate([tasks, np.asarray(masks)], axis=1)
+    ref = oracle.backward_paged(t9, widen(Q), widen(Ks), widen(Vs), widen(dO), table, P, 1 / math.sqrt(d))
+    return (dQ, dK, dV), ref, (Qd, Kd, Vd, O, dOd, LSE)
+
+
+def check_grads(got, ref, label):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        gw = widen(g)
+        assert np.isfinite(gw).all(), label + " " + name
+        e = rel_fro(gw, r)
+        print("%s %s relF=%.3e" % (label, name, e), flush=True)
+        assert e <= GRAD_REL_FRO, label + " " + name
+
+
+@pytest.mark.parametrize("P", [128, 512])
+def test_paged_backward_varlen(P):
+    """Distinct pages: one pass; dK/dV of the page store, gathered back to
+    virtual rows, equal the unpaged backward's bit for bit."""
+    announce("paged backward varlen P%d" % P)
+    torch = torch_cuda()
+    hq, hkv, d = 8, 2, 128
+    docs = [1, 127, 129, 300, 700, 65]
+    tasks, n_vp = I.paged_varlen_tasks(docs, P)
+    n_phys = n_vp + 3
+    table = I.page_table(n_vp, n_phys, 2000 + P)
+    got, ref, (Qd, Ks, Vs, O, dOd, LSE) = run_paged_backward(tasks, table, P, n_phys, hq, hkv, d, sum(docs),
+                                                              2010 + P)
+    check_grads(got, ref, "paged backward P%d" % P)
+    used = np.zeros(n_phys, dtype=bool)
+    used[table] = True
+    for g in got[1:]:
+        unread = torch.from_numpy(np.flatnonzero(~used)).to(g.device)
+        assert torch.count_nonzero(g.view(n_phys, -1)[unread]).item() == 0   # unread pages: 0
+    # unpaged backward over the virtual K/V
+    idx = torch.from_numpy(table.astype(np.int64)).to(Ks.device)
+    Kv = Ks.view(n_phys, -1)[idx].view(n_vp * P, hkv, d)
+    Vv = Vs.view(n_phys, -1)[idx].view(n_vp * P, hkv, d)
+    shape = ca.make_shape(hq, hkv, d, sum(docs), n_vp * P, sum(docs))
+    dQu, dKu, dVu = torch.empty_like(Qd), torch.empty_like(Kv), torch.empty_like(Vv)
+    ca.backward(shape, tasks, Qd, Kv, Vv, O, dOd, LSE, dQu, dKu, dVu)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0].view(torch.int16), dQu.view(torch.int16))
+    assert torch.equal(got[1].view(n_phys, -1)[idx].view(torch.int16), dKu.view(n_vp, -1).view(torch.int16))
+    assert torch.equal(got[2].view(n_phys, -1)[idx].view(torch.int16), dVu.view(n_vp, -1).view(torch.int16))
+
+
+def test_paged_backward_shared_prefix_pages():
+    """Two documents whose tables share their first pages: the shared pages
+    collect both documents' gradients (accumulating passes)."""
+    announce("paged backward with shared prefix pages")
+    P = 128
+    hq, hkv, d = 8, 2, 128
+    # doc A: virtual pages 0..5 (700 tokens), doc B: virtual pages 6..9 (500 tokens);
+    # B's first two pages are A's first two
+    tasks = np.array([[0, 0, 0, 700, 700, 0, 0],
+                      [700, 6 * P, 700, 244, 500, 256, 0]], dtype=np.int64)   # B: its last 244 queries
+    table = np.array([3, 7, 0, 5, 9, 2, 3, 7, 1, 8], dtype=np.int32)
+    got, ref, _ = run_paged_backward(tasks, table, P, 11, hq, hkv, d, 944, 2100)
+    check_grads(got, ref, "paged backward shared prefix")
+
+
+def test_paged_backward_lambda_mask():
+    announce("paged backward with sink + sliding-window masks")
+    P = 256
+    docs = [2000, 300]
+    tasks, n_vp = I.paged_varlen_tasks(docs, P)
+    masks = np.array([[300, 16], [64, 0]], dtype=np.int64)
+    table = I.page_table(n_vp, n_vp + 2, 2200)
+    got, ref, _ = run_paged_backward(tasks, table, P, n_vp + 2, 8, 2, 128, sum(docs), 2210, masks=masks)
+    check_grads(got, ref, "paged backward lambda")
