@@ -109,7 +109,7 @@ typedef struct {
   int32_t hq;      /* query heads, >= 1                                    */
   int32_t hkv;     /* key/value heads, >= 1, divides hq                    */
   int32_t d;       /* head dimension: 64 or 128                            */
-  float scale;     /* softmax scale applied to q.k (usually 1/sqrt(d))     */
+  float scale;     /* softmax scale applied to q.k, > 0 (usually 1/sqrt(d)) */
   uint32_t flags;  /* CA_OUT_F32                                           */
   int64_t q_rows;  /* rows of Q (and dQ)                                   */
   int64_t kv_rows; /* rows of K, V (and dK, dV)                            */
@@ -127,7 +127,7 @@ size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, in
 /* O and LSE for every row of every task, in one fused launch over all tasks
  * (fully masked key tiles are never visited).  Rows of O/LSE outside every
  * task are not written.  Errors: CA_ERR_INVALID for a null pointer, hq/hkv
- * not dividing, scale not finite, negative lengths or any row range past
+ * not dividing, scale not finite or not positive, negative lengths or any row range past
  * q_rows/kv_rows/o_rows; CA_ERR_UNSUPPORTED for d not in {64, 128};
  * CA_ERR_WORKSPACE when ws_bytes < ca_forward_workspace(...). */
 ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks,

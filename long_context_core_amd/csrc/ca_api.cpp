@@ -114,7 +114,8 @@ ca_status check_shape(const ca_shape* s) {
   if (s->hq < 1 || s->hkv < 1) return fail(CA_ERR_INVALID, "hq=%d hkv=%d must be >= 1", s->hq, s->hkv);
   if (s->hq % s->hkv != 0) return fail(CA_ERR_INVALID, "hkv=%d does not divide hq=%d", s->hkv, s->hq);
   if (s->d != 64 && s->d != 128) return fail(CA_ERR_UNSUPPORTED, "head dim d=%d not supported (64, 128)", s->d);
-  if (!std::isfinite(s->scale)) return fail(CA_ERR_INVALID, "scale is not finite");
+  // The kernels take row maxima of the unscaled scores: the scale must be positive.
+  if (!std::isfinite(s->scale) || !(s->scale > 0.f)) return fail(CA_ERR_INVALID, "scale must be finite and > 0");
   if (s->q_rows < 0 || s->kv_rows < 0 || s->o_rows < 0)
     return fail(CA_ERR_INVALID, "negative row count");
   if (s->flags & ~(uint32_t)CA_OUT_F32) return fail(CA_ERR_INVALID, "unknown flags 0x%x", s->flags);

@@ -70,6 +70,8 @@ def test_forward_rejects_bad_arguments_without_launching():
     assert call_forward(ca.make_shape(8, 3, 128, 10, 10, 10), good) == ca.CA_ERR_INVALID
     assert call_forward(ca.make_shape(8, 2, 96, 10, 10, 10), good) == ca.CA_ERR_UNSUPPORTED
     assert call_forward(ca.make_shape(8, 2, 128, 10, 10, 10, scale=float("nan")), good) == ca.CA_ERR_INVALID
+    for bad_scale in (0.0, -0.125):   # row maxima are taken before scaling
+        assert call_forward(ca.make_shape(8, 2, 128, 10, 10, 10, scale=bad_scale), good) == ca.CA_ERR_INVALID
     assert call_forward(s, [(0, 0, 0, 11, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past q_rows
     assert call_forward(s, [(0, 1, 0, 10, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past kv_rows
     assert call_forward(s, [(0, 0, 5, 10, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past o_rows
