@@ -85,7 +85,7 @@ struct QTile<128> {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (task, KV head, 128 context rows).
 // ---------------------------------------------------------------------------
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool WIN>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   using Tile = QTile<D>;
   constexpr int BQ = 32;            // query rows per step
@@ -404,12 +404,27 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   };
 
   // step = (query tile, head of the group), head fastest.  Row tiles before
-  // n_diag_rt may hold rows that do not see every key of the workgroup.  Steps
-  // alternate between the two LDS buffers and run in pairs, so that every LDS
-  // address is a lane constant plus an immediate; the band is rounded up to an
-  // even number of steps (its body is correct for any step).
+  // n_diag_rt may hold rows that do not see every key of the workgroup.  With
+  // a window, row tiles from n_win_rt on hold rows whose window ends inside the
+  // workgroup's keys (and a workgroup holding sink keys is masked
+  // throughout).  Steps [n_diag, n_fend) see every key and run the fixed-order
+  // body; the rest run the general one.  Steps alternate between the two LDS
+  // buffers and run in pairs, so that every LDS address is a lane constant
+  // plus an immediate: n_diag is rounded up and n_fend down to even steps
+  // (the general body is correct for any step).
   const int n_diag_rt = (int)clamp64(((int64_t)it.key0 + 127 - delta - r_first + BQ - 1) / BQ, 0, n_rt);
-  const int n_diag = win > 0 ? n_steps : min(n_steps, (n_diag_rt * G + 1) & ~1);   // windowed: all masked
+  int n_diag = min(n_steps, (n_diag_rt * G + 1) & ~1);
+  int n_fend = n_steps;
+  if (!WIN && win > 0) n_diag = n_steps;   // masks without the windowed loop split
+  if (WIN && win > 0) {
+    if (it.key0 < sj) {
+      n_diag = n_steps;
+    } else {
+      const int64_t x = (int64_t)it.key0 - delta + win - BQ - r_first;   // last full row tile start - r_first
+      const int n_win_rt = x < 0 ? 0 : (int)min<int64_t>(x / BQ + 1, n_rt);
+      n_fend = max(n_diag, min(n_steps, (n_win_rt * G) & ~1));
+    }
+  }
   int cur_g = 0, cur_r0 = r_first;
   auto do_step = [&](auto buf_tag, auto diag_tag, int step) {
     constexpr int BUF = decltype(buf_tag)::value;
@@ -445,11 +460,27 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     do_step(B0{}, std::true_type{}, step);
     ++step;
   }
-  for (; step + 1 < n_steps; step += 2) {
-    do_step(B0{}, std::false_type{}, step);
-    do_step(B1{}, std::false_type{}, step + 1);
+  if constexpr (WIN) {
+    for (; step + 1 < n_fend; step += 2) {
+      do_step(B0{}, std::false_type{}, step);
+      do_step(B1{}, std::false_type{}, step + 1);
+    }
+    if (step < n_fend) {                        // odd count: the last step of all
+      do_step(B0{}, std::false_type{}, step);
+      ++step;
+    }
+    for (; step + 1 < n_steps; step += 2) {     // window edge
+      do_step(B0{}, std::true_type{}, step);
+      do_step(B1{}, std::true_type{}, step + 1);
+    }
+    if (step < n_steps) do_step(B0{}, std::true_type{}, step);
+  } else {
+    for (; step + 1 < n_steps; step += 2) {
+      do_step(B0{}, std::false_type{}, step);
+      do_step(B1{}, std::false_type{}, step + 1);
+    }
+    if (step < n_steps) do_step(B0{}, std::false_type{}, step);
   }
-  if (step < n_steps) do_step(B0{}, std::false_type{}, step);
 
   // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
   if (!key_ok) return;
@@ -488,7 +519,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: work items as in the forward (hpw heads x 4/hpw blocks of 32 rows).
 // ---------------------------------------------------------------------------
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool WIN>
 __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   constexpr int BN = 64;
   constexpr int KS = D + 16;      // K is read row-wise and by transpose reads
@@ -591,12 +622,14 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int j16 = lane & 15;
   const int kt_off = ((j16 >> 2) + 4 * hh) * KS + 16 * (g16 & 1) + 4 * (j16 & 3);
 
-  // Key tiles [0, n_full) are visible to every row of the workgroup (no mask,
-  // no skip); the rest go through the general body.  Tiles run in LDS-buffer
-  // pairs so that every LDS address is a lane constant plus an immediate.
-  // Sink + sliding-window mask (win > 0): as in the forward, the workgroup
-  // visits the sink tiles [0, t_a) and the window tiles [t_b, n_tiles), and
-  // every tile goes through the general body.
+  // Visited tiles [k_f0, k_f1) are visible to every row of the workgroup (no
+  // mask, no skip); the rest go through the general body.  Tiles run in
+  // LDS-buffer pairs so that every LDS address is a lane constant plus an
+  // immediate, so k_f0 is rounded up and k_f1 down to even indices.  Sink +
+  // sliding-window mask (win > 0): as in the forward, the workgroup visits the
+  // sink tiles [0, t_a) and the window tiles [t_b, n_tiles); the full ones are
+  // the window tiles inside the last row's window and below the first row's
+  // diagonal.
   int win = 0, sj = 0;
   if (p.masks) {
     win = p.masks[it.task].window;
@@ -619,8 +652,17 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     if (tile >= w_full) return true;
     return win > 0 && !((tile + 1) * BN <= sj || (int64_t)tile * BN >= w_lo_last);
   };
-  const int n_full = win > 0 ? 0
-                             : min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN)) & ~1;
+  const int c_hi = min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN));
+  int k_f0 = 0, k_f1 = c_hi & ~1;
+  if (!WIN && win > 0) k_f1 = 0;   // masks without the windowed loop split
+  if (WIN && win > 0) {
+    const int64_t wl = (int64_t)wg_last + delta - win + 1;             // first key in every row's window
+    const int w_lo_t = (int)clamp64((wl + BN - 1) / BN, 0, n_tiles);   // ceil(wl / BN), at least 0
+    const int f0 = max(t_b, w_lo_t), f1 = c_hi;
+    k_f0 = (t_a + (f0 - t_b) + 1) & ~1;
+    k_f1 = f1 > f0 ? (t_a + (f1 - t_b)) & ~1 : 0;
+    if (k_f1 <= k_f0) k_f0 = k_f1 = 0;
+  }
 
   auto diag_body = [&](int buf, int tile) {
     const int k0 = tile * BN;
@@ -795,7 +837,13 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   int k = 0;
   if (n_visit > 0) gload(tile_of(0), tile_page(tile_of(0)));
   if (n_visit > 1) next_page = tile_page(tile_of(1));
-  for (; k < n_full; k += 2) {
+  if constexpr (WIN) {
+    for (; k < k_f0; k += 2) {
+      do_tile(B0{}, std::false_type{}, k);
+      do_tile(B1{}, std::false_type{}, k + 1);
+    }
+  }
+  for (; k < k_f1; k += 2) {
     do_tile(B0{}, std::true_type{}, k);
     do_tile(B1{}, std::true_type{}, k + 1);
   }
@@ -851,22 +899,34 @@ hipError_t launch_bwd_prep(const __bf16* O, const __bf16* dO, float* Dv, int64_t
   return hipGetLastError();
 }
 
+// WIN: the loop split for sink + sliding-window masks, taken when the call
+// has masks; calls without masks run the variant without it.
+template <int D, bool PAGED>
+hipError_t launch_bwd_kv_dp(const BwdParams& p, hipStream_t s) {
+  if (p.masks)
+    hipLaunchKernelGGL((bwd_kv_kernel<D, PAGED, true>), dim3(p.n_items), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<D, PAGED, false>), dim3(p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_bwd_kv_d(const BwdParams& p, hipStream_t s) {
-  if (p.pages)
-    hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3(p.n_items), dim3(256), 0, s, p);
+  return p.pages ? launch_bwd_kv_dp<D, true>(p, s) : launch_bwd_kv_dp<D, false>(p, s);
+}
+
+template <int D, bool PAGED>
+hipError_t launch_bwd_q_dp(const BwdParams& p, hipStream_t s) {
+  if (p.masks)
+    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, true>), dim3(p.n_qitems), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3(p.n_items), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, false>), dim3(p.n_qitems), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_q_d(const BwdParams& p, hipStream_t s) {
-  if (p.pages)
-    hipLaunchKernelGGL((bwd_q_kernel<D, true>), dim3(p.n_qitems), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_q_kernel<D, false>), dim3(p.n_qitems), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return p.pages ? launch_bwd_q_dp<D, true>(p, s) : launch_bwd_q_dp<D, false>(p, s);
 }
 
 hipError_t launch_bwd_kv(const BwdParams& p, int d, hipStream_t s) {
