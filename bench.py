@@ -125,6 +125,31 @@ def secondary(steps=3, warmup=1):
         ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
         return Q, K, V, O, LSE, shape, tasks, ws
 
+    # Tiny configuration (1,024 tokens, 8 work items): latency regime, timed per
+    # call with its inputs resident in the caches (warm) and after a 1 GiB
+    # write that evicts them from L2 and the 256 MB last-level cache (cold).
+    w = I.tiny_forward()
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 201)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    call = lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
+    warm = timed(call, 50, 5, stream)
+    cold = []
+    for _ in range(20):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold_ms = sorted(cold)[len(cold) // 2]
+    out["tiny_1k"] = {"workload": w.name, "warm_ms": round(warm, 4), "cold_median_ms": round(cold_ms, 4),
+                      "warm_gflops": round(fl / warm / 1e6, 1)}
+    log("tiny 1k: warm %.4f ms, cold (caches flushed) median %.4f ms" % (warm, cold_ms))
+    del Q, K, V, O, LSE, ws, flush
+    torch.cuda.empty_cache()
+
     # CA-tasks re-batched forward (LLaMA-34B shape)
     w = I.ca_tasks_34b()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 203)

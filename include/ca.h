@@ -16,9 +16,9 @@
  *  - Pointers named *_host are host memory; every other pointer is device
  *    memory on the current HIP device.  The caller allocates and owns every
  *    buffer, including the workspace; the library allocates no device memory
- *    and keeps no state between calls other than a reusable pinned host
- *    staging buffer per thread and device, through which host-built work
- *    queues are copied into the workspace.
+ *    and keeps no state between calls other than a small ring of reusable
+ *    pinned host staging buffers per thread and device, through which
+ *    host-built work queues are copied into the workspace.
  *  - Calls are asynchronous on `stream` (a hipStream_t, passed as void*; NULL
  *    is the default stream).  Buffers must stay valid until the stream work
  *    completes.  Host arrays (*_host) are only read during the call.

@@ -205,28 +205,36 @@ ca_status check_forward_args(const ca_shape* s, const ca_task* t, const ca_task_
 int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
 // Upload of a host-built work queue into the caller's workspace, through a
-// pinned staging buffer kept per thread and device (grown, never shrunk, held
-// until the process ends).  An event recorded after the copy guards reuse, so
-// the call never blocks on earlier stream work unless the previous upload of
-// this thread has not even started.
+// ring of pinned staging buffers kept per thread and device (each grown, never
+// shrunk, held until the process ends).  An event recorded after each copy
+// guards that buffer's reuse, so a call waits only when all kStagingSlots
+// earlier uploads of this thread are still queued behind device work; with a
+// single buffer every call waited for the previous call's copy, which put the
+// host wake-up latency between consecutive small launches.
+constexpr int kStagingSlots = 8;
 struct Staging {
   void* buf = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
 };
+struct StagingRing {
+  Staging slot[kStagingSlots];
+  int next = 0;
+};
 constexpr int kMaxDevices = 64;
-thread_local Staging g_staging[kMaxDevices];
+thread_local StagingRing g_staging[kMaxDevices];
 
 ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(CA_ERR_UNSUPPORTED, "device index %d", dev);
-  Staging& st = g_staging[dev];
+  StagingRing& ring = g_staging[dev];
+  Staging& st = ring.slot[ring.next];
   if (st.pending) {
     e = hipEventSynchronize(st.ev);
-    if (e != hipSuccess) return hip_fail(e, "waiting for the previous upload");
+    if (e != hipSuccess) return hip_fail(e, "waiting for an earlier upload");
     st.pending = false;
   }
   if (!st.ev) {
@@ -248,6 +256,7 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
   e = hipEventRecord(st.ev, s);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   st.pending = true;
+  ring.next = (ring.next + 1) % kStagingSlots;
   return CA_OK;
 }
 
