@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   constexpr int NT = 64 * NW;     // threads
   constexpr int BN = 64;          // keys per tile
   constexpr int KS = D + 8;       // K row stride in LDS (elements): 16 B pad
-  constexpr int VS = D + 16;      // V row stride in LDS (elements): 32 B pad
+  constexpr int VS = D + 32;      // V row stride in LDS (elements): 64 B pad, no transpose-read conflicts
   constexpr int NCB = D / 32;     // 32-channel output blocks
   constexpr int NKS = D / 16;     // 16-channel reduction steps of Q.K
   constexpr int CH = D / 8;       // 16-byte chunks per row
