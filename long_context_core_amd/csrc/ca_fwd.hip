@@ -146,7 +146,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // the tile's own rows, so nothing past the context is ever read).  Paged
   // K/V: a tile starts at a multiple of 64 virtual rows and pages hold a
   // multiple of 128 rows, so each tile lies inside one page.
-  uint4 kreg[PASSES], vreg[PASSES];
+  // Two register sets: tile k + 2 is loaded while tile k is computed.
+  uint4 kreg[2][PASSES], vreg[2][PASSES];
   // Paged K/V: the physical page of a tile is read one tile ahead of its
   // loads, through a vector load (waited on in order with the tile loads; a
   // load that had to complete at once would stall on the tile in flight),
@@ -169,22 +170,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
       return v;
     }
   };
-  auto gload = [&](int tile, int64_t r0) {
+  // set: register set, a compile-time constant (registers are not indexable)
+  auto gload = [&](auto set_tag, int tile, int64_t r0) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
     const int n = min(BN, kv_hi - tile * BN);
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase + r0 * kv_stride, n, row_bytes);
     const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(vbase + r0 * kv_stride, n, row_bytes);
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      kreg[r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
-      vreg[r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
+      kreg[SET][r] = buffer_load_16(krs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
+      vreg[SET][r] = buffer_load_16(vrs, ld_voff + (uint32_t)(r * RPP) * row_bytes, 0);
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;   // also the LDS buffer
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       const int row = r * RPP + ld_row;
-      *(uint4*)(&lds_k[buf][row * KS + ld_chunk * 8]) = kreg[r];
-      *(uint4*)(&lds_v[buf][row * VS + ld_chunk * 8]) = vreg[r];
+      *(uint4*)(&lds_k[SET][row * KS + ld_chunk * 8]) = kreg[SET][r];
+      *(uint4*)(&lds_v[SET][row * VS + ld_chunk * 8]) = vreg[SET][r];
     }
   };
 
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   const int v_lane_off = ((j16 >> 2) + 4 * hh) * VS + 16 * (g16 & 1) + 4 * (j16 & 3);
 
   // One key tile for this wave.
-  auto do_tile = [&](int tile, int buf) {
+  auto do_tile = [&](int tile, int buf) __attribute__((always_inline)) {
     const int k0 = tile * BN;
     // S^T chain with the K operands read KPF steps ahead (fixed by fences:
     // left alone, the schedule waits on each read right before its MFMA;
@@ -294,19 +298,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     }
   };
 
+  // Visited tile k is staged from register set k & 1 into LDS buffer k & 1;
+  // right after, tile k + 2 is loaded into the same register set, two tiles
+  // (about 2 us) ahead of its use.  The page of the next tile to load is read
+  // one load ahead.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   int next_page = 0;
-  if (n_visit > 0) gload(tile_of(0), tile_row(tile_of(0), tile_page(tile_of(0))));
-  if (n_visit > 1) next_page = tile_page(tile_of(1));
-  for (int k = 0; k < n_visit; ++k) {
-    const int buf = k & 1;
-    const int tile = tile_of(k);
-    swrite(buf);
+  if (n_visit > 0) gload(S0{}, tile_of(0), tile_row(tile_of(0), tile_page(tile_of(0))));
+  if (n_visit > 1) gload(S1{}, tile_of(1), tile_row(tile_of(1), tile_page(tile_of(1))));
+  if (n_visit > 2) next_page = tile_page(tile_of(2));
+  auto step = [&](auto set_tag, int k) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    swrite(set_tag);
     __syncthreads();
-    if (k + 1 < n_visit) {
-      gload(tile_of(k + 1), tile_row(tile_of(k + 1), next_page));
-      if (k + 2 < n_visit) next_page = tile_page(tile_of(k + 2));
+    if (k + 2 < n_visit) {
+      gload(set_tag, tile_of(k + 2), tile_row(tile_of(k + 2), next_page));
+      if (k + 3 < n_visit) next_page = tile_page(tile_of(k + 3));
     }
-    if (wave_sees(tile)) do_tile(tile, buf);
+    const int tile = tile_of(k);
+    if (wave_sees(tile)) do_tile(tile, SET);
+  };
+  for (int k = 0; k < n_visit; k += 2) {
+    step(S0{}, k);
+    if (k + 1 < n_visit) step(S1{}, k + 1);
   }
 
   // Epilogue: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty rows: 0, -inf.
