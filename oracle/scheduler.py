@@ -22,6 +22,16 @@ Readings where the pages leave a step open (listed with the design notes):
   n_kv to nearest, clamped to [n_q + L_kv - L_q, L_kv].  The sub-Item is the
   query range [n_kv - n_q, n_kv); the rest of the Item stays on the source as
   up to two Items.  A split is a candidate only if n_q >= min_shard.
+* Head-tail shards (head_tail=True).  A split of Item [a, b) moves its first m
+  and its last m queries, [a, a + m) and [b - m, b), mirroring how a
+  head-tail shard of a document pairs a leading stretch of its tokens with the
+  matching trailing stretch; the middle [a + m, b - m) stays on the source.
+  The pair of pieces holds m (a + b + 1) of the Item's (b - a)(a + b + 1) / 2
+  visible pairs, so the
+  FLOPs fraction alpha gives m = alpha (b - a) / 2, rounded to nearest and
+  clamped to [1, (b - a) // 2]; the shard is a candidate if 2 m >= min_shard.
+  Its communication is 2 m queries and the context [0, b) that the tail piece
+  needs (the head's context is inside it).  Whole-Item moves are unchanged.
 * Order and ties.  Deficit servers are taken once each, in descending order of
   their deficit at the start (ties: lower index).  For a deficit server, the
   best candidate over every Item on every server with load above the target is
@@ -197,7 +207,22 @@ def initial_items(doc_lens, k):
     return items
 
 
-def schedule(doc_lens, k, model, hq, hkv, d, eps=0.05, e_min=0.0, min_shard=128, max_moves=10000):
+def head_tail_pairs(a, b, m):
+    """Visible pairs of the head-tail shard [a, a + m) + [b - m, b) of an Item
+    with queries [a, b) and context [0, b): m (a + b + 1)."""
+    return m * (a + b + 1)
+
+
+def head_tail_shard(alpha, a, b):
+    """Half-width m of the head-tail shard holding a FLOPs fraction alpha of
+    Item [a, b)."""
+    half = (b - a) // 2
+    m = int(math.floor(alpha * (b - a) / 2.0 + 0.5))
+    return min(max(m, 1), half)
+
+
+def schedule(doc_lens, k, model, hq, hkv, d, eps=0.05, e_min=0.0, min_shard=128, max_moves=10000,
+             head_tail=False):
     """Returns (items, loads_before, loads_after, comm_bytes, moves) where
     items is a list of [server, doc, a, b] (query range [a, b) of document doc,
     context [0, b)) in creation order."""
@@ -237,6 +262,14 @@ def schedule(doc_lens, k, model, hq, hkv, d, eps=0.05, e_min=0.0, min_shard=128,
                 L_kv = it[3]
                 if dF == Ft:
                     n_q, n_kv, whole = L_q, L_kv, True
+                elif head_tail:
+                    if L_q < 2:
+                        continue
+                    m = head_tail_shard(dF / Ft, it[2], it[3])
+                    n_q, n_kv = 2 * m, L_kv
+                    whole = (n_q == L_q)
+                    if not whole and n_q < min_shard:
+                        continue
                 else:
                     nq, nkv = optimal_shard(dF / Ft, L_q, L_kv, beta)
                     n_q, n_kv = round_shard(nq, nkv, L_q, L_kv)
@@ -257,6 +290,17 @@ def schedule(doc_lens, k, model, hq, hkv, d, eps=0.05, e_min=0.0, min_shard=128,
             if whole:
                 it[0] = dst
                 load[dst] += F(it)
+            elif head_tail:
+                doc, a, b = it[1], it[2], it[3]
+                m = n_q // 2
+                del items[idx]
+                if b - m > a + m:
+                    mid = [src, doc, a + m, b - m]
+                    load[src] += F(mid)
+                    items.insert(idx, mid)
+                for new in ([dst, doc, a, a + m], [dst, doc, b - m, b]):
+                    items.append(new)
+                    load[dst] += F(new)
             else:
                 doc, a, b = it[1], it[2], it[3]
                 sa, sb = n_kv - n_q, n_kv

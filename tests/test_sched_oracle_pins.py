@@ -237,3 +237,93 @@ def test_greedy_choice_is_the_best_candidate_by_brute_force():
     moved = [it for it in items if it[0] == dst and tuple(it) not in {tuple(x) for x in items0}]
     assert moves == 1 and len(moved) == 1
     assert (moved[0][1], moved[0][2], moved[0][3]) == (best[3], best[4], best[5])
+
+
+def brute_range_pairs(a, b):
+    """Visible pairs of queries [a, b) of a causal document, one by one."""
+    return sum(1 for p in range(a, b) for key in range(b) if key <= p)
+
+
+@pytest.mark.parametrize("a,b,m", [(0, 2, 1), (0, 10, 3), (5, 17, 6), (100, 131, 7), (0, 64, 32), (3, 5, 1)])
+def test_head_tail_pairs_brute_force(a, b, m):
+    """The head [a, a + m) plus the tail [b - m, b) of an Item, counted key by
+    key, equal m (a + b + 1) — the per-document balance of a head-tail shard."""
+    assert S.head_tail_pairs(a, b, m) == brute_range_pairs(a, a + m) + brute_range_pairs(b - m, b)
+    # and the middle holds the rest of the Item's pairs
+    assert (brute_range_pairs(a, b) - S.head_tail_pairs(a, b, m)
+            == (brute_range_pairs(a + m, b - m) if b - m > a + m else 0))
+
+
+def test_head_tail_shard_holds_the_requested_fraction():
+    """m from alpha rounds to the nearest integer, so the shard's share of the
+    Item's pairs is within (a + b + 1) / 2 pairs of alpha times the Item, and
+    the clamps hold at both ends."""
+    rng = random.Random(11)
+    for _ in range(3000):
+        a = rng.randint(0, 50000)
+        b = a + rng.randint(2, 50000)
+        alpha = rng.uniform(0.0, 1.0)
+        m = S.head_tail_shard(alpha, a, b)
+        assert 1 <= m <= (b - a) // 2
+        want = alpha * brute_pairs_closed(a, b)
+        if 1 < m < (b - a) // 2:
+            assert abs(S.head_tail_pairs(a, b, m) - want) <= (a + b + 1) / 2.0 + 1e-6 * want
+    assert S.head_tail_shard(0.0, 0, 1000) == 1
+    assert S.head_tail_shard(1.0, 0, 1001) == 500
+
+
+def brute_pairs_closed(a, b):
+    """(b - a)(a + b + 1) / 2: pairs of queries [a, b), context [0, b)."""
+    return (b - a) * (a + b + 1) / 2.0
+
+
+def test_two_servers_head_tail_by_hand():
+    """k = 2, one 4000-token document, FLOPs-proportional cost, head-tail
+    shards.  Device 0 holds [0, 2000) (2,001,000 pairs), device 1 [2000, 4000)
+    (6,001,000 pairs); the target is 4,001,000.  alpha = 2,000,000 / 6,001,000
+    gives m = round(333.28) = 333: device 1 sends [2000, 2333) and
+    [3667, 4000), 333 * 6001 = 1,998,333 pairs, and keeps [2333, 3667).
+    Device 0 ends at 3,999,333 pairs and device 1 at 4,002,667, within the
+    one-percent tolerance, so there is no second move."""
+    m = flops_model()
+    unit = m.flops(1, 1) / m.peak
+    items, before, after, comm, moves = S.schedule([4000], 2, m, 32, 8, 128, eps=0.01, head_tail=True)
+    assert abs(before[0] / unit - 2001000) < 1e-3 and abs(before[1] / unit - 6001000) < 1e-3
+    assert moves == 1
+    assert abs(after[0] / unit - 3999333) < 1e-3 and abs(after[1] / unit - 4002667) < 1e-3
+    assert items == [[0, 0, 0, 2000], [1, 0, 2333, 3667], [0, 0, 2000, 2333], [0, 0, 3667, 4000]]
+    # the shard sends 666 queries and the 4000-row context
+    assert comm == 666 * 32 * 128 * 2 + 4000 * 8 * 128 * 2
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_head_tail_schedule_invariants(seed):
+    rng = random.Random(100 + seed)
+    docs = [int(math.exp(rng.uniform(math.log(64), math.log(60000)))) for _ in range(rng.randint(3, 40))]
+    k = rng.choice([2, 4, 8])
+    m = flops_model()
+    eps = 0.05
+    items, before, after, comm, moves = S.schedule(docs, k, m, 32, 8, 128, eps=eps, head_tail=True)
+    check_partition(items, docs)
+    for x, y in zip(after, loads_of(items, k, m)):
+        assert abs(x - y) <= 1e-9 * max(1e-12, y)
+    tgt = sum(before) / k
+    for s in range(k):
+        if before[s] < tgt:
+            assert after[s] >= before[s] - 1e-12
+    assert max(after) <= max(before) + 1e-12
+    assert (comm == 0) == (moves == 0)
+    # every split left its pieces as head/tail pairs of equal width on one server
+    init = {(d, a, b) for _, d, a, b in S.initial_items(docs, k)}
+    new = [it for it in items if (it[1], it[2], it[3]) not in init]
+    assert all(b - a >= 1 for _, _, a, b in new)
+
+
+def test_head_tail_balances_a_long_document_better_than_contiguous_halves():
+    """One 65536-token document on 4 servers: head-tail shards reach the
+    tolerance, and each server's pair count is within eps of the target."""
+    m = flops_model()
+    items, before, after, comm, moves = S.schedule([65536], 4, m, 32, 8, 128, eps=0.02, head_tail=True)
+    tgt = sum(before) / 4
+    assert max(after) <= 1.02 * tgt + 1e-12 and min(after) >= 0.98 * tgt - 1e-12
+    check_partition(items, [65536])
