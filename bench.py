@@ -274,6 +274,7 @@ def secondary(steps=3, warmup=1):
     k = 8
     init = ca.schedule(docs, k, gq, gkv, grid, fpp, w.hq, w.hkv, w.d, max_moves=0)
     res = ca.schedule(docs, k, gq, gkv, grid, fpp, w.hq, w.hkv, w.d, eps=0.05)
+    res_ht = ca.schedule(docs, k, gq, gkv, grid, fpp, w.hq, w.hkv, w.d, eps=0.05, head_tail=True)
     Q = I.randn_bf16((w.q_rows, w.hq, w.d), 207, device=dev)
     K = I.randn_bf16((w.kv_rows, w.hkv, w.d), 208, device=dev)
     V = I.randn_bf16((w.kv_rows, w.hkv, w.d), 209, device=dev)
@@ -290,7 +291,7 @@ def secondary(steps=3, warmup=1):
                             steps, warmup, stream))
         return ms
 
-    ms_before, ms_after = server_ms(init[0]), server_ms(res[0])
+    ms_before, ms_after, ms_ht = server_ms(init[0]), server_ms(res[0]), server_ms(res_ht[0])
     out["sched_512k_8_servers"] = {
         "workload": w.name + ", forward, 8 attention servers",
         "cost_grid": {"n_q": gq, "n_kv": gkv, "seconds_per_task": grid},
@@ -300,9 +301,16 @@ def secondary(steps=3, warmup=1):
         "measured_ms_after": [round(x, 2) for x in ms_after],
         "max_over_mean_before": round(max(ms_before) / (sum(ms_before) / k), 3),
         "max_over_mean_after": round(max(ms_after) / (sum(ms_after) / k), 3),
-        "bytes_moved": res[3], "migrations": res[4], "items": int(len(res[0]))}
+        "bytes_moved": res[3], "migrations": res[4], "items": int(len(res[0])),
+        "head_tail_shards": {
+            "predicted_ms_after": [round(x * 1e3, 2) for x in res_ht[2]],
+            "measured_ms_after": [round(x, 2) for x in ms_ht],
+            "max_over_mean_after": round(max(ms_ht) / (sum(ms_ht) / k), 3),
+            "bytes_moved": res_ht[3], "migrations": res_ht[4], "items": int(len(res_ht[0]))}}
     log("schedule 512K on 8 servers: measured max/mean %.3f -> %.3f, %d migrations, %.1f MB moved"
         % (max(ms_before) / (sum(ms_before) / k), max(ms_after) / (sum(ms_after) / k), res[4], res[3] / 1e6))
+    log("  head-tail shards: measured max/mean %.3f, %d migrations, %.1f MB moved"
+        % (max(ms_ht) / (sum(ms_ht) / k), res_ht[4], res_ht[3] / 1e6))
     del Q, K, V, O, LSE
     torch.cuda.empty_cache()
 

@@ -252,8 +252,9 @@ ca_status ca_backward_paged(const ca_shape* shape, const ca_task* tasks_host, co
  * Communication-Aware Greedy Scheduler, Steps 1-4) and Appendix B (Optimal
  * Shard Dimension Computation).  A batch of documents, first placed on k
  * devices in equal token blocks, is rebalanced across k attention servers by
- * migrating whole Items or Appendix-B-sized shards, the move that carries the
- * most predicted time per byte of communication first.
+ * migrating whole Items or Appendix-B-sized shards (or head-tail shards,
+ * Section 4.1's per-document balance, when head_tail is set), the move that
+ * carries the most predicted time per byte of communication first.
  *
  * Cost model: a measured grid of times (seconds) of one attention call with
  * n_q queries that are the last n_q tokens of an n_kv-token causal context,
@@ -270,6 +271,11 @@ typedef struct {
   double e_min;            /* migrations need E = dF / bytes > e_min                  */
   int64_t min_shard;       /* shortest query range a split may move (>= 1)           */
   int32_t max_moves;       /* cap on migrations (>= 0)                                */
+  int32_t head_tail;       /* 0: a split moves the Appendix-B shard [n_kv - n_q, n_kv);
+                              1: a split moves a head-tail shard, the first m and the
+                              last m queries of the Item ([a, a+m) and [b-m, b)), with
+                              m (a + b + 1) = alpha (b - a)(a + b + 1) / 2 pairs
+                              rounded to nearest, 1 <= m <= (b - a) / 2, 2m >= min_shard */
   double flops_per_pair;   /* FLOPs the profiled call counts per visible pair (> 0)   */
 } ca_sched_params;
 

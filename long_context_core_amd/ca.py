@@ -82,7 +82,7 @@ def kv_pages(table, page_rows):
 class SchedParams(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("e_min", ctypes.c_double), ("min_shard", ctypes.c_int64),
-                ("max_moves", ctypes.c_int32), ("flops_per_pair", ctypes.c_double)]
+                ("max_moves", ctypes.c_int32), ("head_tail", ctypes.c_int32), ("flops_per_pair", ctypes.c_double)]
 
 
 # numpy view of the C struct ca_sched_item (24 bytes)
@@ -350,15 +350,16 @@ def cost_time(grid_q, grid_kv, grid_time, flops_per_pair, n_q, n_kv):
 
 
 def schedule(doc_lens, k, grid_q, grid_kv, grid_time, flops_per_pair, hq, hkv, d,
-             eps=0.05, e_min=0.0, min_shard=128, max_moves=10000):
-    """Greedy placement of the documents on k attention servers.  Returns
+             eps=0.05, e_min=0.0, min_shard=128, max_moves=10000, head_tail=False):
+    """Greedy placement of the documents on k attention servers (splits move
+    head-tail shards when head_tail is set).  Returns
     (items as SCHED_ITEM_DTYPE records, loads_before[k], loads_after[k],
     bytes moved, number of migrations)."""
     L = lib()
     docs = np.ascontiguousarray(np.asarray(doc_lens, dtype=np.int64))
     gq, gkv, gt = _f64(grid_q), _f64(grid_kv), _f64(grid_time)
     p = SchedParams(int(k), int(hq), int(hkv), int(d), float(eps), float(e_min), int(min_shard),
-                    int(max_moves), float(flops_per_pair))
+                    int(max_moves), 1 if head_tail else 0, float(flops_per_pair))
     cap = L.ca_schedule_max_items(len(docs), int(k), int(max_moves))
     if cap < 0:
         raise CAError(CA_ERR_INVALID, "bad schedule size")

@@ -18,6 +18,13 @@
 //    tokens, the sub-Item is queries [n_kv - n_q, n_kv), the rest stays on the
 //    source as up to two Items; splits shorter than min_shard are not
 //    candidates.
+//  * Head-tail split (head_tail set).  The shard is the first m and the last
+//    m queries of the Item [a, b), [a, a + m) and [b - m, b) (Section 4.1's
+//    head-tail balance of a document, applied to an Item), which hold
+//    m (a + b + 1) of its (b - a)(a + b + 1) / 2 visible pairs; m is
+//    alpha (b - a) / 2 rounded to nearest, clamped to [1, (b - a) / 2].  The
+//    middle [a + m, b - m) stays on the source; the communication is 2 m
+//    queries and the context [0, b).
 //  * Order and ties.  Deficit servers once each, largest deficit first; for
 //    each, the best candidate (highest E) over all Items on servers above the
 //    target is migrated until the deficit is within eps * target, no
@@ -146,6 +153,14 @@ void optimal_shard(double alpha, int64_t L_q, int64_t L_kv, double beta, double*
   *out_nkv = bkv;
 }
 
+// Half-width m of the head-tail shard of Item [a, b) holding a fraction alpha
+// of its pairs: alpha (b - a) / 2 to nearest, clamped to [1, (b - a) / 2].
+int64_t head_tail_shard(double alpha, int64_t a, int64_t b) {
+  const int64_t half = (b - a) / 2;
+  const int64_t m = (int64_t)std::floor(alpha * (double)(b - a) / 2.0 + 0.5);
+  return std::min(std::max(m, (int64_t)1), half);
+}
+
 void round_shard(double nq, double nkv, int64_t L_q, int64_t L_kv, int64_t* n_q, int64_t* n_kv) {
   int64_t a = (int64_t)std::floor(nq + 0.5);
   a = std::min(std::max(a, (int64_t)1), L_q);
@@ -199,6 +214,8 @@ ca_status ca_schedule(const ca_sched_params* p, const int64_t* doc_lens_host, in
   if (p->hq < 1 || p->hkv < 1 || p->d < 1) return ca::set_error(CA_ERR_INVALID, "hq, hkv, d must be >= 1");
   if (!(p->eps >= 0.0) || !std::isfinite(p->e_min) || p->min_shard < 1 || p->max_moves < 0)
     return ca::set_error(CA_ERR_INVALID, "eps >= 0, finite e_min, min_shard >= 1, max_moves >= 0 required");
+  if (p->head_tail != 0 && p->head_tail != 1) return ca::set_error(CA_ERR_INVALID, "head_tail must be 0 or 1");
+  const bool head_tail = p->head_tail == 1;
   if (n_docs < 0 || (n_docs > 0 && !doc_lens_host)) return ca::set_error(CA_ERR_INVALID, "bad document list");
   if (!items_host || !n_items || !load_before_host || !load_after_host || !comm_bytes || !n_moves)
     return ca::set_error(CA_ERR_INVALID, "NULL output pointer");
@@ -278,6 +295,13 @@ ca_status ca_schedule(const ca_sched_params* p, const int64_t* doc_lens_host, in
           n_q = L_q;
           n_kv = L_kv;
           whole = true;
+        } else if (head_tail) {
+          if (L_q < 2) continue;
+          const int64_t m = head_tail_shard(dF / Ft, it.q_begin, it.q_end);
+          n_q = 2 * m;
+          n_kv = L_kv;
+          whole = (n_q == L_q);
+          if (!whole && n_q < p->min_shard) continue;
         } else {
           double nq, nkv;
           optimal_shard(dF / Ft, L_q, L_kv, beta, &nq, &nkv);
@@ -305,6 +329,20 @@ ca_status ca_schedule(const ca_sched_params* p, const int64_t* doc_lens_host, in
       if (bwhole) {
         items[bidx].server = dst;
         load[dst] += F(items[bidx]);
+      } else if (head_tail) {
+        const int64_t m = bnq / 2;
+        items.erase(items.begin() + (ptrdiff_t)bidx);
+        if (it.q_end - m > it.q_begin + m) {
+          const ca_sched_item mid{bsrc, it.doc, it.q_begin + m, it.q_end - m};
+          load[bsrc] += F(mid);
+          items.insert(items.begin() + (ptrdiff_t)bidx, mid);
+        }
+        const ca_sched_item head{dst, it.doc, it.q_begin, it.q_begin + m};
+        const ca_sched_item tail{dst, it.doc, it.q_end - m, it.q_end};
+        items.push_back(head);
+        load[dst] += F(head);
+        items.push_back(tail);
+        load[dst] += F(tail);
       } else {
         const int64_t sa = bnkv - bnq, sb = bnkv;
         items.erase(items.begin() + (ptrdiff_t)bidx);

@@ -27,16 +27,21 @@ def flops_grid():
     return gq, gkv, [[1e-5 + FPP * S.block_pairs(min(x, y), y) / 8e14 for y in gkv] for x in gq]
 
 
-def scheduled(docs, k):
+def scheduled(docs, k, head_tail=False):
     gq, gkv, gt = flops_grid()
     items, before, after, comm, moves = ca.schedule(docs, k, gq, gkv, gt, FPP, HQ, HKV, D,
-                                                    eps=0.02, min_shard=64)
+                                                    eps=0.02, min_shard=64, head_tail=head_tail)
     assert moves > 0
+    if head_tail:
+        # at least one Item was split into a head and a tail on one server
+        firsts = {(int(r["doc"]), int(r["q_begin"])) for r in items}
+        assert any(int(r["q_begin"]) > 0 and (int(r["doc"]), 0) in firsts for r in items)
     return [ca.sched_tasks(items[items["server"] == s], docs) for s in range(k)]
 
 
-def test_scheduled_forward_equals_whole_batch():
-    announce("scheduled forward: 5 documents on 4 servers")
+@pytest.mark.parametrize("head_tail", [False, True])
+def test_scheduled_forward_equals_whole_batch(head_tail):
+    announce("scheduled forward: 5 documents on 4 servers, head_tail=%s" % head_tail)
     torch = torch_cuda()
     dev = torch.device("cuda:0")
     docs = [3000, 700, 1500, 64, 900]
@@ -48,7 +53,7 @@ def test_scheduled_forward_equals_whole_batch():
     shape = ca.make_shape(HQ, HKV, D, T, T, T)
     O = torch.full((T, HQ, D), float("nan"), dtype=torch.bfloat16, device=dev)
     LSE = torch.full((T, HQ), float("nan"), device=dev)
-    for tasks in scheduled(docs, 4):
+    for tasks in scheduled(docs, 4, head_tail):
         if len(tasks):
             ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE)
     torch.cuda.synchronize()
@@ -56,8 +61,9 @@ def test_scheduled_forward_equals_whole_batch():
     check_forward(O, LSE, O_ref, LSE_ref, "scheduled forward")
 
 
-def test_scheduled_backward_sums_to_whole_batch():
-    announce("scheduled backward: 4 documents on 3 servers")
+@pytest.mark.parametrize("head_tail", [False, True])
+def test_scheduled_backward_sums_to_whole_batch(head_tail):
+    announce("scheduled backward: 4 documents on 3 servers, head_tail=%s" % head_tail)
     torch = torch_cuda()
     dev = torch.device("cuda:0")
     docs = [2500, 300, 1800, 600]
@@ -70,7 +76,7 @@ def test_scheduled_backward_sums_to_whole_batch():
     shape = ca.make_shape(HQ, HKV, D, T, T, T)
     O = torch.empty((T, HQ, D), dtype=torch.bfloat16, device=dev)
     LSE = torch.empty((T, HQ), device=dev)
-    per_server = scheduled(docs, 3)
+    per_server = scheduled(docs, 3, head_tail)
     for tasks in per_server:
         if len(tasks):
             ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE)
