@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -233,7 +234,14 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
   StagingRing& ring = g_staging[dev];
   Staging& st = ring.slot[ring.next];
   if (st.pending) {
-    e = hipEventSynchronize(st.ev);
+    // Poll briefly before blocking: with back-to-back calls of a few tens of
+    // microseconds the slot frees within that time, and a blocking wait can
+    // put the thread to sleep for far longer than the kernel it waits for.
+    const auto t0 = std::chrono::steady_clock::now();
+    while ((e = hipEventQuery(st.ev)) == hipErrorNotReady &&
+           std::chrono::steady_clock::now() - t0 < std::chrono::microseconds(200)) {
+    }
+    if (e == hipErrorNotReady) e = hipEventSynchronize(st.ev);
     if (e != hipSuccess) return hip_fail(e, "waiting for an earlier upload");
     st.pending = false;
   }

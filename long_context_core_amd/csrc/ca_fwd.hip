@@ -245,13 +245,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
           s_acc[mb][j] = (r <= lim && (r >= wlo || r < slim)) ? s_acc[mb][j] : -INFINITY;
         }
     }
-    // Tile max of this row, both half-waves.
-    float mx = -INFINITY;
+    // Tile max of this row, both half-waves: one three-input max per two
+    // scores, in two independent chains.
+    float mx0 = fmaxf(s_acc[0][0], s_acc[0][1]);
+    float mx1 = fmaxf(s_acc[1][0], s_acc[1][1]);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s_acc[mb][j], s_acc[mb][j + 1]));
-    mx = max_halves(mx);
+    for (int j = 2; j < 16; j += 2) {
+      mx0 = fmaxf(fmaxf(mx0, s_acc[0][j]), s_acc[0][j + 1]);
+      mx1 = fmaxf(fmaxf(mx1, s_acc[1][j]), s_acc[1][j + 1]);
+    }
+    float mx = max_halves(fmaxf(mx0, mx1));
     const float m_tile = mx * p.scale_log2;
     // Raise the reference only when some row of the wave outgrew it.
     if (__any(m_tile > m2 + kRescaleLog2)) {
