@@ -203,13 +203,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   const int v_lane_off = ((j16 >> 2) + 4 * hh) * VS + 16 * (g16 & 1) + 4 * (j16 & 3);
 
   // One key tile for this wave.
-  auto do_tile = [&](int tile, int buf) __attribute__((always_inline)) {
-    const int k0 = tile * BN;
+  bf16x8 pf[2][2];
+  auto qk = [&](int buf, f32x16* s_acc) __attribute__((always_inline)) {
     // S^T chain with the K operands read KPF steps ahead (fixed by fences:
     // left alone, the schedule waits on each read right before its MFMA;
     // 2 steps measured best against 1, 3 and 4).
     constexpr int KPF = 2;
-    f32x16 s_acc[2];
     const __bf16* kl = &lds_k[buf][k_lane_off];
     bf16x8 kf[NKS][2];
 #pragma unroll
@@ -229,6 +228,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto softmax = [&](int tile, f32x16* s_acc) __attribute__((always_inline)) {
+    const int k0 = tile * BN;
     // Mask only where the tile straddles the diagonal, the context end or a
     // window / sink edge: key k0 + r (r in [0, 64)) is visible iff r <= lim
     // and (no window, or r >= wlo, or r < slim).
@@ -271,7 +273,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     const float m_use = (m2 == -INFINITY) ? 0.f : m2;
     // P^T fragments: registers 8*half .. 8*half+7 of score block mb; the row
     // sum is taken in fp32 before rounding (two independent add chains).
-    bf16x8 pf[2][2];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -284,7 +285,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
           pf[mb][half][i] = (__bf16)e;
         }
     lsum += sum_halves(rs0 + rs1);
-
+  };
+  auto pv = [&](int buf) __attribute__((always_inline)) {
     const __bf16* vl = &lds_v[buf][v_lane_off];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -301,26 +303,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // Visited tile k is staged from register set k & 1 into LDS buffer k & 1;
-  // right after, tile k + 2 is loaded into the same register set, two tiles
-  // (about 2 us) ahead of its use.  The page of the next tile to load is read
-  // one load ahead.
+  // Tile k sits in register set k & 1 from two steps ahead and in LDS
+  // buffer k & 1 from one step ahead.  Step k: one barrier, S(k) from K
+  // buffer k & 1, then tile k + 1 is staged into buffer (k + 1) & 1 and tile
+  // k + 3 loaded into the freed set while the softmax of tile k runs, then
+  // O += P(k) V(k).  The barrier at the start of step k + 1 orders the
+  // staging before its reads; the buffer it overwrites held tile k - 1, read
+  // in step k - 1, before the barrier of step k.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   int next_page = 0;
   if (n_visit > 0) gload(S0{}, tile_of(0), tile_row(tile_of(0), tile_page(tile_of(0))));
   if (n_visit > 1) gload(S1{}, tile_of(1), tile_row(tile_of(1), tile_page(tile_of(1))));
   if (n_visit > 2) next_page = tile_page(tile_of(2));
-  auto step = [&](auto set_tag, int k) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-    swrite(set_tag);
+  if (n_visit > 0) swrite(S0{});
+  if (n_visit > 2) {
+    gload(S0{}, tile_of(2), tile_row(tile_of(2), next_page));
+    if (n_visit > 3) next_page = tile_page(tile_of(3));
+  }
+  auto step = [&](auto kb_tag, int k) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kb_tag)::value;    // buffer of tile k; tile k + 1 is in set 1 - KB
+    using SN = std::integral_constant<int, 1 - KB>;
     __syncthreads();
-    if (k + 2 < n_visit) {
-      gload(set_tag, tile_of(k + 2), tile_row(tile_of(k + 2), next_page));
-      if (k + 3 < n_visit) next_page = tile_page(tile_of(k + 3));
-    }
     const int tile = tile_of(k);
-    if (wave_sees(tile)) do_tile(tile, SET);
+    const bool sees = wave_sees(tile);
+    f32x16 s_acc[2];
+    if (sees) qk(KB, s_acc);
+    if (k + 1 < n_visit) swrite(SN{});
+    if (k + 3 < n_visit) {
+      gload(SN{}, tile_of(k + 3), tile_row(tile_of(k + 3), next_page));
+      if (k + 4 < n_visit) next_page = tile_page(tile_of(k + 4));
+    }
+    if (sees) {
+      softmax(tile, s_acc);
+      pv(KB);
+    }
   };
   for (int k = 0; k < n_visit; k += 2) {
     step(S0{}, k);
