@@ -14,9 +14,12 @@ scheduler  the profiler cost model, Appendix-B shard sizing and the
            communication-aware greedy placement of CA-tasks on servers.
 paging     attention over paged K/V (block tables): the virtual K/V a table
            describes, then the plain forward.
+ring       context-parallel ring planning: the pass-KV / pass-Q time model,
+           thresholds and switching rules, load-balanced sharding, the pass-KV
+           ring schedule and round-robin decode sharding.
 
 Parity status of every function is stated in its own docstring; all of them
-are pinned by ``tests/test_oracle_pins.py`` except where a docstring says
+are pinned by ``tests/test_*oracle_pins.py`` except where a docstring says
 "parity unpinned".
 """
 
