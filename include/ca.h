@@ -317,6 +317,87 @@ ca_status ca_sched_tasks(const ca_sched_item* items_host, int32_t n_items, const
                          int32_t n_docs, ca_task* tasks_host);
 
 /* ---------------------------------------------------------------------- */
+/* Context-parallel ring planning (host only; no device memory, no HIP)    */
+/* ---------------------------------------------------------------------- */
+/* "Context Parallelism for Scalable Million-Token Inference": the time model
+ * and switching rules of ring pass-KV / pass-Q (Section 3.4, Equations 1-3,
+ * Algorithm 1; Appendix C, Algorithm 5, Equation 5), load-balanced sharding
+ * (Section 3.5.1), the pass-KV ring schedule (Section 3.5.2) and round-robin
+ * decode sharding (Section 3.6).  Units: FLOPs = 4 T D (T + P); compute in
+ * FLOP/s per rank; bandwidth in bytes/s per rank (ring SendRecv); seconds. */
+typedef struct {
+  int32_t n_ranks;         /* N (>= 1)                                                */
+  int32_t n_heads;         /* N_H query heads (>= 1)                                  */
+  int32_t n_kv_heads;      /* N_KV key/value heads (>= 1)                             */
+  int32_t elem_bytes;      /* e, bytes per element of Q / K / V / O on the wire (>= 1) */
+  double d_model;          /* D, model dimension (> 0)                                */
+  double compute;          /* C, attention FLOP/s per rank (> 0)                      */
+  double bandwidth;        /* BW, SendRecv bytes/s per rank (> 0)                     */
+} ca_ring_model;
+
+typedef struct {
+  double attn_step;        /* 4 T D (T + P) / (N C): one ring step's attention        */
+  double sendrecv_kv;      /* 2 (T + P) D e N_KV / (N_H BW): one pass-KV message      */
+  double sendrecv_q;       /* T D e / BW: one pass-Q message                          */
+  double all2all;          /* (N - 1)(D + 1) T e / BW: pass-Q's return of partials    */
+  double exposed_kv;       /* (N - 1)(sendrecv_kv - attn_step), may be negative       */
+  double miss_threshold;   /* Equation 1: 2 N_KV / N_H                                */
+  double t_threshold;      /* Equation 2: N C N_KV e / (2 N_H BW)                      */
+  double ctx_threshold;    /* Equation 3: N e C / (4 BW)                               */
+  double eq5_rhs;          /* Equation 5: 2 N_KV / N_H - 4 T BW / (N C e)              */
+} ca_ring_times;
+
+enum { CA_RING_PASS_KV = 0, CA_RING_PASS_Q = 1 };
+
+/* Every term of the model at (T new tokens, P cached tokens); T, P >= 0.
+ * Errors: CA_ERR_INVALID for a bad model or NULL output. */
+ca_status ca_ring_plan(const ca_ring_model* m, int64_t T, int64_t P, ca_ring_times* out);
+
+/* pass-KV (0) or pass-Q (1) for T >= 1 new tokens over P >= 0 cached ones.
+ * refined = 0: Algorithm 1 (pass-KV iff T >= t_threshold or T/(T+P) >=
+ * miss_threshold).  refined = 1: Algorithm 5 (pass-KV iff T >= t_threshold,
+ * else pass-Q iff exposed_kv >= all2all).  -1 on invalid arguments. */
+int32_t ca_ring_select(const ca_ring_model* m, int64_t T, int64_t P, int32_t refined);
+
+/* The same choice from measured per-step times (seconds, >= 0): each ring
+ * exposes (N - 1) max(0, SendRecv - ATTN), pass-Q adds its All2All; pass-Q iff
+ * strictly less exposed.  Writes both exposed times when the pointers are not
+ * NULL.  -1 on invalid arguments. */
+int32_t ca_ring_select_measured(int32_t n_ranks, double sendrecv_kv, double sendrecv_q, double attn,
+                                double all2all, double* exposed_kv, double* exposed_q);
+
+typedef struct {
+  int32_t rank;            /* owning rank, 0..N-1                                      */
+  int32_t seq;             /* sequence index                                           */
+  int64_t begin, end;      /* token positions [begin, end) of the sequence, may be empty */
+} ca_ring_chunk;           /* 24 bytes                                                 */
+
+/* Load-balanced sharding of n_seqs sequences (lengths >= 0) over N ranks:
+ * 2N chunks of ceil(L / 2N) positions per sequence, clipped at L; chunk k
+ * belongs to rank k (k < N) or 2N - 1 - k.  Writes n_seqs * 2N chunks in
+ * (sequence, k) order into caller-owned host memory. */
+ca_status ca_ring_shard(int32_t n_ranks, const int64_t* lens_host, int32_t n_seqs, ca_ring_chunk* chunks_host);
+
+/* Upper bound of the task count of one pass-KV step (-1 if invalid). */
+int32_t ca_ring_kv_step_max_tasks(int32_t n_ranks, int32_t n_seqs);
+
+/* CA-task records of pass-KV step `step` (0..N-1), slot 0 or 1, for the
+ * full prefill of n_seqs packed sequences (Q, K, V, O rows back to back in
+ * sequence order): every rank r's two query chunks of every sequence against
+ * chunk (slot 0: src, slot 1: 2N - 1 - src) of rank src = (r - step) mod N,
+ * with in-sequence positions as q_pos0 / kv_pos0.  Every non-empty query
+ * chunk appears exactly once per (step, slot), so the 2N launches (fp32
+ * partial outputs) merged by ca_merge give the causal attention of every
+ * sequence.  Errors: CA_ERR_INVALID; CA_ERR_WORKSPACE when more than
+ * max_tasks records are needed (*n_tasks then holds the bound). */
+ca_status ca_ring_kv_step_tasks(int32_t n_ranks, int32_t step, int32_t slot, const int64_t* lens_host,
+                                int32_t n_seqs, ca_task* tasks_host, int32_t max_tasks, int32_t* n_tasks);
+
+/* Rank that stores the decode token of batch entry seq at decode iteration
+ * `iteration`: (seq + iteration) mod N.  -1 on invalid arguments. */
+int32_t ca_ring_decode_rank(int32_t n_ranks, int64_t iteration, int32_t seq);
+
+/* ---------------------------------------------------------------------- */
 /* Accounting and errors                                                   */
 /* ---------------------------------------------------------------------- */
 

@@ -44,6 +44,13 @@ EXPORTS = (
     "ca_schedule_max_items",
     "ca_schedule",
     "ca_sched_tasks",
+    "ca_ring_plan",
+    "ca_ring_select",
+    "ca_ring_select_measured",
+    "ca_ring_shard",
+    "ca_ring_kv_step_max_tasks",
+    "ca_ring_kv_step_tasks",
+    "ca_ring_decode_rank",
     "ca_status_string",
     "ca_last_error",
 )
@@ -84,6 +91,23 @@ class SchedParams(ctypes.Structure):
                 ("eps", ctypes.c_double), ("e_min", ctypes.c_double), ("min_shard", ctypes.c_int64),
                 ("max_moves", ctypes.c_int32), ("head_tail", ctypes.c_int32), ("flops_per_pair", ctypes.c_double)]
 
+
+class RingModel(ctypes.Structure):
+    _fields_ = [("n_ranks", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32), ("d_model", ctypes.c_double), ("compute", ctypes.c_double),
+                ("bandwidth", ctypes.c_double)]
+
+
+class RingTimes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in ("attn_step", "sendrecv_kv", "sendrecv_q", "all2all", "exposed_kv",
+                                               "miss_threshold", "t_threshold", "ctx_threshold", "eq5_rhs")]
+
+
+RING_PASS_KV, RING_PASS_Q = 0, 1
+
+# numpy view of the C struct ca_ring_chunk (24 bytes)
+RING_CHUNK_DTYPE = np.dtype([("rank", "<i4"), ("seq", "<i4"), ("begin", "<i8"), ("end", "<i8")])
+assert RING_CHUNK_DTYPE.itemsize == 24
 
 # numpy view of the C struct ca_sched_item (24 bytes)
 SCHED_ITEM_DTYPE = np.dtype([("server", "<i4"), ("doc", "<i4"), ("q_begin", "<i8"), ("q_end", "<i8")])
@@ -153,6 +177,20 @@ def lib():
         L.ca_schedule.restype = ctypes.c_int
         L.ca_sched_tasks.argtypes = [vp, i32, vp, i32, vp]
         L.ca_sched_tasks.restype = ctypes.c_int
+        L.ca_ring_plan.argtypes = [ctypes.POINTER(RingModel), i64, i64, ctypes.POINTER(RingTimes)]
+        L.ca_ring_plan.restype = ctypes.c_int
+        L.ca_ring_select.argtypes = [ctypes.POINTER(RingModel), i64, i64, i32]
+        L.ca_ring_select.restype = i32
+        L.ca_ring_select_measured.argtypes = [i32, dbl, dbl, dbl, dbl, vp, vp]
+        L.ca_ring_select_measured.restype = i32
+        L.ca_ring_shard.argtypes = [i32, vp, i32, vp]
+        L.ca_ring_shard.restype = ctypes.c_int
+        L.ca_ring_kv_step_max_tasks.argtypes = [i32, i32]
+        L.ca_ring_kv_step_max_tasks.restype = i32
+        L.ca_ring_kv_step_tasks.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp]
+        L.ca_ring_kv_step_tasks.restype = ctypes.c_int
+        L.ca_ring_decode_rank.argtypes = [i32, i64, i32]
+        L.ca_ring_decode_rank.restype = i32
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
         L.ca_last_error.argtypes = []
@@ -383,3 +421,63 @@ def sched_tasks(items, doc_lens):
     out = np.zeros(len(it), dtype=TASK_DTYPE)
     _check(lib().ca_sched_tasks(it.ctypes.data, len(it), docs.ctypes.data, len(docs), out.ctypes.data))
     return out
+
+
+def ring_model(n_ranks, n_heads, n_kv_heads, elem_bytes, d_model, compute, bandwidth):
+    """ca_ring_model: N ranks, N_H / N_KV heads, e bytes per element, D model
+    dimension, C attention FLOP/s per rank, BW SendRecv bytes/s per rank."""
+    return RingModel(int(n_ranks), int(n_heads), int(n_kv_heads), int(elem_bytes), float(d_model),
+                     float(compute), float(bandwidth))
+
+
+def ring_plan(model, T, P):
+    """Every term of the ring time model at (T, P), as a dict."""
+    out = RingTimes()
+    _check(lib().ca_ring_plan(ctypes.byref(model), int(T), int(P), ctypes.byref(out)))
+    return {n: getattr(out, n) for n, _ in RingTimes._fields_}
+
+
+def ring_select(model, T, P, refined=True):
+    """RING_PASS_KV or RING_PASS_Q (Algorithm 5 when refined, else Algorithm 1)."""
+    r = lib().ca_ring_select(ctypes.byref(model), int(T), int(P), 1 if refined else 0)
+    if r < 0:
+        raise CAError(CA_ERR_INVALID, lib().ca_last_error().decode())
+    return r
+
+
+def ring_select_measured(n_ranks, sendrecv_kv, sendrecv_q, attn, all2all):
+    """(choice, exposed pass-KV seconds, exposed pass-Q seconds) from measured per-step times."""
+    k, q = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    r = lib().ca_ring_select_measured(int(n_ranks), float(sendrecv_kv), float(sendrecv_q), float(attn),
+                                      float(all2all), ctypes.byref(k), ctypes.byref(q))
+    if r < 0:
+        raise CAError(CA_ERR_INVALID, lib().ca_last_error().decode())
+    return r, k.value, q.value
+
+
+def ring_shard(lens, n_ranks):
+    """Load-balanced chunks (RING_CHUNK_DTYPE records, (sequence, chunk) order)."""
+    ls = np.ascontiguousarray(np.asarray(lens, dtype=np.int64))
+    out = np.zeros(max(1, len(ls) * 2 * int(n_ranks)), dtype=RING_CHUNK_DTYPE)
+    _check(lib().ca_ring_shard(int(n_ranks), ls.ctypes.data, len(ls), out.ctypes.data))
+    return out[:len(ls) * 2 * int(n_ranks)]
+
+
+def ring_kv_step_tasks(lens, n_ranks, step, slot):
+    """ca_task records of pass-KV step `step`, slot 0 / 1, over packed sequences."""
+    ls = np.ascontiguousarray(np.asarray(lens, dtype=np.int64))
+    cap = lib().ca_ring_kv_step_max_tasks(int(n_ranks), len(ls))
+    if cap < 0:
+        raise CAError(CA_ERR_INVALID, "bad ring size")
+    out = np.zeros(max(cap, 1), dtype=TASK_DTYPE)
+    n = ctypes.c_int32(0)
+    _check(lib().ca_ring_kv_step_tasks(int(n_ranks), int(step), int(slot), ls.ctypes.data, len(ls),
+                                       out.ctypes.data, len(out), ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def ring_decode_rank(n_ranks, iteration, seq):
+    r = lib().ca_ring_decode_rank(int(n_ranks), int(iteration), int(seq))
+    if r < 0:
+        raise CAError(CA_ERR_INVALID, lib().ca_last_error().decode())
+    return r
