@@ -180,8 +180,78 @@ def secondary(steps=3, warmup=1):
                                     "merge_gbs": round(mb / ms_m / 1e6, 1)}
     log("ring prefill: partials %.2f ms (%.1f TFLOP/s), merge %.3f ms (%.0f GB/s)"
         % (ms_f, fl / ms_f / 1e9, ms_m, mb / ms_m / 1e6))
-    del Q, K, V, O, LSE, ws, Om, Lm
+    del Q, K, V, O, LSE, ws
     torch.cuda.empty_cache()
+
+    # The same 128K document under load-balanced sharding (16 chunks of 8192,
+    # rank i holding chunks i and 15 - i) and the pass-KV ring over 8 ranks:
+    # each of the 8 steps x 2 source chunks is one launch fusing all ranks'
+    # shares into one fp32 partial slot; then the 16-way merge.
+    N_r, total = 8, w.merged_rows
+    hq, hkv, d = w.hq, w.hkv, w.d
+    lens = [total]
+    Q = I.randn_bf16((total, hq, d), 204, device=dev)
+    K = I.randn_bf16((total, hkv, d), 205, device=dev)
+    V = I.randn_bf16((total, hkv, d), 206, device=dev)
+    n_slots = 2 * N_r
+    Op = torch.empty((n_slots, total, hq, d), device=dev)
+    Lp = torch.empty((n_slots, total, hq), device=dev)
+    rshape = ca.make_shape(hq, hkv, d, total, total, total, out_f32=True)
+    step_tasks = [ca.ring_kv_step_tasks(lens, N_r, st, sl) for st in range(N_r) for sl in (0, 1)]
+    step_ws = [ca.workspace_tensor(ca.forward_workspace(rshape, t), dev) for t in step_tasks]
+
+    def ring_lb():
+        for k, t in enumerate(step_tasks):
+            ca.forward(rshape, t, Q, K, V, Op[k], Lp[k], ws=step_ws[k], stream=stream)
+
+    ms_lb = timed(ring_lb, steps, warmup, stream)
+    fl_lb = oracle.forward_flops(sum(ca.visible_pairs(t) for t in step_tasks), hq, d)
+    ms_lbm = timed(lambda: ca.merge(mshape, Op, Lp, Om, Lm, stream=stream), steps, warmup, stream)
+    # merge bytes: O of every partial row with a visible key (the others carry
+    # LSE = -inf and are not read), all partial LSEs, merged O (bf16) + LSE
+    live = sum(max(0, int(r["q_len"]) - max(0, int(r["kv_pos0"]) - int(r["q_pos0"])))
+               for t in step_tasks for r in t if int(r["kv_len"]) > 0)
+    mb_lb = live * hq * d * 4 + n_slots * total * hq * 4 + total * hq * (d * 2 + 4)
+    # visible pairs of each rank at each ring step (tasks come rank by rank, two per rank)
+    rank_step = np.zeros((N_r, N_r), dtype=np.int64)
+    for k, t in enumerate(step_tasks):
+        for i in range(len(t)):
+            rank_step[i // 2, k // 2] += ca.visible_pairs(t[i:i + 1])
+    per_rank = rank_step.sum(axis=1)
+    out["ring_prefill_405b_tp8_load_balanced"] = {
+        "workload": "llama3-405b-tp8-ring-prefill-128k, load-balanced 16 chunks, pass-KV over 8 ranks",
+        "partials_ms": round(ms_lb, 3), "partials_tflops": round(fl_lb / ms_lb / 1e9, 1),
+        "merge_ms": round(ms_lbm, 3), "merge_bytes": mb_lb, "merge_gbs": round(mb_lb / ms_lbm / 1e6, 1),
+        "rank_pairs_max_over_mean": round(float(per_rank.max() / per_rank.mean()), 4),
+        "rank_step_pairs_max_over_mean_worst_step": round(float(max(
+            rank_step[:, j].max() / rank_step[:, j].mean() for j in range(N_r))), 4)}
+    log("ring prefill, load-balanced pass-KV: partials %.2f ms (%.1f TFLOP/s), merge %.3f ms (%.0f GB/s), "
+        "rank pairs max/mean %.4f" % (ms_lb, fl_lb / ms_lb / 1e9, ms_lbm, mb_lb / ms_lbm / 1e6,
+                                      per_rank.max() / per_rank.mean()))
+    del Q, K, V, Op, Lp, Om, Lm, step_ws
+    torch.cuda.empty_cache()
+
+    # pass-KV / pass-Q choice for Llama3-405B under TP8 on MI355X ranks: C is
+    # the attention rate just measured, BW one xGMI link (153 GB/s), bf16 on
+    # the wire; the miss rates of the pages' 128K sweep
+    C = fl / ms_f * 1e3
+    sel = {}
+    for N_sel in (4, 8):
+        m = ca.ring_model(N_sel, 16, 1, 2, 16 * 128, C, 153e9)
+        plan = ca.ring_plan(m, 1, 0)
+        pts = []
+        for T_new in (1280, 3200, 4160, 6400, 12800, 25600, 64000, 128000):
+            P_c = 128000 - T_new
+            pts.append({"T": T_new, "P": P_c,
+                        "algorithm1": "pass-KV" if ca.ring_select(m, T_new, P_c, refined=False) == 0 else "pass-Q",
+                        "algorithm5": "pass-KV" if ca.ring_select(m, T_new, P_c, refined=True) == 0 else "pass-Q"})
+        sel["N=%d" % N_sel] = {"t_threshold_eq2": round(plan["t_threshold"], 1),
+                               "ctx_threshold_eq3": round(plan["ctx_threshold"], 1),
+                               "miss_threshold_eq1": plan["miss_threshold"], "points": pts}
+    out["ring_select_405b_tp8_mi355x"] = {"compute_flops": round(C, -9), "bandwidth_bytes": 153e9, "by_ranks": sel}
+    log("ring select (C = %.3g FLOP/s, BW = 153 GB/s): Eq.2 T >= %.0f at N=8; Algorithm 5 at N=8: %s"
+        % (C, sel["N=8"]["t_threshold_eq2"], " ".join("%d:%s" % (p_["T"], p_["algorithm5"][5:])
+                                                       for p_ in sel["N=8"]["points"])))
 
     # Pass-Q decode share: 32 tokens x 128K caches, 8 stationary blocks, merge
     w = I.ring_decode_405b_tp8()
