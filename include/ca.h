@@ -244,6 +244,32 @@ ca_status ca_backward_paged(const ca_shape* shape, const ca_task* tasks_host, co
                             void* dV, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* Prepared forward: plan once, launch many times (HIP graph capture)      */
+/* ---------------------------------------------------------------------- */
+/* The decode step of "Context Parallelism for Scalable Million-Token
+ * Inference" (Section 3.6) runs under captured graphs to avoid host launch
+ * overhead.  ca_forward_prepare does a forward call's host work once: it
+ * validates, builds the work queue and uploads it into ws (async on the
+ * stream, not capturable), and fills *plan (host memory owned by the caller;
+ * contents private).  ca_forward_prepared then only launches kernels (no
+ * host planning, no copies, no allocation), reading the queue from the ws
+ * the plan was made with, so it can be captured into a HIP graph and
+ * replayed; Q, K, V, O and LSE may differ from call to call but must have the
+ * shape and task table the plan was made for.  The caller keeps ws unchanged
+ * while the plan is in use.  ws_bytes as for the direct call (ca_forward /
+ * _masked / _paged _workspace).  Errors as for the direct call; the launch
+ * rejects a plan that ca_forward_prepare did not fill. */
+typedef struct {
+  uint64_t opaque[40];
+} ca_forward_plan;
+
+ca_status ca_forward_prepare(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                             int32_t n_tasks, const ca_kv_pages* pages, void* ws, size_t ws_bytes, void* stream,
+                             ca_forward_plan* plan);
+ca_status ca_forward_prepared(const ca_forward_plan* plan, const void* Q, const void* K, const void* V, void* O,
+                              float* LSE, void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* CA-task scheduling (host only; no device memory, no HIP calls)          */
 /* ---------------------------------------------------------------------- */
 /* The profiler cost model and the communication-aware greedy scheduler of

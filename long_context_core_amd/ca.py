@@ -36,6 +36,8 @@ EXPORTS = (
     "ca_forward_masked",
     "ca_forward_paged_workspace",
     "ca_forward_paged",
+    "ca_forward_prepare",
+    "ca_forward_prepared",
     "ca_backward_masked_workspace",
     "ca_backward_masked",
     "ca_backward_paged_workspace",
@@ -90,6 +92,11 @@ class SchedParams(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("e_min", ctypes.c_double), ("min_shard", ctypes.c_int64),
                 ("max_moves", ctypes.c_int32), ("head_tail", ctypes.c_int32), ("flops_per_pair", ctypes.c_double)]
+
+
+class ForwardPlan(ctypes.Structure):
+    """ca_forward_plan: filled by forward_prepare, read by forward_prepared."""
+    _fields_ = [("opaque", ctypes.c_uint64 * 40)]
 
 
 class RingModel(ctypes.Structure):
@@ -191,6 +198,10 @@ def lib():
         L.ca_ring_kv_step_tasks.restype = ctypes.c_int
         L.ca_ring_decode_rank.argtypes = [i32, i64, i32]
         L.ca_ring_decode_rank.restype = i32
+        L.ca_forward_prepare.argtypes = [sp, vp, vp, i32, vp, vp, sz, vp, ctypes.POINTER(ForwardPlan)]
+        L.ca_forward_prepare.restype = ctypes.c_int
+        L.ca_forward_prepared.argtypes = [ctypes.POINTER(ForwardPlan), vp, vp, vp, vp, vp, vp]
+        L.ca_forward_prepared.restype = ctypes.c_int
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
         L.ca_last_error.argtypes = []
@@ -317,6 +328,24 @@ def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None, pag
                                      _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(),
                                      _stream_ptr(stream))
     _check(st)
+    return O, LSE
+
+
+def forward_prepare(shape, tasks, ws, stream=None, masks=None, pages=None):
+    """ca_forward_prepare: the call's host work once (queue built and uploaded
+    into ws on the stream); returns the plan for forward_prepared."""
+    ta, ma = split_tasks(tasks, masks)
+    plan = ForwardPlan()
+    _check(lib().ca_forward_prepare(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
+                                    ctypes.byref(pages) if pages is not None else None, _ptr(ws), ws.numel(),
+                                    _stream_ptr(stream), ctypes.byref(plan)))
+    return plan
+
+
+def forward_prepared(plan, Q, K, V, O, LSE, stream=None):
+    """ca_forward_prepared: kernel launches only (capturable in a HIP graph)."""
+    _check(lib().ca_forward_prepared(ctypes.byref(plan), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE),
+                                     _stream_ptr(stream)))
     return O, LSE
 
 

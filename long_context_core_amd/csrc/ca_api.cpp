@@ -411,14 +411,39 @@ void build_decode_items(const ca_shape* s, const ca_task* t, const ca_task_mask*
   });
 }
 
-ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
-                       const ca_kv_pages* pg, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                       void* ws, size_t ws_bytes, void* stream) {
+// Everything a forward call needs at launch time once its work queue is in
+// the workspace: the shape, the queue layout and counts.  Plain data, so it
+// can live in the caller's ca_forward_plan.
+struct PreparedFwd {
+  uint64_t magic;
+  void* ws;
+  ca_shape shape;
+  int32_t group, hpw;
+  int32_t n_items, n_dec_items, n_split;
+  int32_t has_masks, has_pages, page_shift;
+  uint32_t page_bytes;
+  uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_part_o, off_part_l;
+};
+constexpr uint64_t kPlanMagic = 0x43414657504c414eull;   // plan tag, checked at launch
+static_assert(sizeof(PreparedFwd) <= sizeof(ca_forward_plan), "ca_forward_plan too small");
+
+// Validates, plans, builds the queue and uploads it into ws on the stream.
+// With tensors given (a direct call) they are checked before the upload, so
+// a rejected call changes nothing.
+ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                          const ca_kv_pages* pg, void* ws, size_t ws_bytes, void* stream, PreparedFwd& pf,
+                          const void* const* tensors = nullptr) {
   ca_status st = check_forward_args(s, t, m, n, pg);
   if (st != CA_OK) return st;
   const FwdPlan p = plan_forward(s, t, m, n, pg);
+  std::memset(&pf, 0, sizeof(pf));
+  pf.magic = kPlanMagic;
+  pf.ws = ws;
+  pf.shape = *s;
   if (p.n_items == 0 && p.n_dec_items == 0) return CA_OK;
-  if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
+  if (tensors)
+    for (int i = 0; i < 5; ++i)
+      if (!tensors[i]) return fail(CA_ERR_INVALID, "NULL tensor pointer");
   if (!ws || ws_bytes < p.bytes)
     return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
   if (p.n_items > 0x7fffffffu || p.n_dec_items > 0x7fffffffu || p.n_parts > 0x7fffffffu)
@@ -436,81 +461,116 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
   if (!items.empty()) std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
   if (!ditems.empty()) std::memcpy(host.data() + p.off_dec, ditems.data(), sizeof(ca::DecItem) * ditems.size());
   if (!split.empty()) std::memcpy(host.data() + p.off_split, split.data(), sizeof(int32_t) * split.size());
-  hipStream_t hs = (hipStream_t)stream;
-  st = upload(ws, host, hs);
+  st = upload(ws, host, (hipStream_t)stream);
   if (st != CA_OK) return st;
-  char* w = (char*)ws;
+  pf.group = p.group;
+  pf.hpw = p.hpw;
+  pf.n_items = (int32_t)items.size();
+  pf.n_dec_items = (int32_t)ditems.size();
+  pf.n_split = (int32_t)p.n_split;
+  pf.has_masks = m ? 1 : 0;
+  pf.has_pages = pg ? 1 : 0;
+  pf.page_shift = pg ? page_shift_of(pg) : 0;
+  pf.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
+  pf.off_tasks = p.off_tasks;
+  pf.off_masks = p.off_masks;
+  pf.off_pages = p.off_pages;
+  pf.off_items = p.off_items;
+  pf.off_dec = p.off_dec;
+  pf.off_split = p.off_split;
+  pf.off_part_o = p.off_part_o;
+  pf.off_part_l = p.off_part_l;
+  return CA_OK;
+}
+
+// Kernel launches only: no host planning, no copies, no allocation.
+ca_status launch_prepared_forward(const PreparedFwd& pf, const void* Q, const void* K, const void* V, void* O,
+                                  float* LSE, void* stream) {
+  if (pf.n_items == 0 && pf.n_dec_items == 0) return CA_OK;
+  if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
+  const ca_shape* s = &pf.shape;
+  hipStream_t hs = (hipStream_t)stream;
+  char* w = (char*)pf.ws;
   const float scale_log2 = s->scale * 1.4426950408889634f;
   const int out_f32 = (s->flags & CA_OUT_F32) ? 1 : 0;
-  const int32_t* pages = pg ? (const int32_t*)(w + p.off_pages) : nullptr;
-  const int page_shift = pg ? page_shift_of(pg) : 0;
-  if (!items.empty()) {
+  const int32_t* pages = pf.has_pages ? (const int32_t*)(w + pf.off_pages) : nullptr;
+  if (pf.n_items > 0) {
     ca::FwdParams fp;
     fp.Q = (const __bf16*)Q;
     fp.K = (const __bf16*)K;
     fp.V = (const __bf16*)V;
     fp.O = O;
     fp.LSE = LSE;
-    fp.tasks = (const ca_task*)(w + p.off_tasks);
-    fp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
-    fp.items = (const ca::FwdItem*)(w + p.off_items);
+    fp.tasks = (const ca_task*)(w + pf.off_tasks);
+    fp.masks = pf.has_masks ? (const ca_task_mask*)(w + pf.off_masks) : nullptr;
+    fp.items = (const ca::FwdItem*)(w + pf.off_items);
     fp.pages = pages;
-    fp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
-    fp.page_shift = page_shift;
-    fp.n_items = (int32_t)items.size();
+    fp.page_bytes = pf.page_bytes;
+    fp.page_shift = pf.page_shift;
+    fp.n_items = pf.n_items;
     fp.hq = s->hq;
     fp.hkv = s->hkv;
-    fp.group = p.group;
-    fp.hpw = p.hpw;
+    fp.group = pf.group;
+    fp.hpw = pf.hpw;
     fp.scale_log2 = scale_log2;
     fp.out_f32 = out_f32;
     fp.waves = kFwdWaves;
     hipError_t e = ca::launch_forward(fp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
   }
-  if (!ditems.empty()) {
+  if (pf.n_dec_items > 0) {
     ca::DecParams dp;
     dp.Q = (const __bf16*)Q;
     dp.K = (const __bf16*)K;
     dp.V = (const __bf16*)V;
     dp.O = O;
     dp.LSE = LSE;
-    dp.part_O = (float*)(w + p.off_part_o);
-    dp.part_LSE = (float*)(w + p.off_part_l);
-    dp.tasks = (const ca_task*)(w + p.off_tasks);
-    dp.items = (const ca::DecItem*)(w + p.off_dec);
+    dp.part_O = (float*)(w + pf.off_part_o);
+    dp.part_LSE = (float*)(w + pf.off_part_l);
+    dp.tasks = (const ca_task*)(w + pf.off_tasks);
+    dp.items = (const ca::DecItem*)(w + pf.off_dec);
     dp.pages = pages;
-    dp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
-    dp.page_shift = page_shift;
-    dp.n_items = (int32_t)ditems.size();
+    dp.page_bytes = pf.page_bytes;
+    dp.page_shift = pf.page_shift;
+    dp.n_items = pf.n_dec_items;
     dp.hq = s->hq;
     dp.hkv = s->hkv;
-    dp.group = p.group;
+    dp.group = pf.group;
     dp.scale_log2 = scale_log2;
     dp.out_f32 = out_f32;
     hipError_t e = ca::launch_decode(dp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-    if (p.n_split > 0) {
+    if (pf.n_split > 0) {
       ca::DecMergeParams mp;
-      const int32_t* sp = (const int32_t*)(w + p.off_split);
+      const int32_t* sp = (const int32_t*)(w + pf.off_split);
       mp.part_O = dp.part_O;
       mp.part_LSE = dp.part_LSE;
       mp.first_part = sp;
-      mp.n_parts = sp + p.n_split;
-      mp.task_of = sp + 2 * p.n_split;
-      mp.head_of = sp + 3 * p.n_split;
+      mp.n_parts = sp + pf.n_split;
+      mp.task_of = sp + 2 * pf.n_split;
+      mp.head_of = sp + 3 * pf.n_split;
       mp.tasks = dp.tasks;
       mp.O = O;
       mp.LSE = LSE;
-      mp.n_split = (int32_t)p.n_split;
+      mp.n_split = pf.n_split;
       mp.hq = s->hq;
-      mp.group = p.group;
+      mp.group = pf.group;
       mp.out_f32 = out_f32;
       e = ca::launch_decode_merge(mp, s->d, hs);
       if (e != hipSuccess) return hip_fail(e, "decode merge launch");
     }
   }
   return CA_OK;
+}
+
+ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                       const ca_kv_pages* pg, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       void* ws, size_t ws_bytes, void* stream) {
+  PreparedFwd pf;
+  const void* tensors[5] = {Q, K, V, O, LSE};
+  const ca_status st = prepare_forward(s, t, m, n, pg, ws, ws_bytes, stream, pf, tensors);
+  if (st != CA_OK) return st;
+  return launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -869,6 +929,27 @@ ca_status ca_forward_paged(const ca_shape* shape, const ca_task* tasks_host, con
                            void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
   if (!pages) return fail(CA_ERR_INVALID, "pages is NULL");
   return forward_impl(shape, tasks_host, masks_host, n_tasks, pages, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+ca_status ca_forward_prepare(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                             int32_t n_tasks, const ca_kv_pages* pages, void* ws, size_t ws_bytes, void* stream,
+                             ca_forward_plan* plan) {
+  if (!plan) return fail(CA_ERR_INVALID, "plan is NULL");
+  PreparedFwd pf;
+  const ca_status st = prepare_forward(shape, tasks_host, masks_host, n_tasks, pages, ws, ws_bytes, stream, pf);
+  std::memset(plan, 0, sizeof(*plan));
+  if (st != CA_OK) return st;
+  std::memcpy(plan, &pf, sizeof(pf));
+  return CA_OK;
+}
+
+ca_status ca_forward_prepared(const ca_forward_plan* plan, const void* Q, const void* K, const void* V, void* O,
+                              float* LSE, void* stream) {
+  if (!plan) return fail(CA_ERR_INVALID, "plan is NULL");
+  PreparedFwd pf;
+  std::memcpy(&pf, plan, sizeof(pf));
+  if (pf.magic != kPlanMagic) return fail(CA_ERR_INVALID, "plan was not filled by ca_forward_prepare");
+  return launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
 }
 
 size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu, int32_t n_docs) {

@@ -1,0 +1,104 @@
+"""Prepared forward calls captured in a HIP graph (the captured decode step of
+"Context Parallelism for Scalable Million-Token Inference", Section 3.6):
+ca_forward_prepare once, then ca_forward_prepared (+ ca_merge) recorded by
+torch's graph capture.  Each replay follows eager work that changes Q and
+runs the direct calls; every replay must equal the direct calls bit for bit,
+and the last one the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_core_amd import ca
+from long_context_core_amd import inputs as I
+from tests.gpu_util import announce, check_forward, torch_cuda, widen
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D = 16, 1, 128
+
+
+def decode_blocks(B, ctx, n):
+    """B single-token queries, each over its own ctx-entry cache in n
+    stationary blocks; block s writes partial slot s."""
+    S = ctx // n
+    t = [(b, b * ctx + s * S, s * B + b, 1, S, ctx - 1, s * S) for b in range(B) for s in range(n)]
+    return np.array(t, dtype=np.int64)
+
+
+def decode_whole(B, ctx):
+    return np.array([(b, b * ctx, b, 1, ctx, ctx - 1, 0) for b in range(B)], dtype=np.int64)
+
+
+CASES = {
+    # name: (tasks, q_rows, kv_rows, o_rows, n_parts merged after the call)
+    "decode-4-blocks-merged": (decode_blocks(8, 16384, 4), 8, 8 * 16384, 4 * 8, 4),
+    "decode-whole-cache": (decode_whole(8, 20000), 8, 8 * 20000, 8, 0),
+    "prefill-causal-docs": (I.varlen_tasks([700, 128, 1, 1500]), 2329, 2329, 2329, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_graph_replays_equal_direct_calls(name):
+    announce("graph-captured prepared forward: %s" % name)
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    tasks, q_rows, kv_rows, o_rows, n_parts = CASES[name]
+    merged = n_parts > 0
+    shape = ca.make_shape(HQ, HKV, D, q_rows, kv_rows, o_rows, out_f32=merged)
+    K = I.randn_bf16((kv_rows, HKV, D), 2701, device=dev)
+    V = I.randn_bf16((kv_rows, HKV, D), 2702, device=dev)
+    Q = I.randn_bf16((q_rows, HQ, D), 2700, device=dev)
+    odt = torch.float32 if merged else torch.bfloat16
+    O = torch.empty((o_rows, HQ, D), dtype=odt, device=dev)
+    LSE = torch.empty((o_rows, HQ), device=dev)
+    O2, LSE2 = torch.empty_like(O), torch.empty_like(LSE)
+    if merged:
+        B = o_rows // n_parts
+        mshape = ca.make_shape(HQ, HKV, D, B, B, B)
+        Om = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
+        Lm = torch.empty((B, HQ), device=dev)
+        Om2, Lm2 = torch.empty_like(Om), torch.empty_like(Lm)
+    ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+    ws2 = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+    side = torch.cuda.Stream()
+    plan = ca.forward_prepare(shape, tasks, ws, stream=side)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        ca.forward_prepared(plan, Q, K, V, O, LSE, stream=st)
+        if merged:
+            ca.merge(mshape, O.view(n_parts, B, HQ, D), LSE.view(n_parts, B, HQ), Om, Lm, stream=st)
+    for rep in range(4):
+        Q.copy_(I.randn_bf16((q_rows, HQ, D), 2710 + rep, device=dev))
+        ca.forward(shape, tasks, Q, K, V, O2, LSE2, ws=ws2)
+        if merged:
+            ca.merge(mshape, O2.view(n_parts, B, HQ, D), LSE2.view(n_parts, B, HQ), Om2, Lm2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l, ref_o, ref_l = (Om, Lm, Om2, Lm2) if merged else (O, LSE, O2, LSE2)
+        same = torch.equal(got_o.view(torch.int16) if got_o.dtype == torch.bfloat16 else got_o,
+                           ref_o.view(torch.int16) if ref_o.dtype == torch.bfloat16 else ref_o)
+        print("%s replay %d: identical to the direct calls: %s" % (name, rep, same), flush=True)
+        assert same and torch.equal(got_l, ref_l)
+    # the last replay against the oracle
+    if merged:
+        whole = np.array([(b, b * (kv_rows // B), b, 1, kv_rows // B, kv_rows // B - 1, 0) for b in range(B)],
+                         dtype=np.int64)
+        O_ref, L_ref = oracle.forward(whole, widen(Q), widen(K), widen(V), 1 / math.sqrt(D))
+        check_forward(Om, Lm, O_ref, L_ref, name)
+    else:
+        O_ref, L_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(D))
+        check_forward(O, LSE, O_ref, L_ref, name)
+
+
+def test_prepared_call_rejects_a_foreign_plan():
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    with pytest.raises(ca.CAError):
+        t = torch.zeros(16, device=dev)
+        ca.forward_prepared(ca.ForwardPlan(), t, t, t, t, t)
