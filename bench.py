@@ -266,7 +266,7 @@ def secondary(steps=3, warmup=1):
         ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
         ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream)
 
-    ms = timed(dec_step, max(steps, 10), warmup, stream)
+    ms = ms_dec = timed(dec_step, max(steps, 10), warmup, stream)
     kv_bytes = 2 * w.kv_rows * w.hkv * w.d * 2
     out["ring_decode_405b_tp8"] = {"workload": w.name, "ms": round(ms, 4), "kv_bytes": kv_bytes,
                                    "gbs": round(kv_bytes / ms / 1e6, 1),
@@ -293,7 +293,46 @@ def secondary(steps=3, warmup=1):
     out["ring_decode_405b_tp8_paged256"] = {"workload": w.name + ", K/V in shuffled 256-row pages",
                                             "ms": round(ms, 4), "gbs": round(kv_bytes / ms / 1e6, 1)}
     log("decode, paged K/V (256-row pages): %.3f ms, %.0f GB/s of K+V" % (ms, kv_bytes / ms / 1e6))
-    del Q, K, V, O, LSE, ws, Om, Lm, Ks, Vs, pws
+    del Ks, Vs, pws
+
+    # The decode step captured once in a HIP graph (prepared call + merge) and
+    # replayed, against the same step launched directly: the 128K step above
+    # and a launch-bound step over 4K caches.
+    def graph_of(shape_, tasks_, Q_, K_, V_, O_, LSE_, mshape_, Ov_, Lv_, Om_, Lm_):
+        gws = ca.workspace_tensor(ca.forward_workspace(shape_, tasks_), dev)
+        plan = ca.forward_prepare(shape_, tasks_, gws, stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = torch.cuda.current_stream()
+            ca.forward_prepared(plan, Q_, K_, V_, O_, LSE_, stream=st)
+            ca.merge(mshape_, Ov_, Lv_, Om_, Lm_, stream=st)
+        return g, gws
+
+    g, gws = graph_of(shape, tasks, Q, K, V, O, LSE, mshape, Ov, Lv, Om, Lm)
+    graph_rows = {"131072": {"direct_ms": round(ms_dec, 4),
+                             "graph_ms": round(timed(g.replay, max(steps, 10), warmup, stream), 4)}}
+    del Q, K, V, O, LSE, ws, Om, Lm, g, gws
+    ws_ = I.ring_decode_405b_tp8(context=4096)
+    Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(ws_, 209, out_f32=True)
+    B = ws_.merged_rows
+    Om = torch.empty((B, ws_.hq, ws_.d), dtype=torch.bfloat16, device=dev)
+    Lm = torch.empty((B, ws_.hq), device=dev)
+    Ov, Lv = O.view(ws_.n_parts, B, ws_.hq, ws_.d), LSE.view(ws_.n_parts, B, ws_.hq)
+
+    def dec_small():
+        ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
+        ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream)
+
+    ms_small = timed(dec_small, 50, 5, stream)
+    g, gws = graph_of(shape, tasks, Q, K, V, O, LSE, mshape, Ov, Lv, Om, Lm)
+    graph_rows["4096"] = {"direct_ms": round(ms_small, 4), "graph_ms": round(timed(g.replay, 50, 5, stream), 4)}
+    out["ring_decode_405b_tp8_graph"] = {"workload": "llama3-405b-tp8-decode-b32, 8 blocks + merge, by context",
+                                         "by_context": graph_rows}
+    log("decode step in a HIP graph: 128K %.3f -> %.3f ms, 4K %.4f -> %.4f ms (direct -> replay)"
+        % (graph_rows["131072"]["direct_ms"], graph_rows["131072"]["graph_ms"], ms_small,
+           graph_rows["4096"]["graph_ms"]))
+    del Q, K, V, O, LSE, ws, Om, Lm, g, gws
     torch.cuda.empty_cache()
 
     # Headline forward over paged K/V: documents start on their own 512-row
