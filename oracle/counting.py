@@ -10,7 +10,7 @@ infrastructure only).
   its Table 3).  Counted per unmasked (query, key) pair and per query head of
   width d this is 4 d FLOPs.  The backward pass re-computes Q K^T and adds
   four more d-length products (dO V^T, P^T dO, dS K, dS^T Q): 10 d per pair
-  (a reading; the pages give only "about double the forward").
+  (a reading; the pages only put the backward at roughly twice the forward).
 """
 
 import numpy as np
