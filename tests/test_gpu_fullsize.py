@@ -219,3 +219,39 @@ def test_ring_decode_405b_full():
         o1, l1 = oracle.forward_rows(np.array([b, 0, 0, 1, ctx, ctx - 1, 0]), np.array([0]), qs, ks, vs, w.scale)
         Or[b], Lr[b] = o1[0], l1[0]
     check_forward(Om, Lm, Or, Lr, "decode-merged")
+
+
+def ring_load_balanced(Q, K, V, T, hq, hkv, d, N=8):
+    """The 2N partial launches of a load-balanced pass-KV ring over one T-token
+    document (all ranks' shares of a step fused), merged by Equation 4."""
+    torch = torch_cuda()
+    dev = Q.device
+    Op = torch.empty((2 * N, T, hq, d), device=dev)
+    Lp = torch.empty((2 * N, T, hq), device=dev)
+    shape = ca.make_shape(hq, hkv, d, T, T, T, out_f32=True)
+    for step in range(N):
+        for slot in (0, 1):
+            ca.forward(shape, ca.ring_kv_step_tasks([T], N, step, slot), Q, K, V, Op[2 * step + slot],
+                       Lp[2 * step + slot])
+    Om = torch.empty((T, hq, d), dtype=torch.bfloat16, device=dev)
+    Lm = torch.empty((T, hq), device=dev)
+    ca.merge(ca.make_shape(hq, hkv, d, T, T, T), Op, Lp, Om, Lm)
+    torch.cuda.synchronize()
+    del Op, Lp
+    return Om, Lm
+
+
+def test_ring_prefill_405b_load_balanced_sampled_and_probe():
+    announce("fullsize llama3-405b tp8 ring prefill, load-balanced pass-KV over 8 ranks")
+    w = I.ring_prefill_405b_tp8()
+    T = w.merged_rows
+    whole = I.Workload("whole", w.hq, w.hkv, w.d, np.array([[0, 0, 0, T, T, 0, 0]]), T, T, T)
+    Q, K, V = device_inputs(whole, 214)
+    Om, Lm = ring_load_balanced(Q, K, V, T, w.hq, w.hkv, w.d)
+    c = T // 16
+    rows = np.unique(np.concatenate([np.arange(3), [c - 1, c, 7 * c, 8 * c - 1, 8 * c, 15 * c], np.arange(T - 3, T),
+                                     np.random.default_rng(4).integers(0, T, 20)]))
+    sampled_check(whole, [(0, rows)], Q, K, V, Om, Lm, label="ring-load-balanced-sampled")
+    Q, K, V = probe_tensors(whole, np.arange(T))
+    Om, Lm = ring_load_balanced(Q, K, V, T, w.hq, w.hkv, w.d)
+    check_probe(whole, Om, Lm, "ring-load-balanced-merged")
