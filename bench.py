@@ -144,10 +144,16 @@ def secondary(steps=3, warmup=1):
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
     cold_ms = sorted(cold)[len(cold) // 2]
+    # the same call prepared once (queue built and uploaded once), then
+    # launched back to back with no host planning or copy
+    pws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+    plan = ca.forward_prepare(shape, tasks, pws, stream=stream)
+    warm_prep = timed(lambda: ca.forward_prepared(plan, Q, K, V, O, LSE, stream=stream), 50, 5, stream)
     out["tiny_1k"] = {"workload": w.name, "warm_ms": round(warm, 4), "cold_median_ms": round(cold_ms, 4),
-                      "warm_gflops": round(fl / warm / 1e6, 1)}
-    log("tiny 1k: warm %.4f ms, cold (caches flushed) median %.4f ms" % (warm, cold_ms))
-    del Q, K, V, O, LSE, ws, flush
+                      "warm_gflops": round(fl / warm / 1e6, 1), "warm_prepared_ms": round(warm_prep, 4)}
+    log("tiny 1k: warm %.4f ms (prepared %.4f ms), cold (caches flushed) median %.4f ms"
+        % (warm, warm_prep, cold_ms))
+    del Q, K, V, O, LSE, ws, flush, pws
     torch.cuda.empty_cache()
 
     # CA-tasks re-batched forward (LLaMA-34B shape)
