@@ -25,9 +25,6 @@
 
 #include "ca_internal.h"
 
-#ifndef CA_FWD_WAVES
-#define CA_FWD_WAVES 8
-#endif
 
 namespace {
 
@@ -278,7 +275,7 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
 // the launch has enough work items to cover the chip; chunks of one task are
 // merged by log-sum-exp afterwards.
 
-constexpr int kFwdWaves = CA_FWD_WAVES;   // waves per forward workgroup (4 or 8)
+constexpr int kFwdWaves = 8;   // waves per forward workgroup (two per SIMD)
 constexpr int kDecTargetItems = 1024;      // two rounds of two 4-wave items per CU
 constexpr int kDecMinChunk = 512;
 constexpr int kDecMaxGroup = 16;
@@ -514,7 +511,6 @@ ca_status launch_prepared_forward(const PreparedFwd& pf, const void* Q, const vo
     fp.hpw = pf.hpw;
     fp.scale_log2 = scale_log2;
     fp.out_f32 = out_f32;
-    fp.waves = kFwdWaves;
     hipError_t e = ca::launch_forward(fp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
   }

@@ -386,8 +386,7 @@ hipError_t launch_forward_d(const FwdParams& p, hipStream_t s) {
 
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s) {
   if (p.n_items <= 0) return hipSuccess;
-  if (p.waves == 8) return d == 128 ? launch_forward_d<128, 8>(p, s) : launch_forward_d<64, 8>(p, s);
-  return d == 128 ? launch_forward_d<128, 4>(p, s) : launch_forward_d<64, 4>(p, s);
+  return d == 128 ? launch_forward_d<128, 8>(p, s) : launch_forward_d<64, 8>(p, s);
 }
 
 }  // namespace ca

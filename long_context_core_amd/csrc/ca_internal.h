@@ -9,8 +9,8 @@
 namespace ca {
 
 // One forward work item: a tile of query rows of one task, for a subset of
-// the query heads that share one KV head.  The workgroup's four waves cover
-// hpw heads x (4 / hpw) blocks of 32 rows.
+// the query heads that share one KV head.  The workgroup's eight waves cover
+// hpw heads x (8 / hpw) blocks of 32 rows.
 struct FwdItem {
   int32_t task;
   int32_t kv_head;
@@ -55,7 +55,6 @@ struct FwdParams {
   int32_t hq, hkv, group, hpw;
   float scale_log2;   // softmax scale * log2(e)
   int32_t out_f32;
-  int32_t waves;      // 4 or 8 waves per workgroup
 };
 
 struct DecParams {
