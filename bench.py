@@ -237,6 +237,37 @@ def secondary(steps=3, warmup=1):
     del Q, K, V, Op, Lp, Om, Lm, step_ws
     torch.cuda.empty_cache()
 
+    # Partial prefill at the pages' 10 % miss rate (12,800 new tokens over
+    # 115,200 cached, 4 ranks): 16 partial launches (each rank's two cached
+    # and two new chunks per step) + merge
+    N_p, T_new, P_c = 4, 12800, 115200
+    Q = I.randn_bf16((T_new, hq, d), 210, device=dev)
+    K = I.randn_bf16((T_new + P_c, hkv, d), 211, device=dev)
+    V = I.randn_bf16((T_new + P_c, hkv, d), 212, device=dev)
+    Op = torch.empty((4 * N_p, T_new, hq, d), device=dev)
+    Lp = torch.empty((4 * N_p, T_new, hq), device=dev)
+    pshape = ca.make_shape(hq, hkv, d, T_new, T_new + P_c, T_new, out_f32=True)
+    p_tasks = [ca.ring_prefill_step_tasks([T_new], [P_c], N_p, st, sl) for st in range(N_p) for sl in range(4)]
+    p_ws = [ca.workspace_tensor(ca.forward_workspace(pshape, t), dev) for t in p_tasks]
+    Opm = torch.empty((T_new, hq, d), dtype=torch.bfloat16, device=dev)
+    Lpm = torch.empty((T_new, hq), device=dev)
+    pm_shape = ca.make_shape(hq, hkv, d, T_new, T_new, T_new)
+
+    def partial_prefill():
+        for k, t in enumerate(p_tasks):
+            ca.forward(pshape, t, Q, K, V, Op[k], Lp[k], ws=p_ws[k], stream=stream)
+        ca.merge(pm_shape, Op, Lp, Opm, Lpm, stream=stream)
+
+    ms_pp = timed(partial_prefill, steps, warmup, stream)
+    fl_pp = oracle.forward_flops(sum(ca.visible_pairs(t) for t in p_tasks), hq, d)
+    out["ring_partial_prefill_405b_tp8_miss10"] = {
+        "workload": "llama3-405b-tp8 partial prefill, 12800 new over 115200 cached tokens, 4 ranks",
+        "ms": round(ms_pp, 3), "tflops": round(fl_pp / ms_pp / 1e9, 1)}
+    log("ring partial prefill (10%% miss, 4 ranks, 16 launches + merge): %.2f ms, %.1f TFLOP/s"
+        % (ms_pp, fl_pp / ms_pp / 1e9))
+    del Q, K, V, Op, Lp, p_ws, Opm, Lpm
+    torch.cuda.empty_cache()
+
     # pass-KV / pass-Q choice for Llama3-405B under TP8 on MI355X ranks: C is
     # the attention rate just measured, BW one xGMI link (153 GB/s), bf16 on
     # the wire; the miss rates of the pages' 128K sweep

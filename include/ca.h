@@ -419,6 +419,24 @@ int32_t ca_ring_kv_step_max_tasks(int32_t n_ranks, int32_t n_seqs);
 ca_status ca_ring_kv_step_tasks(int32_t n_ranks, int32_t step, int32_t slot, const int64_t* lens_host,
                                 int32_t n_seqs, ca_task* tasks_host, int32_t max_tasks, int32_t* n_tasks);
 
+/* Partial prefill ([CP] Section 3.5.1 for the new tokens, Section 3.5.2 ring):
+ * sequence s brings new_lens[s] new tokens on top of cached_lens[s] cached
+ * ones.  Q and O rows hold the new tokens, sequences back to back; K and V
+ * rows hold each sequence's cached tokens followed by its new ones.  The new
+ * tokens are sharded load-balanced; the cached tokens keep the load-balanced
+ * sharding of their own earlier prefill.  Step `step`, slot 0..3: every rank
+ * r's two query chunks of every sequence against, of rank (r - step) mod N,
+ * its first / second cached chunk (slots 0, 1; visible to every new query) or
+ * its first / second chunk of new tokens (slots 2, 3; causal).  The 4N
+ * launches (fp32 partial outputs) merged by ca_merge give each new token's
+ * attention over its whole sequence, the same for pass-KV and pass-Q (which
+ * differ only in which rank computes a pair).  With every cached length 0
+ * slots 0 and 1 hold empty contexts.  Errors as for ca_ring_kv_step_tasks. */
+int32_t ca_ring_prefill_step_max_tasks(int32_t n_ranks, int32_t n_seqs);
+ca_status ca_ring_prefill_step_tasks(int32_t n_ranks, int32_t step, int32_t slot, const int64_t* new_lens_host,
+                                     const int64_t* cached_lens_host, int32_t n_seqs, ca_task* tasks_host,
+                                     int32_t max_tasks, int32_t* n_tasks);
+
 /* Rank that stores the decode token of batch entry seq at decode iteration
  * `iteration`: (seq + iteration) mod N.  -1 on invalid arguments. */
 int32_t ca_ring_decode_rank(int32_t n_ranks, int64_t iteration, int32_t seq);

@@ -53,6 +53,8 @@ EXPORTS = (
     "ca_ring_kv_step_max_tasks",
     "ca_ring_kv_step_tasks",
     "ca_ring_decode_rank",
+    "ca_ring_prefill_step_max_tasks",
+    "ca_ring_prefill_step_tasks",
     "ca_status_string",
     "ca_last_error",
 )
@@ -196,6 +198,10 @@ def lib():
         L.ca_ring_kv_step_max_tasks.restype = i32
         L.ca_ring_kv_step_tasks.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp]
         L.ca_ring_kv_step_tasks.restype = ctypes.c_int
+        L.ca_ring_prefill_step_max_tasks.argtypes = [i32, i32]
+        L.ca_ring_prefill_step_max_tasks.restype = i32
+        L.ca_ring_prefill_step_tasks.argtypes = [i32, i32, i32, vp, vp, i32, vp, i32, vp]
+        L.ca_ring_prefill_step_tasks.restype = ctypes.c_int
         L.ca_ring_decode_rank.argtypes = [i32, i64, i32]
         L.ca_ring_decode_rank.restype = i32
         L.ca_forward_prepare.argtypes = [sp, vp, vp, i32, vp, vp, sz, vp, ctypes.POINTER(ForwardPlan)]
@@ -510,3 +516,19 @@ def ring_decode_rank(n_ranks, iteration, seq):
     if r < 0:
         raise CAError(CA_ERR_INVALID, lib().ca_last_error().decode())
     return r
+
+
+def ring_prefill_step_tasks(new_lens, cached_lens, n_ranks, step, slot):
+    """ca_task records of partial-prefill ring step `step`, slot 0..3."""
+    nl = np.ascontiguousarray(np.asarray(new_lens, dtype=np.int64))
+    cl = np.ascontiguousarray(np.asarray(cached_lens, dtype=np.int64))
+    if len(nl) != len(cl):
+        raise CAError(CA_ERR_INVALID, "new_lens and cached_lens differ in length")
+    cap = lib().ca_ring_prefill_step_max_tasks(int(n_ranks), len(nl))
+    if cap < 0:
+        raise CAError(CA_ERR_INVALID, "bad ring size")
+    out = np.zeros(max(cap, 1), dtype=TASK_DTYPE)
+    n = ctypes.c_int32(0)
+    _check(lib().ca_ring_prefill_step_tasks(int(n_ranks), int(step), int(slot), nl.ctypes.data, cl.ctypes.data,
+                                            len(nl), out.ctypes.data, len(out), ctypes.byref(n)))
+    return out[:n.value].copy()

@@ -178,6 +178,64 @@ ca_status ca_ring_kv_step_tasks(int32_t n_ranks, int32_t step, int32_t slot, con
   return CA_OK;
 }
 
+int32_t ca_ring_prefill_step_max_tasks(int32_t n_ranks, int32_t n_seqs) {
+  return ca_ring_kv_step_max_tasks(n_ranks, n_seqs);
+}
+
+ca_status ca_ring_prefill_step_tasks(int32_t n_ranks, int32_t step, int32_t slot, const int64_t* new_lens_host,
+                                     const int64_t* cached_lens_host, int32_t n_seqs, ca_task* tasks_host,
+                                     int32_t max_tasks, int32_t* n_tasks) {
+  if (n_ranks < 1 || n_seqs < 0 || step < 0 || step >= n_ranks || slot < 0 || slot > 3)
+    return ca::set_error(CA_ERR_INVALID, "n_ranks >= 1, n_seqs >= 0, 0 <= step < n_ranks, 0 <= slot < 4");
+  if (!n_tasks || (n_seqs > 0 && (!new_lens_host || !cached_lens_host || !tasks_host)))
+    return ca::set_error(CA_ERR_INVALID, "NULL pointer");
+  for (int32_t s = 0; s < n_seqs; ++s)
+    if (new_lens_host[s] < 0 || cached_lens_host[s] < 0 || new_lens_host[s] + cached_lens_host[s] > 0x7fffffff)
+      return ca::set_error(CA_ERR_INVALID, "sequence %d lengths out of range", s);
+  const int32_t K = 2 * n_ranks;
+  int32_t n = 0;
+  for (int32_t r = 0; r < n_ranks; ++r) {
+    const int32_t src = ((r - step) % n_ranks + n_ranks) % n_ranks;   // KV of rank (r - step) mod N
+    const int32_t kv_chunk = (slot & 1) == 0 ? src : K - 1 - src;
+    int64_t q_base = 0, kv_base = 0;
+    for (int32_t s = 0; s < n_seqs; ++s) {
+      const int64_t T = new_lens_host[s], P = cached_lens_host[s];
+      const int64_t ct = chunk_len(T, n_ranks), cp = chunk_len(P, n_ranks);
+      // slots 0, 1: the source rank's cached chunks (positions < P, visible to
+      // every new query); slots 2, 3: its chunks of the new tokens (causal)
+      int64_t kb, ke;
+      if (slot < 2) {
+        kb = std::min((int64_t)kv_chunk * cp, P);
+        ke = std::min((int64_t)(kv_chunk + 1) * cp, P);
+      } else {
+        kb = P + std::min((int64_t)kv_chunk * ct, T);
+        ke = P + std::min((int64_t)(kv_chunk + 1) * ct, T);
+      }
+      for (int32_t h = 0; h < 2; ++h) {
+        const int32_t q_chunk = h == 0 ? r : K - 1 - r;
+        const int64_t qb = std::min((int64_t)q_chunk * ct, T), qe = std::min((int64_t)(q_chunk + 1) * ct, T);
+        if (qe <= qb) continue;
+        if (n >= max_tasks) {
+          *n_tasks = ca_ring_prefill_step_max_tasks(n_ranks, n_seqs);
+          return ca::set_error(CA_ERR_WORKSPACE, "more than max_tasks=%d tasks", max_tasks);
+        }
+        ca_task& t = tasks_host[n++];
+        t.q_off = q_base + qb;
+        t.kv_off = kv_base + kb;
+        t.o_off = q_base + qb;
+        t.q_len = (int32_t)(qe - qb);
+        t.kv_len = (int32_t)(ke - kb);
+        t.q_pos0 = P + qb;
+        t.kv_pos0 = kb;
+      }
+      q_base += T;
+      kv_base += P + T;
+    }
+  }
+  *n_tasks = n;
+  return CA_OK;
+}
+
 int32_t ca_ring_decode_rank(int32_t n_ranks, int64_t iteration, int32_t seq) {
   if (n_ranks < 1 || iteration < 0 || seq < 0) {
     ca::set_error(CA_ERR_INVALID, "n_ranks >= 1, iteration >= 0 and seq >= 0 required");

@@ -103,3 +103,37 @@ def test_round_robin_decode_shares_merge_to_the_whole_cache():
     whole = np.array([(b, starts[b], b, 1, lens[b], lens[b] - 1, 0) for b in range(B)], dtype=np.int64)
     O_ref, L_ref = oracle.forward(whole, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
     check_forward(Om, Lm, O_ref, L_ref, "round-robin-decode-merged")
+
+
+@pytest.mark.parametrize("N,new,cached", [(4, [700, 1, 333, 64], [3000, 128, 0, 1]), (2, [1500, 90], [777, 4096])])
+def test_partial_prefill_ring_equals_attention_over_cache_and_new_tokens(N, new, cached):
+    announce("ring partial prefill: N=%d new=%s cached=%s" % (N, new, cached))
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    hq, hkv, d = 8, 2, 128
+    Tq = sum(new)
+    Tk = sum(new) + sum(cached)
+    Q = I.randn_bf16((Tq, hq, d), 2621)
+    K = I.randn_bf16((Tk, hkv, d), 2622)
+    V = I.randn_bf16((Tk, hkv, d), 2623)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    S = 4 * N
+    O_p = torch.full((S, Tq, hq, d), float("nan"), device=dev)
+    L_p = torch.full((S, Tq, hq), float("nan"), device=dev)
+    shape = ca.make_shape(hq, hkv, d, Tq, Tk, Tq, out_f32=True)
+    for step in range(N):
+        for slot in range(4):
+            tasks = ca.ring_prefill_step_tasks(new, cached, N, step, slot)
+            ca.forward(shape, tasks, Qd, Kd, Vd, O_p[4 * step + slot], L_p[4 * step + slot])
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(L_p).any()), "a partial row was left unwritten"
+    Om = torch.empty((Tq, hq, d), device=dev, dtype=torch.bfloat16)
+    Lm = torch.empty((Tq, hq), device=dev)
+    ca.merge(ca.make_shape(hq, hkv, d, Tq, Tq, Tq), O_p, L_p, Om, Lm)
+    torch.cuda.synchronize()
+    q0 = np.concatenate([[0], np.cumsum(new)])
+    k0 = np.concatenate([[0], np.cumsum(np.array(new) + np.array(cached))])
+    whole = np.array([(q0[s], k0[s], q0[s], new[s], new[s] + cached[s], cached[s], 0) for s in range(len(new))],
+                     dtype=np.int64)
+    O_ref, L_ref = oracle.forward(whole, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
+    check_forward(Om, Lm, O_ref, L_ref, "ring-partial-prefill")

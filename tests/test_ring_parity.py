@@ -100,3 +100,55 @@ def test_ring_errors():
         ca.ring_kv_step_tasks([100], 4, 0, 2)                               # slot out of range
     with pytest.raises(ca.CAError):
         ca.ring_decode_rank(0, 1, 1)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_partial_prefill_tables_match_the_oracle_and_cover_every_pair_once(seed):
+    """Partial prefill: the C tables equal a construction from the oracle's
+    sharding (new tokens and cached tokens each sharded load-balanced), and
+    over the 4N (step, slot) tables every new query meets each key of its
+    sequence it may see (positions <= its own) exactly once, counted key by
+    key on small sizes."""
+    rng = random.Random(300 + seed)
+    N = rng.choice([1, 2, 3, 4])
+    n_seq = rng.randint(1, 4)
+    new = [rng.choice([0, 1, rng.randint(1, 90)]) for _ in range(n_seq)]
+    cached = [rng.choice([0, rng.randint(1, 120)]) for _ in range(n_seq)]
+    q_start = np.concatenate([[0], np.cumsum(new)]).astype(np.int64)
+    kv_start = np.concatenate([[0], np.cumsum(np.array(new) + np.array(cached))]).astype(np.int64)
+    ch_new, ch_old = R.shard(new, N), R.shard(cached, N)
+    seen = {}
+    for step in range(N):
+        for slot in range(4):
+            want = []
+            for r in range(N):
+                src = R.kv_step_source(r, step, N)
+                kc = src if slot % 2 == 0 else 2 * N - 1 - src
+                for s in range(n_seq):
+                    P = cached[s]
+                    if slot < 2:
+                        _, _, kb, ke = ch_old[s * 2 * N + kc]
+                    else:
+                        _, _, kb, ke = ch_new[s * 2 * N + kc]
+                        kb, ke = P + kb, P + ke
+                    for qc in (r, 2 * N - 1 - r):
+                        _, _, qb, qe = ch_new[s * 2 * N + qc]
+                        if qe > qb:
+                            want.append((q_start[s] + qb, kv_start[s] + kb, q_start[s] + qb, qe - qb, ke - kb,
+                                         P + qb, kb))
+            tasks = ca.ring_prefill_step_tasks(new, cached, N, step, slot)
+            got = [tuple(int(t[f]) for f in ca.TASK_DTYPE.names) for t in tasks]
+            assert got == want
+            for q_off, kv_off, _, q_len, kv_len, q_pos0, kv_pos0 in got:
+                for i in range(q_len):
+                    for j in range(kv_len):
+                        if kv_pos0 + j <= q_pos0 + i:
+                            key = (q_off + i, kv_off + j)
+                            seen[key] = seen.get(key, 0) + 1
+    assert all(v == 1 for v in seen.values())
+    # every query row sees exactly the keys of its sequence at positions <= its own
+    for s in range(n_seq):
+        for i in range(new[s]):
+            row = q_start[s] + i
+            n_keys = sum(1 for (q, k) in seen if q == row)
+            assert n_keys == cached[s] + i + 1
