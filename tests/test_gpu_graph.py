@@ -102,3 +102,60 @@ def test_prepared_call_rejects_a_foreign_plan():
     with pytest.raises(ca.CAError):
         t = torch.zeros(16, device=dev)
         ca.forward_prepared(ca.ForwardPlan(), t, t, t, t, t)
+
+
+def test_graph_replays_masked_and_paged_calls():
+    """A lambda-masked prefill and a paged decode, each prepared once, captured
+    together and replayed: every replay equals the direct calls bit for bit."""
+    announce("graph-captured prepared forward: lambda mask + paged decode")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    lens = [1500, 300, 2200]
+    mt = I.lambda_tasks(lens, window=512, sink=16)
+    T = sum(lens)
+    m_shape = ca.make_shape(HQ, HKV, D, T, T, T)
+    Qm = I.randn_bf16((T, HQ, D), 2720, device=dev)
+    Km = I.randn_bf16((T, HKV, D), 2721, device=dev)
+    Vm = I.randn_bf16((T, HKV, D), 2722, device=dev)
+    Om, Lm = torch.empty((T, HQ, D), dtype=torch.bfloat16, device=dev), torch.empty((T, HQ), device=dev)
+    Om2, Lm2 = torch.empty_like(Om), torch.empty_like(Lm)
+    # paged decode: 4 queries over 4096-token caches in shuffled 256-row pages
+    P, B, ctx = 256, 4, 4096
+    dt = decode_whole(B, ctx)
+    n_vp = B * ctx // P
+    table = I.page_table(n_vp, n_vp + 8, 2723)
+    pages = ca.kv_pages(table, P)
+    d_shape = ca.make_shape(HQ, HKV, D, B, (n_vp + 8) * P, B)
+    Qd = I.randn_bf16((B, HQ, D), 2724, device=dev)
+    Ks = I.randn_bf16(((n_vp + 8) * P, HKV, D), 2725, device=dev)
+    Vs = I.randn_bf16(((n_vp + 8) * P, HKV, D), 2726, device=dev)
+    Od, Ld = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev), torch.empty((B, HQ), device=dev)
+    Od2, Ld2 = torch.empty_like(Od), torch.empty_like(Ld)
+    ws_m = ca.workspace_tensor(ca.forward_workspace(m_shape, mt), dev)
+    ws_d = ca.workspace_tensor(ca.forward_workspace(d_shape, dt, pages=pages), dev)
+    side = torch.cuda.Stream()
+    plan_m = ca.forward_prepare(m_shape, mt, ws_m, stream=side)
+    plan_d = ca.forward_prepare(d_shape, dt, ws_d, stream=side, pages=pages)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        ca.forward_prepared(plan_m, Qm, Km, Vm, Om, Lm, stream=st)
+        ca.forward_prepared(plan_d, Qd, Ks, Vs, Od, Ld, stream=st)
+    for rep in range(3):
+        Qm.copy_(I.randn_bf16((T, HQ, D), 2730 + rep, device=dev))
+        Qd.copy_(I.randn_bf16((B, HQ, D), 2740 + rep, device=dev))
+        ca.forward(m_shape, mt, Qm, Km, Vm, Om2, Lm2)
+        ca.forward(d_shape, dt, Qd, Ks, Vs, Od2, Ld2, pages=pages)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = (torch.equal(Om.view(torch.int16), Om2.view(torch.int16)) and torch.equal(Lm, Lm2)
+                and torch.equal(Od.view(torch.int16), Od2.view(torch.int16)) and torch.equal(Ld, Ld2))
+        print("masked + paged replay %d: identical to the direct calls: %s" % (rep, same), flush=True)
+        assert same
+    # the paged decode against the oracle over the virtual caches
+    Kv = oracle.virtual_rows(widen(Ks), table, P)
+    Vv = oracle.virtual_rows(widen(Vs), table, P)
+    O_ref, L_ref = oracle.forward(dt, widen(Qd), Kv, Vv, 1 / math.sqrt(D))
+    check_forward(Od, Ld, O_ref, L_ref, "paged-decode-replayed")
