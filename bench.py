@@ -84,9 +84,18 @@ def cpu_baseline(w, Q, K, V, seconds_hint):
     dt = time.perf_counter() - t0
     pairs = int(np.sum(np.clip(int(t[5]) + rows - int(t[6]) + 1, 0, n_ctx)))
     flops = oracle.forward_flops(pairs, w.hq, w.d)
+    full = oracle.forward_flops(oracle.visible_pairs(w.tasks), w.hq, w.d)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": "%d random query rows of the largest task (%d tokens), all %d query heads; "
-                      "%d visible pairs per head in %.1f s" % (n_rows, q_len, w.hq, pairs, dt)}
+                      "%d visible pairs per head in %.1f s" % (n_rows, q_len, w.hq, pairs, dt),
+            "ns_per_pair_and_head": round(dt / (pairs * w.hq) * 1e9, 3),
+            "extrapolated_full_s": round(full / (flops / dt), 1), "cpu_model": cpu}
 
 
 def timed(fn, steps, warmup, stream):
@@ -289,6 +298,15 @@ def secondary(steps=3, warmup=1):
     log("ring select (C = %.3g FLOP/s, BW = 153 GB/s): Eq.2 T >= %.0f at N=8; Algorithm 5 at N=8: %s"
         % (C, sel["N=8"]["t_threshold_eq2"], " ".join("%d:%s" % (p_["T"], p_["algorithm5"][5:])
                                                        for p_ in sel["N=8"]["points"])))
+
+    # Device-to-device copy ceiling (1 GiB read + 1 GiB written), the yardstick
+    # for the HBM-bound merge and decode next to the 8 TB/s spec
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ms_cp = timed(lambda: dst.copy_(src), 10, 2, stream)
+    out["hbm_copy_ceiling"] = {"bytes": 2 << 30, "ms": round(ms_cp, 4), "gbs": round((2 << 30) / ms_cp / 1e6, 1)}
+    log("device copy ceiling: %.0f GB/s (read + write)" % ((2 << 30) / ms_cp / 1e6))
+    del src, dst
 
     # Pass-Q decode share: 32 tokens x 128K caches, 8 stationary blocks, merge
     w = I.ring_decode_405b_tp8()
