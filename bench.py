@@ -98,6 +98,17 @@ def cpu_baseline(w, Q, K, V, seconds_hint):
             "extrapolated_full_s": round(full / (flops / dt), 1), "cpu_model": cpu}
 
 
+def fuse_slots(tables, rows):
+    """Task tables of one ring step as one launch: table j writes output rows
+    [j * rows, (j + 1) * rows) of the stacked partial buffer."""
+    out = []
+    for j, t in enumerate(tables):
+        t = t.copy()
+        t["o_off"] += j * rows
+        out.append(t)
+    return np.concatenate(out)
+
+
 def timed(fn, steps, warmup, stream):
     """Average device time (ms) of fn() with HIP events on `stream`."""
     import torch
@@ -214,11 +225,22 @@ def secondary(steps=3, warmup=1):
     rshape = ca.make_shape(hq, hkv, d, total, total, total, out_f32=True)
     step_tasks = [ca.ring_kv_step_tasks(lens, N_r, st, sl) for st in range(N_r) for sl in (0, 1)]
     step_ws = [ca.workspace_tensor(ca.forward_workspace(rshape, t), dev) for t in step_tasks]
+    # the same work with both source chunks of a step in one launch (slot 1's
+    # outputs redirected to the second partial buffer of the step)
+    fshape = ca.make_shape(hq, hkv, d, total, total, 2 * total, out_f32=True)
+    fused_tasks = [fuse_slots(step_tasks[2 * st:2 * st + 2], total) for st in range(N_r)]
+    fused_ws = [ca.workspace_tensor(ca.forward_workspace(fshape, t), dev) for t in fused_tasks]
 
-    def ring_lb():
+    def ring_lb_per_slot():
         for k, t in enumerate(step_tasks):
             ca.forward(rshape, t, Q, K, V, Op[k], Lp[k], ws=step_ws[k], stream=stream)
 
+    def ring_lb():
+        for st, t in enumerate(fused_tasks):
+            ca.forward(fshape, t, Q, K, V, Op[2 * st:2 * st + 2], Lp[2 * st:2 * st + 2], ws=fused_ws[st],
+                       stream=stream)
+
+    ms_lb_slot = timed(ring_lb_per_slot, steps, warmup, stream)
     ms_lb = timed(ring_lb, steps, warmup, stream)
     fl_lb = oracle.forward_flops(sum(ca.visible_pairs(t) for t in step_tasks), hq, d)
     ms_lbm = timed(lambda: ca.merge(mshape, Op, Lp, Om, Lm, stream=stream), steps, warmup, stream)
@@ -235,20 +257,21 @@ def secondary(steps=3, warmup=1):
     per_rank = rank_step.sum(axis=1)
     out["ring_prefill_405b_tp8_load_balanced"] = {
         "workload": "llama3-405b-tp8-ring-prefill-128k, load-balanced 16 chunks, pass-KV over 8 ranks",
-        "partials_ms": round(ms_lb, 3), "partials_tflops": round(fl_lb / ms_lb / 1e9, 1),
+        "launches": N_r, "partials_ms": round(ms_lb, 3), "partials_tflops": round(fl_lb / ms_lb / 1e9, 1),
+        "partials_ms_one_launch_per_slot": round(ms_lb_slot, 3),
         "merge_ms": round(ms_lbm, 3), "merge_bytes": mb_lb, "merge_gbs": round(mb_lb / ms_lbm / 1e6, 1),
         "rank_pairs_max_over_mean": round(float(per_rank.max() / per_rank.mean()), 4),
         "rank_step_pairs_max_over_mean_worst_step": round(float(max(
             rank_step[:, j].max() / rank_step[:, j].mean() for j in range(N_r))), 4)}
-    log("ring prefill, load-balanced pass-KV: partials %.2f ms (%.1f TFLOP/s), merge %.3f ms (%.0f GB/s), "
-        "rank pairs max/mean %.4f" % (ms_lb, fl_lb / ms_lb / 1e9, ms_lbm, mb_lb / ms_lbm / 1e6,
-                                      per_rank.max() / per_rank.mean()))
-    del Q, K, V, Op, Lp, Om, Lm, step_ws
+    log("ring prefill, load-balanced pass-KV: partials %.2f ms (%.1f TFLOP/s; %.2f ms at one launch per slot), "
+        "merge %.3f ms (%.0f GB/s), rank pairs max/mean %.4f"
+        % (ms_lb, fl_lb / ms_lb / 1e9, ms_lb_slot, ms_lbm, mb_lb / ms_lbm / 1e6, per_rank.max() / per_rank.mean()))
+    del Q, K, V, Op, Lp, Om, Lm, step_ws, fused_ws
     torch.cuda.empty_cache()
 
     # Partial prefill at the pages' 10 % miss rate (12,800 new tokens over
-    # 115,200 cached, 4 ranks): 16 partial launches (each rank's two cached
-    # and two new chunks per step) + merge
+    # 115,200 cached, 4 ranks): per ring step one launch holding each rank's
+    # two cached and two new chunk pairs (16 partial slots), then the merge
     N_p, T_new, P_c = 4, 12800, 115200
     Q = I.randn_bf16((T_new, hq, d), 210, device=dev)
     K = I.randn_bf16((T_new + P_c, hkv, d), 211, device=dev)
@@ -258,23 +281,34 @@ def secondary(steps=3, warmup=1):
     pshape = ca.make_shape(hq, hkv, d, T_new, T_new + P_c, T_new, out_f32=True)
     p_tasks = [ca.ring_prefill_step_tasks([T_new], [P_c], N_p, st, sl) for st in range(N_p) for sl in range(4)]
     p_ws = [ca.workspace_tensor(ca.forward_workspace(pshape, t), dev) for t in p_tasks]
+    pfshape = ca.make_shape(hq, hkv, d, T_new, T_new + P_c, 4 * T_new, out_f32=True)
+    pf_tasks = [fuse_slots(p_tasks[4 * st:4 * st + 4], T_new) for st in range(N_p)]
+    pf_ws = [ca.workspace_tensor(ca.forward_workspace(pfshape, t), dev) for t in pf_tasks]
     Opm = torch.empty((T_new, hq, d), dtype=torch.bfloat16, device=dev)
     Lpm = torch.empty((T_new, hq), device=dev)
     pm_shape = ca.make_shape(hq, hkv, d, T_new, T_new, T_new)
 
-    def partial_prefill():
+    def partial_prefill_per_slot():
         for k, t in enumerate(p_tasks):
             ca.forward(pshape, t, Q, K, V, Op[k], Lp[k], ws=p_ws[k], stream=stream)
         ca.merge(pm_shape, Op, Lp, Opm, Lpm, stream=stream)
 
+    def partial_prefill():
+        for st, t in enumerate(pf_tasks):
+            ca.forward(pfshape, t, Q, K, V, Op[4 * st:4 * st + 4], Lp[4 * st:4 * st + 4], ws=pf_ws[st],
+                       stream=stream)
+        ca.merge(pm_shape, Op, Lp, Opm, Lpm, stream=stream)
+
+    ms_pp_slot = timed(partial_prefill_per_slot, steps, warmup, stream)
     ms_pp = timed(partial_prefill, steps, warmup, stream)
     fl_pp = oracle.forward_flops(sum(ca.visible_pairs(t) for t in p_tasks), hq, d)
     out["ring_partial_prefill_405b_tp8_miss10"] = {
         "workload": "llama3-405b-tp8 partial prefill, 12800 new over 115200 cached tokens, 4 ranks",
-        "ms": round(ms_pp, 3), "tflops": round(fl_pp / ms_pp / 1e9, 1)}
-    log("ring partial prefill (10%% miss, 4 ranks, 16 launches + merge): %.2f ms, %.1f TFLOP/s"
-        % (ms_pp, fl_pp / ms_pp / 1e9))
-    del Q, K, V, Op, Lp, p_ws, Opm, Lpm
+        "launches": N_p, "ms": round(ms_pp, 3), "tflops": round(fl_pp / ms_pp / 1e9, 1),
+        "ms_one_launch_per_slot": round(ms_pp_slot, 3)}
+    log("ring partial prefill (10%% miss, 4 ranks, 4 launches + merge): %.2f ms, %.1f TFLOP/s "
+        "(16 launches: %.2f ms)" % (ms_pp, fl_pp / ms_pp / 1e9, ms_pp_slot))
+    del Q, K, V, Op, Lp, p_ws, pf_ws, Opm, Lpm
     torch.cuda.empty_cache()
 
     # pass-KV / pass-Q choice for Llama3-405B under TP8 on MI355X ranks: C is

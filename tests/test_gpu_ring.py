@@ -24,9 +24,21 @@ from tests.gpu_util import announce, check_forward, torch_cuda, widen
 pytestmark = pytest.mark.gpu
 
 
+def fuse_slots(tables, rows):
+    """The tables of one ring step as one launch: slot j's outputs go to rows
+    [j * rows, (j + 1) * rows) of the stacked partial buffer."""
+    out = []
+    for j, t in enumerate(tables):
+        t = t.copy()
+        t["o_off"] += j * rows
+        out.append(t)
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("N,lens", [(4, [700, 1500, 333, 64, 1]), (3, [2048, 100]), (8, [5000, 77, 1029])])
-def test_load_balanced_pass_kv_ring_equals_causal_attention(N, lens):
-    announce("ring pass-KV, load-balanced sharding: N=%d lens=%s" % (N, lens))
+def test_load_balanced_pass_kv_ring_equals_causal_attention(N, lens, fused):
+    announce("ring pass-KV, load-balanced sharding: N=%d lens=%s fused=%s" % (N, lens, fused))
     torch = torch_cuda()
     dev = torch.device("cuda:0")
     hq, hkv, d = 8, 2, 128
@@ -39,10 +51,17 @@ def test_load_balanced_pass_kv_ring_equals_causal_attention(N, lens):
     O_p = torch.full((S, T, hq, d), float("nan"), device=dev)
     L_p = torch.full((S, T, hq), float("nan"), device=dev)
     shape = ca.make_shape(hq, hkv, d, T, T, T, out_f32=True)
-    for step in range(N):
-        for slot in (0, 1):
-            tasks = ca.ring_kv_step_tasks(lens, N, step, slot)
-            ca.forward(shape, tasks, Qd, Kd, Vd, O_p[2 * step + slot], L_p[2 * step + slot])
+    if fused:
+        # both source chunks of a step in one launch
+        fshape = ca.make_shape(hq, hkv, d, T, T, 2 * T, out_f32=True)
+        for step in range(N):
+            tasks = fuse_slots([ca.ring_kv_step_tasks(lens, N, step, slot) for slot in (0, 1)], T)
+            ca.forward(fshape, tasks, Qd, Kd, Vd, O_p[2 * step:2 * step + 2], L_p[2 * step:2 * step + 2])
+    else:
+        for step in range(N):
+            for slot in (0, 1):
+                tasks = ca.ring_kv_step_tasks(lens, N, step, slot)
+                ca.forward(shape, tasks, Qd, Kd, Vd, O_p[2 * step + slot], L_p[2 * step + slot])
     torch.cuda.synchronize()
     assert not bool(torch.isnan(L_p).any()), "a partial row was left unwritten"
     Om = torch.empty((T, hq, d), device=dev, dtype=torch.bfloat16)
@@ -105,9 +124,10 @@ def test_round_robin_decode_shares_merge_to_the_whole_cache():
     check_forward(Om, Lm, O_ref, L_ref, "round-robin-decode-merged")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("N,new,cached", [(4, [700, 1, 333, 64], [3000, 128, 0, 1]), (2, [1500, 90], [777, 4096])])
-def test_partial_prefill_ring_equals_attention_over_cache_and_new_tokens(N, new, cached):
-    announce("ring partial prefill: N=%d new=%s cached=%s" % (N, new, cached))
+def test_partial_prefill_ring_equals_attention_over_cache_and_new_tokens(N, new, cached, fused):
+    announce("ring partial prefill: N=%d new=%s cached=%s fused=%s" % (N, new, cached, fused))
     torch = torch_cuda()
     dev = torch.device("cuda:0")
     hq, hkv, d = 8, 2, 128
@@ -121,10 +141,17 @@ def test_partial_prefill_ring_equals_attention_over_cache_and_new_tokens(N, new,
     O_p = torch.full((S, Tq, hq, d), float("nan"), device=dev)
     L_p = torch.full((S, Tq, hq), float("nan"), device=dev)
     shape = ca.make_shape(hq, hkv, d, Tq, Tk, Tq, out_f32=True)
-    for step in range(N):
-        for slot in range(4):
-            tasks = ca.ring_prefill_step_tasks(new, cached, N, step, slot)
-            ca.forward(shape, tasks, Qd, Kd, Vd, O_p[4 * step + slot], L_p[4 * step + slot])
+    if fused:
+        # the four chunk pairs of a step (two cached, two new) in one launch
+        fshape = ca.make_shape(hq, hkv, d, Tq, Tk, 4 * Tq, out_f32=True)
+        for step in range(N):
+            tasks = fuse_slots([ca.ring_prefill_step_tasks(new, cached, N, step, slot) for slot in range(4)], Tq)
+            ca.forward(fshape, tasks, Qd, Kd, Vd, O_p[4 * step:4 * step + 4], L_p[4 * step:4 * step + 4])
+    else:
+        for step in range(N):
+            for slot in range(4):
+                tasks = ca.ring_prefill_step_tasks(new, cached, N, step, slot)
+                ca.forward(shape, tasks, Qd, Kd, Vd, O_p[4 * step + slot], L_p[4 * step + slot])
     torch.cuda.synchronize()
     assert not bool(torch.isnan(L_p).any()), "a partial row was left unwritten"
     Om = torch.empty((Tq, hq, d), device=dev, dtype=torch.bfloat16)
