@@ -1,8 +1,9 @@
 // K1 — fused core-attention forward over a CA-task table (gfx950).
 //
-// One workgroup (4 waves) per work item: 128 (query row, head) pairs that all
-// read the same KV head — hpw heads x (4 / hpw) blocks of 32 rows — so each
-// K/V tile staged in LDS feeds four MFMA streams.  Per 64-key tile a wave:
+// One workgroup (8 waves, two per SIMD) per work item: 256 (query row, head)
+// pairs that all read the same KV head — hpw heads x (8 / hpw) blocks of 32
+// rows — so each K/V tile staged in LDS feeds eight MFMA streams.  Per 64-key
+// tile a wave:
 //
 //   S^T[64 keys][32 queries] = K_tile . Q^T       (MFMA 32x32x16 bf16, fp32 acc)
 //   online softmax in the exp2 domain              (rows are lane-local)

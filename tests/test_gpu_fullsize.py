@@ -222,17 +222,22 @@ def test_ring_decode_405b_full():
 
 
 def ring_load_balanced(Q, K, V, T, hq, hkv, d, N=8):
-    """The 2N partial launches of a load-balanced pass-KV ring over one T-token
-    document (all ranks' shares of a step fused), merged by Equation 4."""
+    """The 2N partials of a load-balanced pass-KV ring over one T-token
+    document, one launch per step as the bench times them (all ranks' shares
+    and both source chunks of a step fused; slot 1 writes the second block of
+    the step's stacked partial buffer), merged by Equation 4."""
     torch = torch_cuda()
     dev = Q.device
     Op = torch.empty((2 * N, T, hq, d), device=dev)
     Lp = torch.empty((2 * N, T, hq), device=dev)
-    shape = ca.make_shape(hq, hkv, d, T, T, T, out_f32=True)
+    shape = ca.make_shape(hq, hkv, d, T, T, 2 * T, out_f32=True)
     for step in range(N):
+        tables = []
         for slot in (0, 1):
-            ca.forward(shape, ca.ring_kv_step_tasks([T], N, step, slot), Q, K, V, Op[2 * step + slot],
-                       Lp[2 * step + slot])
+            t = ca.ring_kv_step_tasks([T], N, step, slot)
+            t["o_off"] += slot * T
+            tables.append(t)
+        ca.forward(shape, np.concatenate(tables), Q, K, V, Op[2 * step:2 * step + 2], Lp[2 * step:2 * step + 2])
     Om = torch.empty((T, hq, d), dtype=torch.bfloat16, device=dev)
     Lm = torch.empty((T, hq), device=dev)
     ca.merge(ca.make_shape(hq, hkv, d, T, T, T), Op, Lp, Om, Lm)
