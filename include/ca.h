@@ -18,7 +18,8 @@
  *    buffer, including the workspace; the library allocates no device memory
  *    and keeps no state between calls other than a small ring of reusable
  *    pinned host staging buffers per thread and device, through which
- *    host-built work queues are copied into the workspace.
+ *    host-built work queues are copied into the workspace; a thread's ring
+ *    is released when the thread ends.
  *  - Calls are asynchronous on `stream` (a hipStream_t, passed as void*; NULL
  *    is the default stream).  Buffers must stay valid until the stream work
  *    completes.  Host arrays (*_host) are only read during the call.

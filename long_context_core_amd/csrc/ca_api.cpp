@@ -204,7 +204,7 @@ int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
 // Upload of a host-built work queue into the caller's workspace, through a
 // ring of pinned staging buffers kept per thread and device (each grown, never
-// shrunk, held until the process ends).  An event recorded after each copy
+// shrunk, released when the thread ends).  An event recorded after each copy
 // guards that buffer's reuse, so a call waits only when all kStagingSlots
 // earlier uploads of this thread are still queued behind device work; with a
 // single buffer every call waited for the previous call's copy, which put the
@@ -219,6 +219,18 @@ struct Staging {
 struct StagingRing {
   Staging slot[kStagingSlots];
   int next = 0;
+  StagingRing() = default;
+  StagingRing(const StagingRing&) = delete;
+  StagingRing& operator=(const StagingRing&) = delete;
+  // At thread exit: a copy still queued reads its buffer, so wait for it
+  // before the buffer goes back.  Errors cannot be reported from here.
+  ~StagingRing() {
+    for (Staging& st : slot) {
+      if (st.pending && st.ev) (void)hipEventSynchronize(st.ev);
+      if (st.buf) (void)hipHostFree(st.buf);
+      if (st.ev) (void)hipEventDestroy(st.ev);
+    }
+  }
 };
 constexpr int kMaxDevices = 64;
 thread_local StagingRing g_staging[kMaxDevices];

@@ -192,3 +192,60 @@ def test_rows_without_keys_next_to_rows_with_keys(d):
     tasks = np.array([(0, 0, 0, 40, 50, 0, 30), (40, 50, 40, 70, 100, 5, 60), (110, 150, 110, 33, 64, 0, 31)])
     O, LSE, Or, Lr = run_case(tasks, 16, 2, d, 143, 214, 143, 660 + d)
     check_forward(O, LSE, Or, Lr, "partially-empty d%d" % d)
+
+
+def test_calls_from_short_lived_threads():
+    """Calls made from threads that then exit (each thread's ring of pinned
+    staging buffers is released at its end, after its queued copies): every
+    thread's results equal the main thread's bit for bit, concurrent threads
+    included, and the library keeps working afterwards."""
+    import threading
+
+    announce("forward from short-lived threads")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    hq, hkv, d = 8, 2, 128
+    lens = [300, 1, 777, 64]
+    tasks = I.varlen_tasks(lens)
+    T = sum(lens)
+    Q = I.randn_bf16((T, hq, d), 3100, device=dev)
+    K = I.randn_bf16((T, hkv, d), 3101, device=dev)
+    V = I.randn_bf16((T, hkv, d), 3102, device=dev)
+    shape = ca.make_shape(hq, hkv, d, T, T, T)
+    O0 = torch.empty((T, hq, d), dtype=torch.bfloat16, device=dev)
+    L0 = torch.empty((T, hq), device=dev)
+    ca.forward(shape, tasks, Q, K, V, O0, L0)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
+    check_forward(O0, L0, O_ref, L_ref, "main thread")
+    n_threads, calls = 4, 12
+    outs = [[torch.empty_like(O0) for _ in range(calls)] for _ in range(n_threads)]
+    lses = [[torch.empty_like(L0) for _ in range(calls)] for _ in range(n_threads)]
+    errors = []
+
+    def work(i):
+        try:
+            torch.cuda.set_device(dev)
+            for c in range(calls):
+                ca.forward(shape, tasks, Q, K, V, outs[i][c], lses[i][c])
+            # the thread ends with its last copies possibly still queued
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    # two rounds of threads one after another, then all at once
+    for group in ([0], [1], [2, 3]):
+        th = [threading.Thread(target=work, args=(i,)) for i in group]
+        for x in th:
+            x.start()
+        for x in th:
+            x.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(n_threads):
+        for c in range(calls):
+            assert torch.equal(outs[i][c].view(torch.int16), O0.view(torch.int16)) and torch.equal(lses[i][c], L0)
+    O1, L1 = torch.empty_like(O0), torch.empty_like(L0)
+    ca.forward(shape, tasks, Q, K, V, O1, L1)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O0.view(torch.int16)) and torch.equal(L1, L0)
+    print("short-lived threads: %d x %d calls identical to the main thread's" % (n_threads, calls), flush=True)
