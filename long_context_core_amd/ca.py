@@ -252,6 +252,47 @@ def _ptr(x):
     return ctypes.c_void_p(x.data_ptr())
 
 
+def _dtype(name):
+    import torch
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "u8": torch.uint8}[name]
+
+
+def _need(x, what, dtype, numel):
+    """The library reads and writes device buffers through bare pointers, with
+    sizes taken from the shape: check here that each tensor is a contiguous
+    tensor of the right dtype on the current device holding at least that
+    many elements, so that a wrong buffer raises instead of reaching a
+    kernel."""
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise CAError(CA_ERR_INVALID, "%s: expected a torch tensor, got %s" % (what, type(x).__name__))
+    if not x.is_cuda:
+        raise CAError(CA_ERR_INVALID, "%s: not a device tensor (%s)" % (what, x.device))
+    if x.device.index != torch.cuda.current_device():
+        raise CAError(CA_ERR_INVALID, "%s: on %s, the current device is cuda:%d"
+                      % (what, x.device, torch.cuda.current_device()))
+    if x.dtype != _dtype(dtype):
+        raise CAError(CA_ERR_INVALID, "%s: dtype %s, expected %s" % (what, x.dtype, _dtype(dtype)))
+    if not x.is_contiguous():
+        raise CAError(CA_ERR_INVALID, "%s: not contiguous" % what)
+    if x.numel() < numel:
+        raise CAError(CA_ERR_INVALID, "%s: %d elements, the call needs %d" % (what, x.numel(), numel))
+
+
+def _ws_bytes(ws):
+    _need(ws, "workspace", "u8", 0)
+    return ws.numel()
+
+
+def _check_forward_tensors(shape, Q, K, V, O, LSE):
+    hq, hkv, d = int(shape.hq), int(shape.hkv), int(shape.d)
+    _need(Q, "Q", "bf16", shape.q_rows * hq * d)
+    _need(K, "K", "bf16", shape.kv_rows * hkv * d)
+    _need(V, "V", "bf16", shape.kv_rows * hkv * d)
+    _need(O, "O", "f32" if shape.flags & CA_OUT_F32 else "bf16", shape.o_rows * hq * d)
+    _need(LSE, "LSE", "f32", shape.o_rows * hq)
+
+
 def _stream_ptr(stream):
     if stream is None:
         import torch
@@ -320,18 +361,20 @@ def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None, pag
     With masks (or a 9-column table) it calls ca_forward_masked; with pages
     (a KVPages from kv_pages) ca_forward_paged, K/V then being page stores."""
     ta, ma = split_tasks(tasks, masks)
+    _check_forward_tensors(shape, Q, K, V, O, LSE)
     if ws is None:
         ws = workspace_tensor(forward_workspace(shape, ta, ma, pages), Q.device)
+    wb = _ws_bytes(ws)
     if pages is not None:
         st = lib().ca_forward_paged(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
                                     ctypes.byref(pages), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE),
-                                    _ptr(ws), ws.numel(), _stream_ptr(stream))
+                                    _ptr(ws), wb, _stream_ptr(stream))
     elif ma is None:
         st = lib().ca_forward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
-                              _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
+                              _ptr(O), _ptr(LSE), _ptr(ws), wb, _stream_ptr(stream))
     else:
         st = lib().ca_forward_masked(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta), _ptr(Q),
-                                     _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(ws), ws.numel(),
+                                     _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(ws), wb,
                                      _stream_ptr(stream))
     _check(st)
     return O, LSE
@@ -343,13 +386,19 @@ def forward_prepare(shape, tasks, ws, stream=None, masks=None, pages=None):
     ta, ma = split_tasks(tasks, masks)
     plan = ForwardPlan()
     _check(lib().ca_forward_prepare(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
-                                    ctypes.byref(pages) if pages is not None else None, _ptr(ws), ws.numel(),
+                                    ctypes.byref(pages) if pages is not None else None, _ptr(ws), _ws_bytes(ws),
                                     _stream_ptr(stream), ctypes.byref(plan)))
+    plan._shape = make_shape(shape.hq, shape.hkv, shape.d, shape.q_rows, shape.kv_rows, shape.o_rows,
+                             scale=shape.scale, out_f32=bool(shape.flags & CA_OUT_F32))
+    plan._ws = ws     # the queue lives there: keep it alive with the plan
     return plan
 
 
 def forward_prepared(plan, Q, K, V, O, LSE, stream=None):
     """ca_forward_prepared: kernel launches only (capturable in a HIP graph)."""
+    shape = getattr(plan, "_shape", None)
+    if shape is not None:
+        _check_forward_tensors(shape, Q, K, V, O, LSE)
     _check(lib().ca_forward_prepared(ctypes.byref(plan), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE),
                                      _stream_ptr(stream)))
     return O, LSE
@@ -359,10 +408,11 @@ def forward_varlen(shape, cu_seqlens, Q, K, V, O, LSE, ws=None, stream=None):
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     n = len(cu) - 1
     cup = cu.ctypes.data_as(ctypes.c_void_p)
+    _check_forward_tensors(shape, Q, K, V, O, LSE)
     if ws is None:
         ws = workspace_tensor(lib().ca_forward_varlen_workspace(ctypes.byref(shape), cup, n), Q.device)
     st = lib().ca_forward_varlen(ctypes.byref(shape), cup, n, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
-                                 _ptr(LSE), _ptr(ws), ws.numel(), _stream_ptr(stream))
+                                 _ptr(LSE), _ptr(ws), _ws_bytes(ws), _stream_ptr(stream))
     _check(st)
     return O, LSE
 
@@ -370,6 +420,11 @@ def forward_varlen(shape, cu_seqlens, Q, K, V, O, LSE, ws=None, stream=None):
 def merge(shape, O_parts, LSE_parts, O, LSE, stream=None):
     """ca_merge: O_parts [S, n_rows, hq, d] fp32, LSE_parts [S, n_rows, hq] fp32."""
     S, n_rows = int(O_parts.shape[0]), int(O_parts.shape[1])
+    hq, d = int(shape.hq), int(shape.d)
+    _need(O_parts, "O_parts", "f32", S * n_rows * hq * d)
+    _need(LSE_parts, "LSE_parts", "f32", S * n_rows * hq)
+    _need(O, "O", "f32" if shape.flags & CA_OUT_F32 else "bf16", n_rows * hq * d)
+    _need(LSE, "LSE", "f32", n_rows * hq)
     st = lib().ca_merge(ctypes.byref(shape), S, n_rows, _ptr(O_parts), _ptr(LSE_parts), _ptr(O),
                         _ptr(LSE), _stream_ptr(stream))
     _check(st)
@@ -388,21 +443,29 @@ def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None
     """ca_backward (ca_backward_masked with masks or a 9-column table,
     ca_backward_paged with pages: K, V, dK, dV are then page stores)."""
     ta, ma = split_tasks(tasks, masks)
+    hq, hkv, d = int(shape.hq), int(shape.hkv), int(shape.d)
+    for x, what, rows, heads in ((Q, "Q", shape.q_rows, hq), (K, "K", shape.kv_rows, hkv),
+                                 (V, "V", shape.kv_rows, hkv), (O, "O", shape.o_rows, hq),
+                                 (dO, "dO", shape.o_rows, hq), (dQ, "dQ", shape.q_rows, hq),
+                                 (dK, "dK", shape.kv_rows, hkv), (dV, "dV", shape.kv_rows, hkv)):
+        _need(x, what, "bf16", rows * heads * d)
+    _need(LSE, "LSE", "f32", shape.o_rows * hq)
     if ws is None:
         ws = workspace_tensor(backward_workspace(shape, ta, ma, pages), Q.device)
+    wb = _ws_bytes(ws)
     if pages is not None:
         st = lib().ca_backward_paged(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
                                      ctypes.byref(pages), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
-                                     _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws), ws.numel(),
+                                     _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws), wb,
                                      _stream_ptr(stream))
     elif ma is None:
         st = lib().ca_backward(ctypes.byref(shape), _tasks_ptr(ta), len(ta), _ptr(Q), _ptr(K), _ptr(V),
                                _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
-                               ws.numel(), _stream_ptr(stream))
+                               wb, _stream_ptr(stream))
     else:
         st = lib().ca_backward_masked(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta), _ptr(Q),
                                       _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK),
-                                      _ptr(dV), _ptr(ws), ws.numel(), _stream_ptr(stream))
+                                      _ptr(dV), _ptr(ws), wb, _stream_ptr(stream))
     _check(st)
     return dQ, dK, dV
 

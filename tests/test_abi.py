@@ -164,3 +164,28 @@ def test_paged_backward_rejects_a_task_reading_a_page_twice():
                                     ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     1 << 30, None)
     assert st == ca.CA_ERR_INVALID and "twice" in ca.lib().ca_last_error().decode()
+
+
+def test_binding_rejects_host_and_mistyped_tensors_before_the_library():
+    """The Python binding checks every tensor against the shape before it
+    hands bare pointers to the library: host tensors and non-tensors are
+    rejected here (no GPU needed); the device-side checks (dtype, size,
+    contiguity on the current device) run in the GPU tests."""
+    import torch
+    s = ca.make_shape(8, 2, 64, 10, 10, 10)
+    t = [(0, 0, 0, 10, 10, 0, 0)]
+    Q = torch.zeros((10, 8, 64), dtype=torch.bfloat16)
+    K = torch.zeros((10, 2, 64), dtype=torch.bfloat16)
+    O = torch.zeros((10, 8, 64), dtype=torch.bfloat16)
+    L = torch.zeros((10, 8))
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ca.CAError, match="Q: not a device tensor"):
+        ca.forward(s, t, Q, K, K, O, L, ws=ws)
+    with pytest.raises(ca.CAError, match="expected a torch tensor"):
+        ca.forward(s, t, np.zeros((10, 8, 64), np.float32), K, K, O, L, ws=ws)
+    with pytest.raises(ca.CAError, match="O_parts: not a device tensor"):
+        ca.merge(s, torch.zeros((2, 10, 8, 64)), torch.zeros((2, 10, 8)), O, L)
+    with pytest.raises(ca.CAError, match="Q: not a device tensor"):
+        ca.backward(s, t, Q, K, K, O, O, L, Q, K, K, ws=ws)
+    with pytest.raises(ca.CAError, match="Q: not a device tensor"):
+        ca.forward_varlen(s, [0, 10], Q, K, K, O, L, ws=ws)

@@ -249,3 +249,45 @@ def test_calls_from_short_lived_threads():
     torch.cuda.synchronize()
     assert torch.equal(O1.view(torch.int16), O0.view(torch.int16)) and torch.equal(L1, L0)
     print("short-lived threads: %d x %d calls identical to the main thread's" % (n_threads, calls), flush=True)
+
+
+def test_binding_rejects_wrong_device_tensors_before_any_launch():
+    """Wrong dtype, too few elements, a non-contiguous view or a workspace
+    that is not bytes raise CAError in the binding; the outputs keep their
+    sentinel values (nothing was launched) and a correct call still works."""
+    announce("binding tensor checks")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    hq, hkv, d, T = 8, 2, 64, 200
+    tasks = I.varlen_tasks([T])
+    s = ca.make_shape(hq, hkv, d, T, T, T)
+    Q = I.randn_bf16((T, hq, d), 3200, device=dev)
+    K = I.randn_bf16((T, hkv, d), 3201, device=dev)
+    V = I.randn_bf16((T, hkv, d), 3202, device=dev)
+    O = torch.full((T, hq, d), 7.0, dtype=torch.bfloat16, device=dev)
+    L = torch.full((T, hq), 7.0, device=dev)
+    bad = [
+        ("dtype", dict(Q=Q.float())),
+        ("elements", dict(O=O[:T - 1])),
+        ("elements", dict(K=K[:T - 1])),
+        ("dtype", dict(O=torch.empty((T, hq, d), device=dev))),          # fp32 O without out_f32
+        ("contiguous", dict(Q=Q.transpose(0, 1))),
+        ("dtype", dict(L=torch.empty((T, hq), dtype=torch.bfloat16, device=dev))),
+    ]
+    for why, kw in bad:
+        args = dict(Q=Q, K=K, V=V, O=O, L=L)
+        args.update(kw)
+        with pytest.raises(ca.CAError, match=why):
+            ca.forward(s, tasks, args["Q"], args["K"], args["V"], args["O"], args["L"])
+    with pytest.raises(ca.CAError, match="workspace"):
+        ca.forward(s, tasks, Q, K, V, O, L, ws=torch.empty(1 << 16, dtype=torch.float32, device=dev))
+    ws = ca.workspace_tensor(ca.forward_workspace(s, tasks), dev)
+    plan = ca.forward_prepare(s, tasks, ws)
+    with pytest.raises(ca.CAError, match="elements"):
+        ca.forward_prepared(plan, Q, K, V, O[:10], L)
+    torch.cuda.synchronize()
+    assert bool((O == 7.0).all()) and bool((L == 7.0).all()), "a rejected call wrote its outputs"
+    ca.forward_prepared(plan, Q, K, V, O, L)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
+    check_forward(O, L, O_ref, L_ref, "after rejected calls")
