@@ -83,8 +83,8 @@ def cpu_baseline(w, Q, K, V, seconds_hint):
     oracle.forward_rows(local, rows, qs, ks, vs, w.scale)
     dt = time.perf_counter() - t0
     pairs = int(np.sum(np.clip(int(t[5]) + rows - int(t[6]) + 1, 0, n_ctx)))
-    flops = oracle.forward_flops(pairs, w.hq, w.d)
-    full = oracle.forward_flops(oracle.visible_pairs(w.tasks), w.hq, w.d)
+    flops = forward_flops(pairs, w.hq, w.d)
+    full = forward_flops(oracle.visible_pairs(w.tasks), w.hq, w.d)
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -96,6 +96,20 @@ def cpu_baseline(w, Q, K, V, seconds_hint):
                       "%d visible pairs per head in %.1f s" % (n_rows, q_len, w.hq, pairs, dt),
             "ns_per_pair_and_head": round(dt / (pairs * w.hq) * 1e9, 3),
             "extrapolated_full_s": round(full / (flops / dt), 1), "cpu_model": cpu}
+
+
+def forward_flops(pairs, hq, d):
+    """The metric's convention: 4 d FLOPs per unmasked (query, key) pair and
+    query head (two d-long products, S = Q K^T and O = P V, at 2 FLOPs per
+    multiply-add)."""
+    return 4 * int(d) * int(pairs) * int(hq)
+
+
+def backward_flops(pairs, hq, d, per_pair=10):
+    """Backward at 10 d FLOPs per unmasked pair and query head (five d-long
+    products: S, dP, dV, dK, dQ); per_pair=8 gives the "twice the forward"
+    convention."""
+    return int(per_pair) * int(d) * int(pairs) * int(hq)
 
 
 def fuse_slots(tables, rows):
@@ -127,7 +141,6 @@ def timed(fn, steps, warmup, stream):
 def secondary(steps=3, warmup=1):
     """The other configurations, each on its own freshly generated inputs."""
     import torch
-    import oracle
     from long_context_core_amd import ca
     from long_context_core_amd import inputs as I
     dev = torch.device("cuda:0")
@@ -151,7 +164,7 @@ def secondary(steps=3, warmup=1):
     w = I.tiny_forward()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 201)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    fl = forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
     call = lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
     warm = timed(call, 50, 5, stream)
     cold = []
@@ -179,7 +192,7 @@ def secondary(steps=3, warmup=1):
     # CA-tasks re-batched forward (LLaMA-34B shape)
     w = I.ca_tasks_34b()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 203)
-    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    fl = forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
     ms = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
     out["ca_tasks_34b_fwd"] = {"workload": w.name, "ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
                                "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
@@ -194,7 +207,7 @@ def secondary(steps=3, warmup=1):
     Om = torch.empty((T, w.hq, w.d), dtype=torch.bfloat16, device=dev)
     Lm = torch.empty((T, w.hq), device=dev)
     mshape = ca.make_shape(w.hq, w.hkv, w.d, T, T, T)
-    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    fl = forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
     ms_f = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
     Ov, Lv = O.view(w.n_parts, T, w.hq, w.d), LSE.view(w.n_parts, T, w.hq)
     ms_m = timed(lambda: ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream), steps, warmup, stream)
@@ -242,7 +255,7 @@ def secondary(steps=3, warmup=1):
 
     ms_lb_slot = timed(ring_lb_per_slot, steps, warmup, stream)
     ms_lb = timed(ring_lb, steps, warmup, stream)
-    fl_lb = oracle.forward_flops(sum(ca.visible_pairs(t) for t in step_tasks), hq, d)
+    fl_lb = forward_flops(sum(ca.visible_pairs(t) for t in step_tasks), hq, d)
     ms_lbm = timed(lambda: ca.merge(mshape, Op, Lp, Om, Lm, stream=stream), steps, warmup, stream)
     # merge bytes: O of every partial row with a visible key (the others carry
     # LSE = -inf and are not read), all partial LSEs, merged O (bf16) + LSE
@@ -301,7 +314,7 @@ def secondary(steps=3, warmup=1):
 
     ms_pp_slot = timed(partial_prefill_per_slot, steps, warmup, stream)
     ms_pp = timed(partial_prefill, steps, warmup, stream)
-    fl_pp = oracle.forward_flops(sum(ca.visible_pairs(t) for t in p_tasks), hq, d)
+    fl_pp = forward_flops(sum(ca.visible_pairs(t) for t in p_tasks), hq, d)
     out["ring_partial_prefill_405b_tp8_miss10"] = {
         "workload": "llama3-405b-tp8 partial prefill, 12800 new over 115200 cached tokens, 4 ranks",
         "launches": N_p, "ms": round(ms_pp, 3), "tflops": round(fl_pp / ms_pp / 1e9, 1),
@@ -437,7 +450,7 @@ def secondary(steps=3, warmup=1):
     del K, V
     pages = ca.kv_pages(table, 512)
     pws = ca.workspace_tensor(ca.forward_workspace(shape, tasks, pages=pages), dev)
-    fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    fl = forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
     ms = timed(lambda: ca.forward(shape, tasks, Q, Ks, Vs, O, LSE, ws=pws, stream=stream, pages=pages),
                steps, warmup, stream)
     out["llama3_8b_packed_128k_paged512"] = {"workload": w.name, "ms": round(ms, 3),
@@ -451,7 +464,7 @@ def secondary(steps=3, warmup=1):
     for shard in (32, 64, 128, 256, 512, 1024, 2048, 4096, 8192):
         w = I.shard_sweep_32k(shard)
         Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 206)
-        fl = oracle.forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+        fl = forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
         ms = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
         sweep[str(shard)] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
         del Q, K, V, O, LSE, ws
@@ -529,7 +542,7 @@ def secondary(steps=3, warmup=1):
     ms_f = timed(lambda: ca.forward(shape, lt, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
     ms_b = timed(lambda: ca.backward(shape, lt, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
                  steps, warmup, stream)
-    ff, bf = oracle.forward_flops(pairs, w.hq, w.d), oracle.backward_flops(pairs, w.hq, w.d)
+    ff, bf = forward_flops(pairs, w.hq, w.d), backward_flops(pairs, w.hq, w.d)
     out["lambda_mask_512k"] = {"workload": w.name + ", lambda mask sink 64 + window 4096",
                                "visible_pairs_per_head": pairs, "fwd_ms": round(ms_f, 2),
                                "fwd_tflops": round(ff / ms_f / 1e9, 1), "bwd_ms": round(ms_b, 2),
@@ -548,7 +561,7 @@ def secondary(steps=3, warmup=1):
     bws = ca.workspace_tensor(ca.backward_workspace(shape, tasks), dev)
     ms_b = timed(lambda: ca.backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
                  steps, warmup, stream)
-    bf = oracle.backward_flops(ca.visible_pairs(tasks), w.hq, w.d)
+    bf = backward_flops(ca.visible_pairs(tasks), w.hq, w.d)
     out["ca_tasks_34b_bwd"] = {"workload": w.name, "ms": round(ms_b, 2), "tflops_10d": round(bf / ms_b / 1e9, 1)}
     log("CA-tasks bwd: %.1f ms, %.1f TFLOP/s at 10d" % (ms_b, bf / ms_b / 1e9))
     del Q, K, V, O, LSE, ws, dO, dQ, dK, dV, bws
@@ -564,8 +577,8 @@ def secondary(steps=3, warmup=1):
     ms_f = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
     ms_b = timed(lambda: ca.backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
                  steps, warmup, stream)
-    ff = oracle.forward_flops(pairs, w.hq, w.d)
-    bf = oracle.backward_flops(pairs, w.hq, w.d)
+    ff = forward_flops(pairs, w.hq, w.d)
+    bf = backward_flops(pairs, w.hq, w.d)
     out["train_8b_512k"] = {"workload": w.name, "fwd_ms": round(ms_f, 2), "fwd_tflops": round(ff / ms_f / 1e9, 1),
                             "bwd_ms": round(ms_b, 2), "bwd_tflops_10d": round(bf / ms_b / 1e9, 1),
                             "bwd_tflops_8d": round(0.8 * bf / ms_b / 1e9, 1),
@@ -610,7 +623,6 @@ def main():
     import torch
     from long_context_core_amd import ca
     from long_context_core_amd import inputs as I
-    import oracle
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -633,8 +645,7 @@ def main():
     tasks = ca.task_array(w.tasks)
     ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
     pairs = ca.visible_pairs(tasks)
-    assert pairs == oracle.visible_pairs(w.tasks)
-    flops = oracle.forward_flops(pairs, w.hq, w.d)
+    flops = forward_flops(pairs, w.hq, w.d)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -646,7 +657,7 @@ def main():
         dO = I.randn_bf16((w.o_rows, w.hq, w.d), seed + 3, device=dev)
         dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
         bws = ca.workspace_tensor(ca.backward_workspace(shape, tasks), dev)
-        flops = oracle.backward_flops(pairs, w.hq, w.d)
+        flops = backward_flops(pairs, w.hq, w.d)
 
         def step():
             ca.backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream)
