@@ -260,3 +260,50 @@ def test_ring_prefill_405b_load_balanced_sampled_and_probe():
     Q, K, V = probe_tensors(whole, np.arange(T))
     Om, Lm = ring_load_balanced(Q, K, V, T, w.hq, w.hkv, w.d)
     check_probe(whole, Om, Lm, "ring-load-balanced-merged")
+
+
+def ring_partial_prefill(Q, K, V, new, cached, hq, hkv, d, N=4):
+    """Partial prefill over a KV cache as the bench times it: per ring step
+    one launch holding the four chunk pairs of every rank (each pair's
+    outputs in its own block of the stacked fp32 partials), then the merge."""
+    torch = torch_cuda()
+    dev = Q.device
+    Tq = sum(new)
+    Tk = Tq + sum(cached)
+    Op = torch.empty((4 * N, Tq, hq, d), device=dev)
+    Lp = torch.empty((4 * N, Tq, hq), device=dev)
+    shape = ca.make_shape(hq, hkv, d, Tq, Tk, 4 * Tq, out_f32=True)
+    for step in range(N):
+        tables = []
+        for slot in range(4):
+            t = ca.ring_prefill_step_tasks(new, cached, N, step, slot)
+            t["o_off"] += slot * Tq
+            tables.append(t)
+        ca.forward(shape, np.concatenate(tables), Q, K, V, Op[4 * step:4 * step + 4], Lp[4 * step:4 * step + 4])
+    Om = torch.empty((Tq, hq, d), dtype=torch.bfloat16, device=dev)
+    Lm = torch.empty((Tq, hq), device=dev)
+    ca.merge(ca.make_shape(hq, hkv, d, Tq, Tq, Tq), Op, Lp, Om, Lm)
+    torch.cuda.synchronize()
+    del Op, Lp
+    return Om, Lm
+
+
+def test_ring_partial_prefill_405b_miss10_sampled_and_probe():
+    """12,800 new tokens over a 115,200-token cache (10 % miss), Llama3-405B
+    TP8 share, 4 ranks: sampled rows against the oracle of one query block
+    over the whole cache, and the mask probe on every new row."""
+    announce("fullsize ring partial prefill 405b tp8, 12800 new over 115200 cached, 4 ranks")
+    w0 = I.ring_prefill_405b_tp8()
+    hq, hkv, d = w0.hq, w0.hkv, w0.d
+    T_new, P_c = 12800, 115200
+    whole = I.Workload("whole", hq, hkv, d, np.array([[0, 0, 0, T_new, T_new + P_c, P_c, 0]]),
+                       T_new, T_new + P_c, T_new)
+    Q, K, V = device_inputs(whole, 215)
+    Om, Lm = ring_partial_prefill(Q, K, V, [T_new], [P_c], hq, hkv, d)
+    c = T_new // 8
+    rows = np.unique(np.concatenate([np.arange(3), [c - 1, c, 4 * c - 1, 4 * c, 7 * c], np.arange(T_new - 3, T_new),
+                                     np.random.default_rng(6).integers(0, T_new, 16)]))
+    sampled_check(whole, [(0, rows)], Q, K, V, Om, Lm, label="ring-partial-prefill-sampled")
+    Q, K, V = probe_tensors(whole, np.arange(T_new + P_c))
+    Om, Lm = ring_partial_prefill(Q, K, V, [T_new], [P_c], hq, hkv, d)
+    check_probe(whole, Om, Lm, "ring-partial-prefill-merged")
