@@ -1,0 +1,85 @@
+"""Seeded random CA-task tables through the forward and the backward, against
+the fp64 oracle element by element.  The tables mix what the fixed cases
+cover one at a time: empty and single-row query shards (single rows go to
+the split-KV decode kernel, the rest to the tiled kernel, in one call),
+empty contexts, queries positioned before their first key (rows with no
+visible key), contexts shorter or longer than the shard, K/V ranges shared
+between tasks, and every GQA grouping at d = 64 and 128."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_core_amd import ca
+from long_context_core_amd import inputs as I
+from tests.gpu_util import GRAD_REL_FRO, announce, check_forward, rel_fro, torch_cuda, widen
+
+pytestmark = pytest.mark.gpu
+
+GEOMETRIES = [(8, 2), (4, 4), (16, 1), (6, 2), (12, 4), (32, 8)]
+
+
+def random_tables(seed):
+    rng = np.random.default_rng(9000 + seed)
+    hq, hkv = GEOMETRIES[seed % len(GEOMETRIES)]
+    d = (64, 128)[(seed // len(GEOMETRIES)) % 2]
+    kv_rows = int(rng.integers(200, 1500))
+    rows, q0 = [], 0
+    for _ in range(int(rng.integers(1, 7))):
+        q_len = int(rng.choice([0, 1, 1, int(rng.integers(2, 40)), int(rng.integers(40, 400))]))
+        kv_len = int(rng.choice([0, 1] + [int(rng.integers(2, kv_rows + 1))] * 4))
+        kv_off = int(rng.integers(0, kv_rows - kv_len + 1))
+        kv_pos0 = int(rng.integers(0, 600))
+        # mostly inside the context; sometimes before its first position (rows
+        # with no key) or past its end (every key visible)
+        mode = rng.random()
+        if mode < 0.7:
+            shift = int(rng.integers(0, kv_len + 1))
+        elif mode < 0.85:
+            shift = -int(rng.integers(1, 200))
+        else:
+            shift = kv_len + int(rng.integers(0, 300))
+        q_pos0 = max(0, kv_pos0 + shift)
+        rows.append((q0, kv_off, q0, q_len, kv_len, q_pos0, kv_pos0))
+        q0 += q_len
+    return np.array(rows, dtype=np.int64), hq, hkv, d, max(q0, 1), kv_rows
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_task_tables_forward_and_backward(seed):
+    tasks, hq, hkv, d, q_rows, kv_rows = random_tables(seed)
+    announce("random task table seed %d: hq=%d hkv=%d d=%d tasks=%s" % (seed, hq, hkv, d, tasks.tolist()))
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((q_rows, hq, d), 9100 + seed)
+    K = I.randn_bf16((kv_rows, hkv, d), 9200 + seed)
+    V = I.randn_bf16((kv_rows, hkv, d), 9300 + seed)
+    dO = I.randn_bf16((q_rows, hq, d), 9400 + seed)
+    Qd, Kd, Vd, dOd = Q.to(dev), K.to(dev), V.to(dev), dO.to(dev)
+    shape = ca.make_shape(hq, hkv, d, q_rows, kv_rows, q_rows)
+    O = torch.full((q_rows, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((q_rows, hq), float("nan"), device=dev)
+    ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    O_ref, L_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), scale, o_rows=q_rows)
+    if np.isnan(L_ref).all():
+        return                                   # no query rows at all
+    check_forward(O, LSE, O_ref, L_ref, "random-%d" % seed)
+    dQ = torch.full_like(Qd, float("nan"))
+    dK = torch.full_like(Kd, float("nan"))
+    dV = torch.full_like(Vd, float("nan"))
+    ca.backward(shape, tasks, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV)
+    torch.cuda.synchronize()
+    ref = oracle.backward(tasks, widen(Q), widen(K), widen(V), widen(dO), scale)
+    covered = ~np.isnan(L_ref[:, 0])
+    for name, g, r in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+        gw = widen(g)
+        if name == "dQ":
+            gw, r = gw[covered], r[covered]
+        assert np.all(np.isfinite(gw)), "%s not finite" % name
+        e = rel_fro(gw, r)
+        print("random-%d %s relF=%.3e" % (seed, name, e), flush=True)
+        assert e <= GRAD_REL_FRO, name
