@@ -4,7 +4,8 @@ cover one at a time: empty and single-row query shards (single rows go to
 the split-KV decode kernel, the rest to the tiled kernel, in one call),
 empty contexts, queries positioned before their first key (rows with no
 visible key), contexts shorter or longer than the shard, K/V ranges shared
-between tasks, and every GQA grouping at d = 64 and 128."""
+between tasks, and every GQA grouping at d = 64 and 128; each table also runs
+with a random sink + sliding-window mask per task."""
 
 import math
 
@@ -47,10 +48,24 @@ def random_tables(seed):
     return np.array(rows, dtype=np.int64), hq, hkv, d, max(q0, 1), kv_rows
 
 
+def with_masks(tasks, seed):
+    """Columns 8-9: a sliding window (0 = none, else 1-700 positions) and a
+    sink (the first 0-150 positions of the document) per task."""
+    rng = np.random.default_rng(9500 + seed)
+    n = len(tasks)
+    window = np.where(rng.random(n) < 0.2, 0, rng.integers(1, 701, n))
+    sink = np.where(rng.random(n) < 0.3, 0, rng.integers(0, 151, n))
+    return np.concatenate([tasks, window[:, None], sink[:, None]], axis=1).astype(np.int64)
+
+
+@pytest.mark.parametrize("masked", [False, True])
 @pytest.mark.parametrize("seed", range(16))
-def test_random_task_tables_forward_and_backward(seed):
+def test_random_task_tables_forward_and_backward(seed, masked):
     tasks, hq, hkv, d, q_rows, kv_rows = random_tables(seed)
-    announce("random task table seed %d: hq=%d hkv=%d d=%d tasks=%s" % (seed, hq, hkv, d, tasks.tolist()))
+    if masked:
+        tasks = with_masks(tasks, seed)
+    announce("random task table seed %d masked=%s: hq=%d hkv=%d d=%d tasks=%s"
+             % (seed, masked, hq, hkv, d, tasks.tolist()))
     torch = torch_cuda()
     dev = torch.device("cuda:0")
     Q = I.randn_bf16((q_rows, hq, d), 9100 + seed)
