@@ -98,3 +98,49 @@ def test_random_task_tables_forward_and_backward(seed, masked):
         e = rel_fro(gw, r)
         print("random-%d %s relF=%.3e" % (seed, name, e), flush=True)
         assert e <= GRAD_REL_FRO, name
+
+
+def paged_layout(tasks, seed):
+    """The random table's contexts moved into a virtual row space where each
+    starts on a 128-row boundary (a fifth of the tasks reuse the previous
+    task's context start: a shared prefix); random page size."""
+    rng = np.random.default_rng(9600 + seed)
+    P = int(rng.choice([128, 256, 512]))
+    t = tasks.copy()
+    run, prev = 0, None
+    for i in range(len(t)):
+        kv_len = int(t[i, 4])
+        if prev is not None and kv_len <= prev[1] and rng.random() < 0.2:
+            t[i, 1] = prev[0]
+            continue
+        t[i, 1] = run
+        prev = (run, kv_len)
+        run += -(-max(kv_len, 1) // 128) * 128
+    n_vp = max(1, -(-run // P))
+    return t, P, n_vp
+
+
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("seed", range(8))
+def test_random_task_tables_paged(seed, masked):
+    """The same random tables over paged K/V in a shuffled page store: the
+    paged forward equals the unpaged one bit for bit and the oracle; the paged
+    backward's page-store gradients match the oracle."""
+    from tests.test_gpu_paged import check_grads, check_paged, run_paged, run_paged_backward
+
+    tasks, hq, hkv, d, q_rows, _ = random_tables(seed)
+    tasks, P, n_vp = paged_layout(tasks, seed)
+    masks = with_masks(tasks, seed)[:, 7:9] if masked else None
+    announce("random paged table seed %d masked=%s: P=%d n_vp=%d hq=%d hkv=%d d=%d tasks=%s"
+             % (seed, masked, P, n_vp, hq, hkv, d, tasks.tolist()))
+    outs, O_ref, L_ref = run_paged(tasks, masks, hq, hkv, d, q_rows, n_vp, P, 9700 + seed)
+    if np.isnan(L_ref).all():
+        return
+    check_paged(outs, O_ref, L_ref, "random-paged-%d" % seed)
+    n_phys = n_vp + 5
+    table = I.page_table(n_vp, n_phys, 9800 + seed)
+    got, ref, _ = run_paged_backward(tasks, table, P, n_phys, hq, hkv, d, q_rows, 9900 + seed, masks=masks)
+    covered = ~np.isnan(L_ref[:, 0])
+    got = (got[0][torch_cuda().from_numpy(np.flatnonzero(covered))], got[1], got[2])
+    ref = (ref[0][covered], ref[1], ref[2])
+    check_grads(got, ref, "random-paged-bwd-%d" % seed)
