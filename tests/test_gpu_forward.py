@@ -291,3 +291,40 @@ def test_binding_rejects_wrong_device_tensors_before_any_launch():
     torch.cuda.synchronize()
     O_ref, L_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
     check_forward(O, L, O_ref, L_ref, "after rejected calls")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_merge_random_part_counts_and_ranges(seed):
+    """Equation 4 over random part counts (1 to 40, past the kernel's eight
+    partials in flight), row counts and head geometries, with LSEs spread over
+    hundreds of units around large offsets and random empty (-inf) partials."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(7000 + seed)
+    S = int(rng.choice([1, 2, 3, 7, 8, 9, 16, 36, 40]))
+    T = int(rng.integers(1, 700))
+    hq = int(rng.choice([1, 4, 16, 32]))
+    d = int(rng.choice([64, 128]))
+    announce("merge random seed %d: S=%d T=%d hq=%d d=%d" % (seed, S, T, hq, d))
+    g = torch.Generator().manual_seed(7100 + seed)
+    Op = torch.randn(S, T, hq, d, generator=g)
+    spread = float(rng.choice([1.0, 20.0, 300.0]))
+    offset = float(rng.choice([0.0, 1e4, -1e4]))
+    Lp = torch.randn(S, T, hq, generator=g) * spread + offset
+    empty = torch.from_numpy(rng.random((S, T, hq)) < 0.3)
+    Lp[empty] = -float("inf")
+    Op[empty.unsqueeze(-1).expand_as(Op)] = float("nan")      # never read
+    out_f32 = bool(seed % 2)
+    Om = torch.empty(T, hq, d, device="cuda", dtype=torch.float32 if out_f32 else torch.bfloat16)
+    Lm = torch.empty(T, hq, device="cuda")
+    ca.merge(ca.make_shape(hq, 1, d, T, T, T, out_f32=out_f32), Op.cuda(), Lp.cuda(), Om, Lm)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.merge(np.nan_to_num(Op.double().numpy(), nan=0.0), Lp.double().numpy())
+    got_o, got_l = widen(Om), widen(Lm)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(Lref))
+    fin = np.isfinite(Lref)
+    # fp32 LSE around |offset| = 1e4 carries ~1e-3 of absolute rounding
+    ltol = 1e-5 * max(1.0, abs(offset) + spread)
+    assert np.max(np.abs(got_l[fin] - Lref[fin]), initial=0.0) <= ltol
+    assert np.all(np.isfinite(got_o))
+    assert np.max(np.abs(got_o - Oref)) < (2e-5 if out_f32 else 2e-2)
+    assert np.all(got_o[~fin] == 0)
