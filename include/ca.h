@@ -258,8 +258,12 @@ ca_status ca_backward_paged(const ca_shape* shape, const ca_task* tasks_host, co
  * replayed; Q, K, V, O and LSE may differ from call to call but must have the
  * shape and task table the plan was made for.  The caller keeps ws unchanged
  * while the plan is in use.  ws_bytes as for the direct call (ca_forward /
- * _masked / _paged _workspace).  Errors as for the direct call; the launch
- * rejects a plan that ca_forward_prepare did not fill. */
+ * _masked / _paged _workspace).  The plan records the device current at
+ * ca_forward_prepare (where ws lives); ca_forward_prepared must run with the
+ * same device current.  Errors as for the direct call; the launch returns
+ * CA_ERR_INVALID for a plan that ca_forward_prepare did not fill or that was
+ * prepared on another device, and CA_ERR_HIP if the current device cannot be
+ * read. */
 typedef struct {
   uint64_t opaque[40];
 } ca_forward_plan;

@@ -426,6 +426,7 @@ void build_decode_items(const ca_shape* s, const ca_task* t, const ca_task_mask*
 struct PreparedFwd {
   uint64_t magic;
   void* ws;
+  int32_t device;           // current device at preparation: ws lives there
   ca_shape shape;
   int32_t group, hpw;
   int32_t n_items, n_dec_items, n_split;
@@ -449,6 +450,14 @@ ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mas
   pf.magic = kPlanMagic;
   pf.ws = ws;
   pf.shape = *s;
+  if (!tensors) {
+    // a plan is launched later, perhaps with another device current
+    const hipError_t e = hipGetDevice(&pf.device);
+    if (e != hipSuccess) {
+      pf.magic = 0;
+      return hip_fail(e, "hipGetDevice");
+    }
+  }
   if (p.n_items == 0 && p.n_dec_items == 0) return CA_OK;
   if (tensors)
     for (int i = 0; i < 5; ++i)
@@ -957,6 +966,11 @@ ca_status ca_forward_prepared(const ca_forward_plan* plan, const void* Q, const 
   PreparedFwd pf;
   std::memcpy(&pf, plan, sizeof(pf));
   if (pf.magic != kPlanMagic) return fail(CA_ERR_INVALID, "plan was not filled by ca_forward_prepare");
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != pf.device)
+    return fail(CA_ERR_INVALID, "plan was prepared on device %d, device %d is current", pf.device, dev);
   return launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
 }
 

@@ -159,3 +159,34 @@ def test_graph_replays_masked_and_paged_calls():
     Vv = oracle.virtual_rows(widen(Vs), table, P)
     O_ref, L_ref = oracle.forward(dt, widen(Qd), Kv, Vv, 1 / math.sqrt(D))
     check_forward(Od, Ld, O_ref, L_ref, "paged-decode-replayed")
+
+
+def test_prepared_call_rejects_a_plan_from_another_device():
+    """A plan records the device current at preparation (its queue lives in
+    that device's workspace); a launch with another device current is
+    rejected.  With one GPU the recorded device is edited instead: it is the
+    third 8-byte word of the plan (after the tag and the workspace pointer),
+    a layout private to this test and the library."""
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    tasks = I.varlen_tasks([300])
+    s = ca.make_shape(8, 2, 128, 300, 300, 300)
+    Q = I.randn_bf16((300, 8, 128), 2750, device=dev)
+    K = I.randn_bf16((300, 2, 128), 2751, device=dev)
+    O = torch.full((300, 8, 128), 3.0, dtype=torch.bfloat16, device=dev)
+    L = torch.full((300, 8), 3.0, device=dev)
+    ws = ca.workspace_tensor(ca.forward_workspace(s, tasks), dev)
+    plan = ca.forward_prepare(s, tasks, ws)
+    assert plan.opaque[2] & 0xffffffff == torch.cuda.current_device()
+    saved = plan.opaque[2]
+    plan.opaque[2] = 7
+    with pytest.raises(ca.CAError, match="prepared on device 7"):
+        ca.forward_prepared(plan, Q, K, K, O, L)
+    torch.cuda.synchronize()
+    assert bool((O == 3.0).all())
+    plan.opaque[2] = saved
+    ca.forward_prepared(plan, Q, K, K, O, L)
+    O2, L2 = torch.empty_like(O), torch.empty_like(L)
+    ca.forward(s, tasks, Q, K, K, O2, L2)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O2.view(torch.int16)) and torch.equal(L, L2)
