@@ -190,3 +190,61 @@ def test_prepared_call_rejects_a_plan_from_another_device():
     ca.forward(s, tasks, Q, K, K, O2, L2)
     torch.cuda.synchronize()
     assert torch.equal(O.view(torch.int16), O2.view(torch.int16)) and torch.equal(L, L2)
+
+
+def test_graph_replays_a_partial_prefill_ring():
+    """The partial-prefill ring's per-step launches (each step's four chunk
+    pairs fused into one table, one prepared plan per step) and the merge,
+    captured in one graph: every replay equals the direct calls bit for bit
+    and the last one the oracle of the whole query block over the cache."""
+    announce("graph-captured partial prefill ring: N=4")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    N, hq, hkv, d = 4, 8, 2, 128
+    new, cached = [700, 1, 333], [1500, 0, 64]
+    Tq, Tk = sum(new), sum(new) + sum(cached)
+    K = I.randn_bf16((Tk, hkv, d), 2761, device=dev)
+    V = I.randn_bf16((Tk, hkv, d), 2762, device=dev)
+    Q = I.randn_bf16((Tq, hq, d), 2760, device=dev)
+    fshape = ca.make_shape(hq, hkv, d, Tq, Tk, 4 * Tq, out_f32=True)
+    mshape = ca.make_shape(hq, hkv, d, Tq, Tq, Tq)
+    tables = []
+    for step in range(N):
+        parts = []
+        for slot in range(4):
+            t = ca.ring_prefill_step_tasks(new, cached, N, step, slot)
+            t["o_off"] += slot * Tq
+            parts.append(t)
+        tables.append(np.concatenate(parts))
+    bufs = [(torch.empty((4 * N, Tq, hq, d), device=dev), torch.empty((4 * N, Tq, hq), device=dev),
+             torch.empty((Tq, hq, d), dtype=torch.bfloat16, device=dev), torch.empty((Tq, hq), device=dev))
+            for _ in range(2)]
+    side = torch.cuda.Stream()
+    ws = [ca.workspace_tensor(ca.forward_workspace(fshape, t), dev) for t in tables]
+    plans = [ca.forward_prepare(fshape, t, w, stream=side) for t, w in zip(tables, ws)]
+    side.synchronize()
+    Op, Lp, Om, Lm = bufs[0]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for step, plan in enumerate(plans):
+            ca.forward_prepared(plan, Q, K, V, Op[4 * step:4 * step + 4], Lp[4 * step:4 * step + 4], stream=st)
+        ca.merge(mshape, Op, Lp, Om, Lm, stream=st)
+    Op2, Lp2, Om2, Lm2 = bufs[1]
+    for rep in range(3):
+        Q.copy_(I.randn_bf16((Tq, hq, d), 2770 + rep, device=dev))
+        for step, t in enumerate(tables):
+            ca.forward(fshape, t, Q, K, V, Op2[4 * step:4 * step + 4], Lp2[4 * step:4 * step + 4])
+        ca.merge(mshape, Op2, Lp2, Om2, Lm2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(Om.view(torch.int16), Om2.view(torch.int16)) and torch.equal(Lm, Lm2)
+        print("partial prefill ring replay %d: identical to the direct calls: %s" % (rep, same), flush=True)
+        assert same
+    q0 = np.concatenate([[0], np.cumsum(new)])
+    k0 = np.concatenate([[0], np.cumsum(np.array(new) + np.array(cached))])
+    whole = np.array([(q0[s], k0[s], q0[s], new[s], new[s] + cached[s], cached[s], 0) for s in range(len(new))],
+                     dtype=np.int64)
+    O_ref, L_ref = oracle.forward(whole, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
+    check_forward(Om, Lm, O_ref, L_ref, "partial-prefill-ring-replayed")
