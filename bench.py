@@ -314,14 +314,25 @@ def secondary(steps=3, warmup=1):
 
     ms_pp_slot = timed(partial_prefill_per_slot, steps, warmup, stream)
     ms_pp = timed(partial_prefill, steps, warmup, stream)
+    # the same four launches and merge from prepared plans, captured in a graph
+    side = torch.cuda.Stream()
+    pp_plans = [ca.forward_prepare(pfshape, t, w_, stream=side) for t, w_ in zip(pf_tasks, pf_ws)]
+    side.synchronize()
+    g_pp = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_pp):
+        st_ = torch.cuda.current_stream()
+        for k_, plan_ in enumerate(pp_plans):
+            ca.forward_prepared(plan_, Q, K, V, Op[4 * k_:4 * k_ + 4], Lp[4 * k_:4 * k_ + 4], stream=st_)
+        ca.merge(pm_shape, Op, Lp, Opm, Lpm, stream=st_)
+    ms_pp_graph = timed(g_pp.replay, steps, warmup, stream)
     fl_pp = forward_flops(sum(ca.visible_pairs(t) for t in p_tasks), hq, d)
     out["ring_partial_prefill_405b_tp8_miss10"] = {
         "workload": "llama3-405b-tp8 partial prefill, 12800 new over 115200 cached tokens, 4 ranks",
         "launches": N_p, "ms": round(ms_pp, 3), "tflops": round(fl_pp / ms_pp / 1e9, 1),
-        "ms_one_launch_per_slot": round(ms_pp_slot, 3)}
+        "ms_one_launch_per_slot": round(ms_pp_slot, 3), "ms_graph_replay": round(ms_pp_graph, 3)}
     log("ring partial prefill (10%% miss, 4 ranks, 4 launches + merge): %.2f ms, %.1f TFLOP/s "
-        "(16 launches: %.2f ms)" % (ms_pp, fl_pp / ms_pp / 1e9, ms_pp_slot))
-    del Q, K, V, Op, Lp, p_ws, pf_ws, Opm, Lpm
+        "(16 launches: %.2f ms; graph replay: %.2f ms)" % (ms_pp, fl_pp / ms_pp / 1e9, ms_pp_slot, ms_pp_graph))
+    del Q, K, V, Op, Lp, p_ws, pf_ws, Opm, Lpm, g_pp, pp_plans
     torch.cuda.empty_cache()
 
     # pass-KV / pass-Q choice for Llama3-405B under TP8 on MI355X ranks: C is
