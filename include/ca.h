@@ -126,9 +126,19 @@ typedef struct {
 size_t ca_forward_workspace(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks);
 
 /* O and LSE for every row of every task, in one fused launch over all tasks
- * (fully masked key tiles are never visited).  Rows of O/LSE outside every
- * task are not written.  Errors: CA_ERR_INVALID for a null pointer, hq/hkv
- * not dividing, scale not finite or not positive, negative lengths or any row range past
+ * (fully masked key tiles are never visited).  A CA-task is a query shard and
+ * the key/value context it attends to; any set of them, from any documents,
+ * composes into one call ("Efficient Long-context Language Model Training by
+ * Core Attention Disaggregation", Section 3.4, The CA-Task Abstraction and
+ * Property 2, Composability); the per-row LSE is the log of the softmax
+ * normaliser ("Context Parallelism for Scalable Million-Token Inference",
+ * Section 3.4, Merge Attention).  Rows of O/LSE outside every task are not
+ * written.  The call builds its work queue on the host and copies it into ws
+ * on the stream, so it refuses a stream that is being captured into a graph
+ * (CA_ERR_INVALID; ca_forward_prepare / ca_forward_prepared is the
+ * capturable form).  Errors: CA_ERR_INVALID for a null pointer, hq/hkv not
+ * dividing, hq above 4096, scale not finite or not positive, negative
+ * lengths, row counts above 2^40 or any row range past
  * q_rows/kv_rows/o_rows; CA_ERR_UNSUPPORTED for d not in {64, 128};
  * CA_ERR_WORKSPACE when ws_bytes < ca_forward_workspace(...). */
 ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks,
@@ -177,9 +187,13 @@ ca_status ca_forward_paged(const ca_shape* shape, const ca_task* tasks_host, con
                            int32_t n_tasks, const ca_kv_pages* pages, const void* Q, const void* K,
                            const void* V, void* O, float* LSE, void* ws, size_t ws_bytes, void* stream);
 
-/* Packed causal documents: document i occupies rows [cu[i], cu[i+1]) of Q,
- * K, V, O and LSE (the task {cu[i], cu[i], cu[i], l, l, 0, 0}).
- * cu_seqlens_host has n_docs + 1 non-decreasing entries starting at 0. */
+/* Packed causal documents: several documents concatenated into one chunk,
+ * each token attending only to earlier tokens of its own document ("Efficient
+ * Long-context Language Model Training by Core Attention Disaggregation",
+ * Section 2, document packing).  Document i occupies rows [cu[i], cu[i+1])
+ * of Q, K, V, O and LSE (the task {cu[i], cu[i], cu[i], l, l, 0, 0}).
+ * cu_seqlens_host has n_docs + 1 non-decreasing entries starting at 0.
+ * Errors and graph capture as ca_forward. */
 size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu_seqlens_host,
                                    int32_t n_docs);
 ca_status ca_forward_varlen(const ca_shape* shape, const int32_t* cu_seqlens_host, int32_t n_docs,
@@ -212,10 +226,14 @@ size_t ca_backward_workspace(const ca_shape* shape, const ca_task* tasks_host, i
 
 /* Gradients of sum(O * dO): dQ, dK, dV (bf16, accumulated in fp32).  O, dO
  * (bf16) and LSE (fp32) are the forward's outputs at rows o_off..; the
- * attention probabilities are recomputed from Q, K and LSE.  dK and dV sum
- * over the query heads of each KV head's group and over every task whose
- * context covers a row.  Every row of dQ, dK and dV is written (rows that no
- * task touches get 0).  Errors as for ca_forward (CA_OUT_F32 is rejected). */
+ * attention probabilities are recomputed from Q, K and the saved per-row
+ * softmax statistics rather than stored ("Efficient Long-context Language
+ * Model Training by Core Attention Disaggregation", Section 3.4, Property 1).
+ * dK and dV sum over the query heads of each KV head's group and over every
+ * task whose context covers a row.  Every row of dQ, dK and dV is written
+ * (rows that no task touches get 0).  No atomics: tasks that share rows run
+ * in separate passes, so results are bitwise reproducible.  Errors and graph
+ * capture as for ca_forward (CA_OUT_F32 is rejected). */
 ca_status ca_backward(const ca_shape* shape, const ca_task* tasks_host, int32_t n_tasks,
                       const void* Q, const void* K, const void* V, const void* O,
                       const void* dO, const float* LSE, void* dQ, void* dK, void* dV,

@@ -350,9 +350,16 @@ def forward_workspace(shape, tasks, masks=None, pages=None):
     return int(lib().ca_forward_masked_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta)))
 
 
-def workspace_tensor(nbytes, device):
+def workspace_tensor(nbytes, device, stream=None):
+    """A temporary workspace from torch's caching allocator.  Its memory is
+    tied to the stream that was current when it was allocated; when the call
+    runs on another stream, record_stream keeps the allocator from handing the
+    block to a later allocation before that stream's kernels are done."""
     import torch
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(ws.device):
+        ws.record_stream(stream)
+    return ws
 
 
 def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None, pages=None):
@@ -363,7 +370,7 @@ def forward(shape, tasks, Q, K, V, O, LSE, ws=None, stream=None, masks=None, pag
     ta, ma = split_tasks(tasks, masks)
     _check_forward_tensors(shape, Q, K, V, O, LSE)
     if ws is None:
-        ws = workspace_tensor(forward_workspace(shape, ta, ma, pages), Q.device)
+        ws = workspace_tensor(forward_workspace(shape, ta, ma, pages), Q.device, stream)
     wb = _ws_bytes(ws)
     if pages is not None:
         st = lib().ca_forward_paged(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
@@ -410,7 +417,7 @@ def forward_varlen(shape, cu_seqlens, Q, K, V, O, LSE, ws=None, stream=None):
     cup = cu.ctypes.data_as(ctypes.c_void_p)
     _check_forward_tensors(shape, Q, K, V, O, LSE)
     if ws is None:
-        ws = workspace_tensor(lib().ca_forward_varlen_workspace(ctypes.byref(shape), cup, n), Q.device)
+        ws = workspace_tensor(lib().ca_forward_varlen_workspace(ctypes.byref(shape), cup, n), Q.device, stream)
     st = lib().ca_forward_varlen(ctypes.byref(shape), cup, n, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
                                  _ptr(LSE), _ptr(ws), _ws_bytes(ws), _stream_ptr(stream))
     _check(st)
@@ -451,7 +458,7 @@ def backward(shape, tasks, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=None, stream=None
         _need(x, what, "bf16", rows * heads * d)
     _need(LSE, "LSE", "f32", shape.o_rows * hq)
     if ws is None:
-        ws = workspace_tensor(backward_workspace(shape, ta, ma, pages), Q.device)
+        ws = workspace_tensor(backward_workspace(shape, ta, ma, pages), Q.device, stream)
     wb = _ws_bytes(ws)
     if pages is not None:
         st = lib().ca_backward_paged(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),

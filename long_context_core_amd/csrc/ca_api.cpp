@@ -107,6 +107,11 @@ ca_status check_masks(const ca_task_mask* m, int32_t n) {
   return CA_OK;
 }
 
+// Bounds that keep every size product (rows x heads x d x 4 bytes) inside
+// int64: far beyond any buffer a device holds.
+constexpr int64_t kMaxRows = int64_t(1) << 40;
+constexpr int32_t kMaxHeads = 4096;
+
 ca_status check_shape(const ca_shape* s) {
   if (!s) return fail(CA_ERR_INVALID, "shape is NULL");
   if (s->hq < 1 || s->hkv < 1) return fail(CA_ERR_INVALID, "hq=%d hkv=%d must be >= 1", s->hq, s->hkv);
@@ -114,8 +119,11 @@ ca_status check_shape(const ca_shape* s) {
   if (s->d != 64 && s->d != 128) return fail(CA_ERR_UNSUPPORTED, "head dim d=%d not supported (64, 128)", s->d);
   // The kernels take row maxima of the unscaled scores: the scale must be positive.
   if (!std::isfinite(s->scale) || !(s->scale > 0.f)) return fail(CA_ERR_INVALID, "scale must be finite and > 0");
+  if (s->hq > kMaxHeads) return fail(CA_ERR_INVALID, "hq=%d > %d", s->hq, kMaxHeads);
   if (s->q_rows < 0 || s->kv_rows < 0 || s->o_rows < 0)
     return fail(CA_ERR_INVALID, "negative row count");
+  if (s->q_rows > kMaxRows || s->kv_rows > kMaxRows || s->o_rows > kMaxRows)
+    return fail(CA_ERR_INVALID, "row count above 2^40");
   if (s->flags & ~(uint32_t)CA_OUT_F32) return fail(CA_ERR_INVALID, "unknown flags 0x%x", s->flags);
   return CA_OK;
 }
@@ -129,15 +137,18 @@ ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n, int64_t kv
     const ca_task& k = t[i];
     if (k.q_len < 0 || k.kv_len < 0) return fail(CA_ERR_INVALID, "task %d: negative length", i);
     if (k.q_off < 0 || k.kv_off < 0 || k.o_off < 0) return fail(CA_ERR_INVALID, "task %d: negative offset", i);
-    if (k.q_off + k.q_len > s->q_rows)
-      return fail(CA_ERR_INVALID, "task %d: query rows [%lld, %lld) past q_rows=%lld", i,
-                  (long long)k.q_off, (long long)(k.q_off + k.q_len), (long long)s->q_rows);
-    if (k.kv_off + k.kv_len > kv_limit)
-      return fail(CA_ERR_INVALID, "task %d: context rows [%lld, %lld) past %lld", i,
-                  (long long)k.kv_off, (long long)(k.kv_off + k.kv_len), (long long)kv_limit);
-    if (k.o_off + k.q_len > s->o_rows)
-      return fail(CA_ERR_INVALID, "task %d: output rows [%lld, %lld) past o_rows=%lld", i,
-                  (long long)k.o_off, (long long)(k.o_off + k.q_len), (long long)s->o_rows);
+    // Compared as off > rows - len: the lengths are non-negative int32 and the
+    // row counts non-negative, so nothing here can overflow (off + len could,
+    // for offsets near INT64_MAX).
+    if (k.q_off > s->q_rows - k.q_len)
+      return fail(CA_ERR_INVALID, "task %d: %d query rows from row %lld past q_rows=%lld", i, k.q_len,
+                  (long long)k.q_off, (long long)s->q_rows);
+    if (k.kv_off > kv_limit - k.kv_len)
+      return fail(CA_ERR_INVALID, "task %d: %d context rows from row %lld past %lld", i, k.kv_len,
+                  (long long)k.kv_off, (long long)kv_limit);
+    if (k.o_off > s->o_rows - k.q_len)
+      return fail(CA_ERR_INVALID, "task %d: %d output rows from row %lld past o_rows=%lld", i, k.q_len,
+                  (long long)k.o_off, (long long)s->o_rows);
     if (k.q_pos0 < -(int64_t(1) << 40) || k.q_pos0 > (int64_t(1) << 40) ||
         k.kv_pos0 < -(int64_t(1) << 40) || k.kv_pos0 > (int64_t(1) << 40))
       return fail(CA_ERR_INVALID, "task %d: positions out of range", i);
@@ -235,7 +246,23 @@ struct StagingRing {
 constexpr int kMaxDevices = 64;
 thread_local StagingRing g_staging[kMaxDevices];
 
+// A graph captured around the copy would keep reading a staging buffer that
+// later calls overwrite, so calls that upload refuse a capturing stream (the
+// prepared forward is the capturable form).  Checked before anything is
+// enqueued.
+ca_status check_not_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(CA_ERR_INVALID, "the stream is capturing: calls that upload a work queue are not capturable "
+                                "(capture ca_forward_prepared instead)");
+  return CA_OK;
+}
+
 ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
+  ca_status cst = check_not_capturing(s);
+  if (cst != CA_OK) return cst;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -420,50 +447,27 @@ void build_decode_items(const ca_shape* s, const ca_task* t, const ca_task_mask*
   });
 }
 
-// Everything a forward call needs at launch time once its work queue is in
-// the workspace: the shape, the queue layout and counts.  Plain data, so it
-// can live in the caller's ca_forward_plan.
-struct PreparedFwd {
-  uint64_t magic;
-  void* ws;
-  int32_t device;           // current device at preparation: ws lives there
-  ca_shape shape;
-  int32_t group, hpw;
-  int32_t n_items, n_dec_items, n_split;
-  int32_t has_masks, has_pages, page_shift;
-  uint32_t page_bytes;
-  uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_part_o, off_part_l;
-};
 constexpr uint64_t kPlanMagic = 0x43414657504c414eull;   // plan tag, checked at launch
-static_assert(sizeof(PreparedFwd) <= sizeof(ca_forward_plan), "ca_forward_plan too small");
+static_assert(sizeof(ca::PreparedFwd) <= sizeof(ca_forward_plan), "ca_forward_plan too small");
 
-// Validates, plans, builds the queue and uploads it into ws on the stream.
-// With tensors given (a direct call) they are checked before the upload, so
-// a rejected call changes nothing.
-ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
-                          const ca_kv_pages* pg, void* ws, size_t ws_bytes, void* stream, PreparedFwd& pf,
-                          const void* const* tensors = nullptr) {
+}  // namespace
+
+// Validates, plans and builds the queue on the host; see ca_internal.h.
+ca_status ca::build_forward_queue(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                                  const ca_kv_pages* pg, const void* const* tensors, PreparedFwd& pf,
+                                  std::vector<char>& host, size_t* bytes_needed) {
+  *bytes_needed = 0;
+  host.clear();
   ca_status st = check_forward_args(s, t, m, n, pg);
   if (st != CA_OK) return st;
   const FwdPlan p = plan_forward(s, t, m, n, pg);
   std::memset(&pf, 0, sizeof(pf));
   pf.magic = kPlanMagic;
-  pf.ws = ws;
   pf.shape = *s;
-  if (!tensors) {
-    // a plan is launched later, perhaps with another device current
-    const hipError_t e = hipGetDevice(&pf.device);
-    if (e != hipSuccess) {
-      pf.magic = 0;
-      return hip_fail(e, "hipGetDevice");
-    }
-  }
   if (p.n_items == 0 && p.n_dec_items == 0) return CA_OK;
   if (tensors)
     for (int i = 0; i < 5; ++i)
       if (!tensors[i]) return fail(CA_ERR_INVALID, "NULL tensor pointer");
-  if (!ws || ws_bytes < p.bytes)
-    return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.bytes);
   if (p.n_items > 0x7fffffffu || p.n_dec_items > 0x7fffffffu || p.n_parts > 0x7fffffffu)
     return fail(CA_ERR_UNSUPPORTED, "too many work items");
   std::vector<ca::FwdItem> items;
@@ -471,7 +475,7 @@ ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mas
   std::vector<ca::DecItem> ditems;
   std::vector<int32_t> split;
   build_decode_items(s, t, m, n, p, ditems, split);
-  std::vector<char> host(p.off_part_o, 0);
+  host.assign(p.off_part_o, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
   if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
   if (pg && pg->n_pages > 0)
@@ -479,8 +483,6 @@ ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mas
   if (!items.empty()) std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
   if (!ditems.empty()) std::memcpy(host.data() + p.off_dec, ditems.data(), sizeof(ca::DecItem) * ditems.size());
   if (!split.empty()) std::memcpy(host.data() + p.off_split, split.data(), sizeof(int32_t) * split.size());
-  st = upload(ws, host, (hipStream_t)stream);
-  if (st != CA_OK) return st;
   pf.group = p.group;
   pf.hpw = p.hpw;
   pf.n_items = (int32_t)items.size();
@@ -498,12 +500,43 @@ ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mas
   pf.off_split = p.off_split;
   pf.off_part_o = p.off_part_o;
   pf.off_part_l = p.off_part_l;
+  *bytes_needed = p.bytes;
   return CA_OK;
 }
 
+namespace {
+
+using ca::PreparedFwd;
+
+// Validates, plans, builds the queue and uploads it into ws on the stream.
+// With tensors given (a direct call) they are checked before the upload, so
+// a rejected call changes nothing.
+ca_status prepare_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                          const ca_kv_pages* pg, void* ws, size_t ws_bytes, void* stream, PreparedFwd& pf,
+                          const void* const* tensors = nullptr) {
+  std::vector<char> host;
+  size_t need = 0;
+  ca_status st = ca::build_forward_queue(s, t, m, n, pg, tensors, pf, host, &need);
+  if (st != CA_OK) return st;
+  pf.ws = ws;
+  if (!tensors) {
+    // a plan is launched later, perhaps with another device current
+    const hipError_t e = hipGetDevice(&pf.device);
+    if (e != hipSuccess) {
+      pf.magic = 0;
+      return hip_fail(e, "hipGetDevice");
+    }
+  }
+  if (pf.n_items == 0 && pf.n_dec_items == 0) return CA_OK;
+  if (!ws || ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  return upload(ws, host, (hipStream_t)stream);
+}
+
+}  // namespace
+
 // Kernel launches only: no host planning, no copies, no allocation.
-ca_status launch_prepared_forward(const PreparedFwd& pf, const void* Q, const void* K, const void* V, void* O,
-                                  float* LSE, void* stream) {
+ca_status ca::launch_prepared_forward(const PreparedFwd& pf, const void* Q, const void* K, const void* V, void* O,
+                                      float* LSE, void* stream) {
   if (pf.n_items == 0 && pf.n_dec_items == 0) return CA_OK;
   if (!Q || !K || !V || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
   const ca_shape* s = &pf.shape;
@@ -580,6 +613,8 @@ ca_status launch_prepared_forward(const PreparedFwd& pf, const void* Q, const vo
   return CA_OK;
 }
 
+namespace {
+
 ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
                        const ca_kv_pages* pg, const void* Q, const void* K, const void* V, void* O, float* LSE,
                        void* ws, size_t ws_bytes, void* stream) {
@@ -587,7 +622,7 @@ ca_status forward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask* 
   const void* tensors[5] = {Q, K, V, O, LSE};
   const ca_status st = prepare_forward(s, t, m, n, pg, ws, ws_bytes, stream, pf, tensors);
   if (st != CA_OK) return st;
-  return launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
+  return ca::launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -971,7 +1006,7 @@ ca_status ca_forward_prepared(const ca_forward_plan* plan, const void* Q, const 
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != pf.device)
     return fail(CA_ERR_INVALID, "plan was prepared on device %d, device %d is current", pf.device, dev);
-  return launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
+  return ca::launch_prepared_forward(pf, Q, K, V, O, LSE, stream);
 }
 
 size_t ca_forward_varlen_workspace(const ca_shape* shape, const int32_t* cu, int32_t n_docs) {
@@ -992,11 +1027,11 @@ ca_status ca_forward_varlen(const ca_shape* shape, const int32_t* cu, int32_t n_
 ca_status ca_merge(const ca_shape* shape, int32_t n_parts, int64_t n_rows, const float* O_parts,
                    const float* LSE_parts, void* O, float* LSE, void* stream) {
   if (!shape) return fail(CA_ERR_INVALID, "shape is NULL");
-  if (shape->hq < 1) return fail(CA_ERR_INVALID, "hq=%d must be >= 1", shape->hq);
+  if (shape->hq < 1 || shape->hq > kMaxHeads) return fail(CA_ERR_INVALID, "hq=%d not in [1, %d]", shape->hq, kMaxHeads);
   if (shape->d != 64 && shape->d != 128) return fail(CA_ERR_UNSUPPORTED, "head dim d=%d not supported", shape->d);
   if (shape->flags & ~(uint32_t)CA_OUT_F32) return fail(CA_ERR_INVALID, "unknown flags 0x%x", shape->flags);
   if (n_parts < 1) return fail(CA_ERR_INVALID, "n_parts=%d must be >= 1", n_parts);
-  if (n_rows < 0) return fail(CA_ERR_INVALID, "n_rows < 0");
+  if (n_rows < 0 || n_rows > kMaxRows) return fail(CA_ERR_INVALID, "n_rows=%lld not in [0, 2^40]", (long long)n_rows);
   if (n_rows == 0) return CA_OK;
   if (!O_parts || !LSE_parts || !O || !LSE) return fail(CA_ERR_INVALID, "NULL tensor pointer");
   if (n_rows * shape->hq * (shape->d / 4) / 256 >= 0x7fffffffLL) return fail(CA_ERR_UNSUPPORTED, "too many rows");

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/ca.h"
 
 namespace ca {
@@ -129,6 +131,36 @@ struct BwdParams {
   float scale_log2;
   int32_t accumulate;
 };
+
+// A forward call whose work queue is built: what its launch needs once the
+// queue is in a device buffer (ws): the shape, the queue layout and counts.
+// Plain data, so it can live in the caller's ca_forward_plan.
+struct PreparedFwd {
+  uint64_t magic;
+  void* ws;                 // device buffer holding the queue (and decode staging)
+  int32_t device;           // current device at preparation: ws lives there
+  ca_shape shape;
+  int32_t group, hpw;
+  int32_t n_items, n_dec_items, n_split;
+  int32_t has_masks, has_pages, page_shift;
+  uint32_t page_bytes;
+  uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_part_o, off_part_l;
+};
+
+// Validates a forward call (tensors: Q, K, V, O, LSE, or nullptr to skip the
+// pointer checks) and builds its work queue on the host: `host` receives the
+// bytes that must be at the start of the device buffer before the launch
+// (task table, masks, page table, work items, decode merge records), and
+// *bytes_needed the whole buffer size (the rest is staging the kernels write
+// before reading).  Fills pf except pf.ws and pf.device.  No HIP calls.
+ca_status build_forward_queue(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
+                              const ca_kv_pages* pg, const void* const* tensors, PreparedFwd& pf,
+                              std::vector<char>& host, size_t* bytes_needed);
+
+// The kernel launches of a built queue whose bytes are in pf.ws: no host
+// planning, no copies, no allocation.
+ca_status launch_prepared_forward(const PreparedFwd& pf, const void* Q, const void* K, const void* V, void* O,
+                                  float* LSE, void* stream);
 
 // Kernel launchers (defined in the .hip files).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s);

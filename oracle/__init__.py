@@ -32,6 +32,9 @@ from .attention import (  # noqa: F401
     forward_rows,
     merge,
     backward,
+    backward_dq_rows,
+    forward_listed,
+    backward_listed,
 )
 from .paging import virtual_rows, forward_paged, backward_paged  # noqa: F401
 from .counting import (  # noqa: F401

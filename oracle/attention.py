@@ -275,3 +275,94 @@ def backward(tasks, Q, K, V, dO, scale, dq_rows=None, dkv_rows=None):
                 dQ[q_off + chunk, h, :] += scale * (dS @ k)
                 dK[kv_off:kv_off + n, g, :] += scale * (dS.T @ q)
     return dQ, dK, dV
+
+
+def backward_dq_rows(task, rows, Q, K, V, dO, scale, heads=None):
+    """dQ [len(rows), len(heads), d] of selected rows of one task: the rows
+    of ``backward``'s dQ, computed from those rows alone.
+
+    dQ_i depends only on row i (its probabilities P_i over its visible keys,
+    D_i = <dO_i, O_i> and dP_i = dO_i V^T), so the gradient of
+    L = sum(O * dO) with respect to query row i is
+        dQ_i = scale sum_j P_ij (dP_ij - D_i) K_j
+    whichever other rows exist; this is how the full-size checks sample it.
+    ``heads`` lists the query heads (default: all); O and P come from the
+    oracle's own float64 forward of the rows.
+    """
+    task = _as_tasks(task)[0]
+    q_off, kv_off, o_off = int(task[0]), int(task[1]), int(task[2])
+    hq, d = Q.shape[1], Q.shape[2]
+    hkv = K.shape[1]
+    heads = list(range(hq)) if heads is None else [int(h) for h in heads]
+    rows = np.asarray(rows, dtype=np.int64)
+    dQ = np.zeros((len(rows), len(heads), d))
+    pos = 0
+    for chunk in _row_chunks(task, rows):
+        for k, h in enumerate(heads):
+            g = _group_of(h, hq, hkv)
+            o, _, P, n = _head_rows(task, chunk, h, Q, K, V, scale, hq, hkv)
+            if n == 0:
+                continue
+            do = dO[o_off + chunk, h, :]
+            D = np.sum(do * o, axis=1)
+            dP = do @ V[kv_off:kv_off + n, g, :].T
+            dS = P * (dP - D[:, None])
+            dQ[pos:pos + len(chunk), k, :] = scale * (dS @ K[kv_off:kv_off + n, g, :])
+        pos += len(chunk)
+    return dQ
+
+
+def forward_listed(Q, K, V, scale, rows_keys):
+    """O [R, Hq, d], LSE [R, Hq] where output row r is the softmax attention
+    of query row r over exactly the key rows listed in rows_keys[r]: the
+    definition with the mask given as an explicit key list, which is how the
+    sparse masks of "Dynamic Context Parallelism" (Section 2.4, Figure 6) are
+    described — every query sees a union of ranges.  An empty list gives
+    O = 0, LSE = -inf.  One row at a time, float64."""
+    hq, d = Q.shape[1], Q.shape[2]
+    hkv = K.shape[1]
+    R = len(rows_keys)
+    O = np.zeros((R, hq, d))
+    LSE = np.full((R, hq), -np.inf)
+    for r, keys in enumerate(rows_keys):
+        ks = np.asarray(keys, dtype=np.int64)
+        if ks.size == 0:
+            continue
+        for h in range(hq):
+            g = _group_of(h, hq, hkv)
+            s = scale * (K[ks, g] @ Q[r, h])
+            m = s.max()
+            w = np.exp(s - m)
+            l = w.sum()
+            O[r, h] = (w @ V[ks, g]) / l
+            LSE[r, h] = m + np.log(l)
+    return O, LSE
+
+
+def backward_listed(Q, K, V, dO, scale, rows_keys):
+    """Gradients of L = sum(O * dO) for the O of ``forward_listed``: row r
+    attends to the listed key rows only.  The plain chain rule, one row and
+    head at a time: with p the row's probabilities and o its output,
+        dV_k += p_k dO_r,   ds_k = p_k (<dO_r, V_k> - <dO_r, o>),
+        dQ_r += scale sum_k ds_k K_k,   dK_k += scale ds_k Q_r,
+    dK and dV summed over the query heads of the KV head's group and over
+    every row that lists the key.  Returns (dQ, dK, dV) shaped like Q, K, V."""
+    hq = Q.shape[1]
+    hkv = K.shape[1]
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for r, keys in enumerate(rows_keys):
+        ks = np.asarray(keys, dtype=np.int64)
+        if ks.size == 0:
+            continue
+        for h in range(hq):
+            g = _group_of(h, hq, hkv)
+            s = scale * (K[ks, g] @ Q[r, h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = p @ V[ks, g]
+            dp = V[ks, g] @ dO[r, h]
+            ds = p * (dp - dO[r, h] @ o)
+            np.add.at(dV[:, g], ks, p[:, None] * dO[r, h][None])
+            dQ[r, h] += scale * (ds @ K[ks, g])
+            np.add.at(dK[:, g], ks, scale * ds[:, None] * Q[r, h][None])
+    return dQ, dK, dV

@@ -1,5 +1,6 @@
 // Host-only fuzz of argument validation and work planning (workspace queries,
 // visible-pair counts) under ASan/UBSan; kernel launchers are stubs.
+#include <cstdint>
 #include <cstdio>
 #include <random>
 #include <algorithm>
@@ -25,6 +26,8 @@ int main() {
     ca_shape s{};
     s.hkv = (int)U(1, 8); s.hq = s.hkv * (int)U(1, 16); s.d = U(0, 5) ? 128 : 64; s.scale = U(0, 20) ? 0.088f : -1.f;
     s.flags = U(0, 1); s.q_rows = U(0, 100000); s.kv_rows = U(0, 100000); s.o_rows = s.q_rows * U(1, 3);
+    if (!U(0, 30)) s.q_rows = INT64_MAX - U(0, 10);    // huge row counts are rejected, not multiplied
+    if (!U(0, 30)) s.hq = s.hkv * (int)U(1 << 12, 1 << 20);
     int n = (int)U(0, 30);
     std::vector<ca_task> t(n + 1);
     std::vector<ca_task_mask> m(n + 1);
@@ -32,6 +35,10 @@ int main() {
       ca_task& x = t[i];
       x.q_len = (int)U(U(0, 50) ? 0 : -3, 3000); x.kv_len = (int)U(U(0, 50) ? 0 : -3, 9000);
       x.q_off = U(0, 1) ? U(0, 100000) : U(-5, 5); x.kv_off = U(0, 100000); x.o_off = U(0, 100000);
+      if (!U(0, 8)) {   // offsets at and near INT64_MAX: range checks must not overflow
+        int64_t* off[3] = {&x.q_off, &x.kv_off, &x.o_off};
+        *off[U(0, 2)] = INT64_MAX - U(0, 4000);
+      }
       x.q_pos0 = U(0, 20000); x.kv_pos0 = U(0, 20000);
       m[i].window = (int)U(0, 3) ? 0 : (int)U(-1, 5000); m[i].sink = (int)U(-1, 100);
     }

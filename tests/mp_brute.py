@@ -55,3 +55,24 @@ def loss(tasks, Q, K, V, dO, scale):
         for c, oc in enumerate(o):
             total += oc * _val(dO[row, h, c])
     return total
+
+
+def loss_listed(rows_keys, Q, K, V, dO, scale):
+    """L = sum_r <O_r, dO_r> in 50 digits, where O_r is the softmax attention
+    of query row r over exactly the key rows listed in rows_keys[r]
+    (GQA: query head h reads KV head h // (hq // hkv))."""
+    hq, d = Q.shape[1], Q.shape[2]
+    group = hq // K.shape[1]
+    sc = mp.mpf(scale) if not isinstance(scale, mp.mpf) else scale
+    total = mp.mpf(0)
+    for r, keys in enumerate(rows_keys):
+        if not keys:
+            continue
+        for h in range(hq):
+            g = h // group
+            s = [sc * mp.fsum(_val(Q[r, h, c]) * _val(K[k, g, c]) for c in range(d)) for k in keys]
+            z = mp.fsum(mp.exp(x) for x in s)
+            for c in range(d):
+                oc = mp.fsum(mp.exp(x) * _val(V[k, g, c]) for x, k in zip(s, keys)) / z
+                total += oc * _val(dO[r, h, c])
+    return total

@@ -76,6 +76,14 @@ def test_forward_rejects_bad_arguments_without_launching():
     assert call_forward(s, [(0, 1, 0, 10, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past kv_rows
     assert call_forward(s, [(0, 0, 5, 10, 10, 0, 0)]) == ca.CA_ERR_INVALID     # past o_rows
     assert call_forward(s, [(0, 0, 0, -1, 10, 0, 0)]) == ca.CA_ERR_INVALID
+    big = 2 ** 63 - 1                                                           # off + len would overflow
+    for k in range(3):
+        for off in (big, big - 5, big - 9):
+            t = [0, 0, 0, 10, 10, 0, 0]
+            t[k] = off
+            assert call_forward(s, [tuple(t)]) == ca.CA_ERR_INVALID, (k, off)
+    assert call_forward(ca.make_shape(8, 2, 128, big, 10, 10), good) == ca.CA_ERR_INVALID   # rows > 2^40
+    assert call_forward(ca.make_shape(8192, 2, 128, 10, 10, 10), good) == ca.CA_ERR_INVALID  # hq > 4096
     assert call_forward(s, good, ptr=None) == ca.CA_ERR_INVALID                # NULL tensors
     need = ca.forward_workspace(s, good)
     assert need > 0

@@ -121,9 +121,14 @@ def doc_positions(w):
 # --------------------------------------------------------------------------
 
 
-def test_llama8b_131k_sampled():
-    announce("fullsize llama3-8b packed 131k sampled rows")
-    w = I.llama8b_packed_131k()
+# Length seed 102 is the benchmark's headline draw (10 documents, 2.41e9
+# visible pairs per head, two documents over 40K tokens); seed 103 is the
+# draw with the median pair count of seeds 100-107 (30 documents, median
+# length 1,349, 1.26e9 pairs).
+@pytest.mark.parametrize("length_seed", [102, 103])
+def test_llama8b_131k_sampled(length_seed):
+    announce("fullsize llama3-8b packed 131k sampled rows, length seed %d" % length_seed)
+    w = I.llama8b_packed_131k(seed=length_seed)
     Q, K, V = device_inputs(w, 202)
     O, LSE = run_forward(w, Q, K, V)
     rng = np.random.default_rng(1)
@@ -136,9 +141,10 @@ def test_llama8b_131k_sampled():
     sampled_check(w, tr, Q, K, V, O, LSE, label="131k-sampled")
 
 
-def test_llama8b_131k_probe_all_rows():
-    announce("fullsize llama3-8b packed 131k probe")
-    w = I.llama8b_packed_131k()
+@pytest.mark.parametrize("length_seed", [102, 103])
+def test_llama8b_131k_probe_all_rows(length_seed):
+    announce("fullsize llama3-8b packed 131k probe, length seed %d" % length_seed)
+    w = I.llama8b_packed_131k(seed=length_seed)
     Q, K, V = probe_tensors(w, doc_positions(w))
     O, LSE = run_forward(w, Q, K, V)
     check_probe(w, O, LSE, "131k")
@@ -151,7 +157,7 @@ def test_ca_tasks_34b_sampled_and_probe():
     Q, K, V = device_inputs(w, 203)
     O, LSE = run_forward(w, Q, K, V)
     tr = [(ti, np.array([0, int(t[3]) // 2, int(t[3]) - 1])) for ti, t in enumerate(w.tasks)]
-    sampled_check(w, tr, Q, K, V, O, LSE, heads=list(range(0, 64, 8)), label="ca-tasks-sampled")
+    sampled_check(w, tr, Q, K, V, O, LSE, label="ca-tasks-sampled")      # all 64 heads
     del Q, K, V, O, LSE
     torch.cuda.empty_cache()
     Q, K, V = probe_tensors(w, doc_positions(w))

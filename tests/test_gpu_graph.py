@@ -248,3 +248,86 @@ def test_graph_replays_a_partial_prefill_ring():
                      dtype=np.int64)
     O_ref, L_ref = oracle.forward(whole, widen(Q), widen(K), widen(V), 1 / math.sqrt(d))
     check_forward(Om, Lm, O_ref, L_ref, "partial-prefill-ring-replayed")
+
+
+def test_direct_calls_refuse_a_capturing_stream():
+    """ca_forward and ca_backward copy a host-built work queue into the
+    workspace; a captured copy would replay stale host memory, so both refuse
+    a stream under capture before enqueuing anything: the outputs stay
+    untouched."""
+    announce("direct forward / backward refused under graph capture")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    tasks = I.varlen_tasks([300, 77])
+    T = 377
+    shape = ca.make_shape(HQ, HKV, D, T, T, T)
+    Q = I.randn_bf16((T, HQ, D), 2750, device=dev)
+    K = I.randn_bf16((T, HKV, D), 2751, device=dev)
+    V = I.randn_bf16((T, HKV, D), 2752, device=dev)
+    O = torch.full((T, HQ, D), 7.0, dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((T, HQ), 7.0, device=dev)
+    dQ, dK, dV = torch.full_like(Q, 7.0), torch.full_like(K, 7.0), torch.full_like(V, 7.0)
+    ws = ca.workspace_tensor(ca.forward_workspace(shape, tasks), dev)
+    bws = ca.workspace_tensor(ca.backward_workspace(shape, tasks), dev)
+    torch.cuda.synchronize()
+    errors = []
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for call in (lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=st),
+                     lambda: ca.backward(shape, tasks, Q, K, V, O, Q, LSE, dQ, dK, dV, ws=bws, stream=st)):
+            try:
+                call()
+            except ca.CAError as e:
+                errors.append(e)
+    assert len(errors) == 2, errors
+    assert all(e.status == ca.CA_ERR_INVALID and "capturing" in str(e) for e in errors), errors
+    torch.cuda.synchronize()
+    for x in (O, LSE, dQ, dK, dV):
+        assert bool((x.float() == 7.0).all())
+    # the same calls outside capture run normally
+    ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(LSE).all()) and not bool((LSE == 7.0).any())
+
+
+def test_temporary_workspace_on_a_side_stream_is_not_reused_early():
+    """A workspace the binding allocates for a call on a non-current stream
+    is tied to that stream (record_stream): while the stream still has work
+    queued, freeing it must not hand its block to the next allocation on the
+    current stream.  Then a side-stream call without a workspace, followed at
+    once by allocations that write on the current stream, still matches the
+    same call on the current stream."""
+    announce("temporary workspace on a side stream")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream()
+    nbytes = 3 << 20
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(100_000_000)          # keeps the side stream busy (bounded spin)
+    ws = ca.workspace_tensor(nbytes, dev, stream=side)
+    p = ws.data_ptr()
+    del ws
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    assert x.data_ptr() != p
+    torch.cuda.synchronize()
+    del x
+    tasks = I.varlen_tasks([2000, 513, 1])
+    T = 2514
+    shape = ca.make_shape(HQ, HKV, D, T, T, T)
+    Q = I.randn_bf16((T, HQ, D), 2760, device=dev)
+    K = I.randn_bf16((T, HKV, D), 2761, device=dev)
+    V = I.randn_bf16((T, HKV, D), 2762, device=dev)
+    O, LSE = torch.empty((T, HQ, D), dtype=torch.bfloat16, device=dev), torch.empty((T, HQ), device=dev)
+    O2, LSE2 = torch.empty_like(O), torch.empty_like(LSE)
+    ca.forward(shape, tasks, Q, K, V, O2, LSE2)
+    torch.cuda.synchronize()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    ca.forward(shape, tasks, Q, K, V, O, LSE, stream=side)
+    junk = [torch.zeros(ca.forward_workspace(shape, tasks), dtype=torch.uint8, device=dev) for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(O.view(torch.int16), O2.view(torch.int16)) and torch.equal(LSE, LSE2)

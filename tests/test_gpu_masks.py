@@ -124,29 +124,6 @@ def gpu_grads(fwd_tasks, bwd_tasks, parts, T, hq, hkv, d, seed):
     return (dQ, dK, dV), Q, K, V, dO
 
 
-def brute_grads(Q, K, V, dO, scale, rows_keys, hq, hkv):
-    """Gradient of sum(O * dO) for O defined row by row as the softmax over
-    the listed keys (float64 numpy, one row at a time)."""
-    Q, K, V, dO = widen(Q), widen(K), widen(V), widen(dO)
-    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
-    for r, keys in enumerate(rows_keys):
-        if not keys:
-            continue
-        ks = np.asarray(keys)
-        for h in range(hq):
-            g = (h * hkv) // hq
-            s = scale * (K[ks, g] @ Q[r, h])
-            p = np.exp(s - s.max())
-            p /= p.sum()
-            o = p @ V[ks, g]
-            dp = V[ks, g] @ dO[r, h]
-            ds = p * (dp - dO[r, h] @ o)
-            dV[ks, g] += p[:, None] * dO[r, h][None]
-            dQ[r, h] += scale * (ds @ K[ks, g])
-            dK[ks, g] += scale * ds[:, None] * Q[r, h][None]
-    return dQ, dK, dV
-
-
 def check_grads(got, ref, label):
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         e = rel_fro(widen(g), r)
@@ -192,7 +169,8 @@ def test_blockwise_mask_backward():
                 keys = sorted(set(range(min(block, p + 1))) | set(range(max(0, b - w + 1) * block, p + 1)))
             rows_keys.append([start + k for k in keys])
         start += L
-    check_grads(got, brute_grads(Q, K, V, dO, 1 / math.sqrt(d), rows_keys, hq, hkv), "blockwise bwd")
+    ref = oracle.backward_listed(widen(Q), widen(K), widen(V), widen(dO), 1 / math.sqrt(d), rows_keys)
+    check_grads(got, ref, "blockwise bwd")
 
 
 def test_shared_question_mask_backward():
@@ -207,4 +185,5 @@ def test_shared_question_mask_backward():
     for a in answers:
         rows_keys += [list(range(question)) + [off + j for j in range(i + 1)] for i in range(a)]
         off += a
-    check_grads(got, brute_grads(Q, K, V, dO, 1 / math.sqrt(d), rows_keys, hq, hkv), "shared-question bwd")
+    ref = oracle.backward_listed(widen(Q), widen(K), widen(V), widen(dO), 1 / math.sqrt(d), rows_keys)
+    check_grads(got, ref, "shared-question bwd")

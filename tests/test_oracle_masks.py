@@ -131,3 +131,112 @@ def test_shared_question_recipe_matches_brute_force():
         off += a
     Ob, Lb = brute_rows(Q, K, V, 0.3, rows_keys, hq, hkv)
     assert np.abs(O - Ob).max() < 1e-12 and np.abs(LSE - Lb).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# attention over explicit key lists (the reference for sparse-mask gradients)
+# ---------------------------------------------------------------------------
+
+from tests import mp_brute  # noqa: E402
+import mpmath as mp  # noqa: E402
+
+
+def _random_lists(rng, T, max_keys):
+    return [sorted(rng.choice(T, size=int(rng.integers(0, max_keys + 1)), replace=False).tolist())
+            for _ in range(T)]
+
+
+def test_forward_listed_closed_forms_and_causal_lists():
+    """K = 0: every listed key weighs the same, so LSE = ln(#keys) and O is
+    the mean of the listed V rows; the causal key lists of a packed chunk
+    reproduce oracle.forward (itself pinned to the 50-digit brute force);
+    the key order does not matter."""
+    rng = np.random.default_rng(40)
+    T, hq, hkv, d = 12, 4, 2, 8
+    Q, K, V = tensors(T, hq, hkv, d, 41)
+    lists = _random_lists(rng, T, 7)
+    O, LSE = oracle.forward_listed(Q, np.zeros_like(K), V, 0.3, lists)
+    for r, keys in enumerate(lists):
+        for h in range(hq):
+            if not keys:
+                assert np.isneginf(LSE[r, h]) and not O[r, h].any()
+                continue
+            assert abs(LSE[r, h] - math.log(len(keys))) < 1e-13
+            assert np.abs(O[r, h] - V[keys, h // 2].mean(axis=0)).max() < 1e-13
+    docs = [5, 7]
+    causal = [list(range(p + 1)) for p in range(5)] + [[5 + k for k in range(p + 1)] for p in range(7)]
+    O1, L1 = oracle.forward_listed(Q, K, V, 0.3, causal)
+    O2, L2 = oracle.forward(I.varlen_tasks(docs), Q, K, V, 0.3)
+    assert np.abs(O1 - O2).max() < 1e-13 and np.abs(L1 - L2).max() < 1e-13
+    O3, L3 = oracle.forward_listed(Q, K, V, 0.3, [list(reversed(k)) for k in causal])
+    assert np.abs(O1 - O3).max() < 1e-13 and np.abs(L1 - L3).max() < 1e-13
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_listed_matches_finite_differences(seed):
+    """Central differences (50 digits) of L = sum(O * dO) over random key
+    lists, GQA 4:2, for every element of Q, K and V."""
+    rng = np.random.default_rng(50 + seed)
+    T, hq, hkv, d = 4, 4, 2, 2
+    Q, K, V = tensors(T, hq, hkv, d, 60 + seed)
+    dO = rng.standard_normal((T, hq, d))
+    lists = _random_lists(rng, T, 4)
+    dQ, dK, dV = oracle.backward_listed(Q, K, V, dO, 0.7, lists)
+    eps = mp.mpf("1e-18")
+
+    def fd(which, idx):
+        args = {"Q": Q.astype(object), "K": K.astype(object), "V": V.astype(object)}
+        x = float(args[which][idx])
+        args[which][idx] = mp.mpf(x) + eps
+        lp = mp_brute.loss_listed(lists, args["Q"], args["K"], args["V"], dO, mp.mpf(0.7))
+        args[which][idx] = mp.mpf(x) - eps
+        lm = mp_brute.loss_listed(lists, args["Q"], args["K"], args["V"], dO, mp.mpf(0.7))
+        return float((lp - lm) / (2 * eps))
+
+    for which, grad in (("Q", dQ), ("K", dK), ("V", dV)):
+        for idx in np.ndindex(*grad.shape):
+            assert abs(grad[idx] - fd(which, idx)) < 1e-11, (which, idx)
+
+
+def test_backward_listed_causal_lists_equal_oracle_backward():
+    """With each row's causal key list, the listed gradient is the task
+    gradient of oracle.backward (pinned by finite differences itself)."""
+    docs = [9, 1, 14]
+    T, hq, hkv, d = sum(docs), 6, 2, 8
+    Q, K, V = tensors(T, hq, hkv, d, 70)
+    dO = np.random.default_rng(71).standard_normal((T, hq, d))
+    lists, start = [], 0
+    for L in docs:
+        lists += [[start + k for k in range(p + 1)] for p in range(L)]
+        start += L
+    a = oracle.backward_listed(Q, K, V, dO, 0.35, lists)
+    b = oracle.backward(I.varlen_tasks(docs), Q, K, V, dO, 0.35)
+    for x, y in zip(a, b):
+        assert np.abs(x - y).max() < 1e-12
+
+
+def test_backward_dq_rows_matches_finite_differences_and_backward():
+    """dQ of sampled rows of a CA-task shard (context = document prefix, rows
+    not tile-aligned): each equals the central difference of the whole
+    task's loss in that query row (50 digits), and the same rows of
+    oracle.backward."""
+    rng = np.random.default_rng(80)
+    hq, hkv, d = 4, 2, 2
+    task = np.array([[0, 0, 0, 4, 6, 2, 0]])               # queries at positions 2..5 over keys 0..5
+    Q, K, V = tensors(6, hq, hkv, d, 81)
+    dO = rng.standard_normal((4, hq, d))
+    rows = np.array([3, 0])
+    got = oracle.backward_dq_rows(task, rows, Q, K, V, dO, 0.6, heads=[1, 3])
+    full = oracle.backward(task, Q, K, V, dO, 0.6)[0]
+    assert np.abs(got - full[rows][:, [1, 3]]).max() < 1e-13
+    eps = mp.mpf("1e-18")
+    for k, r in enumerate(rows):
+        for j, h in enumerate((1, 3)):
+            for c in range(d):
+                qp = Q.astype(object)
+                x = float(Q[r, h, c])
+                qp[r, h, c] = mp.mpf(x) + eps
+                lp = mp_brute.loss(task, qp, K, V, dO, mp.mpf(0.6))
+                qp[r, h, c] = mp.mpf(x) - eps
+                lm = mp_brute.loss(task, qp, K, V, dO, mp.mpf(0.6))
+                assert abs(got[k, j, c] - float((lp - lm) / (2 * eps))) < 1e-11
