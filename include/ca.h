@@ -293,6 +293,35 @@ ca_status ca_forward_prepared(const ca_forward_plan* plan, const void* Q, const 
                               float* LSE, void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* Forward without allocation                                               */
+/* ---------------------------------------------------------------------- */
+/* For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  ca_forward_masked without
+ * a workspace (masks_host may be NULL: all causal): the work queue and the
+ * split-decode staging live in a fixed device array of the library, one per
+ * GPU, of CA_NOALLOC_SCRATCH_BYTES, held from the library's load until the
+ * process ends.  The host-built queue reaches it by value in the arguments of
+ * small store kernels on `stream`, so the call makes no device or pinned
+ * host allocation (the host-side planning uses ordinary heap memory), keeps
+ * no host buffer alive after it returns, and may be captured into a graph
+ * (replays store the same queue again, then run the same kernels).  Results
+ * are bit-identical to ca_forward_masked on the same tasks.
+ *   - The array is shared by every call on a GPU and keeps the last call's
+ *     queue: calls that overlap on one GPU (different streams, or graphs
+ *     replayed concurrently with other calls) race and give wrong results;
+ *     serialise them.
+ *   - The first call on each device looks the array's address up
+ *     (hipGetSymbolAddress) with that device current; make that first call
+ *     outside graph capture.
+ * Errors as ca_forward_masked, plus CA_ERR_WORKSPACE when the call's queue
+ * and staging (ca_forward_masked_workspace) exceed CA_NOALLOC_SCRATCH_BYTES,
+ * CA_ERR_HIP if the array's address cannot be obtained. */
+#define CA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ca_status ca_forward_noalloc(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                             int32_t n_tasks, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* CA-task scheduling (host only; no device memory, no HIP calls)          */
 /* ---------------------------------------------------------------------- */
 /* The profiler cost model and the communication-aware greedy scheduler of

@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libca.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["ca_api.cpp", "ca_sched.cpp", "ca_ring.cpp", "ca_fwd.hip", "ca_merge.hip", "ca_decode.hip", "ca_bwd.hip"]
+SOURCES = ["ca_api.cpp", "ca_sched.cpp", "ca_ring.cpp", "ca_fwd.hip", "ca_merge.hip", "ca_decode.hip", "ca_bwd.hip",
+           "ca_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -38,6 +38,7 @@ EXPORTS = (
     "ca_forward_paged",
     "ca_forward_prepare",
     "ca_forward_prepared",
+    "ca_forward_noalloc",
     "ca_backward_masked_workspace",
     "ca_backward_masked",
     "ca_backward_paged_workspace",
@@ -208,6 +209,8 @@ def lib():
         L.ca_forward_prepare.restype = ctypes.c_int
         L.ca_forward_prepared.argtypes = [ctypes.POINTER(ForwardPlan), vp, vp, vp, vp, vp, vp]
         L.ca_forward_prepared.restype = ctypes.c_int
+        L.ca_forward_noalloc.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.ca_forward_noalloc.restype = ctypes.c_int
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
         L.ca_last_error.argtypes = []
@@ -409,6 +412,19 @@ def forward_prepared(plan, Q, K, V, O, LSE, stream=None):
     _check(lib().ca_forward_prepared(ctypes.byref(plan), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE),
                                      _stream_ptr(stream)))
     return O, LSE
+
+
+def forward_noalloc(shape, tasks, Q, K, V, O, LSE, stream=None, masks=None):
+    """ca_forward_noalloc: the forward with its queue in the library's fixed
+    per-GPU scratch array (no workspace, no allocation; capturable)."""
+    ta, ma = split_tasks(tasks, masks)
+    _check_forward_tensors(shape, Q, K, V, O, LSE)
+    _check(lib().ca_forward_noalloc(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta), _ptr(Q), _ptr(K),
+                                    _ptr(V), _ptr(O), _ptr(LSE), _stream_ptr(stream)))
+    return O, LSE
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def forward_varlen(shape, cu_seqlens, Q, K, V, O, LSE, ws=None, stream=None):
