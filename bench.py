@@ -590,6 +590,59 @@ def secondary(steps=3, warmup=1):
     del Q, K, V, dO, O, LSE, dQ, dK, dV, ws, bws
     torch.cuda.empty_cache()
 
+    # Causal-blockwise (256-token blocks, window of 2 blocks, sink block) over
+    # the 512K training mix, and a 512K batch of shared-question groups: each
+    # as query shards over several contexts, forward and backward in one
+    # launch each; the blockwise forward also as the earlier two fp32 partial
+    # slots + Equation-4 merge, for comparison
+    for key, (tasks_m, wm) in (
+            ("blockwise_mask_512k", (I.blockwise_shards(w.doc_lens, block=256, win_blocks=2), w)),
+            ("shared_question_512k", (lambda b: (b[0].tasks, b[0]))(I.shared_question_batch()))):
+        Q = I.randn_bf16((wm.q_rows, wm.hq, wm.d), 216, device=dev)
+        K = I.randn_bf16((wm.kv_rows, wm.hkv, wm.d), 217, device=dev)
+        V = I.randn_bf16((wm.kv_rows, wm.hkv, wm.d), 218, device=dev)
+        dO = I.randn_bf16((wm.o_rows, wm.hq, wm.d), 219, device=dev)
+        O = torch.empty((wm.o_rows, wm.hq, wm.d), dtype=torch.bfloat16, device=dev)
+        LSE = torch.empty((wm.o_rows, wm.hq), device=dev)
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        shape = ca.make_shape(wm.hq, wm.hkv, wm.d, wm.q_rows, wm.kv_rows, wm.o_rows)
+        tm = ca.task_array(tasks_m)
+        ws = ca.workspace_tensor(ca.forward_workspace(shape, tm), dev)
+        bws = ca.workspace_tensor(ca.backward_workspace(shape, tm), dev)
+        pairs = ca.visible_pairs(tm)
+        ms_f = timed(lambda: ca.forward(shape, tm, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
+        ms_b = timed(lambda: ca.backward(shape, tm, Q, K, V, O, dO, LSE, dQ, dK, dV, ws=bws, stream=stream),
+                     steps, warmup, stream)
+        ff, bf = forward_flops(pairs, wm.hq, wm.d), backward_flops(pairs, wm.hq, wm.d)
+        rec = {"workload": wm.name + (", causal-blockwise 256-token blocks, window 2 blocks"
+                                      if key.startswith("blockwise") else ""),
+               "visible_pairs_per_head": pairs, "launches": "1 forward, 1 backward (one per pass)",
+               "fwd_ms": round(ms_f, 3), "fwd_tflops": round(ff / ms_f / 1e9, 1), "bwd_ms": round(ms_b, 3),
+               "bwd_tflops_10d": round(bf / ms_b / 1e9, 1)}
+        if key.startswith("blockwise"):
+            # the same mask as two fp32 partial slots and a merge
+            t2, parts = I.blockwise_tasks(w.doc_lens, block=256, win_blocks=2)
+            t2 = ca.task_array(t2)
+            s2 = ca.make_shape(wm.hq, wm.hkv, wm.d, wm.q_rows, wm.kv_rows, parts * wm.o_rows, out_f32=True)
+            Op = torch.zeros((parts * wm.o_rows, wm.hq, wm.d), device=dev)
+            Lp = torch.full((parts * wm.o_rows, wm.hq), -float("inf"), device=dev)
+            ws2 = ca.workspace_tensor(ca.forward_workspace(s2, t2), dev)
+            mv = (Op.view(parts, wm.o_rows, wm.hq, wm.d), Lp.view(parts, wm.o_rows, wm.hq))
+
+            def two_slots():
+                ca.forward(s2, t2, Q, K, V, Op, Lp, ws=ws2, stream=stream)
+                ca.merge(shape, mv[0], mv[1], O, LSE, stream=stream)
+            ms_2 = timed(two_slots, steps, warmup, stream)
+            rec["fwd_ms_two_slots_and_merge"] = round(ms_2, 3)
+            del Op, Lp, ws2, mv
+        out[key] = rec
+        log("%s: fwd %.2f ms (%.1f TFLOP/s), bwd %.2f ms (%.1f TFLOP/s at 10d)%s"
+            % (key, ms_f, ff / ms_f / 1e9, ms_b, bf / ms_b / 1e9,
+               (", two slots + merge %.2f ms" % rec["fwd_ms_two_slots_and_merge"])
+               if "fwd_ms_two_slots_and_merge" in rec else ""))
+        del Q, K, V, dO, O, LSE, dQ, dK, dV, ws, bws
+        torch.cuda.empty_cache()
+
     # CA-tasks backward (34B shape: each re-batched task carries its own context)
     w = I.ca_tasks_34b()
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(w, 214)

@@ -72,8 +72,22 @@ typedef enum {
  *   - decode of one token at position p over a cache block [b, b+m):
  *         {q, kv, o, 1, m, p, b}
  * A row that sees no key gets O = 0 and LSE = -inf.
- * Output row ranges [o_off, o_off + q_len) of different tasks must not
- * overlap (documented, not checked).  Context ranges may overlap.
+ *
+ * Query shards over several contexts: consecutive tasks with the same q_off,
+ * o_off, q_len and q_pos0 (q_len > 0) are one query shard whose rows attend
+ * to the union of the tasks' visible keys with one softmax (a key listed by
+ * two of them counts twice).  The sparse masks of "DCP: Addressing Input
+ * Dynamism In Long-Context Training via Dynamic Context Parallelism"
+ * (Section 2.4, Figure 6c / 6d) are such unions of key ranges:
+ *   - causal-blockwise, block b of a document at row r with a window
+ *     starting at block w0 > 0:  {q, r, q, n, B, q - r, 0} (the sink block,
+ *     all visible) followed by {q, r + w0 B, q, n, q + n - r - w0 B, q - r, w0 B}
+ *     with q = r + b B;
+ *   - shared question, an answer of a rows at row x after a question of qn
+ *     rows at row 0:  {x, 0, x, a, qn, qn, 0} then {x, x, x, a, a, qn, qn}.
+ * Apart from the tasks of one shard, output row ranges [o_off, o_off +
+ * q_len) of different tasks must not overlap (documented, not checked).
+ * Context ranges may overlap.
  */
 typedef struct {
   int64_t q_off;   /* first row in Q (and dQ)                              */
@@ -93,9 +107,9 @@ typedef struct {
  *     kp <= qp  and  (window == 0  or  kp > qp - window  or  kp < sink):
  * the query sees its `window` latest positions (itself included) and every
  * position below `sink`.  window == 0 is the plain causal task (sink unused).
- * Causal-blockwise and shared-question masks are unions of causal task
- * contexts: write them as tasks into separate partial slots and combine the
- * slots with ca_merge.
+ * Causal-blockwise and shared-question masks are unions of key ranges:
+ * write them as query shards over several contexts (see ca_task), one launch
+ * with no partial slots and no merge.
  */
 typedef struct {
   int32_t window;  /* >= 0                                                 */

@@ -323,6 +323,42 @@ bool is_decode_task(const ca_task& k, int group, int32_t window) {
   return k.q_len == 1 && group <= kDecMaxGroup && window == 0;
 }
 
+// Query shards: maximal runs of consecutive tasks with the same q_off, o_off,
+// q_len and q_pos0 (q_len > 0) are one shard, whose rows attend to the union
+// of the tasks' contexts under one softmax.  Returns, per task, the number of
+// tasks of the shard it starts (0 for the later tasks of a shard).
+std::vector<int32_t> query_shards(const ca_task* t, int32_t n) {
+  std::vector<int32_t> len((size_t)n, 1);
+  for (int32_t i = 0; i < n;) {
+    int32_t j = i + 1;
+    if (t[i].q_len > 0)
+      while (j < n && t[j].q_off == t[i].q_off && t[j].o_off == t[i].o_off && t[j].q_len == t[i].q_len &&
+             t[j].q_pos0 == t[i].q_pos0)
+        ++j;
+    len[(size_t)i] = j - i;
+    for (int32_t k = i + 1; k < j; ++k) len[(size_t)k] = 0;
+    i = j;
+  }
+  return len;
+}
+
+// A shard of one task with a single query row goes to the split-KV decode
+// kernel (when its group and mask allow); every other shard to the tiled one.
+bool is_decode_shard(const ca_task* t, const ca_task_mask* m, const std::vector<int32_t>& shard, int32_t i,
+                     int group) {
+  return shard[(size_t)i] == 1 && is_decode_task(t[i], group, task_window(m, i));
+}
+
+// Visible pairs of query rows [r0, r1] of the shard starting at task i, per
+// head (every context of the shard).
+int64_t shard_range_pairs(const ca_task* t, const ca_task_mask* m, int32_t i, int32_t n_seg, int64_t r0, int64_t r1) {
+  int64_t total = 0;
+  for (int32_t k = i; k < i + n_seg; ++k)
+    total += range_pairs_masked(r0, r1, t[k].q_pos0 - t[k].kv_pos0, t[k].kv_len, task_window(m, k),
+                                task_sink_keys(t, m, k));
+  return total;
+}
+
 // keys of a decode task that its single row can see: [0, vis)
 int64_t decode_visible(const ca_task& k) {
   return std::min<int64_t>(k.kv_len, std::max<int64_t>(0, k.q_pos0 - k.kv_pos0 + 1));
@@ -330,6 +366,8 @@ int64_t decode_visible(const ca_task& k) {
 
 struct FwdPlan {
   int hpw = 1, rt = 128, group = 1;
+  std::vector<int32_t> shard;   // query_shards()
+  int multi = 0;               // some shard has several contexts
   size_t n_items = 0;        // tiled-kernel items
   size_t n_dec_items = 0;    // decode items
   size_t n_split = 0;        // decode (task, kv head) pairs cut into > 1 chunk
@@ -345,10 +383,12 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m,
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, kFwdWaves);
   p.rt = 32 * (kFwdWaves / p.hpw);
+  p.shard = query_shards(t, n);
   int64_t dec_keys = 0;
   for (int32_t i = 0; i < n; ++i) {
-    if (t[i].q_len <= 0) continue;
-    if (is_decode_task(t[i], p.group, task_window(m, i))) {
+    if (t[i].q_len <= 0 || p.shard[(size_t)i] == 0) continue;
+    if (p.shard[(size_t)i] > 1) p.multi = 1;
+    if (is_decode_shard(t, m, p.shard, i, p.group)) {
       dec_keys += decode_visible(t[i]) * s->hkv;
       continue;
     }
@@ -358,7 +398,7 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m,
   const int64_t per_item = (dec_keys + kDecTargetItems - 1) / kDecTargetItems;
   p.dec_chunk = std::max<int64_t>(kDecMinChunk, (per_item + 127) / 128 * 128);
   for (int32_t i = 0; i < n; ++i) {
-    if (t[i].q_len <= 0 || !is_decode_task(t[i], p.group, task_window(m, i))) continue;
+    if (t[i].q_len <= 0 || !is_decode_shard(t, m, p.shard, i, p.group)) continue;
     const int64_t vis = decode_visible(t[i]);
     const int64_t chunks = std::max<int64_t>(1, (vis + p.dec_chunk - 1) / p.dec_chunk);
     p.n_dec_items += (size_t)chunks * s->hkv;
@@ -389,16 +429,15 @@ void build_forward_items(const ca_shape* s, const ca_task* t, const ca_task_mask
   tmp.reserve(p.n_items);
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& k = t[i];
-    const int32_t win = task_window(m, i);
-    if (k.q_len <= 0 || is_decode_task(k, p.group, win)) continue;
-    const int64_t delta = k.q_pos0 - k.kv_pos0;
-    const int64_t sj = task_sink_keys(t, m, i);
+    const int32_t n_seg = p.shard[(size_t)i];
+    if (k.q_len <= 0 || n_seg == 0 || is_decode_shard(t, m, p.shard, i, p.group)) continue;
     for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
       const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
       // pairs of the tile (per head) plus a per-row epilogue term
-      const int64_t cost = range_pairs_masked(r0, r1, delta, k.kv_len, win, sj) * p.hpw + (r1 - r0 + 1) * 64;
+      const int64_t cost = shard_range_pairs(t, m, i, n_seg, r0, r1) * p.hpw + (r1 - r0 + 1) * 64;
       for (int32_t g = 0; g < s->hkv; ++g)
-        for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
+        for (int32_t hs = 0; hs < p.group / p.hpw; ++hs)
+          tmp.push_back({cost, {i, (int16_t)g, (int16_t)hs, r0, n_seg}});
     }
   }
   // Longest first.  Items of equal cost (the KV heads of one query tile) stay
@@ -420,7 +459,7 @@ void build_decode_items(const ca_shape* s, const ca_task* t, const ca_task_mask*
   int32_t part = 0;
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& k = t[i];
-    if (k.q_len <= 0 || !is_decode_task(k, p.group, task_window(m, i))) continue;
+    if (k.q_len <= 0 || !is_decode_shard(t, m, p.shard, i, p.group)) continue;
     const int64_t vis = decode_visible(k);
     const int64_t chunks = std::max<int64_t>(1, (vis + p.dec_chunk - 1) / p.dec_chunk);
     for (int32_t g = 0; g < s->hkv; ++g) {
@@ -489,6 +528,7 @@ ca_status ca::build_forward_queue(const ca_shape* s, const ca_task* t, const ca_
   pf.n_dec_items = (int32_t)ditems.size();
   pf.n_split = (int32_t)p.n_split;
   pf.has_masks = m ? 1 : 0;
+  pf.multi = p.multi;
   pf.has_pages = pg ? 1 : 0;
   pf.page_shift = pg ? page_shift_of(pg) : 0;
   pf.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
@@ -565,6 +605,7 @@ ca_status ca::launch_prepared_forward(const PreparedFwd& pf, const void* Q, cons
     fp.hpw = pf.hpw;
     fp.scale_log2 = scale_log2;
     fp.out_f32 = out_f32;
+    fp.multi = pf.multi;
     hipError_t e = ca::launch_forward(fp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
   }
@@ -695,14 +736,47 @@ int partition_page_passes(const ca_task* t, int32_t n, const ca_kv_pages* pg, in
   return std::max<int>(1, (int)used.size());
 }
 
+// Context groups of the dK/dV kernel: active tasks (q_len > 0, kv_len > 0)
+// with the same context rows [kv_off, kv_off + kv_len).  A work item of a
+// group sweeps the query rows of every member, so context rows that several
+// tasks read (a shared sink block or question, a ring block) are written once,
+// by one item.
+struct KvGroups {
+  std::vector<int32_t> members;        // task indices, group after group, each in table order
+  std::vector<int32_t> first, count;   // per group: its members' range in `members`
+  std::vector<ca_task> rep;            // per group: its first member
+};
+
+KvGroups kv_groups(const ca_task* t, int32_t n) {
+  KvGroups g;
+  for (int32_t i = 0; i < n; ++i)
+    if (t[i].q_len > 0 && t[i].kv_len > 0) g.members.push_back(i);
+  std::stable_sort(g.members.begin(), g.members.end(), [&](int32_t a, int32_t b) {
+    return t[a].kv_off != t[b].kv_off ? t[a].kv_off < t[b].kv_off : t[a].kv_len < t[b].kv_len;
+  });
+  for (size_t k = 0; k < g.members.size(); ++k) {
+    const ca_task& x = t[g.members[k]];
+    if (k == 0 || x.kv_off != g.rep.back().kv_off || x.kv_len != g.rep.back().kv_len) {
+      g.first.push_back((int32_t)k);
+      g.count.push_back(0);
+      g.rep.push_back(x);
+    }
+    ++g.count.back();
+  }
+  return g;
+}
+
 struct BwdPlan {
   int group = 1, hpw = 1, rt = 128;
   int q_passes = 1, kv_passes = 1;
-  std::vector<int> q_pass_of, kv_pass_of;
+  std::vector<int32_t> shard;                    // query_shards()
+  KvGroups groups;
+  std::vector<int> q_pass_of, kv_pass_of;        // per task (shard starts) / per context group
   bool q_full = false, kv_full = false;          // every row covered by some task
+  int multi = 0;                                 // a shard or a context group with several tasks
   size_t n_qitems = 0, n_kvitems = 0;
-  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_qitems = 0, off_kvitems = 0, off_d = 0, off_dq = 0,
-         off_dk = 0, off_dv = 0, bytes = 0;
+  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_members = 0, off_qitems = 0, off_kvitems = 0, off_d = 0,
+         off_dq = 0, off_dk = 0, off_dv = 0, bytes = 0;
 };
 
 BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
@@ -711,28 +785,38 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, 4);
   p.rt = 32 * (4 / p.hpw);
-  std::vector<std::pair<int64_t, int64_t>> qiv(n), kviv(n);
+  p.shard = query_shards(t, n);
+  p.groups = kv_groups(t, n);
+  const size_t n_groups = p.groups.rep.size();
+  std::vector<std::pair<int64_t, int64_t>> qiv(n), kviv(n_groups);
   int64_t q_cover = 0, kv_cover = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const bool active = t[i].q_len > 0;
+    const bool active = t[i].q_len > 0 && p.shard[(size_t)i] > 0;
     qiv[i] = {t[i].q_off, active ? t[i].q_len : 0};
-    kviv[i] = {t[i].kv_off, active ? t[i].kv_len : 0};
     if (active) {
+      if (p.shard[(size_t)i] > 1) p.multi = 1;
       p.n_qitems += (size_t)((t[i].q_len + p.rt - 1) / p.rt) * s->hkv * (p.group / p.hpw);
-      p.n_kvitems += (size_t)((t[i].kv_len + kBwdKeyTile - 1) / kBwdKeyTile) * s->hkv;
       q_cover += t[i].q_len;
-      kv_cover += t[i].kv_len;
     }
   }
+  for (size_t g = 0; g < n_groups; ++g) {
+    const ca_task& x = p.groups.rep[g];
+    kviv[g] = {x.kv_off, x.kv_len};
+    if (p.groups.count[g] > 1) p.multi = 1;
+    p.n_kvitems += (size_t)((x.kv_len + kBwdKeyTile - 1) / kBwdKeyTile) * s->hkv;
+    kv_cover += x.kv_len;
+  }
   p.q_passes = partition_passes(qiv, p.q_pass_of);
-  p.kv_passes = pg ? partition_page_passes(t, n, pg, s->kv_rows / pg->page_rows, p.kv_pass_of)
+  p.kv_passes = pg ? partition_page_passes(p.groups.rep.data(), (int32_t)n_groups, pg, s->kv_rows / pg->page_rows,
+                                           p.kv_pass_of)
                    : partition_passes(kviv, p.kv_pass_of);
   p.q_full = p.q_passes == 1 && q_cover == s->q_rows;
   p.kv_full = !pg && p.kv_passes == 1 && kv_cover == s->kv_rows;   // paged: unread page rows stay zero
   p.off_tasks = 0;
   p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
   p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
-  p.off_qitems = p.off_pages + (pg ? align_up(sizeof(int32_t) * (size_t)pg->n_pages) : 0);
+  p.off_members = p.off_pages + (pg ? align_up(sizeof(int32_t) * (size_t)pg->n_pages) : 0);
+  p.off_qitems = p.off_members + align_up(sizeof(int32_t) * p.groups.members.size());
   p.off_kvitems = p.off_qitems + align_up(sizeof(ca::FwdItem) * p.n_qitems);
   p.off_d = p.off_kvitems + align_up(sizeof(ca::BwdItem) * p.n_kvitems);
   p.off_dq = p.off_d + align_up(sizeof(float) * (size_t)s->o_rows * s->hq);
@@ -758,41 +842,47 @@ void build_backward_items(const ca_shape* s, const ca_task* t, const ca_task_mas
     std::vector<K> tmp;
     for (int32_t i = 0; i < n; ++i) {
       const ca_task& k = t[i];
-      if (k.q_len <= 0 || p.q_pass_of[i] != pass) continue;
-      const int64_t delta = k.q_pos0 - k.kv_pos0;
-      const int32_t win = task_window(m, i);
-      const int64_t sj = task_sink_keys(t, m, i);
+      const int32_t n_seg = p.shard[(size_t)i];
+      if (k.q_len <= 0 || n_seg == 0 || p.q_pass_of[i] != pass) continue;
       for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
         const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
-        const int64_t cost = range_pairs_masked(r0, r1, delta, k.kv_len, win, sj) * p.hpw + (r1 - r0 + 1) * 64;
+        const int64_t cost = shard_range_pairs(t, m, i, n_seg, r0, r1) * p.hpw + (r1 - r0 + 1) * 64;
         for (int32_t g = 0; g < s->hkv; ++g)
-          for (int32_t hs = 0; hs < p.group / p.hpw; ++hs) tmp.push_back({cost, {i, g, hs, r0}});
+          for (int32_t hs = 0; hs < p.group / p.hpw; ++hs)
+            tmp.push_back({cost, {i, (int16_t)g, (int16_t)hs, r0, n_seg}});
       }
     }
     std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
     for (auto& k : tmp) qitems.push_back(k.it);
     q_begin.push_back(qitems.size());
   }
+  const KvGroups& G = p.groups;
   for (int pass = 0; pass < p.kv_passes; ++pass) {
     struct K { int64_t c; ca::BwdItem it; };
     std::vector<K> tmp;
-    for (int32_t i = 0; i < n; ++i) {
-      const ca_task& k = t[i];
-      if (k.q_len <= 0 || p.kv_pass_of[i] != pass) continue;
-      const int64_t delta = k.q_pos0 - k.kv_pos0;
-      const int32_t win = task_window(m, i);
-      const int64_t sj = task_sink_keys(t, m, i);
-      for (int32_t k0 = 0; k0 < k.kv_len; k0 += kBwdKeyTile) {
-        // rows that see the block: i >= k0 - delta, and (window, no sink key)
-        // i < last key - delta + win
-        const int64_t r_lo = std::min<int64_t>(k.q_len, std::max<int64_t>(0, k0 - delta));
-        int64_t r_end = k.q_len;
-        if (win > 0 && k0 >= sj) {
-          const int64_t last = std::min<int64_t>(k0 + kBwdKeyTile, k.kv_len) - 1;
-          r_end = std::min<int64_t>(k.q_len, std::max<int64_t>(r_lo, last - delta + win));
+    for (size_t gi = 0; gi < G.rep.size(); ++gi) {
+      if (p.kv_pass_of[gi] != pass) continue;
+      const int32_t kv_len = G.rep[gi].kv_len;
+      for (int32_t k0 = 0; k0 < kv_len; k0 += kBwdKeyTile) {
+        int64_t rows = 0;
+        for (int32_t q = G.first[gi]; q < G.first[gi] + G.count[gi]; ++q) {
+          const int32_t i = G.members[(size_t)q];
+          const ca_task& k = t[i];
+          const int64_t delta = k.q_pos0 - k.kv_pos0;
+          const int32_t win = task_window(m, i);
+          const int64_t sj = task_sink_keys(t, m, i);
+          // rows that see the block: i >= k0 - delta, and (window, no sink
+          // key) i < last key - delta + win
+          const int64_t r_lo = std::min<int64_t>(k.q_len, std::max<int64_t>(0, k0 - delta));
+          int64_t r_end = k.q_len;
+          if (win > 0 && k0 >= sj) {
+            const int64_t last = std::min<int64_t>(k0 + kBwdKeyTile, k.kv_len) - 1;
+            r_end = std::min<int64_t>(k.q_len, std::max<int64_t>(r_lo, last - delta + win));
+          }
+          rows += r_end - r_lo;
         }
-        const int64_t cost = (r_end - r_lo) * p.group * kBwdKeyTile + 64 * kBwdKeyTile;
-        for (int32_t g = 0; g < s->hkv; ++g) tmp.push_back({cost, {i, g, k0, 0}});
+        const int64_t cost = rows * p.group * kBwdKeyTile + 64 * kBwdKeyTile;
+        for (int32_t g = 0; g < s->hkv; ++g) tmp.push_back({cost, {G.first[gi], g, k0, G.count[gi]}});
       }
     }
     std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
@@ -861,6 +951,8 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
   if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
   if (pg && pg->n_pages > 0)
     std::memcpy(host.data() + p.off_pages, pg->table_host, sizeof(int32_t) * (size_t)pg->n_pages);
+  if (!p.groups.members.empty())
+    std::memcpy(host.data() + p.off_members, p.groups.members.data(), sizeof(int32_t) * p.groups.members.size());
   if (!qitems.empty()) std::memcpy(host.data() + p.off_qitems, qitems.data(), sizeof(ca::FwdItem) * qitems.size());
   if (!kvitems.empty()) std::memcpy(host.data() + p.off_kvitems, kvitems.data(), sizeof(ca::BwdItem) * kvitems.size());
   hipStream_t hs = (hipStream_t)stream;
@@ -901,6 +993,8 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
   bp.dVacc = (float*)(w + p.off_dv);
   bp.tasks = (const ca_task*)(w + p.off_tasks);
   bp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
+  bp.members = (const int32_t*)(w + p.off_members);
+  bp.multi = p.multi;
   bp.pages = pg ? (const int32_t*)(w + p.off_pages) : nullptr;
   bp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
   bp.page_shift = pg ? page_shift_of(pg) : 0;

@@ -18,6 +18,10 @@
 //                      dV^T += dO^T P,  dK^T += Q^T dS (dO^T, Q^T by LDS transpose reads)
 //   bwd_q_kernel     Q-stationary, shaped like the forward: S^T = K Q^T,
 //                    dP^T = V dO^T, dQ^T += K^T dS^T (K^T by transpose reads).
+// Query shards over several contexts (consecutive tasks sharing their query
+// rows) and context groups (tasks sharing their context rows) are swept one
+// task after another inside one work item (the MULTI instantiations), so
+// every gradient row is still written once per pass.
 // Rows are written once per pass (read-modify-write in fp32 when several
 // tasks share rows), so results are deterministic.
 
@@ -85,7 +89,7 @@ struct QTile<128> {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (task, KV head, 128 context rows).
 // ---------------------------------------------------------------------------
-template <int D, bool PAGED, bool WIN>
+template <int D, bool PAGED, bool WIN, bool MULTI>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   using Tile = QTile<D>;
   constexpr int BQ = 32;            // query rows per step
@@ -100,13 +104,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float lds_d[2][BQ];
 
   const BwdItem it = p.items[blockIdx.x];
-  const ca_task t = p.tasks[it.task];
+  // The item's context group: tasks p.members[it.member0 ..] share the
+  // context rows; t is the task whose query rows are being swept (the only
+  // one unless MULTI).
+  int task_idx = p.members[it.member0];
+  ca_task t = p.tasks[task_idx];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int64_t delta = t.q_pos0 - t.kv_pos0;
+  int64_t delta = t.q_pos0 - t.kv_pos0;
   const int G = p.group;
   const int kw0 = it.key0 + 32 * wave;           // first (task-relative) key of this wave
   const int my_key = kw0 + l32;
@@ -144,21 +152,24 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int wg_keys = min(128, t.kv_len - it.key0);
   // Sink + sliding-window mask (win > 0): key j is also required to lie in
   // the row's win latest positions (j > i + delta - win) or among the sink
-  // keys [0, sj).
-  int win = 0, sj = 0;
-  if (p.masks) {
-    win = p.masks[it.task].window;
-    if (win > 0) sj = (int)clamp64((int64_t)p.masks[it.task].sink - t.kv_pos0, 0, t.kv_len);
-  }
-  const int r_lo = (int)clamp64((int64_t)it.key0 - delta, 0, t.q_len);
-  // Rows past the window of the workgroup's last key see none of its keys,
-  // unless it holds sink keys.
-  const int r_end = (win > 0 && it.key0 >= sj)
-                        ? (int)clamp64((int64_t)it.key0 + wg_keys - 1 - delta + win, r_lo, t.q_len)
-                        : t.q_len;
-  const int r_first = (r_lo / BQ) * BQ;
-  const int n_rt = (r_end - r_first + BQ - 1) / BQ;
-  const int n_steps = (wg_keys > 0 && r_end > r_lo) ? n_rt * G : 0;
+  // keys [0, sj).  Rows past the window of the workgroup's last key see none
+  // of its keys, unless it holds sink keys.
+  int win, sj, r_lo, r_end, r_first, n_rt, n_steps;
+  auto member = [&]() __attribute__((always_inline)) {
+    win = 0;
+    sj = 0;
+    if (p.masks) {
+      win = p.masks[task_idx].window;
+      if (win > 0) sj = (int)clamp64((int64_t)p.masks[task_idx].sink - t.kv_pos0, 0, t.kv_len);
+    }
+    r_lo = (int)clamp64((int64_t)it.key0 - delta, 0, t.q_len);
+    r_end = (win > 0 && it.key0 >= sj) ? (int)clamp64((int64_t)it.key0 + wg_keys - 1 - delta + win, r_lo, t.q_len)
+                                       : t.q_len;
+    r_first = (r_lo / BQ) * BQ;
+    n_rt = (r_end - r_first + BQ - 1) / BQ;
+    n_steps = (wg_keys > 0 && r_end > r_lo) ? n_rt * G : 0;
+  };
+  member();
 
   // Tile loads through range-checked buffers based at the tile's first row:
   // rows past the task read as 0 (Q = dO = 0 there, so such rows add nothing
@@ -172,12 +183,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const uint32_t lse_voff = (uint32_t)tid * (uint32_t)p.hq * 4;
   const int head0 = it.kv_head * G;
   // next tile to load: head nx_g of the group, rows from the one nq points at
-  const __bf16* nq = p.Q + (t.q_off + r_first) * q_stride + head0 * D;
-  const __bf16* no = p.dO + (t.o_off + r_first) * q_stride + head0 * D;
-  const float* nl = p.LSE + (t.o_off + r_first) * p.hq + head0;
-  const float* nd = p.Dvec + (t.o_off + r_first) * p.hq + head0;
-  int nx_g = 0;
-  int nx_left = t.q_len - r_first;               // task rows from the next tile's first row
+  const __bf16* nq;
+  const __bf16* no;
+  const float* nl;
+  const float* nd;
+  int nx_g, nx_left;                             // nx_left: task rows from the next tile's first row
+  auto member_rows = [&]() __attribute__((always_inline)) {
+    nq = p.Q + (t.q_off + r_first) * q_stride + head0 * D;
+    no = p.dO + (t.o_off + r_first) * q_stride + head0 * D;
+    nl = p.LSE + (t.o_off + r_first) * p.hq + head0;
+    nd = p.Dvec + (t.o_off + r_first) * p.hq + head0;
+    nx_g = 0;
+    nx_left = t.q_len - r_first;
+  };
+  member_rows();
   uint4 qreg[PASSES], oreg[PASSES];
   float lse_reg = 0.f, d_reg = 0.f;
   auto gload = [&]() {
@@ -412,6 +431,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // buffers and run in pairs, so that every LDS address is a lane constant
   // plus an immediate: n_diag is rounded up and n_fend down to even steps
   // (the general body is correct for any step).
+  auto sweep = [&]() __attribute__((always_inline)) {
   const int n_diag_rt = (int)clamp64(((int64_t)it.key0 + 127 - delta - r_first + BQ - 1) / BQ, 0, n_rt);
   int n_diag = min(n_steps, (n_diag_rt * G + 1) & ~1);
   int n_fend = n_steps;
@@ -481,6 +501,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     }
     if (step < n_steps) do_step(B0{}, std::false_type{}, step);
   }
+  };
+  sweep();
+  if constexpr (MULTI) {
+    // the group's further tasks: dK and dV keep accumulating
+    for (int k = 1; k < it.n_members; ++k) {
+      __syncthreads();   // the previous task's last step may still be read from LDS
+      task_idx = p.members[it.member0 + k];
+      t = p.tasks[task_idx];
+      delta = t.q_pos0 - t.kv_pos0;
+      member();
+      member_rows();
+      sweep();
+    }
+  }
 
   // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
   if (!key_ok) return;
@@ -519,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: work items as in the forward (hpw heads x 4/hpw blocks of 32 rows).
 // ---------------------------------------------------------------------------
-template <int D, bool PAGED, bool WIN>
+template <int D, bool PAGED, bool WIN, bool MULTI>
 __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   constexpr int BN = 64;
   constexpr int KS = D + 16;      // K is read row-wise and by transpose reads
@@ -533,7 +567,10 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][BN * VS];
 
   const FwdItem it = p.qitems[blockIdx.x];
-  const ca_task t = p.tasks[it.task];
+  // The item's query shard: tasks it.task .. it.task + n_seg - 1 share the
+  // query rows; t is the context being swept (the only one unless MULTI).
+  ca_task t = p.tasks[it.task];
+  int task_idx = it.task;
   const int tid = threadIdx.x;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -542,14 +579,19 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int hpw = p.hpw;
   const int head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
   const int wrow0 = it.row0 + (wave_u / hpw) * 32;
-  const int64_t delta = t.q_pos0 - t.kv_pos0;
-  const int kv_len = t.kv_len;
   const int rt = 32 * (4 / hpw);
   const int wg_last = min(it.row0 + rt, t.q_len) - 1;
-  const int kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
   const int w_last = min(wrow0 + 32, t.q_len) - 1;
-  const int w_kv_hi = (w_last < wrow0) ? 0 : (int)clamp64((int64_t)w_last + delta + 1, 0, kv_len);
-  const int w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
+  int64_t delta;
+  int kv_len, kv_hi, w_kv_hi, w_full;
+  auto context = [&]() __attribute__((always_inline)) {
+    delta = t.q_pos0 - t.kv_pos0;
+    kv_len = t.kv_len;
+    kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
+    w_kv_hi = (w_last < wrow0) ? 0 : (int)clamp64((int64_t)w_last + delta + 1, 0, kv_len);
+    w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
+  };
+  context();
 
   const int qrow = wrow0 + l32;
   const bool qvalid = qrow < t.q_len;
@@ -571,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
 #pragma unroll
   for (int c = 0; c < NCB; ++c) dq_acc[c] = f32x16_zero();
 
-  const int n_tiles = (kv_hi + BN - 1) / BN;
+  int n_tiles = (kv_hi + BN - 1) / BN;
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
   const __bf16* kbase = p.K + it.kv_head * D;
@@ -630,19 +672,26 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   // sink tiles [0, t_a) and the window tiles [t_b, n_tiles); the full ones are
   // the window tiles inside the last row's window and below the first row's
   // diagonal.
-  int win = 0, sj = 0;
-  if (p.masks) {
-    win = p.masks[it.task].window;
-    if (win > 0) sj = (int)clamp64((int64_t)p.masks[it.task].sink - t.kv_pos0, 0, kv_len);
-  }
-  const int64_t w_lo_first = (int64_t)wrow0 + delta - win + 1;
-  const int64_t w_lo_last = (int64_t)w_last + delta - win + 1;
-  int t_a = 0, t_b = 0;
-  if (win > 0) {
-    t_a = min((sj + BN - 1) / BN, n_tiles);
-    t_b = min(max(t_a, (int)(clamp64((int64_t)it.row0 + delta - win + 1, 0, kv_len) / BN)), n_tiles);
-  }
-  const int n_visit = t_a + (n_tiles - t_b);
+  int win, sj, t_a, t_b, n_visit;
+  int64_t w_lo_first, w_lo_last;
+  auto context_tiles = [&]() __attribute__((always_inline)) {
+    win = 0;
+    sj = 0;
+    if (p.masks) {
+      win = p.masks[task_idx].window;
+      if (win > 0) sj = (int)clamp64((int64_t)p.masks[task_idx].sink - t.kv_pos0, 0, kv_len);
+    }
+    w_lo_first = (int64_t)wrow0 + delta - win + 1;
+    w_lo_last = (int64_t)w_last + delta - win + 1;
+    t_a = 0;
+    t_b = 0;
+    if (win > 0) {
+      t_a = min((sj + BN - 1) / BN, n_tiles);
+      t_b = min(max(t_a, (int)(clamp64((int64_t)it.row0 + delta - win + 1, 0, kv_len) / BN)), n_tiles);
+    }
+    n_visit = t_a + (n_tiles - t_b);
+  };
+  context_tiles();
   auto tile_of = [&](int k) { return k < t_a ? k : t_b + (k - t_a); };
   auto wave_sees = [&](int tile) {
     if (tile * BN >= w_kv_hi) return false;
@@ -652,6 +701,7 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     if (tile >= w_full) return true;
     return win > 0 && !((tile + 1) * BN <= sj || (int64_t)tile * BN >= w_lo_last);
   };
+  auto sweep = [&]() __attribute__((always_inline)) {
   const int c_hi = min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN));
   int k_f0 = 0, k_f1 = c_hi & ~1;
   if (!WIN && win > 0) k_f1 = 0;   // masks without the windowed loop split
@@ -852,6 +902,20 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     do_tile(B1{}, std::false_type{}, k + 1);
   }
   if (k < n_visit) do_tile(B0{}, std::false_type{}, k);
+  };
+  sweep();
+  if constexpr (MULTI) {
+    // the shard's further contexts: dQ keeps accumulating
+    for (int sg = 1; sg < it.n_seg; ++sg) {
+      __syncthreads();   // the previous context's last tile may still be read from LDS
+      task_idx = it.task + sg;
+      t = p.tasks[task_idx];
+      context();
+      n_tiles = (kv_hi + BN - 1) / BN;
+      context_tiles();
+      sweep();
+    }
+  }
 
   if (!qvalid) return;
   const int64_t base = (t.q_off + qrow) * q_stride + head * D;
@@ -899,15 +963,22 @@ hipError_t launch_bwd_prep(const __bf16* O, const __bf16* dO, float* Dv, int64_t
   return hipGetLastError();
 }
 
+// MULTI: calls with query shards over several contexts or context groups of
+// several tasks; all others run the single-task kernels.
+template <int D, bool PAGED, bool WIN>
+hipError_t launch_bwd_kv_dpw(const BwdParams& p, hipStream_t s) {
+  if (p.multi)
+    hipLaunchKernelGGL((bwd_kv_kernel<D, PAGED, WIN, true>), dim3(p.n_items), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<D, PAGED, WIN, false>), dim3(p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 // WIN: the loop split for sink + sliding-window masks, taken when the call
 // has masks; calls without masks run the variant without it.
 template <int D, bool PAGED>
 hipError_t launch_bwd_kv_dp(const BwdParams& p, hipStream_t s) {
-  if (p.masks)
-    hipLaunchKernelGGL((bwd_kv_kernel<D, PAGED, true>), dim3(p.n_items), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel<D, PAGED, false>), dim3(p.n_items), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return p.masks ? launch_bwd_kv_dpw<D, PAGED, true>(p, s) : launch_bwd_kv_dpw<D, PAGED, false>(p, s);
 }
 
 template <int D>
@@ -915,13 +986,18 @@ hipError_t launch_bwd_kv_d(const BwdParams& p, hipStream_t s) {
   return p.pages ? launch_bwd_kv_dp<D, true>(p, s) : launch_bwd_kv_dp<D, false>(p, s);
 }
 
+template <int D, bool PAGED, bool WIN>
+hipError_t launch_bwd_q_dpw(const BwdParams& p, hipStream_t s) {
+  if (p.multi)
+    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, WIN, true>), dim3(p.n_qitems), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, WIN, false>), dim3(p.n_qitems), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, bool PAGED>
 hipError_t launch_bwd_q_dp(const BwdParams& p, hipStream_t s) {
-  if (p.masks)
-    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, true>), dim3(p.n_qitems), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, false>), dim3(p.n_qitems), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return p.masks ? launch_bwd_q_dpw<D, PAGED, true>(p, s) : launch_bwd_q_dpw<D, PAGED, false>(p, s);
 }
 
 template <int D>

@@ -31,6 +31,12 @@
 // instruction).  Pages hold a multiple of 128 rows and contexts start on a
 // 128-row boundary, so every 64-key tile lies inside one page.
 //
+// Query shards over several contexts (MULTI): consecutive tasks with the
+// same query rows are swept one after another by the same online softmax,
+// so the item attends to the union of their keys (the causal-blockwise and
+// shared-question masks of "DCP: Addressing Input Dynamism In Long-Context
+// Training via Dynamic Context Parallelism", Section 2.4, Figure 6c / 6d).
+//
 // Outputs: O (bf16, or fp32 partials) and LSE = ln sum exp(scale q.k), the
 // statistic that makes partials mergeable by Equation 4 ("Context Parallelism
 // for Scalable Million-Token Inference", Section 3.4 Merge Attention).
@@ -48,7 +54,7 @@ namespace ca {
 // regardless of when the reference moved.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int NW, bool PAGED>
+template <int D, int NW, bool PAGED, bool MULTI>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   constexpr int NT = 64 * NW;     // threads
   constexpr int BN = 64;          // keys per tile
@@ -64,7 +70,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][BN * VS];
 
   const FwdItem it = p.items[blockIdx.x];
-  const ca_task t = p.tasks[it.task];
+  // The item's query shard: tasks it.task .. it.task + n_seg - 1 share the
+  // query rows; t is the context being swept (the only one unless MULTI).
+  ca_task t = p.tasks[it.task];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -76,30 +84,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
   const int wrow0 = it.row0 + (wave_u / hpw) * 32;
-  const int64_t delta = t.q_pos0 - t.kv_pos0;
-  const int kv_len = t.kv_len;
-
-  // Key range of the workgroup and of this wave.
   const int rt = 32 * (NW / hpw);
   const int wg_last = min(it.row0 + rt, t.q_len) - 1;
-  const int kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
   const int w_last = min(wrow0 + 32, t.q_len) - 1;
-  const int w_kv_hi = (w_last < wrow0) ? 0 : (int)clamp64((int64_t)w_last + delta + 1, 0, kv_len);
-  // Tiles [0, w_full) are visible to every row of the wave: no mask.
-  const int w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
 
-  // Sink + sliding-window mask (win > 0): besides being causal, key j must lie
+  // Per context: the key range of the workgroup and of this wave; tiles
+  // [0, w_full) are visible to every row of the wave (no mask).  Sink +
+  // sliding-window mask (win > 0): besides being causal, key j must lie
   // within the row's win latest positions (j > i + delta - win) or be one of
   // the sink keys [0, sj).  The workgroup visits the sink tiles [0, t_a) and
   // the window tiles [t_b, n_tiles); win == 0 visits [0, n_tiles).
-  int win = 0, sj = 0;
-  if (p.masks) {
-    win = p.masks[it.task].window;
-    if (win > 0) sj = (int)clamp64((int64_t)p.masks[it.task].sink - t.kv_pos0, 0, kv_len);
-  }
-  // window starts (first visible window key) of the wave's first and last rows
-  const int64_t w_lo_first = (int64_t)wrow0 + delta - win + 1;
-  const int64_t w_lo_last = (int64_t)w_last + delta - win + 1;
+  int64_t delta, w_lo_first, w_lo_last;   // window starts of the wave's first and last rows
+  int kv_len, kv_hi, w_kv_hi, w_full, win, sj;
+  auto context = [&](int task_idx) __attribute__((always_inline)) {
+    delta = t.q_pos0 - t.kv_pos0;
+    kv_len = t.kv_len;
+    kv_hi = (int)clamp64((int64_t)wg_last + delta + 1, 0, kv_len);
+    w_kv_hi = (w_last < wrow0) ? 0 : (int)clamp64((int64_t)w_last + delta + 1, 0, kv_len);
+    w_full = (int)clamp64(((int64_t)wrow0 + delta + 1) / BN, 0, (kv_len / BN));
+    win = 0;
+    sj = 0;
+    if (p.masks) {
+      win = p.masks[task_idx].window;
+      if (win > 0) sj = (int)clamp64((int64_t)p.masks[task_idx].sink - t.kv_pos0, 0, kv_len);
+    }
+    w_lo_first = (int64_t)wrow0 + delta - win + 1;
+    w_lo_last = (int64_t)w_last + delta - win + 1;
+  };
+  context(it.task);
 
   // Q^T operand: this lane's query row, channels 16 s + 8 hh .. + 7.
   const int qrow = wrow0 + l32;
@@ -117,14 +129,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   float m2 = -INFINITY;   // reference max, log2 units
   float lsum = 0.f;       // sum of exp2(s * c - m2)
 
-  const int n_tiles = (kv_hi + BN - 1) / BN;
-  int t_a = 0, t_b = 0;
-  if (win > 0) {
-    t_a = min((sj + BN - 1) / BN, n_tiles);
-    t_b = max(t_a, (int)(clamp64((int64_t)it.row0 + delta - win + 1, 0, kv_len) / BN));
-    t_b = min(t_b, n_tiles);
-  }
-  const int n_visit = t_a + (n_tiles - t_b);
+  int n_tiles, t_a, t_b, n_visit;
+  auto context_tiles = [&]() __attribute__((always_inline)) {
+    n_tiles = (kv_hi + BN - 1) / BN;
+    t_a = 0;
+    t_b = 0;
+    if (win > 0) {
+      t_a = min((sj + BN - 1) / BN, n_tiles);
+      t_b = max(t_a, (int)(clamp64((int64_t)it.row0 + delta - win + 1, 0, kv_len) / BN));
+      t_b = min(t_b, n_tiles);
+    }
+    n_visit = t_a + (n_tiles - t_b);
+  };
+  context_tiles();
   auto tile_of = [&](int k) { return k < t_a ? k : t_b + (k - t_a); };
   // Does this wave see any key of the tile, and does every row see all of it?
   auto wave_sees = [&](int tile) {
@@ -313,6 +330,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // in step k - 1, before the barrier of step k.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  auto sweep = [&]() __attribute__((always_inline)) {
   int next_page = 0;
   if (n_visit > 0) gload(S0{}, tile_of(0), tile_row(tile_of(0), tile_page(tile_of(0))));
   if (n_visit > 1) gload(S1{}, tile_of(1), tile_row(tile_of(1), tile_page(tile_of(1))));
@@ -343,6 +361,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   for (int k = 0; k < n_visit; k += 2) {
     step(S0{}, k);
     if (k + 1 < n_visit) step(S1{}, k + 1);
+  }
+  };
+  sweep();
+  if constexpr (MULTI) {
+    // the shard's further contexts: the online softmax state carries over
+    for (int sg = 1; sg < it.n_seg; ++sg) {
+      __syncthreads();   // the previous context's last tiles may still be read from LDS
+      t = p.tasks[it.task + sg];
+      context(it.task + sg);
+      context_tiles();
+      sweep();
+    }
   }
 
   // Epilogue: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty rows: 0, -inf.
@@ -376,13 +406,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   }
 }
 
+// MULTI: calls with query shards over several contexts; all others run the
+// single-context kernel.
+template <int D, int NW, bool PAGED>
+hipError_t launch_forward_dp(const FwdParams& p, hipStream_t s) {
+  if (p.multi)
+    hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, true>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, false>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, int NW>
 hipError_t launch_forward_d(const FwdParams& p, hipStream_t s) {
-  if (p.pages)
-    hipLaunchKernelGGL((fwd_kernel<D, NW, true>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<D, NW, false>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
-  return hipGetLastError();
+  return p.pages ? launch_forward_dp<D, NW, true>(p, s) : launch_forward_dp<D, NW, false>(p, s);
 }
 
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t s) {

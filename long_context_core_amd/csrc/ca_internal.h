@@ -10,14 +10,16 @@
 
 namespace ca {
 
-// One forward work item: a tile of query rows of one task, for a subset of
-// the query heads that share one KV head.  The workgroup's eight waves cover
-// hpw heads x (8 / hpw) blocks of 32 rows.
+// One forward work item: a tile of query rows of one query shard (tasks
+// task .. task + n_seg - 1, which share their query rows and are swept by one
+// online softmax), for a subset of the query heads that share one KV head.
+// The workgroup's eight waves cover hpw heads x (8 / hpw) blocks of 32 rows.
 struct FwdItem {
   int32_t task;
-  int32_t kv_head;
-  int32_t head_sub;  // which group of hpw heads inside the KV head's group
+  int16_t kv_head;
+  int16_t head_sub;  // which group of hpw heads inside the KV head's group
   int32_t row0;      // first task-relative query row
+  int32_t n_seg;     // contexts of the shard (consecutive tasks)
 };
 
 // Split-KV decode work item: one task (a single query row), one KV head, all
@@ -33,12 +35,15 @@ struct DecItem {
   int32_t pad[3];
 };
 
-// Backward work item (dK/dV kernel): 128 context rows of a task, one KV head.
+// Backward work item (dK/dV kernel): 128 context rows of a context group
+// (tasks with the same context rows, listed at members[member0 ..
+// member0 + n_members)), one KV head; it sweeps the query rows of every
+// member.
 struct BwdItem {
-  int32_t task;
+  int32_t member0;
   int32_t kv_head;
-  int32_t key0;      // first task-relative context row of the tile
-  int32_t pad;
+  int32_t key0;      // first context-relative row of the tile
+  int32_t n_members;
 };
 
 struct FwdParams {
@@ -57,6 +62,7 @@ struct FwdParams {
   int32_t hq, hkv, group, hpw;
   float scale_log2;   // softmax scale * log2(e)
   int32_t out_f32;
+  int32_t multi;      // some item has n_seg > 1
 };
 
 struct DecParams {
@@ -119,6 +125,7 @@ struct BwdParams {
   float* dVacc;
   const ca_task* tasks;
   const ca_task_mask* masks;   // per task, or nullptr: causal only
+  const int32_t* members;      // task indices of the context groups (dK/dV items)
   const int32_t* pages;   // as in FwdParams
   uint32_t page_bytes;
   int32_t page_shift;
@@ -130,6 +137,7 @@ struct BwdParams {
   float scale;
   float scale_log2;
   int32_t accumulate;
+  int32_t multi;          // a shard (dQ items) or a context group (dK/dV items) of several tasks
 };
 
 // A forward call whose work queue is built: what its launch needs once the
@@ -144,6 +152,7 @@ struct PreparedFwd {
   int32_t n_items, n_dec_items, n_split;
   int32_t has_masks, has_pages, page_shift;
   uint32_t page_bytes;
+  int32_t multi;            // some query shard has several contexts
   uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_part_o, off_part_l;
 };
 

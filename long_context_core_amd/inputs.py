@@ -184,6 +184,43 @@ def blockwise_tasks(doc_lens, block=256, win_blocks=2):
     return np.array(t, dtype=np.int64).reshape(-1, 7), 2
 
 
+def blockwise_shards(doc_lens, block=256, win_blocks=2):
+    """The causal-blockwise mask of blockwise_tasks in one launch: every block
+    of a document is one query shard; a non-final block whose window does not
+    reach the sink block lists two contexts, the sink block [0, block) (all
+    visible) and the causal window from its first window block; the others
+    list one.  Consecutive tasks with the same query rows are one shard (one
+    softmax over the union of their keys), so the output needs no merge."""
+    t = []
+    off = 0
+    for L in doc_lens:
+        nb = -(-L // block)
+        for b in range(nb):
+            q0, q1 = b * block, min(L, (b + 1) * block)
+            last = b == nb - 1
+            k0 = 0 if last else max(0, b - win_blocks + 1) * block
+            if not last and k0 > 0:
+                t.append((off + q0, off, off + q0, q1 - q0, block, q0, 0))
+            t.append((off + q0, off + k0, off + q0, q1 - q0, q1 - k0, q0, k0))
+        off += L
+    return np.array(t, dtype=np.int64).reshape(-1, 7)
+
+
+def shared_question_shards(question, answers):
+    """The shared-question mask of shared_question_tasks in one launch: the
+    question is causal; every answer is one query shard over two contexts,
+    the whole question (all visible) and the answer itself (causal).  Both
+    contexts of an answer carry the answer's position after the question, so
+    the two tasks name the same query rows and form one shard."""
+    t = [(0, 0, 0, question, question, 0, 0)]
+    off = question
+    for a in answers:
+        t.append((off, 0, off, a, question, question, 0))
+        t.append((off, off, off, a, a, question, question))
+        off += a
+    return np.array(t, dtype=np.int64).reshape(-1, 7)
+
+
 def shared_question_tasks(question, answers):
     """Shared-question mask (one question, several answers packed after it):
     the question is causal; each answer sees the whole question and itself
@@ -198,6 +235,38 @@ def shared_question_tasks(question, answers):
         t.append((off, 0, T + off, a, question, question, 0))
         off += a
     return np.array(t, dtype=np.int64).reshape(-1, 7), 2
+
+
+def shared_question_batch(seed=107, total=524288, q_median=2048, a_median=512, answers=(4, 16)):
+    """A packed batch of shared-question groups (one question followed by
+    its answers, as in RL / preference data) filling ``total`` tokens,
+    Llama-3-8B attention shape: question lengths lognormal (median q_median,
+    sigma 1, clipped to [256, 16384]), 4-16 answers per group with lognormal
+    lengths (median a_median, sigma 1, clipped to [16, 4096]); the last group
+    is cut to fit.  Returns (Workload over the one-launch shard table, list
+    of (question, [answers]) per group)."""
+    rng = np.random.default_rng(seed)
+    groups, left = [], total
+    while left > 0:
+        q = int(min(max(round(math.exp(rng.normal(math.log(q_median), 1.0))), 256), 16384))
+        q = min(q, left)
+        left -= q
+        ans = []
+        for _ in range(int(rng.integers(answers[0], answers[1] + 1))):
+            if left <= 0:
+                break
+            a = int(min(max(round(math.exp(rng.normal(math.log(a_median), 1.0))), 16), 4096, left))
+            ans.append(a)
+            left -= a
+        groups.append((q, ans))
+    tables, off = [], 0
+    for q, ans in groups:
+        t = shared_question_shards(q, ans)
+        t[:, [0, 1, 2]] += off
+        tables.append(t)
+        off += q + sum(ans)
+    return (Workload("llama3-8b-shared-question-%dk" % (total // 1024), 32, 8, 128, np.concatenate(tables),
+                     total, total, total), groups)
 
 
 def ring_prefill_405b_tp8(total=131072, n=8):

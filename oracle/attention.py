@@ -46,8 +46,17 @@ Parallelism", Section 2.4 / Figure 6b): an attention sink plus a sliding
 window.  With kp = kv_pos0 + j and qp = q_pos0 + i, the key is visible iff
 kp <= qp and (window == 0 or kp > qp - window or kp < sink): every query sees
 the first ``sink`` positions and its ``window`` latest positions (itself
-included).  Causal-blockwise and shared-question masks are unions of causal
-task contexts and are written as several tasks merged by Equation 4.
+included).
+
+A query shard may attend to several contexts: consecutive tasks with the
+same q_off, o_off, q_len and q_pos0 (and q_len > 0) are one shard whose rows
+attend to the union of the tasks' visible keys, with one softmax over all of
+them.  This is how the causal-blockwise and shared-question masks ("Dynamic
+Context Parallelism", Section 2.4, Figure 6c / 6d) are written: every query
+sees a sink block or the question plus its own causal window, i.e. a union of
+key ranges (the DCP executor's blockwise attention takes lists of query and
+key blocks).  A key listed by two tasks of one shard counts twice.
+
 A row with no visible key has O = 0 and LSE = -inf (a reading: the pages do
 not discuss empty rows; this is the value that gives the row zero weight in
 Equation 4).
@@ -123,36 +132,68 @@ def _context_len(task, rows):
     return max(0, min(kv_len, last))
 
 
-def _row_chunks(task, rows):
-    n = max(1, _context_len(task, rows))
+def _shards(tasks):
+    """Split a task table into query shards: maximal runs of consecutive
+    tasks with the same q_off, o_off, q_len and q_pos0 (q_len > 0); every
+    other task is a shard of its own.  Yields (n_seg, 9) arrays."""
+    t = _as_tasks(tasks)
+    i = 0
+    while i < len(t):
+        j = i + 1
+        if t[i, 3] > 0:
+            while j < len(t) and all(t[j, c] == t[i, c] for c in (0, 2, 3, 5)):
+                j += 1
+        yield t[i:j]
+        i = j
+
+
+def _as_shard(task):
+    """A single task or the segments of one shard, as an (n_seg, 9) array."""
+    segs = _as_tasks(task)
+    for c in (0, 2, 3, 5):
+        if np.any(segs[:, c] != segs[0, c]):
+            raise ValueError("the segments of a shard must share q_off, o_off, q_len and q_pos0")
+    return segs
+
+
+def _row_chunks(segs, rows):
+    n = max(1, sum(_context_len(t, rows) for t in segs))
     step = max(1, _CHUNK_ELEMS // n)
     for s in range(0, len(rows), step):
         yield rows[s:s + step]
 
 
-def _head_rows(task, rows, h, Q, K, V, scale, hq, hkv):
-    """Softmax attention of one query head over one task, for selected rows.
+def _head_rows(segs, rows, h, Q, K, V, scale, hq, hkv):
+    """Softmax attention of one query head over one shard, for selected rows.
 
-    Returns (O [r, d], LSE [r], P [r, n], n) where P is the full materialised
-    probability block over the first n context keys (the rest are masked for
-    every selected row).  The plain definition: s = scale * q.k over visible
-    keys, m = max s, w = exp(s - m), l = sum w, O = sum w v / l,
-    LSE = m + ln l.  No online rescaling, no blocking of the key axis.
+    Returns (O [r, d], LSE [r], [(P_s [r, n_s], n_s) per segment]) where P_s
+    is the materialised probability block over the first n_s context keys of
+    segment s (the rest are masked for every selected row).  The plain
+    definition over the union of the segments' visible keys: s = scale * q.k,
+    m = max s, w = exp(s - m), l = sum w, O = sum w v / l, LSE = m + ln l.
+    No online rescaling, no blocking of the key axis.
     """
-    q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in task[:7])
+    q_off = int(segs[0][0])
     g = _group_of(h, hq, hkv)
-    n = _context_len(task, rows)
     d = Q.shape[2]
     r = len(rows)
     O = np.zeros((r, d))
     LSE = np.full(r, -np.inf)
-    if n == 0 or r == 0:
-        return O, LSE, np.zeros((r, 0)), 0
-    q = Q[q_off + rows, h, :]                      # [r, d]
-    k = K[kv_off:kv_off + n, g, :]                 # [n, d]
-    v = V[kv_off:kv_off + n, g, :]                 # [n, d]
-    s = scale * (q @ k.T)                          # [r, n]
-    vis = visible_mask(task, rows, n)
+    q = Q[q_off + rows, h, :]                          # [r, d]
+    S, VIS, VV, ns = [], [], [], []
+    for t in segs:
+        kv_off = int(t[1])
+        n = _context_len(t, rows) if r else 0
+        ns.append(n)
+        k = K[kv_off:kv_off + n, g, :]                 # [n, d]
+        VV.append(V[kv_off:kv_off + n, g, :])
+        S.append(scale * (q @ k.T))                    # [r, n]
+        VIS.append(visible_mask(t, rows, n))
+    if sum(ns) == 0 or r == 0:
+        return O, LSE, [(np.zeros((r, n)), n) for n in ns]
+    s = np.concatenate(S, axis=1)
+    vis = np.concatenate(VIS, axis=1)
+    v = np.concatenate(VV, axis=0)
     s = np.where(vis, s, -np.inf)
     has = vis.any(axis=1)
     m = np.where(has, np.max(np.where(vis, s, -np.inf), axis=1), 0.0)
@@ -162,13 +203,15 @@ def _head_rows(task, rows, h, Q, K, V, scale, hq, hkv):
     P = w / safe_l[:, None]
     O = P @ v
     LSE = np.where(has, m + np.log(safe_l), -np.inf)
-    return O, LSE, P, n
+    bounds = np.cumsum([0] + ns)
+    return O, LSE, [(P[:, bounds[i]:bounds[i + 1]], ns[i]) for i in range(len(ns))]
 
 
 def forward_rows(task, rows, Q, K, V, scale, hq=None, hkv=None):
     """O [r, Hq, d] and LSE [r, Hq] for the given rows (task-relative indices)
-    of one CA-task.  Used directly for sampled checks at full size."""
-    task = _as_tasks(task)[0]
+    of one CA-task, or of one query shard given as its segment tasks.  Used
+    directly for sampled checks at full size."""
+    segs = _as_shard(task)
     hq = Q.shape[1] if hq is None else hq
     hkv = K.shape[1] if hkv is None else hkv
     rows = np.asarray(rows, dtype=np.int64)
@@ -176,9 +219,9 @@ def forward_rows(task, rows, Q, K, V, scale, hq=None, hkv=None):
     O = np.zeros((len(rows), hq, d))
     LSE = np.full((len(rows), hq), -np.inf)
     pos = 0
-    for chunk in _row_chunks(task, rows):
+    for chunk in _row_chunks(segs, rows):
         for h in range(hq):
-            o, lse, _, _ = _head_rows(task, chunk, h, Q, K, V, scale, hq, hkv)
+            o, lse, _ = _head_rows(segs, chunk, h, Q, K, V, scale, hq, hkv)
             O[pos:pos + len(chunk), h, :] = o
             LSE[pos:pos + len(chunk), h] = lse
         pos += len(chunk)
@@ -186,7 +229,7 @@ def forward_rows(task, rows, Q, K, V, scale, hq=None, hkv=None):
 
 
 def forward(tasks, Q, K, V, scale, o_rows=None):
-    """Core attention over every task of the table.
+    """Core attention over every query shard of the table.
 
     Returns O [o_rows, Hq, d] and LSE [o_rows, Hq] in float64.  Output rows
     that no task covers hold NaN so that a comparison cannot pass on them by
@@ -198,10 +241,10 @@ def forward(tasks, Q, K, V, scale, o_rows=None):
         o_rows = int(max([t[2] + t[3] for t in tasks] + [0]))
     O = np.full((o_rows, hq, d), np.nan)
     LSE = np.full((o_rows, hq), np.nan)
-    for t in tasks:
-        q_len = int(t[3])
-        o_off = int(t[2])
-        o, lse = forward_rows(t, np.arange(q_len), Q, K, V, scale)
+    for segs in _shards(tasks):
+        q_len = int(segs[0][3])
+        o_off = int(segs[0][2])
+        o, lse = forward_rows(segs, np.arange(q_len), Q, K, V, scale)
         O[o_off:o_off + q_len] = o
         LSE[o_off:o_off + q_len] = lse
     return O, LSE
@@ -240,7 +283,8 @@ def backward(tasks, Q, K, V, dO, scale, dq_rows=None, dkv_rows=None):
     probabilities from the saved per-row statistics instead of storing them
     (Core Attention Disaggregation, Sections 3.2 and 3.4).  The oracle takes
     the plain gradient of the forward definition: with P the softmax
-    probabilities of a row, D_i = <dO_i, O_i>,
+    probabilities of a row (over all the keys its shard sees), D_i =
+    <dO_i, O_i>,
         dV_j = sum_i P_ij dO_i,    dP_ij = <dO_i, V_j>,
         dS_ij = P_ij (dP_ij - D_i),
         dQ_i = scale sum_j dS_ij K_j,    dK_j = scale sum_i dS_ij Q_i,
@@ -256,30 +300,33 @@ def backward(tasks, Q, K, V, dO, scale, dq_rows=None, dkv_rows=None):
     dQ = np.zeros((dq_rows, hq, d))
     dK = np.zeros((dkv_rows, hkv, d))
     dV = np.zeros((dkv_rows, hkv, d))
-    for t in tasks:
-        q_off, kv_off, o_off, q_len = int(t[0]), int(t[1]), int(t[2]), int(t[3])
-        for chunk in _row_chunks(t, np.arange(q_len)):
+    for segs in _shards(tasks):
+        q_off, o_off, q_len = int(segs[0][0]), int(segs[0][2]), int(segs[0][3])
+        for chunk in _row_chunks(segs, np.arange(q_len)):
             for h in range(hq):
                 g = _group_of(h, hq, hkv)
-                o, _, P, n = _head_rows(t, chunk, h, Q, K, V, scale, hq, hkv)
-                if n == 0:
-                    continue
+                o, _, parts = _head_rows(segs, chunk, h, Q, K, V, scale, hq, hkv)
                 do = dO[o_off + chunk, h, :]           # [r, d]
-                k = K[kv_off:kv_off + n, g, :]
-                v = V[kv_off:kv_off + n, g, :]
                 q = Q[q_off + chunk, h, :]
                 D = np.sum(do * o, axis=1)             # [r]
-                dV[kv_off:kv_off + n, g, :] += P.T @ do
-                dP = do @ v.T                          # [r, n]
-                dS = P * (dP - D[:, None])
-                dQ[q_off + chunk, h, :] += scale * (dS @ k)
-                dK[kv_off:kv_off + n, g, :] += scale * (dS.T @ q)
+                for t, (P, n) in zip(segs, parts):
+                    if n == 0:
+                        continue
+                    kv_off = int(t[1])
+                    k = K[kv_off:kv_off + n, g, :]
+                    v = V[kv_off:kv_off + n, g, :]
+                    dV[kv_off:kv_off + n, g, :] += P.T @ do
+                    dP = do @ v.T                      # [r, n]
+                    dS = P * (dP - D[:, None])
+                    dQ[q_off + chunk, h, :] += scale * (dS @ k)
+                    dK[kv_off:kv_off + n, g, :] += scale * (dS.T @ q)
     return dQ, dK, dV
 
 
 def backward_dq_rows(task, rows, Q, K, V, dO, scale, heads=None):
-    """dQ [len(rows), len(heads), d] of selected rows of one task: the rows
-    of ``backward``'s dQ, computed from those rows alone.
+    """dQ [len(rows), len(heads), d] of selected rows of one task (or of one
+    query shard given as its segment tasks): the rows of ``backward``'s dQ,
+    computed from those rows alone.
 
     dQ_i depends only on row i (its probabilities P_i over its visible keys,
     D_i = <dO_i, O_i> and dP_i = dO_i V^T), so the gradient of
@@ -289,25 +336,27 @@ def backward_dq_rows(task, rows, Q, K, V, dO, scale, heads=None):
     ``heads`` lists the query heads (default: all); O and P come from the
     oracle's own float64 forward of the rows.
     """
-    task = _as_tasks(task)[0]
-    q_off, kv_off, o_off = int(task[0]), int(task[1]), int(task[2])
+    segs = _as_shard(task)
+    o_off = int(segs[0][2])
     hq, d = Q.shape[1], Q.shape[2]
     hkv = K.shape[1]
     heads = list(range(hq)) if heads is None else [int(h) for h in heads]
     rows = np.asarray(rows, dtype=np.int64)
     dQ = np.zeros((len(rows), len(heads), d))
     pos = 0
-    for chunk in _row_chunks(task, rows):
+    for chunk in _row_chunks(segs, rows):
         for k, h in enumerate(heads):
             g = _group_of(h, hq, hkv)
-            o, _, P, n = _head_rows(task, chunk, h, Q, K, V, scale, hq, hkv)
-            if n == 0:
-                continue
+            o, _, parts = _head_rows(segs, chunk, h, Q, K, V, scale, hq, hkv)
             do = dO[o_off + chunk, h, :]
             D = np.sum(do * o, axis=1)
-            dP = do @ V[kv_off:kv_off + n, g, :].T
-            dS = P * (dP - D[:, None])
-            dQ[pos:pos + len(chunk), k, :] = scale * (dS @ K[kv_off:kv_off + n, g, :])
+            for t, (P, n) in zip(segs, parts):
+                if n == 0:
+                    continue
+                kv_off = int(t[1])
+                dP = do @ V[kv_off:kv_off + n, g, :].T
+                dS = P * (dP - D[:, None])
+                dQ[pos:pos + len(chunk), k, :] += scale * (dS @ K[kv_off:kv_off + n, g, :])
         pos += len(chunk)
     return dQ
 

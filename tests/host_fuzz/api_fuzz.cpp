@@ -80,6 +80,35 @@ int main() {
     sink += (size_t)ca_visible_pairs(t.data(), n) + (size_t)ca_visible_pairs_masked(t.data(), m.data(), n);
     valid_nonzero += a > 0;
   }
+  // query shards over several contexts (runs of tasks sharing their query
+  // rows) and context groups (tasks sharing their context rows)
+  for (int it = 0; it < 3000; ++it) {
+    ca_shape s{};
+    s.hkv = (int)U(1, 4); s.hq = s.hkv * (int)U(1, 8); s.d = U(0, 1) ? 128 : 64; s.scale = 0.088f;
+    s.q_rows = U(1, 5000); s.kv_rows = U(1, 5000); s.o_rows = s.q_rows;
+    std::vector<ca_task> t;
+    std::vector<ca_task_mask> m;
+    const int n_shards = (int)U(1, 12);
+    for (int k = 0; k < n_shards; ++k) {
+      ca_task base{};
+      base.q_len = (int)U(0, std::min<int64_t>(s.q_rows, 700));
+      base.q_off = U(0, s.q_rows - base.q_len); base.o_off = base.q_off;
+      base.q_pos0 = U(0, 9000);
+      const int n_seg = (int)U(1, 4);
+      for (int j = 0; j < n_seg; ++j) {
+        ca_task x = base;
+        if (!t.empty() && !U(0, 3)) { x.kv_off = t.back().kv_off; x.kv_len = t.back().kv_len; }
+        else { x.kv_len = (int)U(0, s.kv_rows); x.kv_off = U(0, s.kv_rows - x.kv_len); }
+        x.kv_pos0 = U(0, 9000);
+        t.push_back(x);
+        m.push_back({(int)U(0, 2) ? 0 : (int)U(1, 3000), (int)U(0, 50)});
+      }
+    }
+    const int n = (int)t.size();
+    sink += ca_forward_workspace(&s, t.data(), n) + ca_forward_masked_workspace(&s, t.data(), m.data(), n);
+    sink += ca_backward_workspace(&s, t.data(), n) + ca_backward_masked_workspace(&s, t.data(), m.data(), n);
+    sink += (size_t)ca_visible_pairs_masked(t.data(), m.data(), n);
+  }
   std::printf("api host fuzz done %zu (valid cases with a workspace: %d)\n", sink % 7, valid_nonzero);
   return 0;
 }

@@ -16,6 +16,19 @@ def _val(x):
     return mp.mpf(float(x))
 
 
+def _groups(tasks):
+    """Consecutive tasks naming the same query rows (q_off, o_off, q_len,
+    q_pos0, q_len > 0) form one query that attends to all their contexts."""
+    rows = [tuple(int(x) for x in t[:7]) for t in tasks]
+    out = []
+    for t in rows:
+        if out and t[3] > 0 and all(out[-1][-1][c] == t[c] for c in (0, 2, 3, 5)):
+            out[-1].append(t)
+        else:
+            out.append([t])
+    return out
+
+
 def attention(tasks, Q, K, V, scale):
     """Returns dict {(o_row, h): (O list of mpf, LSE mpf)}."""
     out = {}
@@ -23,25 +36,26 @@ def attention(tasks, Q, K, V, scale):
     hkv = K.shape[1]
     group = hq // hkv
     sc = mp.mpf(scale) if not isinstance(scale, mp.mpf) else scale
-    for t in tasks:
-        q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 = (int(x) for x in t)
+    for grp in _groups(tasks):
+        q_off, _, o_off, q_len, _, q_pos0, _ = grp[0]
         for i in range(q_len):
             my_pos = q_pos0 + i
             for h in range(hq):
                 g = h // group
-                keys = []
-                for j in range(kv_len):
-                    if kv_pos0 + j > my_pos:
-                        continue
-                    s = mp.mpf(0)
-                    for c in range(d):
-                        s += _val(Q[q_off + i, h, c]) * _val(K[kv_off + j, g, c])
-                    keys.append((j, s * sc))
+                keys = []          # (K/V row, score) over every context of the query
+                for (_, kv_off, _, _, kv_len, _, kv_pos0) in grp:
+                    for j in range(kv_len):
+                        if kv_pos0 + j > my_pos:
+                            continue
+                        s = mp.mpf(0)
+                        for c in range(d):
+                            s += _val(Q[q_off + i, h, c]) * _val(K[kv_off + j, g, c])
+                        keys.append((kv_off + j, s * sc))
                 if not keys:
                     out[(o_off + i, h)] = ([mp.mpf(0)] * d, -mp.inf)
                     continue
                 z = mp.fsum(mp.exp(s) for _, s in keys)
-                o = [mp.fsum(mp.exp(s) * _val(V[kv_off + j, g, c]) for j, s in keys) / z
+                o = [mp.fsum(mp.exp(s) * _val(V[row, g, c]) for row, s in keys) / z
                      for c in range(d)]
                 out[(o_off + i, h)] = (o, mp.log(z))
     return out

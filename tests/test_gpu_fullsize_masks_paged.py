@@ -194,3 +194,124 @@ def test_ca_tasks_34b_backward_invariants():
     print("34b CA-task backward: max|sum dK|/sum|dK| = %.3e, rel max|sum dV - sum dO| = %.3e"
           % (worst_k, worst_v), flush=True)
     assert worst_k < 1e-2 and worst_v < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# causal-blockwise and shared-question masks at 512K, one launch each
+# ---------------------------------------------------------------------------
+
+def shard_starts(tasks):
+    """Indices of the first task of every query shard (consecutive tasks
+    with the same q_off, o_off, q_len, q_pos0 form one)."""
+    t = np.asarray(tasks)
+    same = np.zeros(len(t), dtype=bool)
+    same[1:] = np.all(t[1:, [0, 2, 3, 5]] == t[:-1, [0, 2, 3, 5]], axis=1) & (t[1:, 3] > 0)
+    return np.flatnonzero(~same)
+
+
+def probe_expect_ranges(tasks, T):
+    """K = 0 and V = (-1)^(buffer row): every visible key weighs the same, so a
+    row's O is the mean of (-1)^row over its visible key rows and LSE the log
+    of their count.  Each context contributes the key rows
+    [kv_off, kv_off + n_i), n_i = clip(q_pos0 + i - kv_pos0 + 1, 0, kv_len)."""
+    ssum = np.zeros(T)
+    cnt = np.zeros(T)
+    for q_off, kv_off, o_off, q_len, kv_len, q_pos0, kv_pos0 in np.asarray(tasks):
+        i = np.arange(q_len)
+        n = np.clip(q_pos0 + i - kv_pos0 + 1, 0, kv_len)
+        ssum[o_off:o_off + q_len] += sign_sum(np.full(q_len, kv_off), kv_off + n - 1)
+        cnt[o_off:o_off + q_len] += n
+    return ssum / np.maximum(cnt, 1), cnt
+
+
+def run_probe_512k(tasks, w, label):
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    T = w.q_rows
+    Q = I.randn_bf16((T, w.hq, w.d), 291, device=dev)
+    K = torch.zeros((T, w.hkv, w.d), dtype=torch.bfloat16, device=dev)
+    sign = torch.from_numpy(np.where(np.arange(T) % 2 == 0, 1.0, -1.0).astype(np.float32)).to(dev)
+    V = sign[:, None, None].expand(T, w.hkv, w.d).to(torch.bfloat16).contiguous()
+    O = torch.empty((T, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((T, w.hq), device=dev)
+    ca.forward(ca.make_shape(w.hq, w.hkv, w.d, T, T, T), tasks, Q, K, V, O, LSE)
+    torch.cuda.synchronize()
+    exp_o, cnt = probe_expect_ranges(tasks, T)
+    e = torch.from_numpy(exp_o).to(dev)
+    c = torch.from_numpy(cnt).to(dev)
+    err = (O.float() - e[:, None, None].float()).abs().amax(dim=(1, 2))
+    bad = int((err >= (0.25 / c).float()).sum())
+    dl = float((LSE.double() - torch.log(c)[:, None]).abs().max())
+    print("%s probe: rows=%d bad_rows=%d max|dLSE|=%.2e" % (label, T, bad, dl), flush=True)
+    assert bad == 0 and dl < 1e-4
+
+
+def sampled_shards_512k(tasks, w, picks, label, seed):
+    """O and LSE of sampled rows of the picked shards (start indices into the
+    table) against the oracle on the shard's own key rows."""
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    T = w.q_rows
+    Q = I.randn_bf16((T, w.hq, w.d), seed, device=dev)
+    K = I.randn_bf16((T, w.hkv, w.d), seed + 1, device=dev)
+    V = I.randn_bf16((T, w.hkv, w.d), seed + 2, device=dev)
+    O = torch.empty((T, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((T, w.hq), device=dev)
+    ca.forward(ca.make_shape(w.hq, w.hkv, w.d, T, T, T), tasks, Q, K, V, O, LSE)
+    torch.cuda.synchronize()
+    starts = list(shard_starts(tasks)) + [len(tasks)]
+    rng = np.random.default_rng(seed)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for s0 in picks:
+        s1 = starts[starts.index(s0) + 1]
+        segs = np.array(tasks[s0:s1], dtype=np.int64)
+        q_off, q_len = int(segs[0, 0]), int(segs[0, 3])
+        rows = np.unique(np.concatenate([[0, q_len - 1], rng.integers(0, q_len, 3)]))
+        # the shard's key rows, gathered context after context
+        local = segs.copy()
+        ks, vs, at = [], [], 0
+        for k, sg in enumerate(segs):
+            ks.append(widen(K[int(sg[1]):int(sg[1]) + int(sg[4])]))
+            vs.append(widen(V[int(sg[1]):int(sg[1]) + int(sg[4])]))
+            local[k, 1] = at
+            at += int(sg[4])
+        local[:, 0] = 0
+        local[:, 2] = 0
+        qs = widen(Q[q_off:q_off + q_len])
+        o1, l1 = oracle.forward_rows(local, rows, qs, np.concatenate(ks), np.concatenate(vs), w.scale)
+        ref_o.append(o1)
+        ref_l.append(l1)
+        idx = torch.from_numpy(int(segs[0, 2]) + rows).to(dev)
+        got_o.append(widen(O[idx]))
+        got_l.append(widen(LSE[idx]))
+    check_forward(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(ref_o), np.concatenate(ref_l), label)
+
+
+def test_blockwise_512k_one_launch_probe_and_sampled():
+    """Causal-blockwise mask (256-token blocks, window of 2 blocks, sink block,
+    final block sees everything) over the 512K training mix, one launch: the
+    probe on every row and head, and the oracle on sampled rows of blocks of
+    the longest document (its final block included) and of short documents."""
+    announce("fullsize 512k causal-blockwise, one launch: probe + sampled rows")
+    w = I.train_8b_prolong_512k()
+    tasks = I.blockwise_shards(w.doc_lens, block=256, win_blocks=2)
+    run_probe_512k(tasks, w, "512k blockwise")
+    starts = shard_starts(tasks)
+    longest = int(np.argmax(w.doc_lens))
+    d0 = int(np.sum(w.doc_lens[:longest]))
+    in_long = [s for s in starts if d0 <= tasks[s][0] < d0 + w.doc_lens[longest]]
+    picks = [in_long[0], in_long[1], in_long[2], in_long[len(in_long) // 2], in_long[-2], in_long[-1],
+             int(starts[0]), int(starts[-1])]
+    sampled_shards_512k(tasks, w, picks, "512k-blockwise-sampled", 295)
+
+
+def test_shared_question_512k_one_launch_probe_and_sampled():
+    """Shared-question batch (49 groups of one question and 4-16 answers over
+    512K tokens), one launch: the probe on every row and head, and the oracle
+    on sampled rows of questions and answers."""
+    announce("fullsize 512k shared question, one launch: probe + sampled rows")
+    w, groups = I.shared_question_batch()
+    run_probe_512k(w.tasks, w, "512k shared question")
+    starts = shard_starts(w.tasks)
+    picks = [int(x) for x in starts[[0, 1, 2, len(starts) // 2, len(starts) // 2 + 1, -2, -1]]]
+    sampled_shards_512k(w.tasks, w, picks, "512k-shared-question-sampled", 297)

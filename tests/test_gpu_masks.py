@@ -187,3 +187,90 @@ def test_shared_question_mask_backward():
         off += a
     ref = oracle.backward_listed(widen(Q), widen(K), widen(V), widen(dO), 1 / math.sqrt(d), rows_keys)
     check_grads(got, ref, "shared-question bwd")
+
+
+# ---------------------------------------------------------------------------
+# one launch: query shards over several contexts (no partial slots, no merge)
+# ---------------------------------------------------------------------------
+
+def fused_grads(tasks, T, hq, hkv, d, seed, masks=None):
+    """Forward and backward of one shard table in single launches; returns
+    device O, LSE, the gradients and the host inputs."""
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((T, hq, d), seed)
+    K = I.randn_bf16((T, hkv, d), seed + 1)
+    V = I.randn_bf16((T, hkv, d), seed + 2)
+    dO = I.randn_bf16((T, hq, d), seed + 3)
+    Qd, Kd, Vd, dOd = Q.to(dev), K.to(dev), V.to(dev), dO.to(dev)
+    shape = ca.make_shape(hq, hkv, d, T, T, T)
+    O = torch.full((T, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((T, hq), float("nan"), device=dev)
+    ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE, masks=masks)
+    dQ, dK, dV = torch.empty_like(Qd), torch.empty_like(Kd), torch.empty_like(Vd)
+    ca.backward(shape, tasks, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV, masks=masks)
+    torch.cuda.synchronize()
+    return O, LSE, (dQ, dK, dV), Q, K, V, dO
+
+
+@pytest.mark.parametrize("block,w,hq,hkv,d", [(256, 2, 8, 2, 128), (128, 3, 4, 4, 64), (64, 1, 16, 1, 128)])
+def test_blockwise_one_launch(block, w, hq, hkv, d):
+    """Causal-blockwise mask as query shards over two contexts (sink block
+    and causal window): forward and backward in one launch each, against
+    the oracle (and the oracle's listed-key gradient)."""
+    announce("causal-blockwise in one launch: block %d window %d hq%d hkv%d d%d" % (block, w, hq, hkv, d))
+    docs = [2100, 300, 1024, 77]
+    T = sum(docs)
+    tasks = I.blockwise_shards(docs, block=block, win_blocks=w)
+    O, LSE, got, Q, K, V, dO = fused_grads(tasks, T, hq, hkv, d, 1540 + block)
+    Qw, Kw, Vw, dOw = widen(Q), widen(K), widen(V), widen(dO)
+    O_ref, LSE_ref = oracle.forward(tasks, Qw, Kw, Vw, 1 / math.sqrt(d))
+    check_forward(O, LSE, O_ref, LSE_ref, "blockwise one launch")
+    check_grads(got, oracle.backward(tasks, Qw, Kw, Vw, dOw, 1 / math.sqrt(d)), "blockwise one launch bwd")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (4, 1, 64)])
+def test_shared_question_one_launch(hq, hkv, d):
+    announce("shared question in one launch: hq%d hkv%d d%d" % (hq, hkv, d))
+    question, answers = 700, [300, 129, 1000, 64, 1]
+    T = question + sum(answers)
+    tasks = I.shared_question_shards(question, answers)
+    O, LSE, got, Q, K, V, dO = fused_grads(tasks, T, hq, hkv, d, 1560 + d)
+    Qw, Kw, Vw, dOw = widen(Q), widen(K), widen(V), widen(dO)
+    O_ref, LSE_ref = oracle.forward(tasks, Qw, Kw, Vw, 1 / math.sqrt(d))
+    check_forward(O, LSE, O_ref, LSE_ref, "shared question one launch")
+    check_grads(got, oracle.backward(tasks, Qw, Kw, Vw, dOw, 1 / math.sqrt(d)), "shared question one launch bwd")
+
+
+def random_shard_table(rng, T):
+    """Random query shards of 1-3 contexts each over one T-row buffer: query
+    row ranges tile [0, T) (ragged lengths, single rows included); each
+    context is a random key range with random positions, some of them
+    windowed; keys of a shard's contexts may repeat (they then count twice)."""
+    rows, masks, q = [], [], 0
+    while q < T:
+        ql = int(min(T - q, rng.choice([1, 5, 31, 64, 100, 257, 600])))
+        qp = int(rng.integers(0, 3000))
+        for _ in range(int(rng.integers(1, 4))):
+            kl = int(rng.integers(0, min(T, 1500)))
+            ko = int(rng.integers(0, T - kl + 1))
+            kp = int(rng.integers(max(0, qp - kl - 50), qp + 60))
+            rows.append((q, ko, q, ql, kl, qp, kp))
+            win = int(rng.choice([0, 0, 0, 1, 40, 700]))
+            masks.append((win, int(rng.integers(0, 80)) if win else 0))
+        q += ql
+    return np.array(rows, dtype=np.int64), np.array(masks, dtype=np.int64)
+
+
+@pytest.mark.parametrize("seed,hq,hkv,d", [(0, 8, 2, 128), (1, 4, 4, 64), (2, 16, 1, 128), (3, 6, 2, 64)])
+def test_random_multi_context_shards(seed, hq, hkv, d):
+    announce("random multi-context shards seed=%d hq%d hkv%d d%d" % (seed, hq, hkv, d))
+    rng = np.random.default_rng(1580 + seed)
+    T = 2400
+    tasks, masks = random_shard_table(rng, T)
+    O, LSE, got, Q, K, V, dO = fused_grads(tasks, T, hq, hkv, d, 1590 + seed, masks=masks)
+    Qw, Kw, Vw, dOw = widen(Q), widen(K), widen(V), widen(dO)
+    full = np.concatenate([tasks, masks], axis=1)
+    O_ref, LSE_ref = oracle.forward(full, Qw, Kw, Vw, 1 / math.sqrt(d))
+    check_forward(O, LSE, O_ref, LSE_ref, "random shards")
+    check_grads(got, oracle.backward(full, Qw, Kw, Vw, dOw, 1 / math.sqrt(d)), "random shards bwd")

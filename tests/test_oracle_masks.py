@@ -240,3 +240,124 @@ def test_backward_dq_rows_matches_finite_differences_and_backward():
                 qp[r, h, c] = mp.mpf(x) - eps
                 lm = mp_brute.loss(task, qp, K, V, dO, mp.mpf(0.6))
                 assert abs(got[k, j, c] - float((lp - lm) / (2 * eps))) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# query shards over several contexts (one softmax over the union of keys)
+# ---------------------------------------------------------------------------
+
+def _multi_context_case(seed):
+    """A tiny table with a two-context shard (a prefix block and a causal
+    window, tile-unaligned), a three-context shard and a plain task."""
+    T = 8
+    Q, K, V = tensors(T, 2, 1, 3, 90 + seed)
+    t = np.array([[0, 0, 0, 2, 2, 5, 0],          # rows 0-1 at positions 5, 6: keys 0-1 (all visible)
+                  [0, 4, 0, 2, 3, 5, 4],          #   and keys 4-6 at positions 4-6 (causal)
+                  [2, 2, 2, 1, 1, 3, 0],          # row 2 at position 3: key 2
+                  [2, 6, 2, 1, 2, 3, 2],          #   keys 6-7 at positions 2, 3
+                  [2, 0, 2, 1, 1, 3, 9],          #   key 0 at position 9: invisible
+                  [3, 3, 3, 4, 5, 0, 0]])         # a plain causal task
+    return t, Q, K, V
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_multi_context_shards_match_brute_force(seed):
+    """The oracle's shard semantics against the 50-digit brute force, which
+    derives every row's key set from the positions of all its contexts."""
+    t, Q, K, V = _multi_context_case(seed)
+    O, LSE = oracle.forward(t, Q, K, V, 0.4)
+    ref = mp_brute.attention(t, Q, K, V, mp.mpf(0.4))
+    for (row, h), (o, lse) in ref.items():
+        if lse == -mp.inf:
+            assert np.isneginf(LSE[row, h])
+        else:
+            assert abs(LSE[row, h] - float(lse)) < 1e-12
+        assert np.abs(O[row, h] - np.array([float(x) for x in o])).max() < 1e-12
+
+
+def test_multi_context_backward_matches_finite_differences():
+    t, Q, K, V = _multi_context_case(0)
+    dO = np.random.default_rng(95).standard_normal(Q.shape)
+    dQ, dK, dV = oracle.backward(t, Q, K, V, dO, 0.4)
+    eps = mp.mpf("1e-18")
+    for which, grad in (("Q", dQ), ("K", dK), ("V", dV)):
+        arr = {"Q": Q, "K": K, "V": V}[which]
+        for idx in np.ndindex(*arr.shape):
+            args = {"Q": Q, "K": K, "V": V}
+            a = arr.astype(object)
+            x = float(arr[idx])
+            a[idx] = mp.mpf(x) + eps
+            args[which] = a
+            lp = mp_brute.loss(t, args["Q"], args["K"], args["V"], dO, mp.mpf(0.4))
+            a[idx] = mp.mpf(x) - eps
+            lm = mp_brute.loss(t, args["Q"], args["K"], args["V"], dO, mp.mpf(0.4))
+            assert abs(grad[idx] - float((lp - lm) / (2 * eps))) < 1e-11, (which, idx)
+
+
+def test_multi_context_shard_equals_merge_of_its_contexts():
+    """A shard's O and LSE equal the Equation-4 merge of its contexts computed
+    as separate partials (each context into its own slot): the union of
+    disjoint key sets under one softmax is the merge of their softmaxes."""
+    docs = [700, 300, 90]
+    hq, hkv, d = 4, 2, 8
+    T = sum(docs)
+    Q, K, V = tensors(T, hq, hkv, d, 96)
+    fused = I.blockwise_shards(docs, block=64, win_blocks=2)
+    O, LSE = oracle.forward(fused, Q, K, V, 0.3)
+    Om, Lm = merged(*I.blockwise_tasks(docs, block=64, win_blocks=2), T, Q, K, V, 0.3)
+    assert np.abs(O - Om).max() < 1e-12 and np.abs(LSE - Lm).max() < 1e-12
+
+
+def _blockwise_lists(docs, block, w):
+    rows_keys, start = [], 0
+    for L in docs:
+        nb = -(-L // block)
+        for p in range(L):
+            b = p // block
+            if b == nb - 1:
+                keys = list(range(p + 1))
+            else:
+                keys = sorted(set(range(min(block, p + 1))) | set(range(max(0, b - w + 1) * block, p + 1)))
+            rows_keys.append([start + k for k in keys])
+        start += L
+    return rows_keys
+
+
+def _shared_question_lists(question, answers):
+    rows_keys = [list(range(p + 1)) for p in range(question)]
+    off = question
+    for a in answers:
+        rows_keys += [list(range(question)) + [off + j for j in range(i + 1)] for i in range(a)]
+        off += a
+    return rows_keys
+
+
+def test_fused_mask_recipes_match_listed_keys():
+    """The one-launch recipes (blockwise_shards, shared_question_shards) give
+    every row exactly the keys the masks' descriptions list: forward and
+    backward against forward_listed / backward_listed (pinned by finite
+    differences), and pair counts equal to the listed totals."""
+    scale = 0.3
+    docs, block, w = [700, 300, 90], 64, 2
+    T = sum(docs)
+    hq, hkv, d = 2, 1, 8
+    Q, K, V = tensors(T, hq, hkv, d, 97)
+    dO = np.random.default_rng(98).standard_normal((T, hq, d))
+    for tasks, lists in ((I.blockwise_shards(docs, block, w), _blockwise_lists(docs, block, w)),):
+        O, LSE = oracle.forward(tasks, Q, K, V, scale)
+        Ob, Lb = oracle.forward_listed(Q, K, V, scale, lists)
+        assert np.abs(O - Ob).max() < 1e-12 and np.abs(LSE - Lb).max() < 1e-12
+        for a, b in zip(oracle.backward(tasks, Q, K, V, dO, scale), oracle.backward_listed(Q, K, V, dO, scale, lists)):
+            assert np.abs(a - b).max() < 1e-12
+        assert oracle.visible_pairs(tasks) == sum(len(k) for k in lists)
+    question, answers = 37, [20, 5, 44]
+    T = question + sum(answers)
+    Q, K, V = tensors(T, hq, hkv, d, 99)
+    dO = np.random.default_rng(100).standard_normal((T, hq, d))
+    tasks, lists = I.shared_question_shards(question, answers), _shared_question_lists(question, answers)
+    O, LSE = oracle.forward(tasks, Q, K, V, scale)
+    Ob, Lb = oracle.forward_listed(Q, K, V, scale, lists)
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(LSE - Lb).max() < 1e-12
+    for a, b in zip(oracle.backward(tasks, Q, K, V, dO, scale), oracle.backward_listed(Q, K, V, dO, scale, lists)):
+        assert np.abs(a - b).max() < 1e-12
+    assert oracle.visible_pairs(tasks) == sum(len(k) for k in lists)
