@@ -364,17 +364,121 @@ int64_t decode_visible(const ca_task& k) {
   return std::min<int64_t>(k.kv_len, std::max<int64_t>(0, k.q_pos0 - k.kv_pos0 + 1));
 }
 
+// Long query shards split over key chunks (forward and dQ kernels).  An item
+// that would sweep far more (row, key) pairs than the call's average work
+// per compute unit makes a tail no scheduling hides; its shard's visible
+// keys are cut into chunks, each a run of derived tasks (sub-ranges of the
+// shard's contexts, appended after the table) whose items write fp32
+// partials to staging rows; the partials are merged afterwards.  Shards with
+// sink / window masks are left whole (their items are short).
+constexpr int64_t kMinSplitPairs = 1 << 21;   // per item and head
+constexpr int64_t kSplitPairsDiv = 1024;
+constexpr int32_t kMaxChunks = 64;
+constexpr int32_t kChunkAlign = 128;          // chunk bounds, in keys (paged tiles stay inside one page)
+
+struct ShardSplits {
+  std::vector<ca_task> tasks;              // derived tasks, indices n ..
+  std::vector<ca_task_mask> masks;
+  struct Split {
+    int32_t task;                          // the shard's first task
+    int64_t stage_row0;
+    std::vector<int32_t> chunk_first, chunk_n;   // derived task runs
+  };
+  std::vector<Split> splits;
+  std::vector<int32_t> split_of;           // per task: index into splits, or -1
+  int64_t stage_rows = 0;
+  int32_t max_q_len = 0;
+};
+
+ShardSplits plan_shard_splits(const ca_task* t, const ca_task_mask* m, int32_t n, const std::vector<int32_t>& shard,
+                              int rt, const std::vector<bool>& tiled) {
+  ShardSplits S;
+  S.split_of.assign((size_t)n, -1);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (shard[(size_t)i] > 0 && tiled[(size_t)i]) total += shard_range_pairs(t, m, i, shard[(size_t)i], 0, t[i].q_len - 1);
+  const int64_t w_max = std::max<int64_t>(kMinSplitPairs, total / kSplitPairsDiv);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t n_seg = shard[(size_t)i];
+    if (n_seg == 0 || !tiled[(size_t)i]) continue;
+    bool windowed = false;
+    for (int32_t k = i; k < i + n_seg; ++k) windowed |= task_window(m, k) > 0;
+    if (windowed) continue;
+    const ca_task& q = t[i];
+    // the costliest row tile: the last, or the one before it when the last is
+    // short; a tile's 32-row blocks run whole, so its rows count padded
+    const int64_t last = (int64_t)(q.q_len - 1) / rt * rt;
+    int64_t w = 0;
+    for (int64_t r0 = last; r0 >= 0 && r0 >= last - rt; r0 -= rt) {
+      const int64_t r1 = std::min<int64_t>(r0 + rt, q.q_len) - 1, rows = r1 - r0 + 1;
+      w = std::max(w, shard_range_pairs(t, m, i, n_seg, r0, r1) / rows * ((rows + 31) / 32 * 32));
+    }
+    if (w <= w_max) continue;
+    // keys the shard's last row sees, context by context
+    std::vector<int64_t> nvis((size_t)n_seg);
+    int64_t keys = 0;
+    for (int32_t k = 0; k < n_seg; ++k) {
+      const ca_task& x = t[i + k];
+      nvis[(size_t)k] = std::min<int64_t>(x.kv_len, std::max<int64_t>(0, x.q_pos0 + x.q_len - x.kv_pos0));
+      keys += nvis[(size_t)k];
+    }
+    int64_t chunks = std::min<int64_t>(kMaxChunks, (w + w_max - 1) / w_max);
+    chunks = std::min<int64_t>(chunks, keys / (2 * kChunkAlign));
+    if (chunks < 2) continue;
+    const int64_t step = ((keys + chunks - 1) / chunks + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    ShardSplits::Split sp;
+    sp.task = i;
+    // walk the contexts, cutting at multiples of `step` keys from each
+    // context's start (so every cut lies on a kChunkAlign boundary)
+    int64_t in_chunk = 0;
+    sp.chunk_first.push_back(n + (int32_t)S.tasks.size());
+    sp.chunk_n.push_back(0);
+    for (int32_t k = 0; k < n_seg; ++k) {
+      const ca_task& x = t[i + k];
+      for (int64_t a = 0; a < nvis[(size_t)k];) {
+        if (in_chunk == step) {
+          sp.chunk_first.push_back(n + (int32_t)S.tasks.size());
+          sp.chunk_n.push_back(0);
+          in_chunk = 0;
+        }
+        const int64_t b = std::min<int64_t>(nvis[(size_t)k], a + (step - in_chunk));
+        ca_task d = x;
+        d.kv_off = x.kv_off + a;
+        d.kv_len = (int32_t)(b - a);
+        d.kv_pos0 = x.kv_pos0 + a;
+        S.tasks.push_back(d);
+        S.masks.push_back(ca_task_mask{0, 0});
+        ++sp.chunk_n.back();
+        in_chunk += b - a;
+        a = b;
+      }
+    }
+    if (sp.chunk_first.size() < 2) {       // nothing to split after all
+      S.tasks.resize((size_t)(sp.chunk_first[0] - n));
+      S.masks.resize(S.tasks.size());
+      continue;
+    }
+    sp.stage_row0 = S.stage_rows;
+    S.stage_rows += (int64_t)q.q_len * (int64_t)sp.chunk_first.size();
+    S.max_q_len = std::max(S.max_q_len, q.q_len);
+    S.split_of[(size_t)i] = (int32_t)S.splits.size();
+    S.splits.push_back(std::move(sp));
+  }
+  return S;
+}
+
 struct FwdPlan {
   int hpw = 1, rt = 128, group = 1;
   std::vector<int32_t> shard;   // query_shards()
-  int multi = 0;               // some shard has several contexts
+  ShardSplits splits;
+  int multi = 0;               // some shard has several contexts or is split
   size_t n_items = 0;        // tiled-kernel items
   size_t n_dec_items = 0;    // decode items
   size_t n_split = 0;        // decode (task, kv head) pairs cut into > 1 chunk
   size_t n_parts = 0;        // staging slots for those chunks
   int64_t dec_chunk = 0;
-  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_items = 0, off_dec = 0, off_split = 0, off_part_o = 0,
-         off_part_l = 0, bytes = 0;
+  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_items = 0, off_dec = 0, off_split = 0, off_merge = 0,
+         off_part_o = 0, off_part_l = 0, off_stage_o = 0, off_stage_l = 0, bytes = 0;
 };
 
 FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
@@ -392,8 +496,18 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m,
       dec_keys += decode_visible(t[i]) * s->hkv;
       continue;
     }
+  }
+  std::vector<bool> tiled((size_t)n, false);
+  for (int32_t i = 0; i < n; ++i)
+    tiled[(size_t)i] = t[i].q_len > 0 && p.shard[(size_t)i] > 0 && !is_decode_shard(t, m, p.shard, i, p.group);
+  p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, tiled);
+  if (!p.splits.splits.empty()) p.multi = 1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!tiled[(size_t)i]) continue;
+    const int32_t sp = p.splits.split_of[(size_t)i];
+    const size_t chunks = sp >= 0 ? p.splits.splits[(size_t)sp].chunk_first.size() : 1;
     const size_t tiles = (t[i].q_len + p.rt - 1) / p.rt;
-    p.n_items += tiles * (size_t)s->hkv * (size_t)(p.group / p.hpw);
+    p.n_items += tiles * (size_t)s->hkv * (size_t)(p.group / p.hpw) * chunks;
   }
   const int64_t per_item = (dec_keys + kDecTargetItems - 1) / kDecTargetItems;
   p.dec_chunk = std::max<int64_t>(kDecMinChunk, (per_item + 127) / 128 * 128);
@@ -407,16 +521,64 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m,
       p.n_parts += (size_t)chunks * s->hkv;
     }
   }
+  const size_t n_all = (size_t)n + p.splits.tasks.size();   // the table and the derived tasks
   p.off_tasks = 0;
-  p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
-  p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
+  p.off_masks = align_up(sizeof(ca_task) * n_all);
+  p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * n_all) : 0);
   p.off_items = p.off_pages + (pg ? align_up(sizeof(int32_t) * (size_t)pg->n_pages) : 0);
   p.off_dec = p.off_items + align_up(sizeof(ca::FwdItem) * p.n_items);
   p.off_split = p.off_dec + align_up(sizeof(ca::DecItem) * p.n_dec_items);
-  p.off_part_o = p.off_split + align_up(4 * sizeof(int32_t) * p.n_split);
+  p.off_merge = p.off_split + align_up(4 * sizeof(int32_t) * p.n_split);
+  p.off_part_o = p.off_merge + align_up(sizeof(ca::ShardMerge) * p.splits.splits.size());
   p.off_part_l = p.off_part_o + align_up(sizeof(float) * p.n_parts * p.group * s->d);
-  p.bytes = p.off_part_l + align_up(sizeof(float) * p.n_parts * p.group);
+  p.off_stage_o = p.off_part_l + align_up(sizeof(float) * p.n_parts * p.group);
+  p.off_stage_l = p.off_stage_o + align_up(sizeof(float) * (size_t)p.splits.stage_rows * s->hq * s->d);
+  p.bytes = p.off_stage_l + align_up(sizeof(float) * (size_t)p.splits.stage_rows * s->hq);
   return p;
+}
+
+// The tasks the kernels index: the table, then the derived tasks of split
+// shards (masks likewise when present).
+const ca_task& task_at(const ca_task* t, int32_t n, const ShardSplits& S, int32_t i) {
+  return i < n ? t[i] : S.tasks[(size_t)(i - n)];
+}
+
+// Items of one shard row tile for every head group: whole, or one per key
+// chunk when the shard is split.
+template <class Push>
+void shard_tile_items(const ca_task* t, const ca_task_mask* m, int32_t n, const ShardSplits& S, int32_t i,
+                      int32_t n_seg, int32_t r0, int64_t r1, int hkv, int head_subs, int hpw, Push push) {
+  const int32_t sp = S.split_of[(size_t)i];
+  if (sp < 0) {
+    const int64_t cost = shard_range_pairs(t, m, i, n_seg, r0, r1) * hpw + (r1 - r0 + 1) * 64;
+    for (int32_t g = 0; g < hkv; ++g)
+      for (int32_t hs = 0; hs < head_subs; ++hs) push(cost, ca::FwdItem{i, (int16_t)g, (int16_t)hs, r0, n_seg, -1});
+    return;
+  }
+  const ShardSplits::Split& spl = S.splits[(size_t)sp];
+  for (size_t c = 0; c < spl.chunk_first.size(); ++c) {
+    int64_t pairs = 0;
+    for (int32_t k = spl.chunk_first[c]; k < spl.chunk_first[c] + spl.chunk_n[c]; ++k) {
+      const ca_task& x = task_at(t, n, S, k);
+      pairs += range_pairs(r0, r1, x.q_pos0 - x.kv_pos0, x.kv_len);
+    }
+    const int64_t cost = pairs * hpw + (r1 - r0 + 1) * 64;
+    const int32_t stage_row = (int32_t)(spl.stage_row0 + (int64_t)c * t[i].q_len);
+    for (int32_t g = 0; g < hkv; ++g)
+      for (int32_t hs = 0; hs < head_subs; ++hs)
+        push(cost, ca::FwdItem{spl.chunk_first[c], (int16_t)g, (int16_t)hs, r0, spl.chunk_n[c], stage_row});
+  }
+}
+
+// Merge records of the split shards (o_off: output rows; for the dQ side the
+// caller passes q_off instead).
+std::vector<ca::ShardMerge> shard_merges(const ca_task* t, const ShardSplits& S, bool dq) {
+  std::vector<ca::ShardMerge> r;
+  for (const ShardSplits::Split& sp : S.splits) {
+    const ca_task& x = t[sp.task];
+    r.push_back({dq ? x.q_off : x.o_off, sp.stage_row0, x.q_len, (int32_t)sp.chunk_first.size()});
+  }
+  return r;
 }
 
 void build_forward_items(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
@@ -434,10 +596,8 @@ void build_forward_items(const ca_shape* s, const ca_task* t, const ca_task_mask
     for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
       const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
       // pairs of the tile (per head) plus a per-row epilogue term
-      const int64_t cost = shard_range_pairs(t, m, i, n_seg, r0, r1) * p.hpw + (r1 - r0 + 1) * 64;
-      for (int32_t g = 0; g < s->hkv; ++g)
-        for (int32_t hs = 0; hs < p.group / p.hpw; ++hs)
-          tmp.push_back({cost, {i, (int16_t)g, (int16_t)hs, r0, n_seg}});
+      shard_tile_items(t, m, n, p.splits, i, n_seg, r0, r1, s->hkv, p.group / p.hpw, p.hpw,
+                       [&](int64_t cost, const ca::FwdItem& it) { tmp.push_back({cost, it}); });
     }
   }
   // Longest first.  Items of equal cost (the KV heads of one query tile) stay
@@ -516,7 +676,18 @@ ca_status ca::build_forward_queue(const ca_shape* s, const ca_task* t, const ca_
   build_decode_items(s, t, m, n, p, ditems, split);
   host.assign(p.off_part_o, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
-  if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+  if (!p.splits.tasks.empty())
+    std::memcpy(host.data() + p.off_tasks + sizeof(ca_task) * (size_t)n, p.splits.tasks.data(),
+                sizeof(ca_task) * p.splits.tasks.size());
+  if (m) {
+    std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+    if (!p.splits.masks.empty())
+      std::memcpy(host.data() + p.off_masks + sizeof(ca_task_mask) * (size_t)n, p.splits.masks.data(),
+                  sizeof(ca_task_mask) * p.splits.masks.size());
+  }
+  const std::vector<ca::ShardMerge> merges = shard_merges(t, p.splits, false);
+  if (!merges.empty())
+    std::memcpy(host.data() + p.off_merge, merges.data(), sizeof(ca::ShardMerge) * merges.size());
   if (pg && pg->n_pages > 0)
     std::memcpy(host.data() + p.off_pages, pg->table_host, sizeof(int32_t) * (size_t)pg->n_pages);
   if (!items.empty()) std::memcpy(host.data() + p.off_items, items.data(), sizeof(ca::FwdItem) * items.size());
@@ -540,6 +711,11 @@ ca_status ca::build_forward_queue(const ca_shape* s, const ca_task* t, const ca_
   pf.off_split = p.off_split;
   pf.off_part_o = p.off_part_o;
   pf.off_part_l = p.off_part_l;
+  pf.off_merge = p.off_merge;
+  pf.off_stage_o = p.off_stage_o;
+  pf.off_stage_l = p.off_stage_l;
+  pf.n_merge = (int32_t)p.splits.splits.size();
+  pf.max_q_len = p.splits.max_q_len;
   *bytes_needed = p.bytes;
   return CA_OK;
 }
@@ -606,8 +782,15 @@ ca_status ca::launch_prepared_forward(const PreparedFwd& pf, const void* Q, cons
     fp.scale_log2 = scale_log2;
     fp.out_f32 = out_f32;
     fp.multi = pf.multi;
+    fp.stage_O = (float*)(w + pf.off_stage_o);
+    fp.stage_LSE = (float*)(w + pf.off_stage_l);
     hipError_t e = ca::launch_forward(fp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
+    if (pf.n_merge > 0) {
+      e = ca::launch_shard_merge((const ca::ShardMerge*)(w + pf.off_merge), pf.n_merge, pf.max_q_len, fp.stage_O,
+                                 fp.stage_LSE, O, LSE, out_f32, s->hq, s->d, hs);
+      if (e != hipSuccess) return hip_fail(e, "split-shard merge launch");
+    }
   }
   if (pf.n_dec_items > 0) {
     ca::DecParams dp;
@@ -766,6 +949,14 @@ KvGroups kv_groups(const ca_task* t, int32_t n) {
   return g;
 }
 
+// One dK/dV work unit (per KV head): 128 keys of a context group, and the
+// query rows it sweeps; split units write partial slots.
+struct KvUnit {
+  int64_t cost;
+  int32_t group, key0, member0, n_members, row_lo, row_hi;
+  int32_t split;       // index of the split tile among the pass's reductions, or -1
+};
+
 struct BwdPlan {
   int group = 1, hpw = 1, rt = 128;
   int q_passes = 1, kv_passes = 1;
@@ -773,11 +964,102 @@ struct BwdPlan {
   KvGroups groups;
   std::vector<int> q_pass_of, kv_pass_of;        // per task (shard starts) / per context group
   bool q_full = false, kv_full = false;          // every row covered by some task
-  int multi = 0;                                 // a shard or a context group with several tasks
-  size_t n_qitems = 0, n_kvitems = 0;
-  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_members = 0, off_qitems = 0, off_kvitems = 0, off_d = 0,
-         off_dq = 0, off_dk = 0, off_dv = 0, bytes = 0;
+  int multi = 0;                                 // a shard or a context group with several tasks, or a split
+  ShardSplits splits;                            // dQ side: long shards split over key chunks
+  std::vector<KvUnit> units;                     // dK/dV work units (replicated per KV head)
+  std::vector<std::pair<int32_t, int32_t>> split_tiles;   // (group, key0) of every split tile
+  size_t n_slots = 0;                            // partial slots (per KV head included)
+  size_t n_qitems = 0, n_kvitems = 0, n_reduce = 0;
+  size_t off_tasks = 0, off_masks = 0, off_pages = 0, off_members = 0, off_qitems = 0, off_kvitems = 0,
+         off_reduce = 0, off_qmerge = 0, off_d = 0, off_dq = 0, off_dk = 0, off_dv = 0, off_slot_k = 0,
+         off_slot_v = 0, off_stage_dq = 0, bytes = 0;
 };
+
+// A tile's query rows above which its dK/dV work is split over several
+// items: 1/512 of the call's rows (a tail of at most about half the ideal
+// time on 256 compute units), at least kMinSplitRows rows per item.
+constexpr int64_t kMinSplitRows = 8192;
+constexpr int64_t kSplitDiv = 512;
+
+// Task-relative query rows [r_lo, r_end) of task i that see any key of the
+// 128-key tile at context row k0.
+std::pair<int64_t, int64_t> tile_rows(const ca_task* t, const ca_task_mask* m, int32_t i, int64_t k0) {
+  const ca_task& k = t[i];
+  const int64_t delta = k.q_pos0 - k.kv_pos0;
+  const int32_t win = task_window(m, i);
+  const int64_t sj = task_sink_keys(t, m, i);
+  // rows that see the tile: i >= k0 - delta, and (window, no sink key)
+  // i < last key - delta + win
+  const int64_t r_lo = std::min<int64_t>(k.q_len, std::max<int64_t>(0, k0 - delta));
+  int64_t r_end = k.q_len;
+  if (win > 0 && k0 >= sj) {
+    const int64_t last = std::min<int64_t>(k0 + kBwdKeyTile, k.kv_len) - 1;
+    r_end = std::min<int64_t>(k.q_len, std::max<int64_t>(r_lo, last - delta + win));
+  }
+  return {r_lo, r_end};
+}
+
+// dK/dV work units of every (context group, key tile), with long tiles split
+// over member ranges, or over 32-aligned row ranges of one member, into
+// items of about equal rows.
+void plan_kv_units(const ca_task* t, const ca_task_mask* m, BwdPlan& p) {
+  const KvGroups& G = p.groups;
+  struct Tile { int32_t group, key0; int64_t rows; };
+  std::vector<Tile> tiles;
+  std::vector<int64_t> member_rows;   // per tile, per member (flattened)
+  int64_t total = 0;
+  for (size_t gi = 0; gi < G.rep.size(); ++gi)
+    for (int32_t k0 = 0; k0 < G.rep[gi].kv_len; k0 += kBwdKeyTile) {
+      int64_t rows = 0;
+      for (int32_t q = G.first[gi]; q < G.first[gi] + G.count[gi]; ++q) {
+        const auto rr = tile_rows(t, m, G.members[(size_t)q], k0);
+        member_rows.push_back(rr.second - rr.first);
+        rows += rr.second - rr.first;
+      }
+      tiles.push_back({(int32_t)gi, k0, rows});
+      total += rows;
+    }
+  const int64_t max_rows = std::max<int64_t>(kMinSplitRows, total / kSplitDiv);
+  size_t mr = 0;
+  for (const Tile& tl : tiles) {
+    const int32_t first = G.first[(size_t)tl.group], count = G.count[(size_t)tl.group];
+    const int64_t* rows_of = member_rows.data() + mr;
+    mr += (size_t)count;
+    auto unit_cost = [&](int64_t rows) { return rows * p.group * kBwdKeyTile + 64 * kBwdKeyTile; };
+    if (tl.rows <= max_rows) {
+      p.units.push_back({unit_cost(tl.rows), tl.group, tl.key0, first, count, 0, INT32_MAX, -1});
+      continue;
+    }
+    const int32_t split = (int32_t)p.split_tiles.size();
+    p.split_tiles.push_back({tl.group, tl.key0});
+    const int64_t n_parts = (tl.rows + max_rows - 1) / max_rows;
+    const int64_t chunk = (tl.rows + n_parts - 1) / n_parts;
+    int32_t open0 = -1;                  // first member of the open unit
+    int64_t open_rows = 0;
+    auto close = [&](int32_t end) {
+      if (open0 >= 0) p.units.push_back({unit_cost(open_rows), tl.group, tl.key0, first + open0, end - open0, 0,
+                                         INT32_MAX, split});
+      open0 = -1;
+      open_rows = 0;
+    };
+    for (int32_t k = 0; k < count; ++k) {
+      const int64_t r = rows_of[k];
+      if (r > chunk) {
+        close(k);
+        const auto rm = tile_rows(t, m, G.members[(size_t)(first + k)], tl.key0);
+        const int64_t step = (chunk + 31) / 32 * 32;
+        for (int64_t a = rm.first / 32 * 32; a < rm.second; a += step)
+          p.units.push_back({unit_cost(std::min(rm.second, a + step) - std::max(a, rm.first)), tl.group, tl.key0,
+                             first + k, 1, (int32_t)a, (int32_t)std::min<int64_t>(rm.second, a + step), split});
+        continue;
+      }
+      if (open0 >= 0 && open_rows + r > chunk) close(k);
+      if (open0 < 0) open0 = k;
+      open_rows += r;
+    }
+    close(count);
+  }
+}
 
 BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n,
                       const ca_kv_pages* pg = nullptr) {
@@ -790,12 +1072,18 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
   const size_t n_groups = p.groups.rep.size();
   std::vector<std::pair<int64_t, int64_t>> qiv(n), kviv(n_groups);
   int64_t q_cover = 0, kv_cover = 0;
+  std::vector<bool> active_q((size_t)n, false);
+  for (int32_t i = 0; i < n; ++i) active_q[(size_t)i] = t[i].q_len > 0 && p.shard[(size_t)i] > 0;
+  p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, active_q);
+  if (!p.splits.splits.empty()) p.multi = 1;
   for (int32_t i = 0; i < n; ++i) {
-    const bool active = t[i].q_len > 0 && p.shard[(size_t)i] > 0;
+    const bool active = active_q[(size_t)i];
     qiv[i] = {t[i].q_off, active ? t[i].q_len : 0};
     if (active) {
       if (p.shard[(size_t)i] > 1) p.multi = 1;
-      p.n_qitems += (size_t)((t[i].q_len + p.rt - 1) / p.rt) * s->hkv * (p.group / p.hpw);
+      const int32_t sp = p.splits.split_of[(size_t)i];
+      const size_t chunks = sp >= 0 ? p.splits.splits[(size_t)sp].chunk_first.size() : 1;
+      p.n_qitems += (size_t)((t[i].q_len + p.rt - 1) / p.rt) * s->hkv * (p.group / p.hpw) * chunks;
       q_cover += t[i].q_len;
     }
   }
@@ -803,40 +1091,59 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
     const ca_task& x = p.groups.rep[g];
     kviv[g] = {x.kv_off, x.kv_len};
     if (p.groups.count[g] > 1) p.multi = 1;
-    p.n_kvitems += (size_t)((x.kv_len + kBwdKeyTile - 1) / kBwdKeyTile) * s->hkv;
     kv_cover += x.kv_len;
   }
+  plan_kv_units(t, m, p);
+  p.n_kvitems = p.units.size() * (size_t)s->hkv;
+  p.n_reduce = p.split_tiles.size() * (size_t)s->hkv;
+  for (const KvUnit& u : p.units)
+    if (u.split >= 0) ++p.n_slots;
+  p.n_slots *= (size_t)s->hkv;
+  if (!p.split_tiles.empty()) p.multi = 1;
   p.q_passes = partition_passes(qiv, p.q_pass_of);
   p.kv_passes = pg ? partition_page_passes(p.groups.rep.data(), (int32_t)n_groups, pg, s->kv_rows / pg->page_rows,
                                            p.kv_pass_of)
                    : partition_passes(kviv, p.kv_pass_of);
   p.q_full = p.q_passes == 1 && q_cover == s->q_rows;
   p.kv_full = !pg && p.kv_passes == 1 && kv_cover == s->kv_rows;   // paged: unread page rows stay zero
+  const size_t n_all = (size_t)n + p.splits.tasks.size();   // the table and the derived tasks
   p.off_tasks = 0;
-  p.off_masks = align_up(sizeof(ca_task) * (size_t)n);
-  p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * (size_t)n) : 0);
+  p.off_masks = align_up(sizeof(ca_task) * n_all);
+  p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * n_all) : 0);
   p.off_members = p.off_pages + (pg ? align_up(sizeof(int32_t) * (size_t)pg->n_pages) : 0);
   p.off_qitems = p.off_members + align_up(sizeof(int32_t) * p.groups.members.size());
   p.off_kvitems = p.off_qitems + align_up(sizeof(ca::FwdItem) * p.n_qitems);
-  p.off_d = p.off_kvitems + align_up(sizeof(ca::BwdItem) * p.n_kvitems);
+  p.off_reduce = p.off_kvitems + align_up(sizeof(ca::BwdItem) * p.n_kvitems);
+  p.off_qmerge = p.off_reduce + align_up(sizeof(ca::KvReduce) * p.n_reduce);
+  p.off_d = p.off_qmerge + align_up(sizeof(ca::ShardMerge) * p.splits.splits.size());
   p.off_dq = p.off_d + align_up(sizeof(float) * (size_t)s->o_rows * s->hq);
   const size_t dq_bytes = p.q_passes > 1 ? sizeof(float) * (size_t)s->q_rows * s->hq * s->d : 0;
   const size_t dkv_bytes = p.kv_passes > 1 ? sizeof(float) * (size_t)s->kv_rows * s->hkv * s->d : 0;
+  const size_t slot_bytes = sizeof(float) * p.n_slots * kBwdKeyTile * s->d;
   p.off_dk = p.off_dq + align_up(dq_bytes);
   p.off_dv = p.off_dk + align_up(dkv_bytes);
-  p.bytes = p.off_dv + align_up(dkv_bytes);
+  p.off_slot_k = p.off_dv + align_up(dkv_bytes);
+  p.off_slot_v = p.off_slot_k + align_up(slot_bytes);
+  p.off_stage_dq = p.off_slot_v + align_up(slot_bytes);
+  p.bytes = p.off_stage_dq + align_up(sizeof(float) * (size_t)p.splits.stage_rows * s->hq * s->d);
   return p;
 }
 
 // Items of every pass, pass-major, each pass longest first; pass_begin has
 // passes + 1 entries.
 void build_backward_items(const ca_shape* s, const ca_task* t, const ca_task_mask* m, int32_t n, const BwdPlan& p,
-                          std::vector<ca::FwdItem>& qitems, std::vector<size_t>& q_begin,
-                          std::vector<ca::BwdItem>& kvitems, std::vector<size_t>& kv_begin) {
+                          const ca_kv_pages* pg, std::vector<ca::FwdItem>& qitems, std::vector<size_t>& q_begin,
+                          std::vector<ca::BwdItem>& kvitems, std::vector<size_t>& kv_begin,
+                          std::vector<ca::KvReduce>& reduces, std::vector<size_t>& reduce_begin,
+                          std::vector<ca::ShardMerge>& qmerges, std::vector<size_t>& qmerge_begin) {
   qitems.clear();
   kvitems.clear();
+  reduces.clear();
+  qmerges.clear();
   q_begin.assign(1, 0);
   kv_begin.assign(1, 0);
+  reduce_begin.assign(1, 0);
+  qmerge_begin.assign(1, 0);
   for (int pass = 0; pass < p.q_passes; ++pass) {
     struct K { int64_t c; ca::FwdItem it; };
     std::vector<K> tmp;
@@ -846,48 +1153,68 @@ void build_backward_items(const ca_shape* s, const ca_task* t, const ca_task_mas
       if (k.q_len <= 0 || n_seg == 0 || p.q_pass_of[i] != pass) continue;
       for (int32_t r0 = 0; r0 < k.q_len; r0 += p.rt) {
         const int64_t r1 = std::min<int64_t>(r0 + p.rt, k.q_len) - 1;
-        const int64_t cost = shard_range_pairs(t, m, i, n_seg, r0, r1) * p.hpw + (r1 - r0 + 1) * 64;
-        for (int32_t g = 0; g < s->hkv; ++g)
-          for (int32_t hs = 0; hs < p.group / p.hpw; ++hs)
-            tmp.push_back({cost, {i, (int16_t)g, (int16_t)hs, r0, n_seg}});
+        shard_tile_items(t, m, n, p.splits, i, n_seg, r0, r1, s->hkv, p.group / p.hpw, p.hpw,
+                         [&](int64_t cost, const ca::FwdItem& it) { tmp.push_back({cost, it}); });
       }
     }
     std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
     for (auto& k : tmp) qitems.push_back(k.it);
     q_begin.push_back(qitems.size());
+    for (size_t sp = 0; sp < p.splits.splits.size(); ++sp) {
+      const ShardSplits::Split& x = p.splits.splits[sp];
+      if (p.q_pass_of[(size_t)x.task] != pass) continue;
+      const ca_task& q = t[x.task];
+      qmerges.push_back({q.q_off, x.stage_row0, q.q_len, (int32_t)x.chunk_first.size()});
+    }
+    qmerge_begin.push_back(qmerges.size());
   }
+  // dK/dV items pass by pass, longest first; the slots of a split tile are
+  // numbered consecutively (per KV head), in unit order, and its reduction
+  // records follow the pass's items.
   const KvGroups& G = p.groups;
+  std::vector<int32_t> slot_of_unit(p.units.size(), -1);
+  std::vector<int32_t> split_slot0(p.split_tiles.size(), -1), split_n(p.split_tiles.size(), 0);
+  {
+    // slots grouped per (split tile, KV head): tile-major, then head, then unit
+    std::vector<std::vector<size_t>> units_of(p.split_tiles.size());
+    for (size_t u = 0; u < p.units.size(); ++u)
+      if (p.units[u].split >= 0) units_of[(size_t)p.units[u].split].push_back(u);
+    int32_t next = 0;
+    for (size_t sp = 0; sp < units_of.size(); ++sp) {
+      split_slot0[sp] = next;
+      split_n[sp] = (int32_t)units_of[sp].size();
+      for (size_t k = 0; k < units_of[sp].size(); ++k) slot_of_unit[units_of[sp][k]] = next + (int32_t)k;
+      next += split_n[sp] * s->hkv;
+    }
+  }
   for (int pass = 0; pass < p.kv_passes; ++pass) {
     struct K { int64_t c; ca::BwdItem it; };
     std::vector<K> tmp;
-    for (size_t gi = 0; gi < G.rep.size(); ++gi) {
-      if (p.kv_pass_of[gi] != pass) continue;
-      const int32_t kv_len = G.rep[gi].kv_len;
-      for (int32_t k0 = 0; k0 < kv_len; k0 += kBwdKeyTile) {
-        int64_t rows = 0;
-        for (int32_t q = G.first[gi]; q < G.first[gi] + G.count[gi]; ++q) {
-          const int32_t i = G.members[(size_t)q];
-          const ca_task& k = t[i];
-          const int64_t delta = k.q_pos0 - k.kv_pos0;
-          const int32_t win = task_window(m, i);
-          const int64_t sj = task_sink_keys(t, m, i);
-          // rows that see the block: i >= k0 - delta, and (window, no sink
-          // key) i < last key - delta + win
-          const int64_t r_lo = std::min<int64_t>(k.q_len, std::max<int64_t>(0, k0 - delta));
-          int64_t r_end = k.q_len;
-          if (win > 0 && k0 >= sj) {
-            const int64_t last = std::min<int64_t>(k0 + kBwdKeyTile, k.kv_len) - 1;
-            r_end = std::min<int64_t>(k.q_len, std::max<int64_t>(r_lo, last - delta + win));
-          }
-          rows += r_end - r_lo;
-        }
-        const int64_t cost = rows * p.group * kBwdKeyTile + 64 * kBwdKeyTile;
-        for (int32_t g = 0; g < s->hkv; ++g) tmp.push_back({cost, {G.first[gi], g, k0, G.count[gi]}});
+    for (size_t u = 0; u < p.units.size(); ++u) {
+      const KvUnit& un = p.units[u];
+      if (p.kv_pass_of[(size_t)un.group] != pass) continue;
+      for (int32_t g = 0; g < s->hkv; ++g) {
+        const int32_t slot = un.split >= 0 ? slot_of_unit[u] + g * split_n[(size_t)un.split] : -1;
+        tmp.push_back({un.cost, {un.member0, g, un.key0, un.n_members, un.row_lo, un.row_hi, slot, 0}});
       }
     }
     std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
     for (auto& k : tmp) kvitems.push_back(k.it);
     kv_begin.push_back(kvitems.size());
+    for (size_t sp = 0; sp < p.split_tiles.size(); ++sp) {
+      const int32_t gi = p.split_tiles[sp].first, k0 = p.split_tiles[sp].second;
+      if (p.kv_pass_of[(size_t)gi] != pass) continue;
+      const ca_task& x = G.rep[(size_t)gi];
+      int64_t row0 = x.kv_off + k0;
+      if (pg) {
+        const int64_t v = x.kv_off + k0;
+        row0 = (int64_t)pg->table_host[v / pg->page_rows] * pg->page_rows + v % pg->page_rows;
+      }
+      for (int32_t g = 0; g < s->hkv; ++g)
+        reduces.push_back({row0, split_slot0[sp] + g * split_n[sp], split_n[sp],
+                           std::min<int32_t>(kBwdKeyTile, x.kv_len - k0), g});
+    }
+    reduce_begin.push_back(reduces.size());
   }
 }
 
@@ -944,17 +1271,30 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
       return fail(CA_ERR_UNSUPPORTED, "task %d: context of %d rows exceeds 2 GiB per K/V", i, t[i].kv_len);
   std::vector<ca::FwdItem> qitems;
   std::vector<ca::BwdItem> kvitems;
-  std::vector<size_t> q_begin, kv_begin;
-  build_backward_items(s, t, m, n, p, qitems, q_begin, kvitems, kv_begin);
+  std::vector<size_t> q_begin, kv_begin, reduce_begin, qmerge_begin;
+  std::vector<ca::KvReduce> reduces;
+  std::vector<ca::ShardMerge> qmerges;
+  build_backward_items(s, t, m, n, p, pg, qitems, q_begin, kvitems, kv_begin, reduces, reduce_begin, qmerges,
+                       qmerge_begin);
   std::vector<char> host(p.off_d, 0);
   std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
-  if (m) std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+  if (!p.splits.tasks.empty())
+    std::memcpy(host.data() + p.off_tasks + sizeof(ca_task) * (size_t)n, p.splits.tasks.data(),
+                sizeof(ca_task) * p.splits.tasks.size());
+  if (m) {
+    std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
+    if (!p.splits.masks.empty())
+      std::memcpy(host.data() + p.off_masks + sizeof(ca_task_mask) * (size_t)n, p.splits.masks.data(),
+                  sizeof(ca_task_mask) * p.splits.masks.size());
+  }
+  if (!qmerges.empty()) std::memcpy(host.data() + p.off_qmerge, qmerges.data(), sizeof(ca::ShardMerge) * qmerges.size());
   if (pg && pg->n_pages > 0)
     std::memcpy(host.data() + p.off_pages, pg->table_host, sizeof(int32_t) * (size_t)pg->n_pages);
   if (!p.groups.members.empty())
     std::memcpy(host.data() + p.off_members, p.groups.members.data(), sizeof(int32_t) * p.groups.members.size());
   if (!qitems.empty()) std::memcpy(host.data() + p.off_qitems, qitems.data(), sizeof(ca::FwdItem) * qitems.size());
   if (!kvitems.empty()) std::memcpy(host.data() + p.off_kvitems, kvitems.data(), sizeof(ca::BwdItem) * kvitems.size());
+  if (!reduces.empty()) std::memcpy(host.data() + p.off_reduce, reduces.data(), sizeof(ca::KvReduce) * reduces.size());
   hipStream_t hs = (hipStream_t)stream;
   st = upload(ws, host, hs);
   if (st != CA_OK) return st;
@@ -995,6 +1335,9 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
   bp.masks = m ? (const ca_task_mask*)(w + p.off_masks) : nullptr;
   bp.members = (const int32_t*)(w + p.off_members);
   bp.multi = p.multi;
+  bp.slot_k = (float*)(w + p.off_slot_k);
+  bp.slot_v = (float*)(w + p.off_slot_v);
+  bp.stage_dQ = (float*)(w + p.off_stage_dq);
   bp.pages = pg ? (const int32_t*)(w + p.off_pages) : nullptr;
   bp.page_bytes = pg ? (uint32_t)(4 * pg->n_pages) : 0u;
   bp.page_shift = pg ? page_shift_of(pg) : 0;
@@ -1015,6 +1358,13 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
     pp.n_items = 0;
     e = ca::launch_bwd_q(pp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "dQ launch");
+    const size_t nm = qmerge_begin[pass + 1] - qmerge_begin[pass];
+    if (nm > 0) {
+      e = ca::launch_dq_reduce((const ca::ShardMerge*)(w + p.off_qmerge) + qmerge_begin[pass], (int32_t)nm,
+                               p.splits.max_q_len, bp.stage_dQ, (__bf16*)dQ, bp.dQacc, acc_q ? 1 : 0, s->hq, s->d,
+                               hs);
+      if (e != hipSuccess) return hip_fail(e, "split-shard dQ reduction launch");
+    }
   }
   for (int pass = 0; pass < p.kv_passes; ++pass) {
     ca::BwdParams pp = bp;
@@ -1025,6 +1375,13 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
     pp.n_qitems = 0;
     e = ca::launch_bwd_kv(pp, s->d, hs);
     if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+    const size_t nr = reduce_begin[pass + 1] - reduce_begin[pass];
+    if (nr > 0) {
+      e = ca::launch_kv_reduce((const ca::KvReduce*)(w + p.off_reduce) + reduce_begin[pass], (int32_t)nr, bp.slot_k,
+                               bp.slot_v, (__bf16*)dK, (__bf16*)dV, bp.dKacc, bp.dVacc, acc_kv ? 1 : 0, s->hkv, s->d,
+                               hs);
+      if (e != hipSuccess) return hip_fail(e, "dK/dV reduction launch");
+    }
   }
   if (acc_q) {
     e = ca::launch_f32_to_bf16(bp.dQacc, (__bf16*)dQ, q_elems, hs);

@@ -165,6 +165,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     r_lo = (int)clamp64((int64_t)it.key0 - delta, 0, t.q_len);
     r_end = (win > 0 && it.key0 >= sj) ? (int)clamp64((int64_t)it.key0 + wg_keys - 1 - delta + win, r_lo, t.q_len)
                                        : t.q_len;
+    if constexpr (MULTI) {
+      // a split item sweeps only its rows [row_lo, row_hi) (32-aligned)
+      r_lo = max(r_lo, it.row_lo);
+      r_end = min(r_end, it.row_hi);
+    }
     r_first = (r_lo / BQ) * BQ;
     n_rt = (r_end - r_first + BQ - 1) / BQ;
     n_steps = (wg_keys > 0 && r_end > r_lo) ? n_rt * G : 0;
@@ -518,6 +523,24 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 
   // Epilogue: lane = key l32, channels c*32 + 8 (j/4) + 4 hh + j%4.
   if (!key_ok) return;
+  if constexpr (MULTI) {
+    if (it.slot >= 0) {
+      // a split item: fp32 partials of its 128 keys, summed by kv_reduce_kernel
+      const int64_t sb = ((int64_t)it.slot * 128 + (my_key - it.key0)) * D;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ch = c * 32 + 8 * q4 + 4 * hh;
+          const f32x16& a = dk_acc[c];
+          const f32x16& b = dv_acc[c];
+          *(float4*)(p.slot_k + sb + ch) = make_float4(a[4 * q4] * p.scale, a[4 * q4 + 1] * p.scale,
+                                                       a[4 * q4 + 2] * p.scale, a[4 * q4 + 3] * p.scale);
+          *(float4*)(p.slot_v + sb + ch) = make_float4(b[4 * q4], b[4 * q4 + 1], b[4 * q4 + 2], b[4 * q4 + 3]);
+        }
+      return;
+    }
+  }
   const int64_t base = (kv_row0 + my_key) * kv_stride + it.kv_head * D;
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
@@ -918,6 +941,21 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   }
 
   if (!qvalid) return;
+  if constexpr (MULTI) {
+    if (it.stage_row >= 0) {
+      // a key chunk of a split shard: fp32 partial dQ to staging, summed by
+      // dq_reduce_kernel
+      float* sq = p.stage_dQ + ((int64_t)it.stage_row + qrow) * q_stride + head * D;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(float4*)(sq + c * 32 + 8 * q4 + 4 * hh) =
+              make_float4(dq_acc[c][4 * q4] * p.scale, dq_acc[c][4 * q4 + 1] * p.scale,
+                          dq_acc[c][4 * q4 + 2] * p.scale, dq_acc[c][4 * q4 + 3] * p.scale);
+      return;
+    }
+  }
   const int64_t base = (t.q_off + qrow) * q_stride + head * D;
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
@@ -939,6 +977,97 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
       }
     }
   }
+}
+
+// dK, dV of split (tile, KV head) pairs: the sum of their partial slots,
+// added in slot order (deterministic), written as bf16 or added into the
+// fp32 accumulators.  One thread per (record, key, 4 channels).
+template <int D>
+__global__ __launch_bounds__(256) void kv_reduce_kernel(const KvReduce* recs, int32_t n_recs, const float* slot_k,
+                                                        const float* slot_v, __bf16* dK, __bf16* dV, float* dKacc,
+                                                        float* dVacc, int accumulate, int hkv) {
+  constexpr int C4 = D / 4;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rec = g / (128 * C4);
+  if (rec >= n_recs) return;
+  const KvReduce r = recs[rec];
+  const int key = (int)((g / C4) % 128);
+  const int c4 = (int)(g % C4);
+  if (key >= r.n_keys) return;
+  float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+  for (int k = 0; k < r.n_slots; ++k) {
+    const int64_t o = ((int64_t)(r.slot0 + k) * 128 + key) * D + 4 * c4;
+    const float4 a = *(const float4*)(slot_k + o), b = *(const float4*)(slot_v + o);
+    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+    sv.x += b.x; sv.y += b.y; sv.z += b.z; sv.w += b.w;
+  }
+  const int64_t base = (r.row0 + key) * (int64_t)hkv * D + (int64_t)r.kv_head * D + 4 * c4;
+  if (accumulate) {
+    float4 ko = *(float4*)(dKacc + base), vo = *(float4*)(dVacc + base);
+    *(float4*)(dKacc + base) = make_float4(ko.x + sk.x, ko.y + sk.y, ko.z + sk.z, ko.w + sk.w);
+    *(float4*)(dVacc + base) = make_float4(vo.x + sv.x, vo.y + sv.y, vo.z + sv.z, vo.w + sv.w);
+  } else {
+    bf16x4 kb, vb;
+    kb[0] = (__bf16)sk.x; kb[1] = (__bf16)sk.y; kb[2] = (__bf16)sk.z; kb[3] = (__bf16)sk.w;
+    vb[0] = (__bf16)sv.x; vb[1] = (__bf16)sv.y; vb[2] = (__bf16)sv.z; vb[3] = (__bf16)sv.w;
+    *(bf16x4*)(dK + base) = kb;
+    *(bf16x4*)(dV + base) = vb;
+  }
+}
+
+// dQ of split shards: the sum of the key chunks' partials, in chunk order
+// (deterministic), written as bf16 or added into the fp32 accumulator.
+// blockIdx.y = shard; one thread per (row, head, 4 channels).
+template <int D>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const ShardMerge* recs, const float* stage_dQ, __bf16* dQ,
+                                                        float* dQacc, int accumulate, int hq) {
+  constexpr int C4 = D / 4;
+  const ShardMerge r = recs[blockIdx.y];
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)r.q_len * hq * C4) return;
+  const int64_t pair = g / C4;                  // (row, head) of the shard
+  const int c4 = (int)(g % C4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < r.n_chunks; ++k) {
+    const float4 v = *(const float4*)(stage_dQ + ((r.stage_row0 + (int64_t)k * r.q_len) * hq + pair) * D + 4 * c4);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  const int64_t at = (r.o_off * hq + pair) * D + 4 * c4;
+  if (accumulate) {
+    const float4 o = *(float4*)(dQacc + at);
+    *(float4*)(dQacc + at) = make_float4(o.x + acc.x, o.y + acc.y, o.z + acc.z, o.w + acc.w);
+  } else {
+    bf16x4 b;
+    b[0] = (__bf16)acc.x; b[1] = (__bf16)acc.y; b[2] = (__bf16)acc.z; b[3] = (__bf16)acc.w;
+    *(bf16x4*)(dQ + at) = b;
+  }
+}
+
+hipError_t launch_dq_reduce(const ShardMerge* recs, int32_t n_recs, int32_t max_q_len, const float* stage_dQ,
+                            __bf16* dQ, float* dQacc, int accumulate, int hq, int d, hipStream_t s) {
+  if (n_recs <= 0) return hipSuccess;
+  const int64_t threads = (int64_t)max_q_len * hq * (d / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_recs);
+  if (d == 128)
+    hipLaunchKernelGGL(dq_reduce_kernel<128>, grid, dim3(256), 0, s, recs, stage_dQ, dQ, dQacc, accumulate, hq);
+  else
+    hipLaunchKernelGGL(dq_reduce_kernel<64>, grid, dim3(256), 0, s, recs, stage_dQ, dQ, dQacc, accumulate, hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_reduce(const KvReduce* recs, int32_t n_recs, const float* slot_k, const float* slot_v,
+                            __bf16* dK, __bf16* dV, float* dKacc, float* dVacc, int accumulate, int hkv, int d,
+                            hipStream_t s) {
+  if (n_recs <= 0) return hipSuccess;
+  const int64_t threads = (int64_t)n_recs * 128 * (d / 4);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (d == 128)
+    hipLaunchKernelGGL(kv_reduce_kernel<128>, dim3(blocks), dim3(256), 0, s, recs, n_recs, slot_k, slot_v, dK, dV,
+                       dKacc, dVacc, accumulate, hkv);
+  else
+    hipLaunchKernelGGL(kv_reduce_kernel<64>, dim3(blocks), dim3(256), 0, s, recs, n_recs, slot_k, slot_v, dK, dV,
+                       dKacc, dVacc, accumulate, hkv);
+  return hipGetLastError();
 }
 
 __global__ void f32_to_bf16_kernel(const float* src, __bf16* dst, int64_t n) {

@@ -378,6 +378,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // Epilogue: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty rows: 0, -inf.
   if (!qvalid) return;
   const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+  if constexpr (MULTI) {
+    if (it.stage_row >= 0) {
+      // a key chunk of a split shard: fp32 partial O and LSE to staging,
+      // merged by Equation 4 afterwards
+      const int64_t srow = (int64_t)it.stage_row + qrow;
+      if (hh == 0)
+        p.stage_LSE[srow * p.hq + head] = lsum > 0.f ? (m2 + __log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
+      float* so = p.stage_O + srow * (int64_t)(p.hq * D) + head * D;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(float4*)(so + c * 32 + 8 * q4 + 4 * hh) =
+              make_float4(o_acc[c][4 * q4] * inv_l, o_acc[c][4 * q4 + 1] * inv_l, o_acc[c][4 * q4 + 2] * inv_l,
+                          o_acc[c][4 * q4 + 3] * inv_l);
+      return;
+    }
+  }
   const int64_t orow = t.o_off + qrow;
   if (hh == 0) {
     p.LSE[orow * p.hq + head] = lsum > 0.f ? (m2 + __log2f(lsum)) * 0.69314718055994530942f : -INFINITY;

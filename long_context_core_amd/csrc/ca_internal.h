@@ -20,6 +20,18 @@ struct FwdItem {
   int16_t head_sub;  // which group of hpw heads inside the KV head's group
   int32_t row0;      // first task-relative query row
   int32_t n_seg;     // contexts of the shard (consecutive tasks)
+  int32_t stage_row; // -1; or a key chunk of a split shard: its fp32 partial
+                     // output goes to staging row stage_row + query row
+};
+
+// A query shard split over key chunks: chunk c's partial outputs are staging
+// rows stage_row0 + c * q_len + (0 .. q_len - 1); the forward merges them by
+// Equation 4 into O / LSE rows o_off.., the dQ kernel's are summed into dQ
+// rows q_off...
+struct ShardMerge {
+  int64_t o_off;     // output rows (forward) / dQ rows (backward)
+  int64_t stage_row0;
+  int32_t q_len, n_chunks;
 };
 
 // Split-KV decode work item: one task (a single query row), one KV head, all
@@ -38,12 +50,25 @@ struct DecItem {
 // Backward work item (dK/dV kernel): 128 context rows of a context group
 // (tasks with the same context rows, listed at members[member0 ..
 // member0 + n_members)), one KV head; it sweeps the query rows of every
-// member.
+// member.  A tile whose query rows are too many for one item is split into
+// several items over member ranges (or, for one member, row ranges [row_lo,
+// row_hi)) that write fp32 partial dK / dV to a slot; a reduction sums the
+// slots in order.
 struct BwdItem {
   int32_t member0;
   int32_t kv_head;
   int32_t key0;      // first context-relative row of the tile
   int32_t n_members;
+  int32_t row_lo, row_hi;  // task-relative query rows swept (all: 0, INT32_MAX)
+  int32_t slot;            // -1: write dK / dV; else the partial slot
+  int32_t pad;
+};
+
+// Reduction of the partial slots of one split (tile, KV head): dK / dV of
+// rows row0 .. row0 + n_keys - 1 = sum of slots slot0 .. slot0 + n_slots - 1.
+struct KvReduce {
+  int64_t row0;      // physical K/V row of the tile's first key
+  int32_t slot0, n_slots, n_keys, kv_head;
 };
 
 struct FwdParams {
@@ -62,7 +87,9 @@ struct FwdParams {
   int32_t hq, hkv, group, hpw;
   float scale_log2;   // softmax scale * log2(e)
   int32_t out_f32;
-  int32_t multi;      // some item has n_seg > 1
+  int32_t multi;      // some item has n_seg > 1 or a staging row
+  float* stage_O;     // [stage rows][hq][d] fp32 partials of split shards
+  float* stage_LSE;   // [stage rows][hq]
 };
 
 struct DecParams {
@@ -131,6 +158,9 @@ struct BwdParams {
   int32_t page_shift;
   const BwdItem* items;   // dK/dV kernel
   int32_t n_items;
+  float* slot_k;          // [slots][128][d] fp32 partial dK of split items (scaled), and dV
+  float* slot_v;
+  float* stage_dQ;        // [stage rows][hq][d] fp32 partial dQ of split shards (scaled)
   const FwdItem* qitems;  // dQ kernel
   int32_t n_qitems;
   int32_t hq, hkv, group, hpw;
@@ -152,8 +182,11 @@ struct PreparedFwd {
   int32_t n_items, n_dec_items, n_split;
   int32_t has_masks, has_pages, page_shift;
   uint32_t page_bytes;
-  int32_t multi;            // some query shard has several contexts
-  uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_part_o, off_part_l;
+  int32_t multi;            // some query shard has several contexts or is split
+  int32_t n_merge;          // split shards
+  int32_t max_q_len;        // longest split shard
+  uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_merge, off_part_o, off_part_l,
+      off_stage_o, off_stage_l;
 };
 
 // Validates a forward call (tensors: Q, K, V, O, LSE, or nullptr to skip the
@@ -179,6 +212,13 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_prep(const __bf16* O, const __bf16* dO, float* Dv, int64_t n_pairs, int d, hipStream_t s);
 hipError_t launch_bwd_kv(const BwdParams& p, int d, hipStream_t s);
 hipError_t launch_bwd_q(const BwdParams& p, int d, hipStream_t s);
+hipError_t launch_shard_merge(const ShardMerge* recs, int32_t n_recs, int32_t max_q_len, const float* stage_O,
+                              const float* stage_LSE, void* O, float* LSE, int out_f32, int hq, int d, hipStream_t s);
+hipError_t launch_dq_reduce(const ShardMerge* recs, int32_t n_recs, int32_t max_q_len, const float* stage_dQ,
+                            __bf16* dQ, float* dQacc, int accumulate, int hq, int d, hipStream_t s);
+hipError_t launch_kv_reduce(const KvReduce* recs, int32_t n_recs, const float* slot_k, const float* slot_v,
+                            __bf16* dK, __bf16* dV, float* dKacc, float* dVacc, int accumulate, int hkv, int d,
+                            hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, __bf16* dst, int64_t n, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_zero_bf16(__bf16* p, int64_t n, hipStream_t s);

@@ -39,6 +39,40 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Split query shards: the key chunks' partials of every (row, head) merged
+// by Equation 4 into the shard's output rows.  blockIdx.y = shard; D / 8
+// lanes per (row, head) as in merge_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void shard_merge_kernel(const ShardMerge* recs, const float* stage_O,
+                                                          const float* stage_LSE, void* O, float* LSE, int out_f32,
+                                                          int hq) {
+  constexpr int LPP = D / (4 * kMergeVec);
+  const ShardMerge r = recs[blockIdx.y];
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPP;   // (row, head) of the shard
+  const int sub = threadIdx.x % LPP;
+  if (pair >= (int64_t)r.q_len * hq) return;
+  const int64_t sp = r.stage_row0 * hq + pair;                            // chunk 0's (row, head)
+  const int64_t stride = (int64_t)r.q_len * hq;                           // chunk to chunk
+  float4 o[kMergeVec];
+  const float lse = merge_lse_parts<D, kMergeVec>(stage_LSE + sp, stride, stage_O + sp * D + sub * 4, stride * D,
+                                                  r.n_chunks, o);
+  const int64_t op = r.o_off * hq + pair;
+  store_row_part<D, kMergeVec>(O, op * D + sub * 4, out_f32 != 0, o);
+  if (sub == 0) LSE[op] = lse;
+}
+
+hipError_t launch_shard_merge(const ShardMerge* recs, int32_t n_recs, int32_t max_q_len, const float* stage_O,
+                              const float* stage_LSE, void* O, float* LSE, int out_f32, int hq, int d, hipStream_t s) {
+  if (n_recs <= 0) return hipSuccess;
+  const int64_t threads = (int64_t)max_q_len * hq * (d / (4 * kMergeVec));
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_recs);
+  if (d == 128)
+    hipLaunchKernelGGL(shard_merge_kernel<128>, grid, dim3(256), 0, s, recs, stage_O, stage_LSE, O, LSE, out_f32, hq);
+  else
+    hipLaunchKernelGGL(shard_merge_kernel<64>, grid, dim3(256), 0, s, recs, stage_O, stage_LSE, O, LSE, out_f32, hq);
+  return hipGetLastError();
+}
+
 __global__ void zero_f32_kernel(float* p, int64_t n) {
   const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i4 + 3 < n) {

@@ -17,6 +17,12 @@ hipError_t launch_bwd_q(const BwdParams&, int, hipStream_t) { return hipSuccess;
 hipError_t launch_f32_to_bf16(const float*, __bf16*, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_zero_f32(float*, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_zero_bf16(__bf16*, int64_t, hipStream_t) { return hipSuccess; }
+hipError_t launch_shard_merge(const ShardMerge*, int32_t, int32_t, const float*, const float*, void*, float*, int, int,
+                              int, hipStream_t) { return hipSuccess; }
+hipError_t launch_dq_reduce(const ShardMerge*, int32_t, int32_t, const float*, __bf16*, float*, int, int, int,
+                            hipStream_t) { return hipSuccess; }
+hipError_t launch_kv_reduce(const KvReduce*, int32_t, const float*, const float*, __bf16*, __bf16*, float*, float*, int,
+                            int, int, hipStream_t) { return hipSuccess; }
 }
 int main() {
   std::mt19937_64 rng(11);

@@ -189,3 +189,108 @@ def test_backward_train_prolong_like_64th_scale_full_oracle():
     announce("backward prolong-like 1/64 scale vs oracle")
     w = I.train_8b_prolong_512k(div=64)
     run_small(w.tasks, w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, 990, "bwd-prolong-1/64")
+
+
+# --------------------------------------------------------------------------
+# dK/dV tiles with more query rows than one work item should sweep: split
+# into items over member or row ranges whose fp32 partial slots are summed
+# --------------------------------------------------------------------------
+
+def test_backward_split_tiles_vs_oracle():
+    """A 9,000-token causal document (its first key tiles are seen by more
+    than 8,192 rows: split by row ranges) and a shared question read by 30
+    answers of 300 rows (split by member ranges), element by element against
+    the oracle."""
+    announce("backward split dK/dV tiles (row and member splits) vs oracle")
+    docs = I.varlen_tasks([9000, 300])
+    sq = I.shared_question_shards(200, [300] * 30)
+    sq[:, [0, 1, 2]] += 9300
+    tasks = np.concatenate([docs, sq])
+    T = 9300 + 200 + 9000
+    run_small(tasks, 2, 1, 64, T, T, T, 1010, "bwd-split-tiles")
+
+
+def test_backward_split_tiles_probe():
+    """Probe closed forms (K = 0, V = (-1)^position: dQ = 0 exactly, dV and
+    dK by in-document suffix sums) for documents whose early key tiles are
+    split over many row ranges, Llama-3-8B heads."""
+    announce("backward split dK/dV tiles: probe closed forms, 40K + 20K + 5K docs")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    lens = [40000, 20000, 5000, 77]
+    w = I.Workload("split-probe", 32, 8, 128, I.varlen_tasks(lens), sum(lens), sum(lens), sum(lens), doc_lens=lens)
+    T, hq, hkv, d, G = w.q_rows, w.hq, w.hkv, w.d, w.hq // w.hkv
+    shape = ca.make_shape(hq, hkv, d, T, T, T)
+    pos, end = doc_layout(w)
+    end_t = torch.from_numpy(end).to(dev)
+    Q = I.randn_bf16((T, hq, d), 1015, device=dev)
+    dO = I.randn_bf16((T, hq, d), 1018, device=dev)
+    K = torch.zeros((T, hkv, d), dtype=torch.bfloat16, device=dev)
+    pos_t = torch.from_numpy(pos).to(dev)
+    sign = torch.where(pos_t % 2 == 0, 1.0, -1.0).double()
+    V = sign.float()[:, None, None].expand(T, hkv, d).to(torch.bfloat16).contiguous()
+    O = torch.empty_like(Q)
+    LSE = torch.empty((T, hq), device=dev)
+    ca.forward(shape, w.tasks, Q, K, V, O, LSE)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    ca.backward(shape, w.tasks, Q, K, V, O, dO, LSE, dQ, dK, dV)
+    torch.cuda.synchronize()
+    assert float(dQ.float().abs().max()) == 0.0
+    inv = 1.0 / (pos_t.double() + 1.0)
+    o_i = torch.where(pos_t % 2 == 0, inv, torch.zeros_like(inv))
+    dOd = dO.double()
+    dv_ref = suffix_in_doc(torch, (dOd * inv[:, None, None]).view(T, hkv, G, d).sum(2), end_t)
+    e_dv = float(torch.linalg.norm(dV.double() - dv_ref) / torch.linalg.norm(dv_ref))
+    a = dOd.sum(2)
+    Qd = Q.double()
+    A = suffix_in_doc(torch, (a * inv[:, None])[:, :, None].mul(Qd).view(T, hkv, G, d).sum(2), end_t)
+    B = suffix_in_doc(torch, (a * inv[:, None] * o_i[:, None])[:, :, None].mul(Qd).view(T, hkv, G, d).sum(2), end_t)
+    dk_ref = (1.0 / math.sqrt(d)) * (sign[:, None, None] * A - B)
+    e_dk = float(torch.linalg.norm(dK.double() - dk_ref) / torch.linalg.norm(dk_ref))
+    # the split tiles themselves: the first 256 keys of the 40K document
+    e_dk0 = float(torch.linalg.norm(dK[:256].double() - dk_ref[:256]) / torch.linalg.norm(dk_ref[:256]))
+    e_dv0 = float(torch.linalg.norm(dV[:256].double() - dv_ref[:256]) / torch.linalg.norm(dv_ref[:256]))
+    print("split probe: relF(dV)=%.3e relF(dK)=%.3e, first 256 keys: relF(dV)=%.3e relF(dK)=%.3e"
+          % (e_dv, e_dk, e_dv0, e_dk0), flush=True)
+    assert max(e_dv, e_dk, e_dv0, e_dk0) <= GRAD_REL_FRO
+
+
+# --------------------------------------------------------------------------
+# query shards whose items would sweep very long contexts: split over key
+# chunks (fp32 partials merged by Equation 4 in the forward, summed for dQ)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (4, 1, 64)])
+def test_split_long_shards_forward_and_backward_vs_oracle(hq, hkv, d):
+    """A 64-row shard at the end of a 70,000-token context, a 32-row shard
+    over three contexts (two 30,000-key prefixes, all visible, and its own
+    rows, causal) and a short document: the long shards' items are split
+    over key chunks.  O, LSE and dQ, dK, dV element by element against the
+    oracle."""
+    announce("split long shards (forward merge, dQ sum) hq%d hkv%d d%d" % (hq, hkv, d))
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    tasks = np.array([(0, 0, 0, 64, 70000, 69936, 0),                 # shard A
+                      (64, 70000, 64, 32, 30000, 80000, 0),           # shard B: prefix 1
+                      (64, 100000, 64, 32, 30000, 80000, 30000),      #          prefix 2
+                      (64, 130000, 64, 32, 32, 80000, 80000),         #          own rows, causal
+                      (96, 130032, 96, 300, 300, 0, 0)], dtype=np.int64)
+    q_rows, kv_rows = 396, 130332
+    shape = ca.make_shape(hq, hkv, d, q_rows, kv_rows, q_rows)
+    assert ca.forward_workspace(shape, tasks) > ca.forward_workspace(shape, tasks[4:]) + 64 * hq * d * 4
+    Q = I.randn_bf16((q_rows, hq, d), 1031)
+    K = I.randn_bf16((kv_rows, hkv, d), 1032)
+    V = I.randn_bf16((kv_rows, hkv, d), 1033)
+    dO = I.randn_bf16((q_rows, hq, d), 1034)
+    Qd, Kd, Vd, dOd = Q.to(dev), K.to(dev), V.to(dev), dO.to(dev)
+    O = torch.full((q_rows, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((q_rows, hq), float("nan"), device=dev)
+    ca.forward(shape, tasks, Qd, Kd, Vd, O, LSE)
+    dQ, dK, dV = torch.empty_like(Qd), torch.empty_like(Kd), torch.empty_like(Vd)
+    ca.backward(shape, tasks, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV)
+    torch.cuda.synchronize()
+    Qw, Kw, Vw, dOw = widen(Q), widen(K), widen(V), widen(dO)
+    O_ref, LSE_ref = oracle.forward(tasks, Qw, Kw, Vw, 1 / math.sqrt(d))
+    from tests.gpu_util import check_forward
+    check_forward(O, LSE, O_ref, LSE_ref, "split shards fwd")
+    check_grads((dQ, dK, dV), oracle.backward(tasks, Qw, Kw, Vw, dOw, 1 / math.sqrt(d)), "split shards bwd")
