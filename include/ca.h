@@ -117,7 +117,16 @@ typedef struct {
 } ca_task_mask;
 
 enum {
-  CA_OUT_F32 = 1u << 0 /* forward/merge: write O as fp32 (partials for a later merge) */
+  CA_OUT_F32 = 1u << 0, /* forward/merge: write O as fp32 (partials for a later merge) */
+  /* Forward launch of the tiled kernel (at most one of the two; results are
+   * bit-identical either way).  By default the library picks: persistent
+   * (one workgroup per compute unit, each claiming items from the
+   * longest-first queue of its XCD and loading the next item's Q and first
+   * K/V tiles under the current item's epilogue) when the call has at least
+   * 32,768 work items, else one workgroup per item, dispatched by the
+   * hardware. */
+  CA_LAUNCH_PERSISTENT = 1u << 1,
+  CA_LAUNCH_PER_ITEM = 1u << 2
 };
 
 typedef struct {
@@ -125,7 +134,7 @@ typedef struct {
   int32_t hkv;     /* key/value heads, >= 1, divides hq                    */
   int32_t d;       /* head dimension: 64 or 128                            */
   float scale;     /* softmax scale applied to q.k, > 0 (usually 1/sqrt(d)) */
-  uint32_t flags;  /* CA_OUT_F32                                           */
+  uint32_t flags;  /* CA_OUT_F32, CA_LAUNCH_* (forward only)               */
   int64_t q_rows;  /* rows of Q (and dQ)                                   */
   int64_t kv_rows; /* rows of K, V (and dK, dV)                            */
   int64_t o_rows;  /* rows of O and LSE (and dO)                           */

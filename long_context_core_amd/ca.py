@@ -21,6 +21,9 @@ CA_ERR_UNSUPPORTED = -2
 CA_ERR_WORKSPACE = -3
 CA_ERR_HIP = -4
 CA_OUT_F32 = 1
+CA_LAUNCH_PERSISTENT = 2
+CA_LAUNCH_PER_ITEM = 4
+_LAUNCH = {None: 0, "persistent": CA_LAUNCH_PERSISTENT, "per_item": CA_LAUNCH_PER_ITEM}
 
 EXPORTS = (
     "ca_forward_workspace",
@@ -240,11 +243,13 @@ def task_array(tasks):
     return a
 
 
-def make_shape(hq, hkv, d, q_rows, kv_rows, o_rows, scale=None, out_f32=False):
+def make_shape(hq, hkv, d, q_rows, kv_rows, o_rows, scale=None, out_f32=False, launch=None):
+    """launch: None (the library picks), "persistent" or "per_item": how the
+    forward's tiled kernel is launched (results are bit-identical)."""
     s = Shape()
     s.hq, s.hkv, s.d = int(hq), int(hkv), int(d)
     s.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
-    s.flags = CA_OUT_F32 if out_f32 else 0
+    s.flags = (CA_OUT_F32 if out_f32 else 0) | _LAUNCH[launch]
     s.q_rows, s.kv_rows, s.o_rows = int(q_rows), int(kv_rows), int(o_rows)
     return s
 
@@ -398,8 +403,7 @@ def forward_prepare(shape, tasks, ws, stream=None, masks=None, pages=None):
     _check(lib().ca_forward_prepare(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
                                     ctypes.byref(pages) if pages is not None else None, _ptr(ws), _ws_bytes(ws),
                                     _stream_ptr(stream), ctypes.byref(plan)))
-    plan._shape = make_shape(shape.hq, shape.hkv, shape.d, shape.q_rows, shape.kv_rows, shape.o_rows,
-                             scale=shape.scale, out_f32=bool(shape.flags & CA_OUT_F32))
+    plan._shape = Shape.from_buffer_copy(shape)
     plan._ws = ws     # the queue lives there: keep it alive with the plan
     return plan
 

@@ -54,7 +54,7 @@ namespace ca {
 // regardless of when the reference moved.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int NW, bool PAGED, bool MULTI>
+template <int D, int NW, bool PAGED, bool MULTI, bool PERSIST>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   constexpr int NT = 64 * NW;     // threads
   constexpr int BN = 64;          // keys per tile
@@ -69,11 +69,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KS];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][BN * VS];
 
-  const FwdItem it = p.items[blockIdx.x];
+  // PERSIST: n_slots resident workgroups (a multiple of 8).  Workgroups are
+  // dealt to the 8 XCDs in turn, so workgroup b runs on XCD x = b % 8; it
+  // starts with item b and then claims, from XCD x's counter, the next
+  // unclaimed item of x's share of the longest-first queue (items x, x + 8,
+  // x + 16, ...: the share the one-item-per-workgroup launch also gives x,
+  // which keeps each XCD's L2 on its own KV heads).  The claim for the next
+  // item is taken when an item starts (its latency hides under the item), and
+  // the claimed item's loads are issued before this item's epilogue.
+  // Otherwise item b alone.  lds_next[parity]: the claimed item, written by
+  // thread 0 and read by every wave after the item's last barrier.
+  __shared__ int32_t lds_next[2];
+  int parity = 0;
+  const int tid = threadIdx.x;
+  const int xcd = blockIdx.x & 7;
+  uint32_t claim = 0;
+  auto claimed_item = [&]() { return (int32_t)(xcd + 8 * (claim + (uint32_t)(p.n_slots >> 3))); };
+  if constexpr (PERSIST) {
+    if (tid == 0) claim = atomicAdd(p.counter + xcd, 1u);
+  }
+  FwdItem it = p.items[blockIdx.x];
   // The item's query shard: tasks it.task .. it.task + n_seg - 1 share the
   // query rows; t is the context being swept (the only one unless MULTI).
   ca_task t = p.tasks[it.task];
-  const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
@@ -82,11 +100,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   const int hpw = p.hpw;
   // wave-uniform values, kept in scalar registers
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
-  const int wrow0 = it.row0 + (wave_u / hpw) * 32;
   const int rt = 32 * (NW / hpw);
-  const int wg_last = min(it.row0 + rt, t.q_len) - 1;
-  const int w_last = min(wrow0 + 32, t.q_len) - 1;
+  int head, wrow0, wg_last, w_last;
+  auto item_rows = [&]() __attribute__((always_inline)) {
+    head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
+    wrow0 = it.row0 + (wave_u / hpw) * 32;
+    wg_last = min(it.row0 + rt, t.q_len) - 1;
+    w_last = min(wrow0 + 32, t.q_len) - 1;
+  };
+  item_rows();
 
   // Per context: the key range of the workgroup and of this wave; tiles
   // [0, w_full) are visible to every row of the wave (no mask).  Sink +
@@ -105,8 +127,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     win = 0;
     sj = 0;
     if (p.masks) {
-      win = p.masks[task_idx].window;
-      if (win > 0) sj = (int)clamp64((int64_t)p.masks[task_idx].sink - t.kv_pos0, 0, kv_len);
+      if constexpr (PERSIST) {
+        const ca_task_mask mk = wave_uniform(p.masks[task_idx]);
+        win = mk.window;
+        if (win > 0) sj = (int)clamp64((int64_t)mk.sink - t.kv_pos0, 0, kv_len);
+      } else {
+        win = p.masks[task_idx].window;
+        if (win > 0) sj = (int)clamp64((int64_t)p.masks[task_idx].sink - t.kv_pos0, 0, kv_len);
+      }
     }
     w_lo_first = (int64_t)wrow0 + delta - win + 1;
     w_lo_last = (int64_t)w_last + delta - win + 1;
@@ -114,14 +142,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   context(it.task);
 
   // Q^T operand: this lane's query row, channels 16 s + 8 hh .. + 7.
-  const int qrow = wrow0 + l32;
-  const bool qvalid = qrow < t.q_len;
+  int qrow;
+  bool qvalid;
   bf16x8 qf[NKS];
-  {
+  auto load_q = [&]() __attribute__((always_inline)) {
+    qrow = wrow0 + l32;
+    qvalid = qrow < t.q_len;
     const __bf16* qp = p.Q + (t.q_off + qrow) * (int64_t)(p.hq * D) + head * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) qf[s] = qvalid ? *(const bf16x8*)(qp + 16 * s) : bf16x8_zero();
-  }
+  };
+  load_q();
 
   f32x16 o_acc[NCB];
 #pragma unroll
@@ -154,7 +185,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   };
   const int64_t kv_stride = (int64_t)p.hkv * D;
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
-  const __bf16* kbase = p.K + it.kv_head * D;
+  const __bf16* kbase = p.K + it.kv_head * D;   // the item's KV head (PERSIST: reset per item)
   const __bf16* vbase = p.V + it.kv_head * D;
   const int ld_row = tid / CH;
   const int ld_chunk = tid % CH;
@@ -330,11 +361,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
   // in step k - 1, before the barrier of step k.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto sweep = [&]() __attribute__((always_inline)) {
+  // A context's sweep in two parts: sweep_issue() starts the loads of its
+  // first two tiles (registers only), sweep_run() stages them and runs the
+  // steps; the next context's loads can thus be in flight while the current
+  // one finishes (after its last step every register set is free).
   int next_page = 0;
+  auto sweep_issue = [&]() __attribute__((always_inline)) {
+  next_page = 0;
   if (n_visit > 0) gload(S0{}, tile_of(0), tile_row(tile_of(0), tile_page(tile_of(0))));
   if (n_visit > 1) gload(S1{}, tile_of(1), tile_row(tile_of(1), tile_page(tile_of(1))));
   if (n_visit > 2) next_page = tile_page(tile_of(2));
+  };
+  auto sweep_run = [&]() __attribute__((always_inline)) {
   if (n_visit > 0) swrite(S0{});
   if (n_visit > 2) {
     gload(S0{}, tile_of(2), tile_row(tile_of(2), next_page));
@@ -363,63 +401,112 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     if (k + 1 < n_visit) step(S1{}, k + 1);
   }
   };
-  sweep();
-  if constexpr (MULTI) {
-    // the shard's further contexts: the online softmax state carries over
-    for (int sg = 1; sg < it.n_seg; ++sg) {
-      __syncthreads();   // the previous context's last tiles may still be read from LDS
-      t = p.tasks[it.task + sg];
-      context(it.task + sg);
-      context_tiles();
-      sweep();
-    }
-  }
-
-  // Epilogue: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty rows: 0, -inf.
-  if (!qvalid) return;
-  const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
-  if constexpr (MULTI) {
-    if (it.stage_row >= 0) {
-      // a key chunk of a split shard: fp32 partial O and LSE to staging,
-      // merged by Equation 4 afterwards
-      const int64_t srow = (int64_t)it.stage_row + qrow;
-      if (hh == 0)
-        p.stage_LSE[srow * p.hq + head] = lsum > 0.f ? (m2 + __log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
-      float* so = p.stage_O + srow * (int64_t)(p.hq * D) + head * D;
+  // Epilogue of one item: O = acc / l, LSE = ln 2 * (m2 + log2 l); empty
+  // rows: 0, -inf.  Row orow of O / LSE, or staging row srow (>= 0) for a
+  // key chunk of a split shard (fp32 partials, merged by Equation 4 later).
+  auto epilogue = [&](bool valid, int e_head, int64_t orow, int64_t srow) __attribute__((always_inline)) {
+    if (!valid) return;
+    const float inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+    if constexpr (MULTI) {
+      if (srow >= 0) {
+        if (hh == 0)
+          p.stage_LSE[srow * p.hq + e_head] =
+              lsum > 0.f ? (m2 + __log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
+        float* so = p.stage_O + srow * (int64_t)(p.hq * D) + e_head * D;
 #pragma unroll
-      for (int c = 0; c < NCB; ++c)
+        for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(float4*)(so + c * 32 + 8 * q4 + 4 * hh) =
-              make_float4(o_acc[c][4 * q4] * inv_l, o_acc[c][4 * q4 + 1] * inv_l, o_acc[c][4 * q4 + 2] * inv_l,
-                          o_acc[c][4 * q4 + 3] * inv_l);
-      return;
-    }
-  }
-  const int64_t orow = t.o_off + qrow;
-  if (hh == 0) {
-    p.LSE[orow * p.hq + head] = lsum > 0.f ? (m2 + __log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
-  }
-  const int64_t obase = orow * (int64_t)(p.hq * D) + head * D;
-#pragma unroll
-  for (int c = 0; c < NCB; ++c) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int ch = c * 32 + 8 * q4 + 4 * hh;
-      const float v0 = o_acc[c][4 * q4 + 0] * inv_l;
-      const float v1 = o_acc[c][4 * q4 + 1] * inv_l;
-      const float v2 = o_acc[c][4 * q4 + 2] * inv_l;
-      const float v3 = o_acc[c][4 * q4 + 3] * inv_l;
-      if (p.out_f32) {
-        *(float4*)((float*)p.O + obase + ch) = make_float4(v0, v1, v2, v3);
-      } else {
-        bf16x4 o4;
-        o4[0] = (__bf16)v0;
-        o4[1] = (__bf16)v1;
-        o4[2] = (__bf16)v2;
-        o4[3] = (__bf16)v3;
-        *(bf16x4*)((__bf16*)p.O + obase + ch) = o4;
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(float4*)(so + c * 32 + 8 * q4 + 4 * hh) =
+                make_float4(o_acc[c][4 * q4] * inv_l, o_acc[c][4 * q4 + 1] * inv_l, o_acc[c][4 * q4 + 2] * inv_l,
+                            o_acc[c][4 * q4 + 3] * inv_l);
+        return;
       }
+    }
+    if (hh == 0) {
+      p.LSE[orow * p.hq + e_head] = lsum > 0.f ? (m2 + __log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
+    }
+    const int64_t obase = orow * (int64_t)(p.hq * D) + e_head * D;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int ch = c * 32 + 8 * q4 + 4 * hh;
+        const float v0 = o_acc[c][4 * q4 + 0] * inv_l;
+        const float v1 = o_acc[c][4 * q4 + 1] * inv_l;
+        const float v2 = o_acc[c][4 * q4 + 2] * inv_l;
+        const float v3 = o_acc[c][4 * q4 + 3] * inv_l;
+        if (p.out_f32) {
+          *(float4*)((float*)p.O + obase + ch) = make_float4(v0, v1, v2, v3);
+        } else {
+          bf16x4 o4;
+          o4[0] = (__bf16)v0;
+          o4[1] = (__bf16)v1;
+          o4[2] = (__bf16)v2;
+          o4[3] = (__bf16)v3;
+          *(bf16x4*)((__bf16*)p.O + obase + ch) = o4;
+        }
+      }
+    }
+  };
+
+  sweep_issue();
+  if constexpr (PERSIST) {
+    if (tid == 0) lds_next[0] = claimed_item();   // after the loads above: waits for the claim only
+  }
+  for (;;) {
+    sweep_run();
+    if constexpr (MULTI) {
+      // the shard's further contexts: the online softmax state carries over
+      for (int sg = 1; sg < it.n_seg; ++sg) {
+        if constexpr (PERSIST)
+          t = wave_uniform(p.tasks[it.task + sg]);
+        else
+          t = p.tasks[it.task + sg];
+        context(it.task + sg);
+        context_tiles();
+        sweep_issue();
+        __syncthreads();   // the previous context's last tiles may still be read from LDS
+        sweep_run();
+      }
+    }
+    const int64_t orow = t.o_off + qrow;
+    const int64_t srow = MULTI && it.stage_row >= 0 ? (int64_t)it.stage_row + qrow : -1;
+    if constexpr (!PERSIST) {
+      epilogue(qvalid, head, orow, srow);
+      return;
+    } else {
+      // The claimed item: its Q and first tiles are loaded while this item's
+      // outputs are written; the claim after it is taken at once.
+      __syncthreads();   // this item's last tiles are read; the claim is visible
+      // wave-uniform: keeps the item's fields, and everything derived from
+      // them, in scalar registers
+      const int nxt = __builtin_amdgcn_readfirstlane(lds_next[parity]);
+      parity ^= 1;
+      const bool more = nxt < p.n_items;
+      const bool e_valid = qvalid;
+      const int e_head = head;
+      if (more) {
+        if (tid == 0) claim = atomicAdd(p.counter + xcd, 1u);
+        it = wave_uniform(p.items[nxt]);
+        t = wave_uniform(p.tasks[it.task]);
+        kbase = p.K + it.kv_head * D;
+        vbase = p.V + it.kv_head * D;
+        item_rows();
+        context(it.task);
+        load_q();
+        context_tiles();
+        sweep_issue();
+      }
+      epilogue(e_valid, e_head, orow, srow);
+      if (!more) return;
+      // lds_next[parity] was last read after the previous item's last
+      // barrier, which every wave has passed since
+      if (tid == 0) lds_next[parity] = claimed_item();
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) o_acc[c] = f32x16_zero();
+      m2 = -INFINITY;
+      lsum = 0.f;
     }
   }
 }
@@ -428,10 +515,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
 // single-context kernel.
 template <int D, int NW, bool PAGED>
 hipError_t launch_forward_dp(const FwdParams& p, hipStream_t s) {
-  if (p.multi)
-    hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, true>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, false>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+  if (p.counter) {
+    if (p.multi)
+      hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, true, true>), dim3(min(p.n_slots, p.n_items)), dim3(64 * NW), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, false, true>), dim3(min(p.n_slots, p.n_items)), dim3(64 * NW), 0, s, p);
+  } else {
+    if (p.multi)
+      hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, true, false>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<D, NW, PAGED, false, false>), dim3(p.n_items), dim3(64 * NW), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -90,6 +90,9 @@ struct FwdParams {
   int32_t multi;      // some item has n_seg > 1 or a staging row
   float* stage_O;     // [stage rows][hq][d] fp32 partials of split shards
   float* stage_LSE;   // [stage rows][hq]
+  uint32_t* counter;  // persistent launch: 8 claim counters, one per XCD (zero at launch); nullptr: one
+                      // workgroup per item
+  int32_t n_slots;    // persistent workgroups (a multiple of 8; the grid is min(n_slots, n_items))
 };
 
 struct DecParams {
@@ -185,8 +188,9 @@ struct PreparedFwd {
   int32_t multi;            // some query shard has several contexts or is split
   int32_t n_merge;          // split shards
   int32_t max_q_len;        // longest split shard
+  int32_t n_slots;          // persistent workgroups (0: one workgroup per item)
   uint64_t off_tasks, off_masks, off_pages, off_items, off_dec, off_split, off_merge, off_part_o, off_part_l,
-      off_stage_o, off_stage_l;
+      off_stage_o, off_stage_l, off_counter;
 };
 
 // Validates a forward call (tensors: Q, K, V, O, LSE, or nullptr to skip the

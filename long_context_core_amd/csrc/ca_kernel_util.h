@@ -41,6 +41,23 @@ __device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
 // under a select.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
 
+// A struct of 32-bit words that every lane loaded from the same address,
+// moved to scalar registers.  Needed where the load cannot be a scalar load
+// (the kernel has already stored to global memory, so the compiler cannot
+// prove the data unchanged): without it every value derived from the struct
+// lives in vector registers and each scalar use (buffer descriptors, loop
+// bounds) pays a readfirstlane.
+template <class T>
+__device__ __forceinline__ T wave_uniform(const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "whole 32-bit words");
+  T r;
+  const int32_t* src = reinterpret_cast<const int32_t*>(&v);
+  int32_t* dst = reinterpret_cast<int32_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+  return r;
+}
+
 // 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -31,7 +31,7 @@ int main() {
   for (int it = 0; it < 4000; ++it) {
     ca_shape s{};
     s.hkv = (int)U(1, 8); s.hq = s.hkv * (int)U(1, 16); s.d = U(0, 5) ? 128 : 64; s.scale = U(0, 20) ? 0.088f : -1.f;
-    s.flags = U(0, 1); s.q_rows = U(0, 100000); s.kv_rows = U(0, 100000); s.o_rows = s.q_rows * U(1, 3);
+    s.flags = U(0, 7); s.q_rows = U(0, 100000); s.kv_rows = U(0, 100000); s.o_rows = s.q_rows * U(1, 3);
     if (!U(0, 30)) s.q_rows = INT64_MAX - U(0, 10);    // huge row counts are rejected, not multiplied
     if (!U(0, 30)) s.hq = s.hkv * (int)U(1 << 12, 1 << 20);
     int n = (int)U(0, 30);
@@ -69,7 +69,7 @@ int main() {
   for (int it = 0; it < 4000; ++it) {
     ca_shape s{};
     s.hkv = (int)U(1, 8); s.hq = s.hkv * (int)U(1, 16); s.d = U(0, 1) ? 128 : 64; s.scale = 0.088f;
-    s.flags = U(0, 1); s.q_rows = U(1, 20000); s.kv_rows = U(1, 20000); s.o_rows = s.q_rows;
+    s.flags = U(0, 7); s.q_rows = U(1, 20000); s.kv_rows = U(1, 20000); s.o_rows = s.q_rows;
     int n = (int)U(1, 20);
     std::vector<ca_task> t(n);
     std::vector<ca_task_mask> m(n);

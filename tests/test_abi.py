@@ -91,6 +91,20 @@ def test_forward_rejects_bad_arguments_without_launching():
     assert "workspace" in ca.lib().ca_last_error().decode()
     # nothing to do: OK without touching the device
     assert call_forward(s, [(0, 0, 0, 0, 10, 0, 0)]) == ca.CA_OK
+    # launch flags: one of the two, forward only
+    both = ca.make_shape(8, 2, 128, 10, 10, 10)
+    both.flags = ca.CA_LAUNCH_PERSISTENT | ca.CA_LAUNCH_PER_ITEM
+    assert call_forward(both, good) == ca.CA_ERR_INVALID
+    unknown = ca.make_shape(8, 2, 128, 10, 10, 10)
+    unknown.flags = 8
+    assert call_forward(unknown, good) == ca.CA_ERR_INVALID
+    for launch in ("persistent", "per_item"):
+        sl = ca.make_shape(8, 2, 128, 10, 10, 10, launch=launch)
+        assert ca.forward_workspace(sl, good) == need
+        assert call_forward(sl, good, ws_bytes=need - 1) == ca.CA_ERR_WORKSPACE
+        ta = ca.task_array(good)
+        assert ca.lib().ca_backward_workspace(ctypes.byref(sl), ta.ctypes.data_as(ctypes.c_void_p), len(ta)) == 0
+        assert "forward flags" in ca.lib().ca_last_error().decode()
 
 
 def test_merge_rejects_bad_arguments():
@@ -102,6 +116,8 @@ def test_merge_rejects_bad_arguments():
     s2 = ca.make_shape(4, 1, 80, 0, 0, 0)
     assert L.ca_merge(ctypes.byref(s2), 2, 10, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_ERR_UNSUPPORTED
     assert L.ca_merge(ctypes.byref(s), 2, 0, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_OK
+    s3 = ca.make_shape(4, 1, 128, 0, 0, 0, launch="persistent")
+    assert L.ca_merge(ctypes.byref(s3), 2, 10, FAKE, FAKE, FAKE, FAKE, None) == ca.CA_ERR_INVALID
 
 
 def test_varlen_rejects_bad_cu_seqlens():

@@ -328,3 +328,70 @@ def test_merge_random_part_counts_and_ranges(seed):
     assert np.all(np.isfinite(got_o))
     assert np.max(np.abs(got_o - Oref)) < (2e-5 if out_f32 else 2e-2)
     assert np.all(got_o[~fin] == 0)
+
+
+@pytest.mark.parametrize("hq,hkv,d,blockwise", [(8, 4, 64, False), (16, 2, 128, False), (8, 2, 128, True)])
+def test_persistent_launch_claims_items_bit_identical(hq, hkv, d, blockwise):
+    """Thousands of work items, far more than the resident workgroups of the
+    persistent launch, so that most are claimed from the queue one after
+    another by workgroups that already ran items of other KV heads, head
+    groups, documents and (blockwise) multi-context shards.  The persistent
+    launch equals the one-workgroup-per-item launch bit for bit, and both
+    equal the oracle on every row and head."""
+    announce("forward persistent vs per-item hq%d hkv%d d%d blockwise=%s" % (hq, hkv, d, blockwise))
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(4242 + hq + d)
+    lens = [int(x) for x in rng.integers(1, 300, size=400)]
+    tasks = I.blockwise_shards(lens, 64, 2) if blockwise else I.varlen_tasks(lens)
+    T = sum(lens)
+    Q = I.randn_bf16((T, hq, d), 5150 + hq + d)
+    K = I.randn_bf16((T, hkv, d), 5151 + hq + d)
+    V = I.randn_bf16((T, hkv, d), 5152 + hq + d)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    outs = []
+    for launch in ("persistent", "per_item"):
+        O = torch.full((T, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        LSE = torch.full((T, hq), float("nan"), device=dev)
+        ca.forward(ca.make_shape(hq, hkv, d, T, T, T, launch=launch), tasks, Qd, Kd, Vd, O, LSE)
+        outs.append((O, LSE))
+    torch.cuda.synchronize()
+    (Op, Lp), (Oi, Li) = outs
+    assert torch.equal(Op.view(torch.int16), Oi.view(torch.int16))
+    assert torch.equal(Lp, Li)
+    O_ref, LSE_ref = oracle.forward(tasks, widen(Q), widen(K), widen(V), 1 / math.sqrt(d), o_rows=T)
+    check_forward(Op, Lp, O_ref, LSE_ref, "persistent hq%d hkv%d d%d" % (hq, hkv, d))
+
+
+def test_persistent_launch_paged_and_masked_bit_identical():
+    """The paged and sink/window-masked instantiations of the persistent
+    launch: bit-identical to one workgroup per item over many claimed items
+    (every output is also checked against the oracle by the per-item launch's
+    own tests)."""
+    announce("forward persistent vs per-item, paged + lambda mask")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(977)
+    P = 256
+    lens = [int(x) for x in rng.integers(1, 700, size=300)]
+    tasks, n_vp = I.paged_varlen_tasks(lens, P)
+    hq, hkv, d = 16, 4, 128
+    T = sum(lens)
+    masks = np.array([(int(rng.integers(0, 200)), int(rng.integers(0, 64))) for _ in range(len(tasks))], dtype=np.int32)
+    n_phys = n_vp + 5
+    table = I.page_table(n_vp, n_phys, 978)
+    Q = I.randn_bf16((T, hq, d), 979).to(dev)
+    Ks = I.page_store(I.randn_bf16((n_vp * P, hkv, d), 980), table, P, n_phys).to(dev)
+    Vs = I.page_store(I.randn_bf16((n_vp * P, hkv, d), 981), table, P, n_phys).to(dev)
+    outs = []
+    for launch in ("persistent", "per_item"):
+        O = torch.full((T, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        LSE = torch.full((T, hq), float("nan"), device=dev)
+        ca.forward(ca.make_shape(hq, hkv, d, T, n_phys * P, T, launch=launch), tasks, Q, Ks, Vs, O, LSE,
+                   masks=masks, pages=ca.kv_pages(table, P))
+        outs.append((O, LSE))
+    torch.cuda.synchronize()
+    (Op, Lp), (Oi, Li) = outs
+    assert bool(torch.isfinite(Lp).all())
+    assert torch.equal(Op.view(torch.int16), Oi.view(torch.int16))
+    assert torch.equal(Lp, Li)
