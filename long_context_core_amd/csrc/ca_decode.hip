@@ -107,9 +107,9 @@ __global__ __launch_bounds__(256, 2) void dec_kernel(DecParams p) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int s = 0; s < NT; ++s) kr[b][s] = buffer_load_16(krs, k_voff[b] + 64 * s, 0);
+      for (int s = 0; s < NT; ++s) kr[b][s] = buffer_load_16_stream(krs, k_voff[b] + 64 * s, 0);
 #pragma unroll
-    for (int r = 0; r < VPASS; ++r) vr[r] = buffer_load_16(vrs, v_voff + (uint32_t)(r * VROWS) * row_bytes, 0);
+    for (int r = 0; r < VPASS; ++r) vr[r] = buffer_load_16_stream(vrs, v_voff + (uint32_t)(r * VROWS) * row_bytes, 0);
   };
 
   f32x4 o_acc[NCB];
