@@ -839,7 +839,10 @@ def main():
         kernel = "ca_backward: bwd_prep_kernel, bwd_q_kernel, bwd_kv_kernel"
     else:
         traffic = traffic_for("ca_fwd.hip", w.name)
-        kernel = "ca::fwd_kernel<%d, 8, false>" % w.d
+        # template arguments: D, waves, paged, multi-context shards, persistent
+        qi = ca.forward_queue_info(shape, tasks)
+        kernel = "ca::fwd_kernel<%d, 8, false, %s, %s>" % (w.d, str(qi["multi"]).lower(),
+                                                           str(qi["persistent_workgroups"] > 0).lower())
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": kernel,

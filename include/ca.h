@@ -178,6 +178,17 @@ ca_status ca_forward_masked(const ca_shape* shape, const ca_task* tasks_host, co
                             int32_t n_tasks, const void* Q, const void* K, const void* V, void* O,
                             float* LSE, void* ws, size_t ws_bytes, void* stream);
 
+/* How ca_forward_masked would launch this call (host only, no device work):
+ * info[0] work items of the tiled kernel, info[1] split-KV decode items,
+ * info[2] persistent workgroups of the tiled kernel (0: one workgroup per
+ * item), info[3] 1 when some query shard sweeps several contexts or is split
+ * over key chunks, info[4] query shards split over key chunks.  The work queue
+ * is the one a call would build (H1's longest-first items, "Efficient
+ * Long-context Language Model Training by Core Attention Disaggregation",
+ * Section 3.4).  Errors as ca_forward_masked (info untouched then). */
+ca_status ca_forward_queue_info(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                int32_t n_tasks, int64_t info[5]);
+
 /*
  * Paged K/V: block tables as in the Blockwise Attention instruction of "DCP:
  * Addressing Input Dynamism In Long-Context Training via Dynamic Context

@@ -36,6 +36,7 @@ EXPORTS = (
     "ca_visible_pairs",
     "ca_visible_pairs_masked",
     "ca_forward_masked_workspace",
+    "ca_forward_queue_info",
     "ca_forward_masked",
     "ca_forward_paged_workspace",
     "ca_forward_paged",
@@ -166,6 +167,8 @@ def lib():
         L.ca_visible_pairs_masked.restype = i64
         L.ca_forward_masked_workspace.argtypes = [sp, vp, vp, i32]
         L.ca_forward_masked_workspace.restype = sz
+        L.ca_forward_queue_info.argtypes = [sp, vp, vp, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.ca_forward_queue_info.restype = ctypes.c_int
         L.ca_forward_masked.argtypes = [sp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.ca_forward_masked.restype = ctypes.c_int
         L.ca_forward_paged_workspace.argtypes = [sp, vp, vp, i32, vp]
@@ -356,6 +359,18 @@ def forward_workspace(shape, tasks, masks=None, pages=None):
         return int(lib().ca_forward_paged_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta),
                                                     ctypes.byref(pages)))
     return int(lib().ca_forward_masked_workspace(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta)))
+
+
+def forward_queue_info(shape, tasks, masks=None):
+    """How the forward would launch (host only): dict with the tiled kernel's
+    work items, the split-KV decode items, the persistent workgroups (0: one
+    workgroup per item), whether some shard is multi-context or split, and
+    the number of split shards."""
+    ta, ma = split_tasks(tasks, masks)
+    info = (ctypes.c_int64 * 5)()
+    _check(lib().ca_forward_queue_info(ctypes.byref(shape), _tasks_ptr(ta), _mask_ptr(ma), len(ta), info))
+    return {"items": int(info[0]), "decode_items": int(info[1]), "persistent_workgroups": int(info[2]),
+            "multi": bool(info[3]), "split_shards": int(info[4])}
 
 
 def workspace_tensor(nbytes, device, stream=None):

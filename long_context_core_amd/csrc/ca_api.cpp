@@ -377,14 +377,14 @@ int64_t decode_visible(const ca_task& k) {
 }
 
 // Long query shards split over key chunks (forward and dQ kernels).  An item
-// that would sweep far more (row, key) pairs than the call's average work
-// per compute unit makes a tail no scheduling hides; its shard's visible
-// keys are cut into chunks, each a run of derived tasks (sub-ranges of the
-// shard's contexts, appended after the table) whose items write fp32
-// partials to staging rows; the partials are merged afterwards.  Shards with
-// sink / window masks are left whole (their items are short).
+// whose work exceeds a quarter of one compute unit's share of the call
+// (256 CUs) makes a tail no scheduling hides; its shard's visible keys are
+// cut into chunks, each a run of derived tasks (sub-ranges of the shard's
+// contexts, appended after the table) whose items write fp32 partials to
+// staging rows; the partials are merged afterwards.  Shards with sink /
+// window masks are left whole (their items are short).
 constexpr int64_t kMinSplitPairs = 1 << 21;   // per item and head
-constexpr int64_t kSplitPairsDiv = 1024;
+constexpr int64_t kSplitShareDiv = 4 * 256;
 constexpr int32_t kMaxChunks = 64;
 constexpr int32_t kChunkAlign = 128;          // chunk bounds, in keys (paged tiles stay inside one page)
 
@@ -402,14 +402,16 @@ struct ShardSplits {
   int32_t max_q_len = 0;
 };
 
+// hq: query heads of the call; hpw: heads per work item.
 ShardSplits plan_shard_splits(const ca_task* t, const ca_task_mask* m, int32_t n, const std::vector<int32_t>& shard,
-                              int rt, const std::vector<bool>& tiled) {
+                              int rt, int hq, int hpw, const std::vector<bool>& tiled) {
   ShardSplits S;
   S.split_of.assign((size_t)n, -1);
   int64_t total = 0;
   for (int32_t i = 0; i < n; ++i)
     if (shard[(size_t)i] > 0 && tiled[(size_t)i]) total += shard_range_pairs(t, m, i, shard[(size_t)i], 0, t[i].q_len - 1);
-  const int64_t w_max = std::max<int64_t>(kMinSplitPairs, total / kSplitPairsDiv);
+  // an item's work is w * hpw head-pairs, the call's total * hq
+  const int64_t w_max = std::max<int64_t>(kMinSplitPairs, total / (kSplitShareDiv * hpw) * hq);
   for (int32_t i = 0; i < n; ++i) {
     const int32_t n_seg = shard[(size_t)i];
     if (n_seg == 0 || !tiled[(size_t)i]) continue;
@@ -513,7 +515,7 @@ FwdPlan plan_forward(const ca_shape* s, const ca_task* t, const ca_task_mask* m,
   std::vector<bool> tiled((size_t)n, false);
   for (int32_t i = 0; i < n; ++i)
     tiled[(size_t)i] = t[i].q_len > 0 && p.shard[(size_t)i] > 0 && !is_decode_shard(t, m, p.shard, i, p.group);
-  p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, tiled);
+  p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, s->hq, p.hpw, tiled);
   if (!p.splits.splits.empty()) p.multi = 1;
   for (int32_t i = 0; i < n; ++i) {
     if (!tiled[(size_t)i]) continue;
@@ -1101,7 +1103,7 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
   int64_t q_cover = 0, kv_cover = 0;
   std::vector<bool> active_q((size_t)n, false);
   for (int32_t i = 0; i < n; ++i) active_q[(size_t)i] = t[i].q_len > 0 && p.shard[(size_t)i] > 0;
-  p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, active_q);
+  p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, s->hq, p.hpw, active_q);
   if (!p.splits.splits.empty()) p.multi = 1;
   for (int32_t i = 0; i < n; ++i) {
     const bool active = active_q[(size_t)i];
@@ -1434,6 +1436,20 @@ ca_status ca_forward(const ca_shape* shape, const ca_task* tasks_host, int32_t n
                      const void* K, const void* V, void* O, float* LSE, void* ws, size_t ws_bytes,
                      void* stream) {
   return forward_impl(shape, tasks_host, nullptr, n_tasks, nullptr, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+ca_status ca_forward_queue_info(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,
+                                int32_t n_tasks, int64_t info[5]) {
+  if (!info) return fail(CA_ERR_INVALID, "info is NULL");
+  const ca_status st = check_forward_args(shape, tasks_host, masks_host, n_tasks, nullptr);
+  if (st != CA_OK) return st;
+  const FwdPlan p = plan_forward(shape, tasks_host, masks_host, n_tasks);
+  info[0] = (int64_t)p.n_items;
+  info[1] = (int64_t)p.n_dec_items;
+  info[2] = (int64_t)p.n_slots;
+  info[3] = p.multi;
+  info[4] = (int64_t)p.splits.splits.size();
+  return CA_OK;
 }
 
 size_t ca_forward_masked_workspace(const ca_shape* shape, const ca_task* tasks_host, const ca_task_mask* masks_host,

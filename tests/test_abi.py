@@ -213,3 +213,31 @@ def test_binding_rejects_host_and_mistyped_tensors_before_the_library():
         ca.backward(s, t, Q, K, K, O, O, L, Q, K, K, ws=ws)
     with pytest.raises(ca.CAError, match="Q: not a device tensor"):
         ca.forward_varlen(s, [0, 10], Q, K, K, O, L, ws=ws)
+
+
+def test_forward_queue_info_launch_rule_and_splits():
+    """Host-only view of the forward's launch: items, the persistent rule
+    (default from 32,768 items; the flags force either way), multi-context
+    shards and long shards split over key chunks."""
+    w = I.llama8b_packed_131k()
+    s = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
+    info = ca.forward_queue_info(s, w.tasks)
+    assert info["items"] < 32768 and info["persistent_workgroups"] == 0
+    assert not info["multi"] and info["split_shards"] == 0     # no item outlasts a CU's share
+    sp = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, launch="persistent")
+    assert ca.forward_queue_info(sp, w.tasks)["persistent_workgroups"] == 256
+    w = I.ca_tasks_34b()
+    s = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
+    info = ca.forward_queue_info(s, w.tasks)
+    assert info["items"] >= 32768 and info["persistent_workgroups"] == 256
+    si = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, launch="per_item")
+    assert ca.forward_queue_info(si, w.tasks)["persistent_workgroups"] == 0
+    # a few rows at the end of a long context: split; with the same context
+    # short, not split; a single row goes to the decode kernel
+    s = ca.make_shape(8, 2, 128, 64, 200000, 64)
+    assert ca.forward_queue_info(s, [(0, 0, 0, 64, 200000, 199936, 0)])["split_shards"] == 1
+    assert ca.forward_queue_info(s, [(0, 0, 0, 64, 20000, 19936, 0)])["split_shards"] == 0
+    info = ca.forward_queue_info(s, [(0, 0, 0, 1, 200000, 199999, 0)])
+    assert info["items"] == 0 and info["decode_items"] > 0
+    with pytest.raises(ca.CAError):
+        ca.forward_queue_info(s, [(0, 0, 0, 65, 10, 0, 0)])   # past q_rows

@@ -263,7 +263,7 @@ def test_backward_split_tiles_probe():
 @pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (4, 1, 64)])
 def test_split_long_shards_forward_and_backward_vs_oracle(hq, hkv, d):
     """A 64-row shard at the end of a 70,000-token context, a 32-row shard
-    over three contexts (two 30,000-key prefixes, all visible, and its own
+    over three contexts (two 40,000-key prefixes, all visible, and its own
     rows, causal) and a short document: the long shards' items are split
     over key chunks.  O, LSE and dQ, dK, dV element by element against the
     oracle."""
@@ -271,13 +271,13 @@ def test_split_long_shards_forward_and_backward_vs_oracle(hq, hkv, d):
     torch = torch_cuda()
     dev = torch.device("cuda:0")
     tasks = np.array([(0, 0, 0, 64, 70000, 69936, 0),                 # shard A
-                      (64, 70000, 64, 32, 30000, 80000, 0),           # shard B: prefix 1
-                      (64, 100000, 64, 32, 30000, 80000, 30000),      #          prefix 2
-                      (64, 130000, 64, 32, 32, 80000, 80000),         #          own rows, causal
-                      (96, 130032, 96, 300, 300, 0, 0)], dtype=np.int64)
-    q_rows, kv_rows = 396, 130332
+                      (64, 70000, 64, 32, 40000, 100000, 0),          # shard B: prefix 1
+                      (64, 110000, 64, 32, 40000, 100000, 40000),     #          prefix 2
+                      (64, 150000, 64, 32, 32, 100000, 100000),       #          own rows, causal
+                      (96, 150032, 96, 300, 300, 0, 0)], dtype=np.int64)
+    q_rows, kv_rows = 396, 150332
     shape = ca.make_shape(hq, hkv, d, q_rows, kv_rows, q_rows)
-    assert ca.forward_workspace(shape, tasks) > ca.forward_workspace(shape, tasks[4:]) + 64 * hq * d * 4
+    assert ca.forward_queue_info(shape, tasks)["split_shards"] == 2   # both long shards
     Q = I.randn_bf16((q_rows, hq, d), 1031)
     K = I.randn_bf16((kv_rows, hkv, d), 1032)
     V = I.randn_bf16((kv_rows, hkv, d), 1033)
