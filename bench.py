@@ -237,7 +237,9 @@ def secondary(steps=3, warmup=1):
     fl = forward_flops(ca.visible_pairs(tasks), w.hq, w.d)
     ms_f = timed(lambda: ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream), steps, warmup, stream)
     Ov, Lv = O.view(w.n_parts, T, w.hq, w.d), LSE.view(w.n_parts, T, w.hq)
-    ms_m = timed(lambda: ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream), steps, warmup, stream)
+    # sub-millisecond calls: 50 steady-state repetitions, so the host's first
+    # enqueue after the idle start does not weigh on the average
+    ms_m = timed(lambda: ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream), 50, 5, stream)
     # merge bytes: O of every written partial row, all partial LSEs, merged O (bf16) + LSE
     mb = len(w.tasks) * (T // w.n_parts) * w.hq * w.d * 4 + w.n_parts * T * w.hq * 4 + T * w.hq * (w.d * 2 + 4)
     out["ring_prefill_405b_tp8"] = {"workload": w.name, "partials_ms": round(ms_f, 3),
@@ -283,7 +285,7 @@ def secondary(steps=3, warmup=1):
     ms_lb_slot = timed(ring_lb_per_slot, steps, warmup, stream)
     ms_lb = timed(ring_lb, steps, warmup, stream)
     fl_lb = forward_flops(sum(ca.visible_pairs(t) for t in step_tasks), hq, d)
-    ms_lbm = timed(lambda: ca.merge(mshape, Op, Lp, Om, Lm, stream=stream), steps, warmup, stream)
+    ms_lbm = timed(lambda: ca.merge(mshape, Op, Lp, Om, Lm, stream=stream), 50, 5, stream)
     # merge bytes: O of every partial row with a visible key (the others carry
     # LSE = -inf and are not read), all partial LSEs, merged O (bf16) + LSE
     live = sum(max(0, int(r["q_len"]) - max(0, int(r["kv_pos0"]) - int(r["q_pos0"])))
@@ -406,7 +408,7 @@ def secondary(steps=3, warmup=1):
         ca.forward(shape, tasks, Q, K, V, O, LSE, ws=ws, stream=stream)
         ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream)
 
-    ms = ms_dec = timed(dec_step, max(steps, 10), warmup, stream)
+    ms = ms_dec = timed(dec_step, 50, 5, stream)
     kv_bytes = 2 * w.kv_rows * w.hkv * w.d * 2
     out["ring_decode_405b_tp8"] = {"workload": w.name, "ms": round(ms, 4), "kv_bytes": kv_bytes,
                                    "gbs": round(kv_bytes / ms / 1e6, 1),
@@ -429,7 +431,7 @@ def secondary(steps=3, warmup=1):
         ca.forward(shape, tasks, Q, Ks, Vs, O, LSE, ws=pws, stream=stream, pages=pages)
         ca.merge(mshape, Ov, Lv, Om, Lm, stream=stream)
 
-    ms = timed(dec_step_paged, max(steps, 10), warmup, stream)
+    ms = timed(dec_step_paged, 50, 5, stream)
     out["ring_decode_405b_tp8_paged256"] = {"workload": w.name + ", K/V in shuffled 256-row pages",
                                             "ms": round(ms, 4), "gbs": round(kv_bytes / ms / 1e6, 1)}
     log("decode, paged K/V (256-row pages): %.3f ms, %.0f GB/s of K+V" % (ms, kv_bytes / ms / 1e6))
@@ -451,7 +453,7 @@ def secondary(steps=3, warmup=1):
 
     g, gws = graph_of(shape, tasks, Q, K, V, O, LSE, mshape, Ov, Lv, Om, Lm)
     graph_rows = {"131072": {"direct_ms": round(ms_dec, 4),
-                             "graph_ms": round(timed(g.replay, max(steps, 10), warmup, stream), 4)}}
+                             "graph_ms": round(timed(g.replay, 50, 5, stream), 4)}}
     del Q, K, V, O, LSE, ws, Om, Lm, g, gws
     ws_ = I.ring_decode_405b_tp8(context=4096)
     Q, K, V, O, LSE, shape, tasks, ws = fwd_setup(ws_, 209, out_f32=True)
