@@ -38,6 +38,10 @@ CASES = {
     "decode-whole-cache": (decode_whole(8, 20000), 8, 8 * 20000, 8, 0),
     "prefill-causal-docs": (I.varlen_tasks([700, 128, 1, 1500]), 2329, 2329, 2329, 0),
 }
+# persistent launch (claim counters reset by a kernel inside the graph): many
+# short documents, far more work items than resident workgroups
+_LENS = [int(x) for x in np.random.default_rng(2733).integers(1, 300, size=300)]
+CASES["prefill-many-docs-persistent"] = (I.varlen_tasks(_LENS), sum(_LENS), sum(_LENS), sum(_LENS), 0)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -47,7 +51,10 @@ def test_graph_replays_equal_direct_calls(name):
     dev = torch.device("cuda:0")
     tasks, q_rows, kv_rows, o_rows, n_parts = CASES[name]
     merged = n_parts > 0
-    shape = ca.make_shape(HQ, HKV, D, q_rows, kv_rows, o_rows, out_f32=merged)
+    launch = "persistent" if name.endswith("persistent") else None
+    shape = ca.make_shape(HQ, HKV, D, q_rows, kv_rows, o_rows, out_f32=merged, launch=launch)
+    if launch:
+        assert ca.forward_queue_info(shape, tasks)["persistent_workgroups"] == 256
     K = I.randn_bf16((kv_rows, HKV, D), 2701, device=dev)
     V = I.randn_bf16((kv_rows, HKV, D), 2702, device=dev)
     Q = I.randn_bf16((q_rows, HQ, D), 2700, device=dev)
@@ -74,6 +81,7 @@ def test_graph_replays_equal_direct_calls(name):
             ca.merge(mshape, O.view(n_parts, B, HQ, D), LSE.view(n_parts, B, HQ), Om, Lm, stream=st)
     for rep in range(4):
         Q.copy_(I.randn_bf16((q_rows, HQ, D), 2710 + rep, device=dev))
+        O.fill_(float("nan"))   # a replay that skipped work would leave NaN
         ca.forward(shape, tasks, Q, K, V, O2, LSE2, ws=ws2)
         if merged:
             ca.merge(mshape, O2.view(n_parts, B, HQ, D), LSE2.view(n_parts, B, HQ), Om2, Lm2)

@@ -66,6 +66,36 @@ def test_noalloc_equals_workspace_call_twice_second_smaller():
         run_pair(torch, dev, tasks, q_rows, kv_rows, o_rows, 2900 + 10 * k)
 
 
+def test_noalloc_persistent_launch_equals_per_item_workspace_call():
+    """The persistent launch from the scratch (its claim counters live there
+    and are reset by a kernel before each launch): two calls in a row, the
+    second smaller, each bit-identical to a one-workgroup-per-item call with a
+    caller workspace."""
+    announce("ca_forward_noalloc, persistent launch, two calls vs per-item workspace calls")
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(2977)
+    for k, n_docs in enumerate((500, 120)):
+        lens = [int(x) for x in rng.integers(1, 400, size=n_docs)]
+        tasks = I.varlen_tasks(lens)
+        T = sum(lens)
+        sp = ca.make_shape(HQ, HKV, D, T, T, T, launch="persistent")
+        si = ca.make_shape(HQ, HKV, D, T, T, T, launch="per_item")
+        assert ca.forward_queue_info(sp, tasks)["persistent_workgroups"] > 0
+        Q = I.randn_bf16((T, HQ, D), 2980 + k, device=dev)
+        K = I.randn_bf16((T, HKV, D), 2990 + k, device=dev)
+        V = I.randn_bf16((T, HKV, D), 3000 + k, device=dev)
+        O1 = torch.full((T, HQ, D), float("nan"), dtype=torch.bfloat16, device=dev)
+        L1 = torch.full((T, HQ), float("nan"), device=dev)
+        O2, L2 = torch.empty_like(O1), torch.empty_like(L1)
+        ca.forward_noalloc(sp, tasks, Q, K, V, O1, L1)
+        ca.forward(si, tasks, Q, K, V, O2, L2)
+        torch.cuda.synchronize()
+        same = torch.equal(O1.view(torch.int16), O2.view(torch.int16)) and torch.equal(L1, L2)
+        print("persistent noalloc call %d (T=%d): identical to the per-item call: %s" % (k, T, same), flush=True)
+        assert same
+
+
 def test_noalloc_rejects_a_queue_beyond_the_scratch():
     """A table whose queue exceeds the scratch is refused before any launch
     (CA_ERR_WORKSPACE), and the outputs stay untouched."""
