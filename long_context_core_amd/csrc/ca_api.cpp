@@ -959,10 +959,10 @@ struct KvGroups {
   std::vector<ca_task> rep;            // per group: its first member
 };
 
-KvGroups kv_groups(const ca_task* t, int32_t n) {
+// Context groups over the candidate tasks cand (indices into t).
+KvGroups kv_groups(const ca_task* t, const std::vector<int32_t>& cand) {
   KvGroups g;
-  for (int32_t i = 0; i < n; ++i)
-    if (t[i].q_len > 0 && t[i].kv_len > 0) g.members.push_back(i);
+  g.members = cand;
   std::stable_sort(g.members.begin(), g.members.end(), [&](int32_t a, int32_t b) {
     return t[a].kv_off != t[b].kv_off ? t[a].kv_off < t[b].kv_off : t[a].kv_len < t[b].kv_len;
   });
@@ -976,6 +976,68 @@ KvGroups kv_groups(const ca_task* t, int32_t n) {
     ++g.count.back();
   }
   return g;
+}
+
+// Context pieces for the dK/dV kernel: every context is cut at the first and
+// the past-the-end rows of every other context that fall strictly inside it,
+// so that contexts which overlap become runs of identical pieces (each a
+// derived task: the same query rows over a sub-range of the keys, positions
+// and mask kept).  Tasks whose pieces coincide form one context group, and
+// groups no longer overlap, so the dK/dV items write their rows in a single
+// pass: no fp32 accumulation, one launch.  (The causal-blockwise mask, whose
+// windows overlap their neighbours', is the case that needs it.)  Paged calls
+// keep whole contexts (their passes follow shared pages), and so does a table
+// whose cuts would multiply its contexts beyond kMaxPieceFactor * n + 65,536.
+constexpr int64_t kMaxPieceFactor = 4;
+
+struct KvPieces {
+  std::vector<ca_task> tasks;         // derived pieces
+  std::vector<ca_task_mask> masks;    // their masks (the source task's)
+  std::vector<int32_t> members;       // dK/dV candidates: table index, or first_index + k for piece k
+};
+
+KvPieces kv_pieces(const ca_task* t, const ca_task_mask* m, int32_t n, int32_t first_index, bool cut) {
+  KvPieces P;
+  std::vector<int64_t> pts;
+  for (int32_t i = 0; i < n; ++i)
+    if (t[i].q_len > 0 && t[i].kv_len > 0) {
+      pts.push_back(t[i].kv_off);
+      pts.push_back(t[i].kv_off + t[i].kv_len);
+    }
+  std::sort(pts.begin(), pts.end());
+  pts.erase(std::unique(pts.begin(), pts.end()), pts.end());
+  int64_t n_cuts = 0;
+  for (int32_t i = 0; i < n && cut; ++i) {
+    if (t[i].q_len <= 0 || t[i].kv_len <= 0) continue;
+    const int64_t lo = t[i].kv_off, hi = lo + t[i].kv_len;
+    n_cuts += std::lower_bound(pts.begin(), pts.end(), hi) - std::upper_bound(pts.begin(), pts.end(), lo);
+  }
+  if (n_cuts > kMaxPieceFactor * n + 65536) cut = false;
+  for (int32_t i = 0; i < n; ++i) {
+    const ca_task& x = t[i];
+    if (x.q_len <= 0 || x.kv_len <= 0) continue;
+    const int64_t lo = x.kv_off, hi = lo + x.kv_len;
+    auto a = std::upper_bound(pts.begin(), pts.end(), lo);
+    auto b = std::lower_bound(pts.begin(), pts.end(), hi);
+    if (!cut || a == b) {
+      P.members.push_back(i);
+      continue;
+    }
+    int64_t from = lo;
+    for (auto it = a;; ++it) {
+      const int64_t to = it == b ? hi : *it;
+      ca_task d = x;
+      d.kv_off = from;
+      d.kv_len = (int32_t)(to - from);
+      d.kv_pos0 = x.kv_pos0 + (from - lo);
+      P.members.push_back(first_index + (int32_t)P.tasks.size());
+      P.tasks.push_back(d);
+      P.masks.push_back(m ? m[i] : ca_task_mask{0, 0});
+      if (it == b) break;
+      from = to;
+    }
+  }
+  return P;
 }
 
 // One dK/dV work unit (per KV head): 128 keys of a context group, and the
@@ -995,6 +1057,9 @@ struct BwdPlan {
   bool q_full = false, kv_full = false;          // every row covered by some task
   int multi = 0;                                 // a shard or a context group with several tasks, or a split
   ShardSplits splits;                            // dQ side: long shards split over key chunks
+  KvPieces pieces;                               // dK/dV side: contexts cut where others start / end
+  std::vector<ca_task> ext_tasks;                // table, split-shard chunks, context pieces
+  std::vector<ca_task_mask> ext_masks;           // likewise (empty without masks)
   std::vector<KvUnit> units;                     // dK/dV work units (replicated per KV head)
   std::vector<std::pair<int32_t, int32_t>> split_tiles;   // (group, key0) of every split tile
   size_t n_slots = 0;                            // partial slots (per KV head included)
@@ -1097,14 +1162,26 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
   p.hpw = gcd_int(p.group, 4);
   p.rt = 32 * (4 / p.hpw);
   p.shard = query_shards(t, n);
-  p.groups = kv_groups(t, n);
-  const size_t n_groups = p.groups.rep.size();
-  std::vector<std::pair<int64_t, int64_t>> qiv(n), kviv(n_groups);
-  int64_t q_cover = 0, kv_cover = 0;
   std::vector<bool> active_q((size_t)n, false);
   for (int32_t i = 0; i < n; ++i) active_q[(size_t)i] = t[i].q_len > 0 && p.shard[(size_t)i] > 0;
   p.splits = plan_shard_splits(t, m, n, p.shard, p.rt, s->hq, p.hpw, active_q);
   if (!p.splits.splits.empty()) p.multi = 1;
+  // the device's task table: the caller's, the split-shard chunks, the pieces
+  p.pieces = kv_pieces(t, m, n, n + (int32_t)p.splits.tasks.size(), pg == nullptr);
+  p.ext_tasks.assign(t, t + n);
+  p.ext_tasks.insert(p.ext_tasks.end(), p.splits.tasks.begin(), p.splits.tasks.end());
+  p.ext_tasks.insert(p.ext_tasks.end(), p.pieces.tasks.begin(), p.pieces.tasks.end());
+  if (m) {
+    p.ext_masks.assign(m, m + n);
+    p.ext_masks.insert(p.ext_masks.end(), p.splits.masks.begin(), p.splits.masks.end());
+    p.ext_masks.insert(p.ext_masks.end(), p.pieces.masks.begin(), p.pieces.masks.end());
+  }
+  const ca_task* et = p.ext_tasks.data();
+  const ca_task_mask* em = m ? p.ext_masks.data() : nullptr;
+  p.groups = kv_groups(et, p.pieces.members);
+  const size_t n_groups = p.groups.rep.size();
+  std::vector<std::pair<int64_t, int64_t>> qiv(n), kviv(n_groups);
+  int64_t q_cover = 0, kv_cover = 0;
   for (int32_t i = 0; i < n; ++i) {
     const bool active = active_q[(size_t)i];
     qiv[i] = {t[i].q_off, active ? t[i].q_len : 0};
@@ -1122,7 +1199,7 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
     if (p.groups.count[g] > 1) p.multi = 1;
     kv_cover += x.kv_len;
   }
-  plan_kv_units(t, m, p);
+  plan_kv_units(et, em, p);
   p.n_kvitems = p.units.size() * (size_t)s->hkv;
   p.n_reduce = p.split_tiles.size() * (size_t)s->hkv;
   for (const KvUnit& u : p.units)
@@ -1135,7 +1212,7 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
                    : partition_passes(kviv, p.kv_pass_of);
   p.q_full = p.q_passes == 1 && q_cover == s->q_rows;
   p.kv_full = !pg && p.kv_passes == 1 && kv_cover == s->kv_rows;   // paged: unread page rows stay zero
-  const size_t n_all = (size_t)n + p.splits.tasks.size();   // the table and the derived tasks
+  const size_t n_all = p.ext_tasks.size();   // the table and the derived tasks
   p.off_tasks = 0;
   p.off_masks = align_up(sizeof(ca_task) * n_all);
   p.off_pages = p.off_masks + (m ? align_up(sizeof(ca_task_mask) * n_all) : 0);
@@ -1306,16 +1383,8 @@ ca_status backward_impl(const ca_shape* s, const ca_task* t, const ca_task_mask*
   build_backward_items(s, t, m, n, p, pg, qitems, q_begin, kvitems, kv_begin, reduces, reduce_begin, qmerges,
                        qmerge_begin);
   std::vector<char> host(p.off_d, 0);
-  std::memcpy(host.data() + p.off_tasks, t, sizeof(ca_task) * (size_t)n);
-  if (!p.splits.tasks.empty())
-    std::memcpy(host.data() + p.off_tasks + sizeof(ca_task) * (size_t)n, p.splits.tasks.data(),
-                sizeof(ca_task) * p.splits.tasks.size());
-  if (m) {
-    std::memcpy(host.data() + p.off_masks, m, sizeof(ca_task_mask) * (size_t)n);
-    if (!p.splits.masks.empty())
-      std::memcpy(host.data() + p.off_masks + sizeof(ca_task_mask) * (size_t)n, p.splits.masks.data(),
-                  sizeof(ca_task_mask) * p.splits.masks.size());
-  }
+  std::memcpy(host.data() + p.off_tasks, p.ext_tasks.data(), sizeof(ca_task) * p.ext_tasks.size());
+  if (m) std::memcpy(host.data() + p.off_masks, p.ext_masks.data(), sizeof(ca_task_mask) * p.ext_masks.size());
   if (!qmerges.empty()) std::memcpy(host.data() + p.off_qmerge, qmerges.data(), sizeof(ca::ShardMerge) * qmerges.size());
   if (pg && pg->n_pages > 0)
     std::memcpy(host.data() + p.off_pages, pg->table_host, sizeof(int32_t) * (size_t)pg->n_pages);
