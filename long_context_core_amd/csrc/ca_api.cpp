@@ -1012,7 +1012,7 @@ KvPieces kv_pieces(const ca_task* t, const ca_task_mask* m, int32_t n, int32_t f
     const int64_t lo = t[i].kv_off, hi = lo + t[i].kv_len;
     n_cuts += std::lower_bound(pts.begin(), pts.end(), hi) - std::upper_bound(pts.begin(), pts.end(), lo);
   }
-  if (n_cuts > kMaxPieceFactor * n + 65536) cut = false;
+  if (n_cuts > kMaxPieceFactor * n + 65536 || (int64_t)first_index + n + n_cuts > INT32_MAX / 2) cut = false;
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& x = t[i];
     if (x.q_len <= 0 || x.kv_len <= 0) continue;
