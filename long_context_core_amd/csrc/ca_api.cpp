@@ -619,10 +619,21 @@ void build_forward_items(const ca_shape* s, const ca_task* t, const ca_task_mask
                        [&](int64_t cost, const ca::FwdItem& it) { tmp.push_back({cost, it}); });
     }
   }
-  // Longest first.  Items of equal cost (the KV heads of one query tile) stay
-  // adjacent, so they land on different XCDs and spread the K/V streams; the
-  // re-reads of long contexts are served by the shared last-level cache.
-  std::stable_sort(tmp.begin(), tmp.end(), [](const Keyed& a, const Keyed& b) { return a.cost > b.cost; });
+  // Shard-major: the costliest query shard first, its row tiles last-first
+  // (the longest), then the next shard.  The KV heads of one row tile stay
+  // adjacent, so they land on different XCDs (workgroups are dealt to the 8
+  // XCDs in turn, and so are persistent claims), and each XCD's workgroups run
+  // the row tiles of the same shard and KV head side by side: they stream the
+  // same context at nearly the same pace, and its tiles are served from that
+  // XCD's L2 instead of being fetched once per row tile.
+  std::vector<int64_t> shard_cost((size_t)n + p.splits.tasks.size(), 0);   // by first task (derived chunks too)
+  for (const Keyed& k : tmp) shard_cost[(size_t)k.it.task] += k.cost;
+  std::stable_sort(tmp.begin(), tmp.end(), [&](const Keyed& a, const Keyed& b) {
+    const int64_t sa = shard_cost[(size_t)a.it.task], sb = shard_cost[(size_t)b.it.task];
+    if (sa != sb) return sa > sb;
+    if (a.it.task != b.it.task) return a.it.task < b.it.task;
+    return a.it.row0 > b.it.row0;
+  });
   items.resize(tmp.size());
   for (size_t i = 0; i < tmp.size(); ++i) items[i] = tmp[i].it;
 }
