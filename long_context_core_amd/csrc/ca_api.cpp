@@ -1274,7 +1274,16 @@ void build_backward_items(const ca_shape* s, const ca_task* t, const ca_task_mas
                          [&](int64_t cost, const ca::FwdItem& it) { tmp.push_back({cost, it}); });
       }
     }
-    std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
+    // shard-major, as the forward's queue: an XCD's workgroups stream the
+    // same context for the row tiles of one shard and KV head
+    std::vector<int64_t> shard_cost((size_t)n + p.splits.tasks.size(), 0);
+    for (const K& k : tmp) shard_cost[(size_t)k.it.task] += k.c;
+    std::stable_sort(tmp.begin(), tmp.end(), [&](const K& a, const K& b) {
+      const int64_t sa = shard_cost[(size_t)a.it.task], sb = shard_cost[(size_t)b.it.task];
+      if (sa != sb) return sa > sb;
+      if (a.it.task != b.it.task) return a.it.task < b.it.task;
+      return a.it.row0 > b.it.row0;
+    });
     for (auto& k : tmp) qitems.push_back(k.it);
     q_begin.push_back(qitems.size());
     for (size_t sp = 0; sp < p.splits.splits.size(); ++sp) {
@@ -1305,17 +1314,27 @@ void build_backward_items(const ca_shape* s, const ca_task* t, const ca_task_mas
     }
   }
   for (int pass = 0; pass < p.kv_passes; ++pass) {
-    struct K { int64_t c; ca::BwdItem it; };
+    struct K { int64_t c; int32_t group; ca::BwdItem it; };
     std::vector<K> tmp;
+    std::vector<int64_t> group_cost(G.rep.size(), 0);
     for (size_t u = 0; u < p.units.size(); ++u) {
       const KvUnit& un = p.units[u];
       if (p.kv_pass_of[(size_t)un.group] != pass) continue;
+      group_cost[(size_t)un.group] += un.cost;
       for (int32_t g = 0; g < s->hkv; ++g) {
         const int32_t slot = un.split >= 0 ? slot_of_unit[u] + g * split_n[(size_t)un.split] : -1;
-        tmp.push_back({un.cost, {un.member0, g, un.key0, un.n_members, un.row_lo, un.row_hi, slot, 0}});
+        tmp.push_back({un.cost, un.group, {un.member0, g, un.key0, un.n_members, un.row_lo, un.row_hi, slot, 0}});
       }
     }
-    std::stable_sort(tmp.begin(), tmp.end(), [](const K& a, const K& b) { return a.c > b.c; });
+    // group-major: the costliest context group first, its key tiles
+    // costliest first; an XCD's workgroups then stream the same query rows
+    // for the key tiles of one group and KV head
+    std::stable_sort(tmp.begin(), tmp.end(), [&](const K& a, const K& b) {
+      const int64_t ga = group_cost[(size_t)a.group], gb = group_cost[(size_t)b.group];
+      if (ga != gb) return ga > gb;
+      if (a.group != b.group) return a.group < b.group;
+      return a.c > b.c;
+    });
     for (auto& k : tmp) kvitems.push_back(k.it);
     kv_begin.push_back(kvitems.size());
     for (size_t sp = 0; sp < p.split_tiles.size(); ++sp) {
