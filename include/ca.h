@@ -123,7 +123,7 @@ enum {
    * (one workgroup per compute unit, each claiming items from the
    * longest-first queue of its XCD and loading the next item's Q and first
    * K/V tiles under the current item's epilogue) when the call has at least
-   * 32,768 work items, else one workgroup per item, dispatched by the
+   * 4,096 work items, else one workgroup per item, dispatched by the
    * hardware. */
   CA_LAUNCH_PERSISTENT = 1u << 1,
   CA_LAUNCH_PER_ITEM = 1u << 2

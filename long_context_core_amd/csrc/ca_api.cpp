@@ -322,11 +322,12 @@ constexpr int kFwdWaves = 8;   // waves per forward workgroup (two per SIMD)
 // MI355X (256 CUs; about 250 VGPRs per wave leave room for one such workgroup
 // per CU); the workgroups claim items from the longest-first queue.  On a
 // part with fewer CUs the extra workgroups wait their turn.  Chosen by
-// default from 128 items per workgroup up: measured against one workgroup
-// per item, it gained 1.6 % on a 65,536-item CA-task batch and 2.4 % on a
-// 65,536-item blockwise-mask batch, and lost 0.3 % on a 16,424-item one.
+// default from 16 items per workgroup up: with the shard-major queue it
+// measured +0.6 % on a 16,424-item batch and +0.7 % on a 65,728-item one
+// against one workgroup per item; a few items gain nothing from claims and
+// would pay the counter reset's extra launch.
 constexpr size_t kPersistSlots = 256;
-constexpr size_t kPersistMinItems = 128 * kPersistSlots;
+constexpr size_t kPersistMinItems = 16 * kPersistSlots;
 constexpr int kDecTargetItems = 1024;      // two rounds of two 4-wave items per CU
 constexpr int kDecMinChunk = 512;
 constexpr int kDecMaxGroup = 16;

@@ -217,19 +217,22 @@ def test_binding_rejects_host_and_mistyped_tensors_before_the_library():
 
 def test_forward_queue_info_launch_rule_and_splits():
     """Host-only view of the forward's launch: items, the persistent rule
-    (default from 32,768 items; the flags force either way), multi-context
+    (default from 4,096 items; the flags force either way), multi-context
     shards and long shards split over key chunks."""
     w = I.llama8b_packed_131k()
     s = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
     info = ca.forward_queue_info(s, w.tasks)
-    assert info["items"] < 32768 and info["persistent_workgroups"] == 0
+    assert info["items"] >= 4096 and info["persistent_workgroups"] == 256
     assert not info["multi"] and info["split_shards"] == 0     # no item outlasts a CU's share
-    sp = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, launch="persistent")
-    assert ca.forward_queue_info(sp, w.tasks)["persistent_workgroups"] == 256
+    si = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, launch="per_item")
+    assert ca.forward_queue_info(si, w.tasks)["persistent_workgroups"] == 0
+    t = I.tiny_forward()                                         # 8 items: one workgroup each
+    st = ca.make_shape(t.hq, t.hkv, t.d, t.q_rows, t.kv_rows, t.o_rows)
+    assert ca.forward_queue_info(st, t.tasks)["persistent_workgroups"] == 0
     w = I.ca_tasks_34b()
     s = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows)
     info = ca.forward_queue_info(s, w.tasks)
-    assert info["items"] >= 32768 and info["persistent_workgroups"] == 256
+    assert info["items"] >= 4096 and info["persistent_workgroups"] == 256
     si = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, launch="per_item")
     assert ca.forward_queue_info(si, w.tasks)["persistent_workgroups"] == 0
     # a few rows at the end of a long context: split; with the same context
