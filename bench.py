@@ -43,7 +43,9 @@ def source_sha(path):
 
 def traffic_for(kernel_file, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel source and the current host planner (the
+    queue order decides how much of the re-read K/V the caches serve); else
+    None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -51,7 +53,9 @@ def traffic_for(kernel_file, workload):
         data = json.load(open(p))
         ent = data.get(workload)
         src = os.path.join(ROOT, "long_context_core_amd", "csrc", kernel_file)
-        if not ent or ent.get("kernel_source_sha") != source_sha(src):
+        planner = os.path.join(ROOT, "long_context_core_amd", "csrc", "ca_api.cpp")
+        if (not ent or ent.get("kernel_source_sha") != source_sha(src)
+                or ent.get("planner_source_sha") != source_sha(planner)):
             return None
         return float(ent["fetch_bytes_per_launch"]) + float(ent["write_bytes_per_launch"])
     except Exception:
