@@ -83,6 +83,15 @@ def test_random_task_tables_forward_and_backward(seed, masked):
     if np.isnan(L_ref).all():
         return                                   # no query rows at all
     check_forward(O, LSE, O_ref, L_ref, "random-%d" % seed)
+    # the persistent launch (resident workgroups claiming the items) equals
+    # the default launch bit for bit
+    Op = torch.full_like(O, float("nan"))
+    Lp = torch.full_like(LSE, float("nan"))
+    ca.forward(ca.make_shape(hq, hkv, d, q_rows, kv_rows, q_rows, launch="persistent"), tasks, Qd, Kd, Vd, Op, Lp)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(np.flatnonzero(~np.isnan(L_ref[:, 0])))
+    assert torch.equal(Op.cpu()[rows].view(torch.int16), O.cpu()[rows].view(torch.int16))
+    assert torch.equal(Lp.cpu()[rows], LSE.cpu()[rows])
     dQ = torch.full_like(Qd, float("nan"))
     dK = torch.full_like(Kd, float("nan"))
     dV = torch.full_like(Vd, float("nan"))
@@ -144,3 +153,59 @@ def test_random_task_tables_paged(seed, masked):
     got = (got[0][torch_cuda().from_numpy(np.flatnonzero(covered))], got[1], got[2])
     ref = (ref[0][covered], ref[1], ref[2])
     check_grads(got, ref, "random-paged-bwd-%d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_long_overlapping_contexts_split_and_pieced(seed):
+    """A few query shards over long, overlapping key ranges of one K/V buffer
+    (most keys visible, some ranges sharing rows, one windowed task): the
+    long shards' items are split over key chunks (forward merge, dQ sum), the
+    overlapping contexts are cut into shared pieces for dK/dV, and the
+    persistent launch runs the forward; O, LSE, dQ, dK, dV vs the oracle."""
+    rng = np.random.default_rng(9700 + seed)
+    hq, hkv, d = 8, 2, 128
+    kv_rows = 90000
+    rows, masks, q0 = [], [], 0
+    for k in range(5):
+        q_len = int(rng.choice([1, 40, 64, 150]))
+        kv_len = int(rng.integers(20000, 80000))
+        kv_off = int(rng.integers(0, kv_rows - kv_len + 1))
+        kv_pos0 = int(rng.integers(0, 1000))
+        q_pos0 = kv_pos0 + kv_len - q_len + int(rng.integers(-2000, 500))
+        rows.append((q0, kv_off, q0, q_len, kv_len, max(0, q_pos0), kv_pos0))
+        masks.append((int(rng.integers(500, 3000)), 64) if k == 4 else (0, 0))
+        q0 += q_len
+    tasks = np.array(rows, dtype=np.int64)
+    full = np.concatenate([tasks, np.array(masks, dtype=np.int64)], axis=1)
+    q_rows = q0
+    announce("random long overlapping contexts seed %d: tasks=%s" % (seed, full.tolist()))
+    shape = ca.make_shape(hq, hkv, d, q_rows, kv_rows, q_rows)
+    info = ca.forward_queue_info(shape, tasks, full[:, 7:9])
+    print("queue:", info, flush=True)
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    Q = I.randn_bf16((q_rows, hq, d), 9710 + seed)
+    K = I.randn_bf16((kv_rows, hkv, d), 9720 + seed)
+    V = I.randn_bf16((kv_rows, hkv, d), 9730 + seed)
+    dO = I.randn_bf16((q_rows, hq, d), 9740 + seed)
+    Qd, Kd, Vd, dOd = Q.to(dev), K.to(dev), V.to(dev), dO.to(dev)
+    O = torch.full((q_rows, hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    LSE = torch.full((q_rows, hq), float("nan"), device=dev)
+    fshape = ca.make_shape(hq, hkv, d, q_rows, kv_rows, q_rows, launch="persistent")
+    ca.forward(fshape, full, Qd, Kd, Vd, O, LSE)
+    dQ, dK, dV = (torch.full_like(x, float("nan")) for x in (Qd, Kd, Vd))
+    ca.backward(shape, full, Qd, Kd, Vd, O, dOd, LSE, dQ, dK, dV)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    O_ref, L_ref = oracle.forward(full, widen(Q), widen(K), widen(V), scale, o_rows=q_rows)
+    check_forward(O, LSE, O_ref, L_ref, "long-overlap-%d" % seed)
+    ref = oracle.backward(full, widen(Q), widen(K), widen(V), widen(dO), scale)
+    covered = ~np.isnan(L_ref[:, 0])
+    for name, g, r in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+        gw = widen(g)
+        if name == "dQ":
+            gw, r = gw[covered], r[covered]
+        assert np.all(np.isfinite(gw)), "%s not finite" % name
+        e = rel_fro(gw, r)
+        print("long-overlap-%d %s relF=%.3e" % (seed, name, e), flush=True)
+        assert e <= GRAD_REL_FRO, name
