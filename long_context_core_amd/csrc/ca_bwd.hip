@@ -19,9 +19,12 @@
 //   bwd_q_kernel     Q-stationary, shaped like the forward: S^T = K Q^T,
 //                    dP^T = V dO^T, dQ^T += K^T dS^T (K^T by transpose reads).
 // Query shards over several contexts (consecutive tasks sharing their query
-// rows) and context groups (tasks sharing their context rows) are swept one
-// task after another inside one work item (the MULTI instantiations), so
-// every gradient row is still written once per pass.
+// rows) and context groups (tasks sharing their context rows; contexts that
+// overlap are first cut into shared pieces) are swept one task after another
+// inside one work item (the MULTI instantiations), so every gradient row is
+// still written once per pass.  Items whose rows are too many for one item
+// write fp32 partials (dK/dV slots, dQ key chunks) that a reduction sums in a
+// fixed order.
 // Rows are written once per pass (read-modify-write in fp32 when several
 // tasks share rows), so results are deterministic.
 

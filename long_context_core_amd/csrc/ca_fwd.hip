@@ -1,8 +1,11 @@
 // K1 — fused core-attention forward over a CA-task table (gfx950).
 //
-// One workgroup (8 waves, two per SIMD) per work item: 256 (query row, head)
+// A workgroup (8 waves, two per SIMD) runs a work item: 256 (query row, head)
 // pairs that all read the same KV head — hpw heads x (8 / hpw) blocks of 32
-// rows — so each K/V tile staged in LDS feeds eight MFMA streams.  Per 64-key
+// rows — so each K/V tile staged in LDS feeds eight MFMA streams.  Either one
+// workgroup per item, or (PERSIST) one resident workgroup per compute unit
+// claiming items from its XCD's share of the queue and loading the next
+// item's Q and first tiles under the current item's epilogue.  Per 64-key
 // tile a wave:
 //
 //   S^T[64 keys][32 queries] = K_tile . Q^T       (MFMA 32x32x16 bf16, fp32 acc)
