@@ -1082,10 +1082,12 @@ struct BwdPlan {
 };
 
 // A tile's query rows above which its dK/dV work is split over several
-// items: 1/512 of the call's rows (a tail of at most about half the ideal
-// time on 256 compute units), at least kMinSplitRows rows per item.
+// items: when the tile's work (rows x the group's heads) exceeds a quarter of
+// one compute unit's share of the call (all tiles' rows x heads over 256
+// CUs), so that no item alone makes a tail; at least kMinSplitRows rows per
+// item.
 constexpr int64_t kMinSplitRows = 8192;
-constexpr int64_t kSplitDiv = 512;
+constexpr int64_t kSplitShareRows = 4 * 256;
 
 // Task-relative query rows [r_lo, r_end) of task i that see any key of the
 // 128-key tile at context row k0.
@@ -1108,7 +1110,7 @@ std::pair<int64_t, int64_t> tile_rows(const ca_task* t, const ca_task_mask* m, i
 // dK/dV work units of every (context group, key tile), with long tiles split
 // over member ranges, or over 32-aligned row ranges of one member, into
 // items of about equal rows.
-void plan_kv_units(const ca_task* t, const ca_task_mask* m, BwdPlan& p) {
+void plan_kv_units(const ca_task* t, const ca_task_mask* m, int hkv, BwdPlan& p) {
   const KvGroups& G = p.groups;
   struct Tile { int32_t group, key0; int64_t rows; };
   std::vector<Tile> tiles;
@@ -1125,7 +1127,8 @@ void plan_kv_units(const ca_task* t, const ca_task_mask* m, BwdPlan& p) {
       tiles.push_back({(int32_t)gi, k0, rows});
       total += rows;
     }
-  const int64_t max_rows = std::max<int64_t>(kMinSplitRows, total / kSplitDiv);
+  // an item's work is rows * G (one KV head), the call's total * G * hkv
+  const int64_t max_rows = std::max<int64_t>(kMinSplitRows, total / kSplitShareRows * hkv);
   size_t mr = 0;
   for (const Tile& tl : tiles) {
     const int32_t first = G.first[(size_t)tl.group], count = G.count[(size_t)tl.group];
@@ -1211,7 +1214,7 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
     if (p.groups.count[g] > 1) p.multi = 1;
     kv_cover += x.kv_len;
   }
-  plan_kv_units(et, em, p);
+  plan_kv_units(et, em, s->hkv, p);
   p.n_kvitems = p.units.size() * (size_t)s->hkv;
   p.n_reduce = p.split_tiles.size() * (size_t)s->hkv;
   for (const KvUnit& u : p.units)
