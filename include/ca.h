@@ -93,8 +93,8 @@ typedef struct {
   int64_t q_off;   /* first row in Q (and dQ)                              */
   int64_t kv_off;  /* first row in K, V (and dK, dV)                       */
   int64_t o_off;   /* first row in O, LSE (and O, dO, LSE in backward)     */
-  int32_t q_len;   /* >= 0                                                 */
-  int32_t kv_len;  /* >= 0                                                 */
+  int32_t q_len;   /* 0 .. 2^30                                            */
+  int32_t kv_len;  /* 0 .. 2^30                                            */
   int64_t q_pos0;  /* document position of query row 0                     */
   int64_t kv_pos0; /* document position of context row 0                   */
 } ca_task;
@@ -533,7 +533,8 @@ int32_t ca_ring_decode_rank(int32_t n_ranks, int64_t iteration, int32_t seq);
 
 /* Number of visible (query, key) pairs of a task table, per query head
  * (FLOPs = 4 d pairs hq forward, 10 d pairs hq backward).  -1 on an invalid
- * table. */
+ * table (negative lengths or lengths above 2^30, a NULL table, a negative
+ * window or sink).  Closed form: the cost does not grow with the lengths. */
 int64_t ca_visible_pairs(const ca_task* tasks_host, int32_t n_tasks);
 /* The same under per-task masks (masks_host may be NULL). */
 int64_t ca_visible_pairs_masked(const ca_task* tasks_host, const ca_task_mask* masks_host, int32_t n_tasks);

@@ -87,15 +87,32 @@ int64_t task_sink_keys(const ca_task* t, const ca_task_mask* m, int32_t i) {
   return std::min<int64_t>(t[i].kv_len, std::max<int64_t>(0, (int64_t)m[i].sink - t[i].kv_pos0));
 }
 
-// range_pairs under the sink + sliding-window mask: row i sees the keys of
-// its causal context [0, c_i) that are >= i + delta - win + 1 or < sj.
+// Keys row u = i + delta sees under the sink + sliding-window mask: the keys
+// of its causal context [0, c) that are >= u - win + 1 (the window) or < sj
+// (the sink).
+int64_t masked_row_keys(int64_t u, int64_t kv_len, int64_t win, int64_t sj) {
+  const int64_t c = std::min(kv_len, std::max<int64_t>(0, u + 1));
+  const int64_t wlo = std::max<int64_t>(0, u - win + 1);
+  return std::max<int64_t>(0, c - wlo) + std::max<int64_t>(0, std::min(std::min(sj, c), wlo));
+}
+
+// range_pairs under the sink + sliding-window mask, in closed form.  The
+// per-row count is piecewise linear in u with integer slopes; its slope can
+// change only between u = k and u = k + 1 for k in the kinks below (where
+// u + 1 reaches 0 or kv_len, the window start reaches 0, the sink end or
+// kv_len).  Between kinks each run of rows is an arithmetic series.
 int64_t range_pairs_masked(int64_t a, int64_t b, int64_t delta, int64_t kv_len, int64_t win, int64_t sj) {
   if (win <= 0) return range_pairs(a, b, delta, kv_len);
+  if (b < a || kv_len <= 0) return 0;
+  const int64_t kinks[6] = {-1, kv_len - 1, win - 1, kv_len + win - 1, sj - 1, sj + win - 1};
   int64_t total = 0;
-  for (int64_t i = a; i <= b; ++i) {
-    const int64_t c = std::min(kv_len, std::max<int64_t>(0, i + delta + 1));
-    const int64_t wlo = std::max<int64_t>(0, i + delta - win + 1);
-    total += std::max<int64_t>(0, c - wlo) + std::max<int64_t>(0, std::min(std::min(sj, c), wlo));
+  for (int64_t r0 = a; r0 <= b;) {
+    int64_t r1 = b;
+    for (int64_t k : kinks)
+      if (k - delta >= r0 && k - delta < r1) r1 = k - delta;
+    const int64_t f0 = masked_row_keys(r0 + delta, kv_len, win, sj), f1 = masked_row_keys(r1 + delta, kv_len, win, sj);
+    total += (f0 + f1) * (r1 - r0 + 1) / 2;   // even: 2 f0 n + slope n (n - 1)
+    r0 = r1 + 1;
   }
   return total;
 }
@@ -111,6 +128,10 @@ ca_status check_masks(const ca_task_mask* m, int32_t n) {
 // int64: far beyond any buffer a device holds.
 constexpr int64_t kMaxRows = int64_t(1) << 40;
 constexpr int32_t kMaxHeads = 4096;
+// Longest task (query rows and context rows): keeps the kernels' and the
+// planners' int32 tile arithmetic (a length plus a tile, twice a length)
+// inside int32.
+constexpr int32_t kMaxTaskLen = int32_t(1) << 30;
 
 ca_status check_shape(const ca_shape* s) {
   if (!s) return fail(CA_ERR_INVALID, "shape is NULL");
@@ -139,6 +160,8 @@ ca_status check_tasks(const ca_shape* s, const ca_task* t, int32_t n, int64_t kv
   for (int32_t i = 0; i < n; ++i) {
     const ca_task& k = t[i];
     if (k.q_len < 0 || k.kv_len < 0) return fail(CA_ERR_INVALID, "task %d: negative length", i);
+    if (k.q_len > kMaxTaskLen || k.kv_len > kMaxTaskLen)
+      return fail(CA_ERR_INVALID, "task %d: q_len=%d or kv_len=%d above 2^30", i, k.q_len, k.kv_len);
     if (k.q_off < 0 || k.kv_off < 0 || k.o_off < 0) return fail(CA_ERR_INVALID, "task %d: negative offset", i);
     // Compared as off > rows - len: the lengths are non-negative int32 and the
     // row counts non-negative, so nothing here can overflow (off + len could,
@@ -1699,7 +1722,7 @@ int64_t ca_visible_pairs_masked(const ca_task* tasks_host, const ca_task_mask* m
   int64_t total = 0;
   for (int32_t i = 0; i < n_tasks; ++i) {
     const ca_task& k = tasks_host[i];
-    if (k.q_len < 0 || k.kv_len < 0) return -1;
+    if (k.q_len < 0 || k.kv_len < 0 || k.q_len > kMaxTaskLen || k.kv_len > kMaxTaskLen) return -1;
     total += range_pairs_masked(0, (int64_t)k.q_len - 1, k.q_pos0 - k.kv_pos0, k.kv_len,
                                 task_window(masks_host, i), task_sink_keys(tasks_host, masks_host, i));
   }

@@ -45,6 +45,10 @@ int main() {
         int64_t* off[3] = {&x.q_off, &x.kv_off, &x.o_off};
         *off[U(0, 2)] = INT64_MAX - U(0, 4000);
       }
+      if (!U(0, 40)) {  // lengths near INT32_MAX: rejected before any tile arithmetic
+        int32_t* len[2] = {&x.q_len, &x.kv_len};
+        *len[U(0, 1)] = INT32_MAX - (int32_t)U(0, 200);
+      }
       x.q_pos0 = U(0, 20000); x.kv_pos0 = U(0, 20000);
       m[i].window = (int)U(0, 3) ? 0 : (int)U(-1, 5000); m[i].sink = (int)U(-1, 100);
     }

@@ -83,6 +83,13 @@ def test_forward_rejects_bad_arguments_without_launching():
             t[k] = off
             assert call_forward(s, [tuple(t)]) == ca.CA_ERR_INVALID, (k, off)
     assert call_forward(ca.make_shape(8, 2, 128, big, 10, 10), good) == ca.CA_ERR_INVALID   # rows > 2^40
+    # task lengths above 2^30 (int32 tile arithmetic), in a shape large enough to hold them
+    huge = ca.make_shape(8, 2, 128, 2 ** 31, 2 ** 31, 2 ** 31)
+    for t in [(0, 0, 0, 2 ** 30 + 1, 10, 0, 0), (0, 0, 0, 10, 2 ** 30 + 1, 0, 0), (0, 0, 0, 10, 2 ** 31 - 1, 0, 0)]:
+        assert call_forward(huge, [t]) == ca.CA_ERR_INVALID, t
+        assert "above 2^30" in ca.lib().ca_last_error().decode()
+        ta = ca.task_array([t])
+        assert ca.lib().ca_backward_workspace(ctypes.byref(huge), ta.ctypes.data_as(ctypes.c_void_p), len(ta)) == 0
     assert call_forward(ca.make_shape(8192, 2, 128, 10, 10, 10), good) == ca.CA_ERR_INVALID  # hq > 4096
     assert call_forward(s, good, ptr=None) == ca.CA_ERR_INVALID                # NULL tensors
     need = ca.forward_workspace(s, good)
@@ -144,6 +151,33 @@ def test_masked_visible_pairs_match_the_oracle():
             t[:, 5] += rng.integers(0, 50, size=len(t))
         assert ca.visible_pairs(t) == oracle.visible_pairs(t)
     assert ca.visible_pairs(I.varlen_tasks([5, 7])) == oracle.visible_pairs(I.varlen_tasks([5, 7]))
+
+
+def test_masked_visible_pairs_closed_form_on_random_tasks():
+    """The closed-form count of ca_visible_pairs_masked against the oracle's
+    row-by-row count, on tasks with arbitrary position offsets (rows before,
+    inside and past the context), windows shorter and longer than the
+    context, and sinks inside and past it."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(11)
+    rows = []
+    for _ in range(400):
+        q_len, kv_len = int(rng.integers(0, 300)), int(rng.integers(0, 300))
+        kv_pos0 = int(rng.integers(0, 200))
+        q_pos0 = kv_pos0 + int(rng.integers(-350, 350))
+        window = int(rng.choice([0, 1, 2, int(rng.integers(1, 400))]))
+        sink = int(rng.choice([0, 1, int(rng.integers(0, 500))]))
+        rows.append((0, 0, 0, q_len, kv_len, q_pos0, kv_pos0, window, sink))
+    for r in rows:
+        assert ca.visible_pairs([r]) == oracle.visible_pairs([r]), r
+    assert ca.visible_pairs(rows) == oracle.visible_pairs(rows)
+    # lengths above 2^30 are refused; 2^30 itself is counted without a row loop
+    with pytest.raises(ca.CAError):
+        ca.visible_pairs([(0, 0, 0, 2 ** 30 + 1, 10, 0, 0, 64, 4)])
+    L = 2 ** 30
+    assert ca.visible_pairs([(0, 0, 0, L, L, 0, 0, 1, 0)]) == L           # window 1: the diagonal
+    assert ca.visible_pairs([(0, 0, 0, L, L, 0, 0, L, 0)]) == L * (L + 1) // 2
 
 
 def call_paged(shape, tasks, table, page_rows, reserved=0, ws_bytes=1 << 20):
