@@ -111,21 +111,23 @@ def test_paged_ca_task_shards_and_shared_prefix():
     check_forward(O, LSE, Or, Lr, "paged CA-tasks shared prefix")
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 1), (8, 2)])
-def test_paged_decode(hq, hkv):
-    """Single-token queries over paged caches (the split-KV decode kernel),
-    caches of ragged length, split into several key chunks."""
-    announce("paged decode hq%d hkv%d" % (hq, hkv))
-    P, d = 256, 128
-    ctx = [5000, 131, 2048, 777, 9000, 1]
+@pytest.mark.parametrize("hq,hkv,P", [(16, 1, 256), (8, 2, 256), (16, 1, 128), (8, 2, 1024)])
+def test_paged_decode(hq, hkv, P):
+    """Single-token queries over paged caches (the split-KV decode kernel,
+    two tiles in flight), caches of ragged length, split into several key
+    chunks; chunks of 1 to 5 tiles and 128-row pages (a new page every tile)
+    cover the pipeline's ends."""
+    announce("paged decode hq%d hkv%d P%d" % (hq, hkv, P))
+    d = 128
+    ctx = [5000, 131, 2048, 777, 9000, 1, 128, 129, 256, 257, 384, 385, 512, 640]
     t = []
     vp = 0
     for b, c in enumerate(ctx):
         t.append((b, vp * P, b, 1, c, c - 1, 0))
         vp += -(-c // P)
     tasks = np.array(t, dtype=np.int64)
-    outs, Or, Lr = run_paged(tasks, None, hq, hkv, d, len(ctx), vp, P, 1700 + hq)
-    check_paged(outs, Or, Lr, "paged decode")
+    outs, Or, Lr = run_paged(tasks, None, hq, hkv, d, len(ctx), vp, P, 1700 + hq + P)
+    check_paged(outs, Or, Lr, "paged decode P%d" % P)
 
 
 def test_paged_lambda_mask():
