@@ -341,6 +341,7 @@ ca_status upload(void* dst, const std::vector<char>& src, hipStream_t s) {
 // merged by log-sum-exp afterwards.
 
 constexpr int kFwdWaves = 8;   // waves per forward workgroup (two per SIMD)
+constexpr int kBwdQWaves = 8;  // waves per dQ workgroup (two per SIMD)
 // Persistent forward launch: one 8-wave workgroup per compute unit of the
 // MI355X (256 CUs; about 250 VGPRs per wave leave room for one such workgroup
 // per CU); the workgroups claim items from the longest-first queue.  On a
@@ -1202,7 +1203,7 @@ BwdPlan plan_backward(const ca_shape* s, const ca_task* t, const ca_task_mask* m
   BwdPlan p;
   p.group = s->hq / s->hkv;
   p.hpw = gcd_int(p.group, 4);
-  p.rt = 32 * (4 / p.hpw);
+  p.rt = 32 * (kBwdQWaves / p.hpw);   // dQ work items: rows of one item
   p.shard = query_shards(t, n);
   std::vector<bool> active_q((size_t)n, false);
   for (int32_t i = 0; i < n; ++i) active_q[(size_t)i] = t[i].q_len > 0 && p.shard[(size_t)i] > 0;

@@ -16,8 +16,9 @@
 //                    registers across heads and tiles.  Per 32x32 block:
 //                      S = Q K^T, dP = dO V^T          (lane = key)
 //                      dV^T += dO^T P,  dK^T += Q^T dS (dO^T, Q^T by LDS transpose reads)
-//   bwd_q_kernel     Q-stationary, shaped like the forward: S^T = K Q^T,
-//                    dP^T = V dO^T, dQ^T += K^T dS^T (K^T by transpose reads).
+//   bwd_q_kernel     Q-stationary, shaped like the forward (eight waves, two
+//                    per SIMD): S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+//                    (K^T by transpose reads).
 // Query shards over several contexts (consecutive tasks sharing their query
 // rows) and context groups (tasks sharing their context rows; contexts that
 // overlap are first cut into shared pieces) are swept one task after another
@@ -577,20 +578,29 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: work items as in the forward (hpw heads x 4/hpw blocks of 32 rows).
+// dQ: work items as in the forward (hpw heads x 8/hpw blocks of 32 rows),
+// eight waves, two per SIMD: while one wave runs its exponentials and dS the
+// other's MFMAs proceed.  That needs at most 256 registers per wave, so the
+// dO^T operands stay in LDS (the wave's own rows, read per tile) instead of
+// registers; each tile runs one body, operands read as the MFMAs need them.
+// One wave per SIMD with every operand in registers and a fixed issue order
+// was 4-5 % slower on the 512K and CA-task backward.
 // ---------------------------------------------------------------------------
-template <int D, bool PAGED, bool WIN, bool MULTI>
-__global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
+template <int D, bool PAGED, bool MULTI>
+__global__ __launch_bounds__(512, 1) void bwd_q_kernel(BwdParams p) {
+  constexpr int NWQ = 8;          // waves
   constexpr int BN = 64;
   constexpr int KS = D + 16;      // K is read row-wise and by transpose reads
   constexpr int VS = D + 8;       // V is read row-wise only
   constexpr int NCB = D / 32;
   constexpr int NKS = D / 16;
   constexpr int CH = D / 8;
-  constexpr int RPP = 256 / CH;
+  constexpr int RPP = 64 * NWQ / CH;
   constexpr int PASSES = BN / RPP;
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KS];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][BN * VS];
+  constexpr int DS = D + 8;       // dO row stride in LDS (elements)
+  __shared__ __attribute__((aligned(16))) __bf16 lds_do[NWQ * 32 * DS];   // each wave's dO rows
 
   const FwdItem it = p.qitems[blockIdx.x];
   // The item's query shard: tasks it.task .. it.task + n_seg - 1 share the
@@ -605,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int hpw = p.hpw;
   const int head = it.kv_head * p.group + it.head_sub * hpw + (wave_u % hpw);
   const int wrow0 = it.row0 + (wave_u / hpw) * 32;
-  const int rt = 32 * (4 / hpw);
+  const int rt = 32 * (NWQ / hpw);
   const int wg_last = min(it.row0 + rt, t.q_len) - 1;
   const int w_last = min(wrow0 + 32, t.q_len) - 1;
   int64_t delta;
@@ -622,14 +632,17 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int qrow = wrow0 + l32;
   const bool qvalid = qrow < t.q_len;
   const int64_t q_stride = (int64_t)p.hq * D;
-  bf16x8 qf[NKS], of[NKS];
+  bf16x8 qf[NKS];
+  // dO^T operands: this lane's query row, channels 16 s + 8 hh .. + 7, in
+  // the wave's own LDS rows (no barrier: written and read by the same wave).
+  const int do_off = (wave_u * 32 + l32) * DS + 8 * hh;
   {
     const __bf16* qp = p.Q + (t.q_off + qrow) * q_stride + head * D + 8 * hh;
     const __bf16* op = p.dO + (t.o_off + qrow) * q_stride + head * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       qf[s] = qvalid ? *(const bf16x8*)(qp + 16 * s) : bf16x8_zero();
-      of[s] = qvalid ? *(const bf16x8*)(op + 16 * s) : bf16x8_zero();
+      *(bf16x8*)(&lds_do[do_off + 16 * s]) = qvalid ? *(const bf16x8*)(op + 16 * s) : bf16x8_zero();
     }
   }
   const float lse2 = qvalid ? lse_log2(p.LSE[(t.o_off + qrow) * p.hq + head]) : INFINITY;
@@ -690,14 +703,8 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
   const int j16 = lane & 15;
   const int kt_off = ((j16 >> 2) + 4 * hh) * KS + 16 * (g16 & 1) + 4 * (j16 & 3);
 
-  // Visited tiles [k_f0, k_f1) are visible to every row of the workgroup (no
-  // mask, no skip); the rest go through the general body.  Tiles run in
-  // LDS-buffer pairs so that every LDS address is a lane constant plus an
-  // immediate, so k_f0 is rounded up and k_f1 down to even indices.  Sink +
-  // sliding-window mask (win > 0): as in the forward, the workgroup visits the
-  // sink tiles [0, t_a) and the window tiles [t_b, n_tiles); the full ones are
-  // the window tiles inside the last row's window and below the first row's
-  // diagonal.
+  // Sink + sliding-window mask (win > 0): as in the forward, the workgroup
+  // visits the sink tiles [0, t_a) and the window tiles [t_b, n_tiles).
   int win, sj, t_a, t_b, n_visit;
   int64_t w_lo_first, w_lo_last;
   auto context_tiles = [&]() __attribute__((always_inline)) {
@@ -728,19 +735,7 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
     return win > 0 && !((tile + 1) * BN <= sj || (int64_t)tile * BN >= w_lo_last);
   };
   auto sweep = [&]() __attribute__((always_inline)) {
-  const int c_hi = min(n_tiles, (int)clamp64(((int64_t)it.row0 + delta + 1) / BN, 0, kv_len / BN));
-  int k_f0 = 0, k_f1 = c_hi & ~1;
-  if (!WIN && win > 0) k_f1 = 0;   // masks without the windowed loop split
-  if (WIN && win > 0) {
-    const int64_t wl = (int64_t)wg_last + delta - win + 1;             // first key in every row's window
-    const int w_lo_t = (int)clamp64((wl + BN - 1) / BN, 0, n_tiles);   // ceil(wl / BN), at least 0
-    const int f0 = max(t_b, w_lo_t), f1 = c_hi;
-    k_f0 = (t_a + (f0 - t_b) + 1) & ~1;
-    k_f1 = f1 > f0 ? (t_a + (f1 - t_b)) & ~1 : 0;
-    if (k_f1 <= k_f0) k_f0 = k_f1 = 0;
-  }
-
-  auto diag_body = [&](int buf, int tile) {
+  auto body = [&](int buf, int tile) {
     const int k0 = tile * BN;
     if (!wave_sees(tile)) return;
     f32x16 s_acc[2], dp_acc[2];
@@ -749,14 +744,17 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
       s_acc[mb] = f32x16_zero();
       dp_acc[mb] = f32x16_zero();
     }
+    int od = do_off;
+    asm volatile("" : "+v"(od));   // dO^T read per tile, not hoisted into registers
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
+      const bf16x8 ob = *(const bf16x8*)(&lds_do[od + 16 * s]);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const bf16x8 ka = *(const bf16x8*)(&lds_k[buf][k_row_off + mb * 32 * KS + 16 * s]);
         s_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s_acc[mb], 0, 0, 0);
         const bf16x8 va = *(const bf16x8*)(&lds_v[buf][v_row_off + mb * 32 * VS + 16 * s]);
-        dp_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[s], dp_acc[mb], 0, 0, 0);
+        dp_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, ob, dp_acc[mb], 0, 0, 0);
       }
     }
     float pv[2][16];
@@ -798,104 +796,10 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
       }
     };
 
-  // Fully visible tile, in a fixed issue order (sched_barrier fences; the
-  // empty asm statements keep each chain step where it is written, since IR
-  // passes sink pure calls towards their uses) for a single wave per SIMD:
-  // S^T chains with the next operand reads, dP^T chains with exp, dQ with dS.
-  auto full_body = [&](int buf) {
-    const __bf16* kb = &lds_k[buf][0];
-    const __bf16* vb = &lds_v[buf][0];
-    bf16x8 ka[2][NKS], va[2][NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) ka[0][s] = *(const bf16x8*)(kb + k_row_off + 16 * s);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s_acc[2], dp_acc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s_acc[mb] = f32x16_zero();
-      dp_acc[mb] = f32x16_zero();
-    }
-    // S^T mb 0, K rows of mb 1
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      s_acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], qf[s], s_acc[0], 0, 0, 0);
-      asm volatile("" : "+v"(s_acc[0]));
-      ka[1][s] = *(const bf16x8*)(kb + k_row_off + 32 * KS + 16 * s);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // S^T mb 1, V rows of mb 0
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      s_acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], qf[s], s_acc[1], 0, 0, 0);
-      asm volatile("" : "+v"(s_acc[1]));
-      va[0][s] = *(const bf16x8*)(vb + v_row_off + 16 * s);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dP^T mb 0, exp of S^T mb 0, V rows of mb 1
-    float pv[2][16];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      dp_acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][s], of[s], dp_acc[0], 0, 0, 0);
-      asm volatile("" : "+v"(dp_acc[0]));
-#pragma unroll
-      for (int k = 0; k < 16 / NKS; ++k) {
-        const int r = s * (16 / NKS) + k;
-        pv[0][r] = exp2_fast(fmaf(s_acc[0][r], p.scale_log2, -lse2));
-      }
-      va[1][s] = *(const bf16x8*)(vb + v_row_off + 32 * VS + 16 * s);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dP^T mb 1, exp of S^T mb 1, K^T operands of mb 0
-    bf16x4 ktr[2][2][NCB][2];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      dp_acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][s], of[s], dp_acc[1], 0, 0, 0);
-      asm volatile("" : "+v"(dp_acc[1]));
-#pragma unroll
-      for (int k = 0; k < 16 / NKS; ++k) {
-        const int r = s * (16 / NKS) + k;
-        pv[1][r] = exp2_fast(fmaf(s_acc[1][r], p.scale_log2, -lse2));
-      }
-      const int half = s / NCB, c = s % NCB;
-      const __bf16* a0 = kb + kt_off + (16 * half) * KS + c * 32;
-      ktr[0][half][c][0] = ds_read_tr16(a0);
-      ktr[0][half][c][1] = ds_read_tr16(a0 + 8 * KS);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dS^T of mb 0
-    bf16x8 dsf[2][2];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) dsf[0][j >> 3][j & 7] = (__bf16)(pv[0][j] * (dp_acc[0][j] - dval));
-    __builtin_amdgcn_sched_barrier(0);
-    // dQ^T += K^T dS^T for mb 0, dS^T of mb 1, K^T operands of mb 1
-#pragma unroll
-    for (int i = 0; i < 2 * NCB; ++i) {
-      const int half = i / NCB, c = i % NCB;
-      dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(ktr[0][half][c][0], ktr[0][half][c][1]),
-                                                          dsf[0][half], dq_acc[c], 0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < 16 / (2 * NCB); ++k) {
-        const int j = i * (16 / (2 * NCB)) + k;
-        dsf[1][j >> 3][j & 7] = (__bf16)(pv[1][j] * (dp_acc[1][j] - dval));
-      }
-      const __bf16* a0 = kb + kt_off + (32 + 16 * half) * KS + c * 32;
-      ktr[1][half][c][0] = ds_read_tr16(a0);
-      ktr[1][half][c][1] = ds_read_tr16(a0 + 8 * KS);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dQ^T for mb 1
-#pragma unroll
-    for (int i = 0; i < 2 * NCB; ++i) {
-      const int half = i / NCB, c = i % NCB;
-      dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(ktr[1][half][c][0], ktr[1][half][c][1]),
-                                                          dsf[1][half], dq_acc[c], 0, 0, 0);
-    }
-  };
-
   int next_page = 0;
-  // k indexes the visited tiles (tile_of(k) == k without a window, so the
-  // fully visible tiles [0, n_full) come first).
-  auto do_tile = [&](auto buf_tag, auto full_tag, int k) {
+  // k indexes the visited tiles; tiles run in LDS-buffer pairs so that every
+  // LDS address is a lane constant plus an immediate.
+  auto do_tile = [&](auto buf_tag, int k) {
     constexpr int BUF = decltype(buf_tag)::value;
     swrite(BUF);
     __syncthreads();
@@ -903,31 +807,18 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(BwdParams p) {
       gload(tile_of(k + 1), next_page);
       if (k + 2 < n_visit) next_page = tile_page(tile_of(k + 2));
     }
-    if constexpr (decltype(full_tag)::value)
-      full_body(BUF);
-    else
-      diag_body(BUF, tile_of(k));
+    body(BUF, tile_of(k));
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   int k = 0;
   if (n_visit > 0) gload(tile_of(0), tile_page(tile_of(0)));
   if (n_visit > 1) next_page = tile_page(tile_of(1));
-  if constexpr (WIN) {
-    for (; k < k_f0; k += 2) {
-      do_tile(B0{}, std::false_type{}, k);
-      do_tile(B1{}, std::false_type{}, k + 1);
-    }
-  }
-  for (; k < k_f1; k += 2) {
-    do_tile(B0{}, std::true_type{}, k);
-    do_tile(B1{}, std::true_type{}, k + 1);
-  }
   for (; k + 1 < n_visit; k += 2) {
-    do_tile(B0{}, std::false_type{}, k);
-    do_tile(B1{}, std::false_type{}, k + 1);
+    do_tile(B0{}, k);
+    do_tile(B1{}, k + 1);
   }
-  if (k < n_visit) do_tile(B0{}, std::false_type{}, k);
+  if (k < n_visit) do_tile(B0{}, k);
   };
   sweep();
   if constexpr (MULTI) {
@@ -1118,18 +1009,13 @@ hipError_t launch_bwd_kv_d(const BwdParams& p, hipStream_t s) {
   return p.pages ? launch_bwd_kv_dp<D, true>(p, s) : launch_bwd_kv_dp<D, false>(p, s);
 }
 
-template <int D, bool PAGED, bool WIN>
-hipError_t launch_bwd_q_dpw(const BwdParams& p, hipStream_t s) {
-  if (p.multi)
-    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, WIN, true>), dim3(p.n_qitems), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, WIN, false>), dim3(p.n_qitems), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 template <int D, bool PAGED>
 hipError_t launch_bwd_q_dp(const BwdParams& p, hipStream_t s) {
-  return p.masks ? launch_bwd_q_dpw<D, PAGED, true>(p, s) : launch_bwd_q_dpw<D, PAGED, false>(p, s);
+  if (p.multi)
+    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, true>), dim3(p.n_qitems), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<D, PAGED, false>), dim3(p.n_qitems), dim3(512), 0, s, p);
+  return hipGetLastError();
 }
 
 template <int D>
