@@ -592,7 +592,7 @@ template <int D, bool PAGED, bool MULTI>
 __global__ __launch_bounds__(512, 1) void bwd_q_kernel(BwdParams p) {
   constexpr int NWQ = 8;          // waves
   constexpr int BN = 64;
-  constexpr int KS = D + 16;      // K is read row-wise and by transpose reads
+  constexpr int KS = D + 32;      // K row stride: rows rotated by (row / 4) % 4 chunks (below)
   constexpr int VS = D + 8;       // V is read row-wise only
   constexpr int NCB = D / 32;
   constexpr int NKS = D / 16;
@@ -601,6 +601,11 @@ __global__ __launch_bounds__(512, 1) void bwd_q_kernel(BwdParams p) {
   constexpr int PASSES = BN / RPP;
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KS];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][BN * VS];
+  // K tile rows are read row-wise (16 lanes, one 16-byte chunk each) and by
+  // transpose reads (4 rows x 4 chunks per 16 lanes); a stride of D + 32 and
+  // a rotation of (row / 4) % 4 chunks keep both free of bank conflicts, and
+  // every address a lane constant plus an immediate.
+  auto krot = [](int row) { return ((row >> 2) & 3) * 8; };
   constexpr int DS = D + 8;       // dO row stride in LDS (elements)
   __shared__ __attribute__((aligned(16))) __bf16 lds_do[NWQ * 32 * DS];   // each wave's dO rows
 
@@ -695,15 +700,17 @@ __global__ __launch_bounds__(512, 1) void bwd_q_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       const int row = r * RPP + ld_row;
-      *(uint4*)(&lds_k[buf][row * KS + ld_chunk * 8]) = kreg[r];
+      *(uint4*)(&lds_k[buf][row * KS + ld_chunk * 8 + krot(row)]) = kreg[r];
       *(uint4*)(&lds_v[buf][row * VS + ld_chunk * 8]) = vreg[r];
     }
   };
-  const int k_row_off = l32 * KS + 8 * hh;       // A of S^T  (key l32, ch 16 s + 8 hh)
+  const int k_row_off = l32 * KS + 8 * hh + krot(l32);   // A of S^T  (key l32, ch 16 s + 8 hh)
   const int v_row_off = l32 * VS + 8 * hh;       // A of dP^T (key l32, ch 16 s + 8 hh)
   const int g16 = lane >> 4;
   const int j16 = lane & 15;
-  const int kt_off = ((j16 >> 2) + 4 * hh) * KS + 16 * (g16 & 1) + 4 * (j16 & 3);
+  // K^T reads: rows kb + j16 / 4 + 4 hh (kb a multiple of 16), rotated by hh
+  // chunks; the second read, 8 rows on, by hh + 2
+  const int kt_off = ((j16 >> 2) + 4 * hh) * KS + 16 * (g16 & 1) + 4 * (j16 & 3) + 8 * hh;
 
   // Sink + sliding-window mask (win > 0): as in the forward, the workgroup
   // visits the sink tiles [0, t_a) and the window tiles [t_b, n_tiles).
@@ -800,7 +807,7 @@ __global__ __launch_bounds__(512, 1) void bwd_q_kernel(BwdParams p) {
 #pragma unroll
         for (int c = 0; c < NCB; ++c) {
           const __bf16* a0 = kl + kb * KS + c * 32;
-          const bf16x8 kt = concat_bf16x4(ds_read_tr16(a0), ds_read_tr16(a0 + 8 * KS));
+          const bf16x8 kt = concat_bf16x4(ds_read_tr16(a0), ds_read_tr16(a0 + 8 * KS + 16));
           dq_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[mb][half], dq_acc[c], 0, 0, 0);
         }
       }
