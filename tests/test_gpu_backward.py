@@ -54,7 +54,7 @@ def run_small(tasks, hq, hkv, d, q_rows, kv_rows, o_rows, seed, label):
     return check_grads(got, ref, label)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (4, 4, 64), (16, 1, 128), (6, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (4, 4, 64), (16, 1, 128), (6, 2, 64), (8, 4, 128), (16, 2, 64)])
 def test_backward_ragged_varlen(hq, hkv, d):
     announce("backward ragged varlen hq%d hkv%d d%d" % (hq, hkv, d))
     lens = [1, 31, 33, 64, 130, 200, 257]

@@ -19,7 +19,7 @@ from tests.gpu_util import GRAD_REL_FRO, announce, check_forward, rel_fro, torch
 
 pytestmark = pytest.mark.gpu
 
-GEOMETRIES = [(8, 2), (4, 4), (16, 1), (6, 2), (12, 4), (32, 8)]
+GEOMETRIES = [(8, 2), (4, 4), (16, 1), (6, 2), (12, 4), (32, 8), (8, 4), (16, 2)]
 
 
 def random_tables(seed):
