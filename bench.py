@@ -398,6 +398,7 @@ def secondary(steps=3, warmup=1):
     out["hbm_copy_ceiling"] = {"bytes": 2 << 30, "ms": round(ms_cp, 4), "gbs": round((2 << 30) / ms_cp / 1e6, 1)}
     log("device copy ceiling: %.0f GB/s (read + write)" % ((2 << 30) / ms_cp / 1e6))
     del src, dst
+    torch.cuda.empty_cache()
 
     # Pass-Q decode share: 32 tokens x 128K caches, 8 stationary blocks, merge
     w = I.ring_decode_405b_tp8()
