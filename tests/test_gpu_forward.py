@@ -144,6 +144,65 @@ def test_decode_rows():
     check_forward(O, LSE, Or, Lr, "decode-partials")
 
 
+def climbing_qkv(pos, hq, hkv, d, seed, rise_log2, period):
+    """Q and K with a shared positive component whose size in K grows with the
+    key's in-document position pos (a sawtooth of the given period): every
+    64-key tile of a period scores about rise_log2 (log2 units) above the one
+    before, so the kernels' running row maximum moves past their lazy-rescale
+    threshold (2^8) again and again, and drops back at each period's end."""
+    torch = torch_cuda()
+    T = len(pos)
+    Q = I.randn_bf16((T, hq, d), seed).float() + 1.0
+    K = I.randn_bf16((T, hkv, d), seed + 1).float()
+    # q . k grows by about d * gamma per unit of gamma; scaled by 1/sqrt(d), in log2 units
+    per_key = rise_log2 / 64 / (math.sqrt(d) * math.log2(math.e))
+    gamma = torch.from_numpy((np.asarray(pos) % period) * per_key).float()
+    K = K + gamma[:, None, None]
+    V = I.randn_bf16((T, hkv, d), seed + 2)
+    return Q.to(torch.bfloat16), K.to(torch.bfloat16), V
+
+
+def climb_natural(rise_log2, period, longest):
+    """Natural-log height of the climb over the longest run of keys."""
+    return rise_log2 * min(period, longest) / 64 * math.log(2)
+
+
+@pytest.mark.parametrize("hq,hkv,d,rise,period", [(8, 2, 128, 12.0, 1 << 30), (16, 1, 128, 20.0, 512),
+                                                  (4, 4, 64, 12.0, 256)])
+def test_running_max_rescales(hq, hkv, d, rise, period):
+    """Scores climbing tile after tile (and falling back at each sawtooth
+    period): the online softmax rescales its accumulators mid-row, which
+    N(0, 1) inputs almost never make it do after the first tile."""
+    announce("forward climbing scores hq%d hkv%d d%d rise%.0f period%d" % (hq, hkv, d, rise, period))
+    lens = [1, 70, 300, 1000, 2100]
+    tasks = I.varlen_tasks(lens)
+    T = sum(lens)
+    pos = np.concatenate([np.arange(l) for l in lens])
+    O, LSE, Or, Lr = run_case(tasks, hq, hkv, d, T, T, T, 0, qkv=climbing_qkv(pos, hq, hkv, d, 760 + d, rise, period))
+    fin = np.isfinite(Lr)
+    # the scores did climb far past the first tile
+    assert np.max(Lr[fin]) > 0.5 * climb_natural(rise, period, max(lens))
+    check_forward(O, LSE, Or, Lr, "climbing scores")
+
+
+def test_decode_running_max_rescales():
+    """Single-token rows over caches whose scores climb along the cache (the
+    split-KV decode kernel's lazy rescale), whole caches and key chunks."""
+    announce("decode climbing scores")
+    batch, ctx = 3, 3000
+    hq, hkv, d = 16, 1, 128
+    pos = np.tile(np.arange(ctx), batch)
+    Qa, K, V = climbing_qkv(pos, hq, hkv, d, 780, 10.0, 1 << 30)
+    Q = Qa[:batch].contiguous()
+    # whole caches, then the same caches in 3 key blocks (partials)
+    tasks = np.array([(b, b * ctx, b, 1, ctx, ctx - 1, 0) for b in range(batch)] +
+                     [(b, b * ctx + s * (ctx // 3), batch + s * batch + b, 1, ctx // 3, ctx - 1, s * (ctx // 3))
+                      for b in range(batch) for s in range(3)], dtype=np.int64)
+    O, LSE, Or, Lr = run_case(tasks, hq, hkv, d, batch, batch * ctx, 4 * batch, 0, out_f32=True, qkv=(Q, K, V))
+    assert np.max(Lr[np.isfinite(Lr)]) > 0.5 * climb_natural(10.0, 1 << 30, ctx)
+    check_forward(O, LSE, Or, Lr, "decode climbing scores")
+
+
 def test_probe_mask_parity_small():
     """K = 0, V = (-1)^position: a leaked or dropped key moves a row by 1/(p+1)."""
     announce("forward probe small")
