@@ -227,6 +227,47 @@ def test_ring_decode_405b_full():
     check_forward(Om, Lm, Or, Lr, "decode-merged")
 
 
+def test_ring_decode_405b_paged_full():
+    """The bench's paged decode step at full size: the 32 caches in shuffled
+    256-row pages (the paged kernel keeps two tiles in flight).  Same work
+    items and arithmetic as the contiguous step, so the partials must match it
+    bit for bit; the merged output is checked against the oracle on a few
+    sequences."""
+    announce("fullsize llama3-405b tp8 pass-Q decode b32 x 128k, shuffled 256-row pages")
+    torch = torch_cuda()
+    w = I.ring_decode_405b_tp8()
+    Q, K, V = device_inputs(w, 205)
+    O, LSE = run_forward(w, Q, K, V, out_f32=True)
+    P = 256
+    n_vp = w.kv_rows // P
+    table = I.page_table(n_vp, n_vp, 206)
+    idx = torch.from_numpy(table.astype(np.int64)).to(Q.device)
+    Ks, Vs = torch.empty_like(K), torch.empty_like(V)
+    Ks.view(n_vp, -1)[idx] = K.view(n_vp, -1)
+    Vs.view(n_vp, -1)[idx] = V.view(n_vp, -1)
+    Op = torch.empty_like(O)
+    Lp = torch.full_like(LSE, -float("inf"))
+    shape = ca.make_shape(w.hq, w.hkv, w.d, w.q_rows, w.kv_rows, w.o_rows, out_f32=True)
+    ca.forward(shape, w.tasks, Q, Ks, Vs, Op, Lp, pages=ca.kv_pages(table, P))
+    torch.cuda.synchronize()
+    assert torch.equal(Op.view(torch.int32), O.view(torch.int32))
+    assert torch.equal(Lp.view(torch.int32), LSE.view(torch.int32))
+    del Ks, Vs
+    B = w.merged_rows
+    Om = torch.empty((B, w.hq, w.d), dtype=torch.bfloat16, device=Q.device)
+    Lm = torch.empty((B, w.hq), device=Q.device)
+    ca.merge(ca.make_shape(w.hq, w.hkv, w.d, B, B, B), Op.view(w.n_parts, B, w.hq, w.d),
+             Lp.view(w.n_parts, B, w.hq), Om, Lm)
+    torch.cuda.synchronize()
+    ctx = 131072
+    qs = widen(Q)
+    for b in (0, 17, B - 1):
+        ks = widen(K[b * ctx:(b + 1) * ctx])
+        vs = widen(V[b * ctx:(b + 1) * ctx])
+        o1, l1 = oracle.forward_rows(np.array([b, 0, 0, 1, ctx, ctx - 1, 0]), np.array([0]), qs, ks, vs, w.scale)
+        check_forward(Om[b:b + 1], Lm[b:b + 1], o1, l1, "paged decode seq %d" % b)
+
+
 def ring_load_balanced(Q, K, V, T, hq, hkv, d, N=8):
     """The 2N partials of a load-balanced pass-KV ring over one T-token
     document, one launch per step as the bench times them (all ranks' shares
